@@ -1,0 +1,337 @@
+#!/usr/bin/env python3
+"""Throughput of the fused dequant-matmul on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+One step = the Whisper large-v3-turbo decoder GEMV set at M=1 in NF4 with
+double-quant: the fused Q/K/V projection (one wq_matmul_qkv, 3840x1280), the
+out-projection (1280x1280), fc1 (5120x1280) and fc2 (1280x5120).  Steps cycle
+through a pool of weight copies of >= 1 GiB so every step streams its weights
+from HBM (the 256 MB Infinity Cache cannot hold them); the launches of all pool
+slots are captured once in a HIP graph and replayed.  `value` is weight bytes
+(codes + scales) per second over exactly K timed steps.
+
+Also reported (same JSON line): the encoder GEMM at M=1500 in NVFP4 (fc1 + fc2,
+TFLOP/s), one encoder layer at batch 4 (M=6000) in q8_0 and q4_0, the decode
+set at M=4 and M=16, a 433 MB streaming GEMV (NF4+DQ, M=1), the dominant
+kernels' roofline fractions, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+DECODER = [("qkv", 3840, 1280), ("out", 1280, 1280), ("fc1", 5120, 1280), ("fc2", 1280, 5120)]
+ENC_D, ENC_FFN, ENC_M = 1280, 5120, 1500
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=416)
+    ap.add_argument("--warmup", type=int, default=104)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-extras", action="store_true", help="only the decode set (for profiling)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from block_quantized_bit_amd import wq
+    from block_quantized_bit_amd.inputs import linear_case
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.Stream()          # default priority
+
+    def quantize_dev(fmt, w_dev, dq):
+        n, k = w_dev.shape
+        d = wq.desc(fmt, n, k, dq)
+        cb, sb = wq.wq_packed_size(d)
+        codes = torch.empty(cb, dtype=torch.uint8, device=dev)
+        scales = torch.empty(sb, dtype=torch.uint8, device=dev)
+        wq.wq_quantize(d, w_dev, codes, scales)
+        return d, codes, scales
+
+    def bf16_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev)
+
+    # plain copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters
+    cal = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+    cal2 = torch.empty_like(cal)
+    cal2.copy_(cal)
+    torch.cuda.synchronize()
+
+    # ---------------- decode set: NF4 + double-quant, pool of weight copies ----------------
+    t0 = time.time()
+    base = []
+    for i, (name, n, k) in enumerate(DECODER):
+        w, b, x16 = linear_case(2000 + i, n, k, 16, outlier_frac=0.001)
+        if name == "qkv":
+            b = b.copy()
+            b[1280:2560] = 0                      # key projection has no bias
+        d, codes, scales = quantize_dev(wq.WQ_NF4, torch.from_numpy(w).to(dev), True)
+        base.append(dict(name=name, n=n, k=k, d=d, codes=codes, scales=scales, bias=bf16_dev(b),
+                         x16=bf16_dev(x16), w=w, b=b, xbits=x16))
+    set_bytes = sum(e["codes"].numel() + e["scales"].numel() for e in base)
+    pool_n = max(1, -(-(1 << 30) // set_bytes))               # >= 1 GiB of weights
+    pool = [[(e["codes"].clone(), e["scales"].clone()) for e in base] for _ in range(pool_n)]
+    torch.cuda.synchronize()
+    log(f"[bench] decode set {set_bytes / 1e6:.3f} MB of packed weights, pool of {pool_n} copies "
+        f"({pool_n * set_bytes / 2**30:.2f} GiB), built in {time.time() - t0:.1f}s")
+
+    def decode_buffers(m):
+        outs, wss = [], []
+        for e in base:
+            outs.append(torch.empty((m, e["n"]), dtype=torch.int16, device=dev))
+            nb = wq.wq_workspace_size(e["d"], m)
+            wss.append((torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev), nb))
+        return outs, wss
+
+    def enqueue_decode_step(m, slot, outs, wss, st):
+        for j, e in enumerate(base):
+            codes, scales = pool[slot][j]
+            y = outs[j]
+            ws, nb = wss[j]
+            if e["name"] == "qkv":
+                ys = [y.data_ptr(), y.data_ptr() + 2 * 1280, y.data_ptr() + 2 * 2560]
+                wq.wq_matmul_qkv(e["d"], m, e["x16"], e["k"], codes, scales, e["bias"], [1280, 1280, 1280],
+                                 ys, [e["n"]] * 3, wq.WQ_BF16, ws if nb else None, nb, stream=st)
+            else:
+                wq.wq_matmul(e["d"], m, e["x16"], e["k"], codes, scales, e["bias"], y, wq.WQ_BF16, e["n"],
+                             ws if nb else None, nb, stream=st)
+
+    def run_graph_steps(enqueue, n_slots, steps, warmup):
+        """Capture one graph over all slots, replay it; returns seconds for `steps` steps."""
+        graphs = {}
+
+        def graph_for(count):
+            if count not in graphs:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.stream(stream):
+                    enqueue(0, stream)                      # untimed eager pass before capture
+                    stream.synchronize()
+                    with torch.cuda.graph(g, stream=stream):
+                        for s in range(count):
+                            enqueue(s % n_slots, stream)
+                graphs[count] = g
+            return graphs[count]
+
+        def replay(total):
+            full, rest = divmod(total, n_slots)
+            for _ in range(full):
+                graph_for(n_slots).replay()
+            if rest:
+                graph_for(rest).replay()
+
+        if warmup:
+            replay(warmup)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        graph_for(n_slots)
+        if steps % n_slots:
+            graph_for(steps % n_slots)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            ev0.record(stream)
+            replay(steps)
+            ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / 1e3
+
+    def decode_bytes(m):
+        """algorithmic bytes of one step: packed weights + X + Y (bf16) + bias"""
+        return sum(e["codes"].numel() + e["scales"].numel() + 2 * m * e["k"] + 2 * m * e["n"] + 2 * e["n"]
+                   for e in base)
+
+    outs1, wss1 = decode_buffers(1)
+    t = run_graph_steps(lambda s, st: enqueue_decode_step(1, s, outs1, wss1, st), pool_n, args.steps, args.warmup)
+    ms_per_step = t * 1e3 / args.steps
+    value = set_bytes * args.steps / t / 1e9
+    per_launch_bytes = decode_bytes(1) / len(base)
+    per_launch_s = t / (args.steps * len(base))
+    achieved = per_launch_bytes / per_launch_s / 1e9
+    log(f"[bench] decode M=1: {ms_per_step * 1e3:.2f} us/step, {value:.1f} GB/s weights, "
+        f"{per_launch_s * 1e6:.2f} us/launch")
+
+    result = {
+        "metric": "decode GEMV weight GB/s (M=1) + encoder TFLOP/s (M=1500), % roofline",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "whisper-large-v3-turbo decoder GEMV set, NF4 + double-quant (64-blocks, int8 absmax "
+                        "in 256-block groups), M=1: fused QKV 1280->3840 (wq_matmul_qkv), out 1280->1280, "
+                        "fc1 1280->5120, fc2 5120->1280; bf16 activations and outputs",
+            "weights": f"{set_bytes} B per step, cycled over {pool_n} copies ({pool_n * set_bytes / 2**30:.2f} GiB) "
+                       "so each step reads from HBM",
+            "launches_per_step": len(base),
+            "timing": "HIP graph replay, HIP events on the launch stream",
+        },
+        "roofline": {
+            "kernel": "k_gemv<NF4,dq,1>",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": int(per_launch_bytes),
+            "us_per_launch": round(per_launch_s * 1e6, 3),
+        },
+    }
+
+    if not args.no_extras:
+        extras = {}
+        # ---- decode set at M = 4 and 16 (16 concurrent requests) ----
+        for m in (4, 16):
+            o, w_ = decode_buffers(m)
+            tm = run_graph_steps(lambda s, st: enqueue_decode_step(m, s, o, w_, st), pool_n, pool_n * 2, pool_n)
+            extras[f"decode_m{m}"] = {"us_per_step": round(tm * 1e6 / (pool_n * 2), 3),
+                                      "weight_GBps": round(set_bytes * pool_n * 2 / tm / 1e9, 2),
+                                      "algorithmic_GBps": round(decode_bytes(m) * pool_n * 2 / tm / 1e9, 2)}
+            log(f"[bench] decode M={m}: {extras[f'decode_m{m}']}")
+
+        # ---- streaming GEMV: one launch reads 433 MB (fc1 geometry, N = 655360) ----
+        gen = torch.Generator(device=dev).manual_seed(7)
+        ns, ks = 655360, 1280
+        wbig = torch.randn((ns, ks), device=dev, generator=gen, dtype=torch.float32) * 0.02
+        d_s, c_s, s_s = quantize_dev(wq.WQ_NF4, wbig, True)
+        del wbig
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        xs = bf16_dev(linear_case(9, 16, ks, 1)[2])
+        ys = torch.empty((1, ns), dtype=torch.int16, device=dev)
+        nbs = wq.wq_workspace_size(d_s, 1)
+        wss_ = torch.zeros(max(nbs, 16), dtype=torch.uint8, device=dev)
+        sbytes = c_s.numel() + s_s.numel()
+        reps = 20
+        ts = run_graph_steps(lambda s, st: wq.wq_matmul(d_s, 1, xs, ks, c_s, s_s, None, ys, wq.WQ_BF16, ns,
+                                                        wss_ if nbs else None, nbs, stream=st), 1, reps, 3)
+        extras["streaming_gemv"] = {"shape": f"M=1 N={ns} K={ks} NF4+DQ", "bytes": sbytes,
+                                    "us": round(ts * 1e6 / reps, 2),
+                                    "GBps": round(sbytes * reps / ts / 1e9, 1),
+                                    "frac_hbm": round(sbytes * reps / ts / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] streaming: {extras['streaming_gemv']}")
+        del c_s, s_s
+        torch.cuda.empty_cache()
+
+        # ---- encoder GEMM, NVFP4, M = 1500: fc1 + fc2 ----
+        enc = []
+        for i, (n, k) in enumerate([(ENC_FFN, ENC_D), (ENC_D, ENC_FFN)]):
+            w, b, x = linear_case(3000 + i, n, k, ENC_M, row_lognormal_sigma=0.3)
+            d, c, s = quantize_dev(wq.WQ_NVFP4, torch.from_numpy(w).to(dev), False)
+            nb = wq.wq_workspace_size(d, ENC_M)
+            enc.append(dict(d=d, c=c, s=s, b=bf16_dev(b), x=bf16_dev(x), n=n, k=k,
+                            y=torch.empty((ENC_M, n), dtype=torch.int16, device=dev),
+                            ws=torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev), nb=nb))
+
+        def enc_step(s_, st, layers=enc, m=ENC_M):
+            for e in layers:
+                wq.wq_matmul(e["d"], m, e["x"], e["k"], e["c"], e["s"], e["b"], e["y"], wq.WQ_BF16, e["n"],
+                             e["ws"] if e["nb"] else None, e["nb"], stream=st)
+
+        reps = 50
+        te = run_graph_steps(enc_step, 1, reps, 5)
+        flops = sum(2.0 * ENC_M * e["n"] * e["k"] for e in enc)
+        tflops = flops * reps / te / 1e12
+        encoder = {
+            "metric": "encoder TFLOP/s (M=1500)",
+            "value": round(tflops, 2),
+            "unit": "TFLOP/s",
+            "config": {"workload": "encoder fc1 1280->5120 and fc2 5120->1280, NVFP4 W4A16, X[1500,1280] bf16"},
+            "us_per_step": round(te * 1e6 / reps, 2),
+            "roofline": {"kernel": "k_gemm<NVFP4>", "bound": "mfma", "achieved": round(tflops, 2),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None},
+        }
+        log(f"[bench] encoder NVFP4 M=1500: {encoder['us_per_step']} us, {tflops:.1f} TFLOP/s")
+
+        # ---- one encoder layer at batch 4 (M = 6000), q8_0 and q4_0 on identical weights ----
+        layer_shapes = [(ENC_D, ENC_D)] * 4 + [(ENC_FFN, ENC_D), (ENC_D, ENC_FFN)]
+        mb4 = 4 * ENC_M
+        for fmt_name, fmt in (("q8_0", wq.WQ_Q8_0), ("q4_0", wq.WQ_Q4_0)):
+            lay = []
+            for i, (n, k) in enumerate(layer_shapes):
+                w, b, x = linear_case(4000 + i, n, k, mb4)
+                d, c, s = quantize_dev(fmt, torch.from_numpy(w).to(dev), False)
+                nb = wq.wq_workspace_size(d, mb4)
+                lay.append(dict(d=d, c=c, s=s, b=bf16_dev(b), x=bf16_dev(x), n=n, k=k,
+                                y=torch.empty((mb4, n), dtype=torch.int16, device=dev),
+                                ws=torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev), nb=nb))
+            reps = 10
+            tl = run_graph_steps(lambda s_, st: enc_step(s_, st, lay, mb4), 1, reps, 2)
+            fl = sum(2.0 * mb4 * n * k for n, k in layer_shapes)
+            extras[f"encoder_layer_b4_{fmt_name}"] = {"us_per_layer": round(tl * 1e6 / reps, 1),
+                                                      "TFLOPs": round(fl * reps / tl / 1e12, 2),
+                                                      "frac_mfma": round(fl * reps / tl / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            log(f"[bench] layer b4 {fmt_name}: {extras[f'encoder_layer_b4_{fmt_name}']}")
+            del lay
+        result["encoder"] = encoder
+        result["extras"] = extras
+
+    # ---------------- CPU oracle baseline (bounded sample) ----------------
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(base, set_bytes)
+        log(f"[bench] cpu baseline: {result['cpu_baseline']}")
+
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(base, set_bytes):
+    """The plain C oracle, as it stands, doing the same step on the host: decode
+    every packed weight of the set (double-quant absmax, NF4 levels) and run the
+    fp32 matmul for one token.  Runs whole steps until ~10 s have passed."""
+    cores = len(os.sched_getaffinity(0))
+    os.environ["OMP_NUM_THREADS"] = str(cores)
+    from oracle import oracle as O
+    prepared = []
+    for e in base:
+        q = O.nf4_quantize(e["w"])
+        codes, a = q
+        qq, d, mu = O.nf4_double_quant(a)
+        prepared.append((codes, qq, d, mu, e["xbits"][:1], e["b"]))
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        for codes, qq, d, mu, x, b in prepared:
+            ahat = O.nf4_dq_absmax(qq, d, mu)
+            w_hat = O.nf4_dequantize(codes, ahat)
+            O.matmul(x, w_hat, b)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el > 10.0 or steps >= 50:
+            break
+    return {"value": round(set_bytes * steps / el / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{steps} whole decode steps (4 matrices, M=1: dequantize to fp32 + fp32 matmul) "
+                      f"in {el:.1f} s; dequantize single-threaded, matmul OpenMP over rows"}
+
+
+if __name__ == "__main__":
+    main()

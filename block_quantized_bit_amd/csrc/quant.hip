@@ -1,0 +1,397 @@
+// quant.hip -- blockwise absmax quantizers and the fp32 dequantizer (bit-exact
+// with the format definitions).  Every arithmetic step is one IEEE binary32
+// operation; this file is compiled with -ffp-contract=off and uses __fmul_rn /
+// __fadd_rn where a product feeds a sum, so no step is fused.
+//
+// Formats: NF4 with optional double-quantized absmax ("asr: add a 4-bit nf4 option
+// for the Whisper engine", "What's here"); NVFP4 ("asr: add a 4-bit nvfp4 option
+// for cards short of VRAM", intro; "mbehr90/whisper-large-v3-turbo-nvfp4", "What
+// is quantized"); q4_0 / q8_0 ("Run quantized Whisper on the fused Metal decode
+// path", "Summary").  One matrix at a time, as the checkpoint streams in ("asr:
+// add a 4-bit nf4 option for the Whisper engine", "Why NF4 and not the NVFP4
+// snapshot Parakeet ships"); the only temporary storage is the codes buffer.
+#include "wq_device.h"
+#include "wq_launch.h"
+
+namespace wq {
+
+ScaleLayout scale_layout(int fmt, bool dq, int64_t n, int64_t k) {
+    ScaleLayout L{};
+    L.nb = n * k / block_k(fmt);
+    switch (fmt) {
+    case kNF4:
+        if (dq) {
+            L.ng = (L.nb + 255) / 256;
+            L.d_off = align16(L.nb);
+            L.mu_off = L.d_off + 4 * L.ng;
+            L.bytes = L.mu_off + 4;
+        } else {
+            L.bytes = 4 * L.nb;
+        }
+        break;
+    case kNVFP4:
+        L.g_off = align16(L.nb);
+        L.bytes = L.g_off + 4;
+        break;
+    default:
+        L.bytes = 2 * L.nb;
+    }
+    return L;
+}
+
+// Byte offset of the 32-bit word holding k0..k0+7 (k0 % 8 == 0) of row n (4-bit).
+__device__ inline int64_t word_off4(int64_t n, int64_t k0, int64_t K) {
+    int64_t band = n >> 4;
+    int r = (int)(n & 15);
+    int64_t kt = k0 >> 7;
+    int kin = (int)(k0 & 127);
+    int j = kin >> 5, h = (kin & 31) >> 3;
+    return (band * (K >> 7) + kt) * kTileBytes + (h * 16 + r) * 16 + j * 4;
+}
+
+// Byte offset of the 8 bytes holding k0..k0+7 of row n (q8_0).
+__device__ inline int64_t word_off8(int64_t n, int64_t k0, int64_t K) {
+    int64_t band = n >> 4;
+    int r = (int)(n & 15);
+    int64_t kt = k0 >> 6;
+    int kin = (int)(k0 & 63);
+    int j = kin >> 5, h = (kin & 31) >> 3;
+    return (band * (K >> 6) + kt) * kTileBytes + (h * 16 + r) * 16 + j * 8;
+}
+
+// Index of the scale entry of block b (block index along K) of row n.
+template <int FMT>
+__device__ inline int64_t scale_slot(int64_t n, int64_t b, int64_t K) {
+    constexpr int bpt = blocks_per_tile_row(FMT);
+    constexpr int tk = tile_k(FMT);
+    int64_t band = n >> 4;
+    int r = (int)(n & 15);
+    int64_t kt = b / bpt;
+    int bin = (int)(b % bpt);
+    return (band * (K / tk) + kt) * (16 * bpt) + r * bpt + bin;
+}
+
+// ---------------------------------------------------------------------------
+// One thread per 8 consecutive K of one row ("chunk").  Blocks of 16/32/64 are
+// 2/4/8 neighbouring threads, reduced with cross-lane shuffles.
+// NF4 modes: 0 = codes + fp32 absmax, 1 = absmax only (logical order, to
+// `scratch`), 2 = codes only (double-quant path).
+// ---------------------------------------------------------------------------
+template <int FMT, int MODE>
+__global__ __launch_bounds__(256) void k_quant_chunks(const float* __restrict__ w, int64_t N, int64_t K,
+                                                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                                                      float* __restrict__ scratch, ScaleLayout L) {
+    const int64_t nchunks = N * K / 8;
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool valid = c < nchunks;
+    const int64_t kc8 = K / 8;
+    const int64_t n = valid ? c / kc8 : 0;
+    const int64_t k0 = valid ? (c % kc8) * 8 : 0;
+    float v[8];
+    if (valid) {
+        const float4 a = *reinterpret_cast<const float4*>(w + n * K + k0);
+        const float4 b = *reinterpret_cast<const float4*>(w + n * K + k0 + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; i++) v[i] = 0.0f;
+    }
+
+    if constexpr (FMT == kNF4) {
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) a = fmaxf(a, fabsf(v[i]));
+        a = fmaxf(a, __shfl_xor(a, 1, 8));
+        a = fmaxf(a, __shfl_xor(a, 2, 8));
+        a = fmaxf(a, __shfl_xor(a, 4, 8));
+        if (!valid) return;
+        const bool lead = (k0 & 63) == 0;
+        if constexpr (MODE == 1) {
+            if (lead) scratch[n * (K / 64) + (k0 >> 6)] = a;
+            return;
+        }
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            uint32_t code = 7;
+            if (a != 0.0f) {
+                const float x = v[i] / a;
+                code = 0;
+#pragma unroll
+                for (int t = 0; t < 15; t++) code += (x > __uint_as_float(kNf4ThresholdBits[t])) ? 1u : 0u;
+            }
+            word |= code << (4 * i);
+        }
+        *reinterpret_cast<uint32_t*>(codes + word_off4(n, k0, K)) = word;
+        if constexpr (MODE == 0) {
+            if (lead) reinterpret_cast<float*>(scales)[scale_slot<kNF4>(n, k0 >> 6, K)] = a;
+        }
+    } else if constexpr (FMT == kNVFP4) {
+        const float g = *reinterpret_cast<const float*>(scales + L.g_off);
+        float ab = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) ab = fmaxf(ab, fabsf(v[i]));
+        ab = fmaxf(ab, __shfl_xor(ab, 1, 2));
+        if (!valid) return;
+        uint32_t sb = 0;
+        float sigma = 0.0f;
+        if (g != 0.0f) {
+            const float t = 6.0f * g;
+            sb = e4m3_round(ab / t);
+            sigma = e4m3_value(sb) * g;
+        }
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            uint32_t code = signbit(v[i]) ? 8u : 0u;
+            if (sigma != 0.0f) code |= e2m1_mag_code(v[i] / sigma);
+            word |= code << (4 * i);
+        }
+        *reinterpret_cast<uint32_t*>(codes + word_off4(n, k0, K)) = word;
+        if ((k0 & 15) == 0) scales[scale_slot<kNVFP4>(n, k0 >> 4, K)] = (uint8_t)sb;
+    } else if constexpr (FMT == kQ8_0) {
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) a = fmaxf(a, fabsf(v[i]));
+        a = fmaxf(a, __shfl_xor(a, 1, 4));
+        a = fmaxf(a, __shfl_xor(a, 2, 4));
+        if (!valid) return;
+        const uint16_t d = f16_sat_bits(a / 127.0f);
+        const float delta = f16_value(d);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            int q = 0;
+            if (delta != 0.0f) q = (int)fminf(fmaxf(rintf(v[i] / delta), -127.0f), 127.0f);
+            const uint32_t b = (uint32_t)(q & 255);
+            if (i < 4) lo |= b << (8 * i); else hi |= b << (8 * (i - 4));
+        }
+        *reinterpret_cast<uint2*>(codes + word_off8(n, k0, K)) = make_uint2(lo, hi);
+        if ((k0 & 31) == 0) reinterpret_cast<uint16_t*>(scales)[scale_slot<kQ8_0>(n, k0 >> 5, K)] = d;
+    } else {  // kQ4_0
+        // signed element of largest magnitude; first index (ascending k) on ties
+        float best_a = -1.0f, best_v = 0.0f;
+        int best_k = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float t = fabsf(v[i]);
+            if (t > best_a) { best_a = t; best_v = v[i]; best_k = (int)(k0 & 31) + i; }
+        }
+#pragma unroll
+        for (int s = 1; s <= 2; s <<= 1) {
+            const float pa = __shfl_xor(best_a, s, 4);
+            const float pv = __shfl_xor(best_v, s, 4);
+            const int pk = __shfl_xor(best_k, s, 4);
+            if (pa > best_a || (pa == best_a && pk < best_k)) { best_a = pa; best_v = pv; best_k = pk; }
+        }
+        if (!valid) return;
+        const uint16_t d = f16_sat_bits(best_v / -8.0f);
+        const float delta = f16_value(d);
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            uint32_t q = 8;
+            if (delta != 0.0f) q = (uint32_t)((int)fminf(fmaxf(rintf(v[i] / delta), -8.0f), 7.0f) + 8);
+            word |= q << (4 * i);
+        }
+        *reinterpret_cast<uint32_t*>(codes + word_off4(n, k0, K)) = word;
+        if ((k0 & 31) == 0) reinterpret_cast<uint16_t*>(scales)[scale_slot<kQ4_0>(n, k0 >> 5, K)] = d;
+    }
+}
+
+// Double-quant mean: one thread sums the nb absmax values in binary64 in
+// ascending block order, divides in binary64 and rounds to binary32.
+__global__ void k_dq_mean(const float* __restrict__ a, int64_t nb, uint8_t* __restrict__ scales, int64_t mu_off) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    double s = 0.0;
+    const float4* a4 = reinterpret_cast<const float4*>(a);
+    for (int64_t i = 0; i < nb / 4; i++) {
+        const float4 t = a4[i];
+        s += (double)t.x;
+        s += (double)t.y;
+        s += (double)t.z;
+        s += (double)t.w;
+    }
+    for (int64_t i = (nb / 4) * 4; i < nb; i++) s += (double)a[i];
+    *reinterpret_cast<float*>(scales + mu_off) = (float)(s / (double)nb);
+}
+
+// Double-quant groups: one wave per 256 consecutive blocks (logical order).
+__global__ __launch_bounds__(64) void k_dq_groups(const float* __restrict__ a, int64_t nb, int64_t K,
+                                                  uint8_t* __restrict__ scales, ScaleLayout L) {
+    const int lane = threadIdx.x;
+    const int64_t g = blockIdx.x;
+    const float mu = *reinterpret_cast<const float*>(scales + L.mu_off);
+    float ap[4];
+    float m = 0.0f;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const int64_t i = g * 256 + r * 64 + lane;
+        ap[r] = (i < nb) ? a[i] - mu : 0.0f;
+        m = fmaxf(m, fabsf(ap[r]));
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+    const float d = m / 127.0f;
+    const int64_t nbk = K / 64;
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+        const int64_t i = g * 256 + r * 64 + lane;
+        if (i >= nb) continue;
+        int q = 0;
+        if (d != 0.0f) q = (int)fminf(fmaxf(rintf(ap[r] / d), -127.0f), 127.0f);
+        scales[scale_slot<kNF4>(i / nbk, i % nbk, K)] = (uint8_t)(int8_t)q;
+    }
+    if (lane == 0) reinterpret_cast<float*>(scales + L.d_off)[g] = d;
+}
+
+// Matrix absmax for NVFP4: per-workgroup partial maxima, then one workgroup
+// combines them and writes the global scale g = A / 2688.
+__global__ __launch_bounds__(256) void k_absmax_partial(const float* __restrict__ w, int64_t count, float* __restrict__ partial) {
+    __shared__ float red[4];
+    float m = 0.0f;
+    const int64_t n4 = count / 4;
+    const float4* w4 = reinterpret_cast<const float4*>(w);
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+        const float4 t = w4[i];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(t.x), fabsf(t.y)), fmaxf(fabsf(t.z), fabsf(t.w))));
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ __launch_bounds__(64) void k_absmax_final(const float* __restrict__ partial, int np, uint8_t* __restrict__ scales, int64_t g_off) {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < np; i += 64) m = fmaxf(m, partial[i]);
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+    if (threadIdx.x == 0) *reinterpret_cast<float*>(scales + g_off) = m / 2688.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Dequantize: one thread per chunk of 8, fp32 out in logical row-major order.
+// ---------------------------------------------------------------------------
+template <int FMT, bool DQ>
+__global__ __launch_bounds__(256) void k_dequant_chunks(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                                                        int64_t N, int64_t K, float* __restrict__ out, ScaleLayout L) {
+    const int64_t nchunks = N * K / 8;
+    const int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (c >= nchunks) return;
+    const int64_t kc8 = K / 8;
+    const int64_t n = c / kc8;
+    const int64_t k0 = (c % kc8) * 8;
+    float o[8];
+    if constexpr (FMT == kQ8_0) {
+        const uint2 u = *reinterpret_cast<const uint2*>(codes + word_off8(n, k0, K));
+        const float delta = f16_value(reinterpret_cast<const uint16_t*>(scales)[scale_slot<kQ8_0>(n, k0 >> 5, K)]);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint32_t wv = i < 4 ? u.x : u.y;
+            const int q = (int)(int8_t)(uint8_t)(wv >> (8 * (i & 3)));
+            o[i] = __fmul_rn((float)q, delta);
+        }
+    } else {
+        const uint32_t word = *reinterpret_cast<const uint32_t*>(codes + word_off4(n, k0, K));
+        if constexpr (FMT == kNF4) {
+            float a;
+            const int64_t b = k0 >> 6;
+            if constexpr (DQ) {
+                const int q = (int)(int8_t)scales[scale_slot<kNF4>(n, b, K)];
+                const int64_t g = (n * (K / 64) + b) / 256;
+                const float d = reinterpret_cast<const float*>(scales + L.d_off)[g];
+                const float mu = *reinterpret_cast<const float*>(scales + L.mu_off);
+                a = __fadd_rn(__fmul_rn((float)q, d), mu);
+            } else {
+                a = reinterpret_cast<const float*>(scales)[scale_slot<kNF4>(n, b, K)];
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++) o[i] = __fmul_rn(nf4_level(word >> (4 * i)), a);
+        } else if constexpr (FMT == kNVFP4) {
+            const float s = e4m3_value(scales[scale_slot<kNVFP4>(n, k0 >> 4, K)]);
+            const float g = *reinterpret_cast<const float*>(scales + L.g_off);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const uint32_t cd = (word >> (4 * i)) & 15u;
+                float v = e2m1_mag_value(cd & 7u);
+                if (cd & 8u) v = -v;
+                o[i] = __fmul_rn(__fmul_rn(v, s), g);
+            }
+        } else {  // kQ4_0
+            const float delta = f16_value(reinterpret_cast<const uint16_t*>(scales)[scale_slot<kQ4_0>(n, k0 >> 5, K)]);
+#pragma unroll
+            for (int i = 0; i < 8; i++) o[i] = __fmul_rn((float)((int)((word >> (4 * i)) & 15u) - 8), delta);
+        }
+    }
+    float4* dst = reinterpret_cast<float4*>(out + n * K + k0);
+    dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+}
+
+static inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
+
+hipError_t launch_quantize(int fmt, bool dq, int64_t n, int64_t k, const float* w, uint8_t* codes,
+                           uint8_t* scales, hipStream_t s) {
+    const ScaleLayout L = scale_layout(fmt, dq, n, k);
+    const int64_t chunks = n * k / 8;
+    const unsigned grid = grid_for(chunks);
+    switch (fmt) {
+    case kNF4:
+        if (!dq) {
+            hipLaunchKernelGGL((k_quant_chunks<kNF4, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
+        } else {
+            float* scratch = reinterpret_cast<float*>(codes);   // nb floats <= n*k/2 bytes
+            hipLaunchKernelGGL((k_quant_chunks<kNF4, 1>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, scratch, L);
+            hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(64), 0, s, scratch, L.nb, scales, L.mu_off);
+            hipLaunchKernelGGL(k_dq_groups, dim3((unsigned)L.ng), dim3(64), 0, s, scratch, L.nb, k, scales, L);
+            hipLaunchKernelGGL((k_quant_chunks<kNF4, 2>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
+        }
+        break;
+    case kNVFP4: {
+        float* partial = reinterpret_cast<float*>(codes);      // <= 256 floats <= n*k/2 bytes
+        const int np = (int)std::min<int64_t>(256, std::max<int64_t>(1, (n * k / 4 + 255) / 256));
+        hipLaunchKernelGGL(k_absmax_partial, dim3(np), dim3(256), 0, s, w, n * k, partial);
+        hipLaunchKernelGGL(k_absmax_final, dim3(1), dim3(64), 0, s, partial, np, scales, L.g_off);
+        hipLaunchKernelGGL((k_quant_chunks<kNVFP4, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
+        break;
+    }
+    case kQ4_0:
+        hipLaunchKernelGGL((k_quant_chunks<kQ4_0, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
+        break;
+    case kQ8_0:
+        hipLaunchKernelGGL((k_quant_chunks<kQ8_0, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_dequantize(int fmt, bool dq, int64_t n, int64_t k, const uint8_t* codes, const uint8_t* scales,
+                             float* out, hipStream_t s) {
+    const ScaleLayout L = scale_layout(fmt, dq, n, k);
+    const unsigned grid = grid_for(n * k / 8);
+    switch (fmt) {
+    case kNF4:
+        if (dq) hipLaunchKernelGGL((k_dequant_chunks<kNF4, true>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);
+        else hipLaunchKernelGGL((k_dequant_chunks<kNF4, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);
+        break;
+    case kNVFP4:
+        hipLaunchKernelGGL((k_dequant_chunks<kNVFP4, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);
+        break;
+    case kQ4_0:
+        hipLaunchKernelGGL((k_dequant_chunks<kQ4_0, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);
+        break;
+    case kQ8_0:
+        hipLaunchKernelGGL((k_dequant_chunks<kQ8_0, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);
+        break;
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace wq

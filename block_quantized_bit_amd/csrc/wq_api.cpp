@@ -1,0 +1,210 @@
+// wq_api.cpp -- the C ABI of libwq (declared in include/wq.h).
+//
+// Every argument is checked on the host before anything is enqueued; a failed
+// check returns a status and launches nothing ("fails loudly" rather than running
+// unquantized: "asr: add a 4-bit nf4 option for the Whisper engine", "What's
+// here"; an actionable error before any work: same page, "Verified").  There is
+// no dense or unfused fallback.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "wq.h"
+#include "wq_launch.h"
+
+namespace {
+
+struct Desc {
+    int fmt;
+    bool dq;
+    int64_t n, k;
+};
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+wq_status check_desc(const wq_desc* d, Desc* out) {
+    if (!d) return WQ_ERR_INVALID_ARG;
+    if (d->reserved != 0) return WQ_ERR_INVALID_ARG;
+    int bk;
+    switch (d->format) {
+    case WQ_NF4: bk = 64; break;
+    case WQ_NVFP4: bk = 16; break;
+    case WQ_Q4_0:
+    case WQ_Q8_0: bk = 32; break;
+    default: return WQ_ERR_INVALID_ARG;
+    }
+    if (d->block != 0 && d->block != bk) return WQ_ERR_UNSUPPORTED;
+    if (d->format == WQ_NF4) {
+        if (d->dq_group != 0 && d->dq_group != 256) return WQ_ERR_UNSUPPORTED;
+    } else if (d->dq_group != 0) {
+        return WQ_ERR_UNSUPPORTED;
+    }
+    const int64_t tk = d->format == WQ_Q8_0 ? 64 : 128;
+    if (d->n <= 0 || d->k <= 0 || d->n % 16 != 0 || d->k % tk != 0) return WQ_ERR_SHAPE;
+    if (d->n > (int64_t(1) << 40) / d->k) return WQ_ERR_SHAPE;   // keep every byte offset far from overflow
+    out->fmt = d->format;
+    out->dq = d->format == WQ_NF4 && d->dq_group == 256;
+    out->n = d->n;
+    out->k = d->k;
+    return WQ_OK;
+}
+
+wq_status check_packed(const wq_packed& w) {
+    if (!w.codes || !w.scales) return WQ_ERR_INVALID_ARG;
+    if (!aligned(w.codes, 16) || !aligned(w.scales, 16)) return WQ_ERR_ALIGNMENT;
+    return WQ_OK;
+}
+
+wq_status from_hip(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_HIP; }
+
+// Common checks of a matmul call; fills everything of the problem except the outputs.
+wq_status check_matmul(const wq_desc* d, int64_t m, const uint16_t* x, int64_t ldx, wq_packed w,
+                       const uint16_t* bias, int32_t ydt, void* ws, size_t ws_bytes, wq::MatmulProblem* p) {
+    Desc dd;
+    wq_status st = check_desc(d, &dd);
+    if (st != WQ_OK) return st;
+    if ((st = check_packed(w)) != WQ_OK) return st;
+    if (m < 0 || m > 0x7FFFFFFF) return WQ_ERR_SHAPE;
+    if (!x) return WQ_ERR_INVALID_ARG;
+    if (ldx < dd.k || ldx % 8 != 0) return WQ_ERR_INVALID_ARG;
+    if (!aligned(x, 16)) return WQ_ERR_ALIGNMENT;
+    if (bias && !aligned(bias, 2)) return WQ_ERR_ALIGNMENT;
+    if (ydt != WQ_BF16 && ydt != WQ_F32) return WQ_ERR_INVALID_ARG;
+    if (ws) {
+        if (!aligned(ws, 16)) return WQ_ERR_ALIGNMENT;
+        if (m > 0 && ws_bytes < wq::matmul_workspace_bytes(dd.fmt, m, dd.n, dd.k)) return WQ_ERR_WORKSPACE;
+    }
+    p->fmt = dd.fmt;
+    p->dq = dd.dq;
+    p->m = m;
+    p->n = dd.n;
+    p->k = dd.k;
+    p->x = x;
+    p->ldx = ldx;
+    p->codes = static_cast<const uint8_t*>(w.codes);
+    p->scales = static_cast<const uint8_t*>(w.scales);
+    p->bias = bias;
+    p->ws = ws;
+    p->ws_bytes = ws_bytes;
+    p->out.f32 = ydt == WQ_F32;
+    return WQ_OK;
+}
+
+wq_status run_matmul(const wq::MatmulProblem& p, void* stream) {
+    if (p.m == 0) return WQ_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return from_hip(p.m <= 16 ? wq::launch_gemv(p, s) : wq::launch_gemm(p, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wq_status_str(wq_status s) {
+    switch (s) {
+    case WQ_OK: return "WQ_OK";
+    case WQ_ERR_INVALID_ARG: return "WQ_ERR_INVALID_ARG";
+    case WQ_ERR_UNSUPPORTED: return "WQ_ERR_UNSUPPORTED";
+    case WQ_ERR_SHAPE: return "WQ_ERR_SHAPE";
+    case WQ_ERR_ALIGNMENT: return "WQ_ERR_ALIGNMENT";
+    case WQ_ERR_MIXED_FORMAT: return "WQ_ERR_MIXED_FORMAT";
+    case WQ_ERR_WORKSPACE: return "WQ_ERR_WORKSPACE";
+    case WQ_ERR_HIP: return "WQ_ERR_HIP";
+    }
+    return "WQ_ERR_UNKNOWN";
+}
+
+wq_status wq_packed_size(const wq_desc* d, size_t* codes_bytes, size_t* scales_bytes) {
+    Desc dd;
+    wq_status st = check_desc(d, &dd);
+    if (st != WQ_OK) return st;
+    if (!codes_bytes || !scales_bytes) return WQ_ERR_INVALID_ARG;
+    *codes_bytes = (size_t)(dd.fmt == WQ_Q8_0 ? dd.n * dd.k : dd.n * dd.k / 2);
+    *scales_bytes = (size_t)wq::scale_layout(dd.fmt, dd.dq, dd.n, dd.k).bytes;
+    return WQ_OK;
+}
+
+wq_status wq_quantize(const wq_desc* d, const float* w, wq_packed out, void* stream) {
+    Desc dd;
+    wq_status st = check_desc(d, &dd);
+    if (st != WQ_OK) return st;
+    if ((st = check_packed(out)) != WQ_OK) return st;
+    if (!w) return WQ_ERR_INVALID_ARG;
+    if (!aligned(w, 16)) return WQ_ERR_ALIGNMENT;
+    return from_hip(wq::launch_quantize(dd.fmt, dd.dq, dd.n, dd.k, w, static_cast<uint8_t*>(out.codes),
+                                        static_cast<uint8_t*>(out.scales), static_cast<hipStream_t>(stream)));
+}
+
+wq_status wq_dequantize(const wq_desc* d, wq_packed in, float* w_out, void* stream) {
+    Desc dd;
+    wq_status st = check_desc(d, &dd);
+    if (st != WQ_OK) return st;
+    if ((st = check_packed(in)) != WQ_OK) return st;
+    if (!w_out) return WQ_ERR_INVALID_ARG;
+    if (!aligned(w_out, 16)) return WQ_ERR_ALIGNMENT;
+    return from_hip(wq::launch_dequantize(dd.fmt, dd.dq, dd.n, dd.k, static_cast<const uint8_t*>(in.codes),
+                                          static_cast<const uint8_t*>(in.scales), w_out, static_cast<hipStream_t>(stream)));
+}
+
+wq_status wq_workspace_size(const wq_desc* d, int64_t m, size_t* bytes) {
+    Desc dd;
+    wq_status st = check_desc(d, &dd);
+    if (st != WQ_OK) return st;
+    if (!bytes) return WQ_ERR_INVALID_ARG;
+    if (m < 0 || m > 0x7FFFFFFF) return WQ_ERR_SHAPE;
+    *bytes = m == 0 ? 0 : wq::matmul_workspace_bytes(dd.fmt, m, dd.n, dd.k);
+    return WQ_OK;
+}
+
+wq_status wq_matmul(const wq_desc* d, int64_t m, const uint16_t* x, int64_t ldx, wq_packed w,
+                    const uint16_t* bias, void* y, int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                    void* stream) {
+    wq::MatmulProblem p{};
+    wq_status st = check_matmul(d, m, x, ldx, w, bias, ydt, ws, ws_bytes, &p);
+    if (st != WQ_OK) return st;
+    if (!y) return WQ_ERR_INVALID_ARG;
+    if (!aligned(y, ydt == WQ_F32 ? 4 : 2)) return WQ_ERR_ALIGNMENT;
+    if (ldy < p.n) return WQ_ERR_INVALID_ARG;
+    p.out.nsplit = 1;
+    p.out.y[0] = y;
+    p.out.ldy[0] = ldy;
+    p.out.end[0] = p.out.end[1] = p.out.end[2] = p.n;
+    return run_matmul(p, stream);
+}
+
+wq_status wq_matmul_qkv(const wq_desc* d, int64_t m, const uint16_t* x, int64_t ldx, wq_packed w,
+                        const uint16_t* bias, int32_t nsplit, const int64_t* split_n, void* const* y,
+                        const int64_t* ldy, int32_t ydt, void* ws, size_t ws_bytes, void* stream) {
+    wq::MatmulProblem p{};
+    wq_status st = check_matmul(d, m, x, ldx, w, bias, ydt, ws, ws_bytes, &p);
+    if (st != WQ_OK) return st;
+    if (nsplit != 2 && nsplit != 3) return WQ_ERR_INVALID_ARG;
+    if (!split_n || !y || !ldy) return WQ_ERR_INVALID_ARG;
+    int64_t sum = 0;
+    for (int i = 0; i < nsplit; i++) {
+        if (split_n[i] <= 0) return WQ_ERR_SHAPE;
+        sum += split_n[i];
+    }
+    if (sum != p.n) return WQ_ERR_SHAPE;
+    for (int i = 0; i < nsplit; i++) {
+        if (!y[i]) return WQ_ERR_INVALID_ARG;
+        if (!aligned(y[i], ydt == WQ_F32 ? 4 : 2)) return WQ_ERR_ALIGNMENT;
+        if (ldy[i] < split_n[i]) return WQ_ERR_INVALID_ARG;
+    }
+    p.out.nsplit = nsplit;
+    int64_t e = 0;
+    for (int i = 0; i < 3; i++) {
+        if (i < nsplit) {
+            e += split_n[i];
+            p.out.y[i] = y[i];
+            p.out.ldy[i] = ldy[i];
+        } else {
+            p.out.y[i] = y[nsplit - 1];
+            p.out.ldy[i] = ldy[nsplit - 1];
+        }
+        p.out.end[i] = e;
+    }
+    return run_matmul(p, stream);
+}
+
+}  // extern "C"

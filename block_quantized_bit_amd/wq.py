@@ -1,0 +1,156 @@
+"""Python binding of libwq (include/wq.h): argument marshalling only.
+
+Every function here has the C entry point's name and arguments.  Tensor
+arguments may be torch tensors (their device pointer is passed) or raw integer
+device addresses.  `stream` defaults to torch's current HIP stream.  A status
+other than WQ_OK raises WqError.  All computation happens in the HIP library;
+if libwq.so is missing the import fails loudly -- there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libwq.so")
+
+WQ_OK = 0
+STATUS_NAMES = {0: "WQ_OK", 1: "WQ_ERR_INVALID_ARG", 2: "WQ_ERR_UNSUPPORTED", 3: "WQ_ERR_SHAPE",
+                4: "WQ_ERR_ALIGNMENT", 5: "WQ_ERR_MIXED_FORMAT", 6: "WQ_ERR_WORKSPACE", 7: "WQ_ERR_HIP"}
+WQ_NF4, WQ_NVFP4, WQ_Q4_0, WQ_Q8_0 = 1, 2, 3, 4
+WQ_BF16, WQ_F32 = 1, 2
+
+EXPORTS = ("wq_status_str", "wq_packed_size", "wq_quantize", "wq_dequantize",
+           "wq_workspace_size", "wq_matmul", "wq_matmul_qkv")
+
+# Format names accepted by the harness; aliases follow the NF4 option's names
+# ("asr: add a 4-bit nf4 option for the Whisper engine": nf4, aliases 4bit, int4).
+_FORMAT_NAMES = {"nf4": WQ_NF4, "4bit": WQ_NF4, "int4": WQ_NF4, "nvfp4": WQ_NVFP4,
+                 "q4_0": WQ_Q4_0, "q8_0": WQ_Q8_0}
+
+
+def format_from_name(name: str) -> int:
+    try:
+        return _FORMAT_NAMES[name.strip().lower()]
+    except KeyError:
+        raise ValueError(f"unknown weight format {name!r}; expected one of {sorted(_FORMAT_NAMES)}") from None
+
+
+class WqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}")
+
+
+class wq_desc(ctypes.Structure):
+    _fields_ = [("format", ctypes.c_int32), ("block", ctypes.c_int32), ("n", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("dq_group", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class wq_packed(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+def desc(fmt, n: int, k: int, dq: bool = False, block: int = 0) -> wq_desc:
+    if isinstance(fmt, str):
+        fmt = format_from_name(fmt)
+    return wq_desc(int(fmt), int(block), int(n), int(k), 256 if dq else 0, 0)
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libwq.so not built ({LIB_PATH}); run `python -m block_quantized_bit_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        pd = ctypes.POINTER(wq_desc)
+        L.wq_status_str.restype = ctypes.c_char_p
+        L.wq_status_str.argtypes = [ctypes.c_int]
+        L.wq_packed_size.restype = ctypes.c_int
+        L.wq_packed_size.argtypes = [pd, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+        L.wq_quantize.restype = ctypes.c_int
+        L.wq_quantize.argtypes = [pd, P, wq_packed, P]
+        L.wq_dequantize.restype = ctypes.c_int
+        L.wq_dequantize.argtypes = [pd, wq_packed, P, P]
+        L.wq_workspace_size.restype = ctypes.c_int
+        L.wq_workspace_size.argtypes = [pd, i64, ctypes.POINTER(ctypes.c_size_t)]
+        L.wq_matmul.restype = ctypes.c_int
+        L.wq_matmul.argtypes = [pd, i64, P, i64, wq_packed, P, P, ctypes.c_int32, i64, P, ctypes.c_size_t, P]
+        L.wq_matmul_qkv.restype = ctypes.c_int
+        L.wq_matmul_qkv.argtypes = [pd, i64, P, i64, wq_packed, P, ctypes.c_int32, ctypes.POINTER(i64),
+                                    ctypes.POINTER(P), ctypes.POINTER(i64), ctypes.c_int32, P, ctypes.c_size_t, P]
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(st: int, where: str, check: bool) -> int:
+    if check and st != WQ_OK:
+        raise WqError(st, where)
+    return st
+
+
+def wq_status_str(status: int) -> str:
+    return lib().wq_status_str(int(status)).decode()
+
+
+def wq_packed_size(d: wq_desc):
+    cb = ctypes.c_size_t()
+    sb = ctypes.c_size_t()
+    _check(lib().wq_packed_size(ctypes.byref(d), ctypes.byref(cb), ctypes.byref(sb)), "wq_packed_size", True)
+    return cb.value, sb.value
+
+
+def wq_quantize(d: wq_desc, w, codes, scales, stream=None, check=True) -> int:
+    st = lib().wq_quantize(ctypes.byref(d), _ptr(w), wq_packed(_ptr(codes), _ptr(scales)), _stream(stream))
+    return _check(st, "wq_quantize", check)
+
+
+def wq_dequantize(d: wq_desc, codes, scales, w_out, stream=None, check=True) -> int:
+    st = lib().wq_dequantize(ctypes.byref(d), wq_packed(_ptr(codes), _ptr(scales)), _ptr(w_out), _stream(stream))
+    return _check(st, "wq_dequantize", check)
+
+
+def wq_workspace_size(d: wq_desc, m: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().wq_workspace_size(ctypes.byref(d), int(m), ctypes.byref(b)), "wq_workspace_size", True)
+    return b.value
+
+
+def wq_matmul(d: wq_desc, m: int, x, ldx: int, codes, scales, bias, y, ydt: int, ldy: int,
+              ws=None, ws_bytes: int = 0, stream=None, check=True) -> int:
+    st = lib().wq_matmul(ctypes.byref(d), int(m), _ptr(x), int(ldx), wq_packed(_ptr(codes), _ptr(scales)),
+                         _ptr(bias), _ptr(y), int(ydt), int(ldy), _ptr(ws), int(ws_bytes), _stream(stream))
+    return _check(st, "wq_matmul", check)
+
+
+def wq_matmul_qkv(d: wq_desc, m: int, x, ldx: int, codes, scales, bias, split_n, ys, ldys, ydt: int,
+                  ws=None, ws_bytes: int = 0, stream=None, check=True) -> int:
+    ns = len(split_n)
+    sn = (ctypes.c_int64 * ns)(*[int(v) for v in split_n])
+    yp = (ctypes.c_void_p * len(ys))(*[_ptr(v) for v in ys])
+    lp = (ctypes.c_int64 * len(ldys))(*[int(v) for v in ldys])
+    st = lib().wq_matmul_qkv(ctypes.byref(d), int(m), _ptr(x), int(ldx), wq_packed(_ptr(codes), _ptr(scales)),
+                             _ptr(bias), ns, sn, yp, lp, int(ydt), _ptr(ws), int(ws_bytes), _stream(stream))
+    return _check(st, "wq_matmul_qkv", check)

@@ -1,0 +1,157 @@
+/*
+ * wq.h -- libwq: weight-only 4-bit (and 8-bit) matmul with dequantization fused
+ * in, for AMD Instinct MI355X (gfx950).
+ *
+ * Y[M,N] = X[M,K] * W^[N,K]^T + b, where X is bf16, W^ is the dequantized form
+ * of a block-quantized weight matrix, accumulation is fp32.
+ *
+ * Formats (what the pages fix):
+ *   NF4    4-bit NormalFloat codes, one absmax per 64 values along K, optional
+ *          double quantization of the absmax values ("asr: add a 4-bit nf4 option
+ *          for the Whisper engine", intro and "What's here": double-quant, bf16
+ *          compute; the fused dequant-matmul is the reason NF4 is 1.66x and not
+ *          4.1x of bf16 -- section "Why NF4 and not the NVFP4 snapshot ...").
+ *   NVFP4  E2M1 codes in 16-value blocks, one E4M3 scale per block and one FP32
+ *          global scale per matrix ("asr: add a 4-bit nvfp4 option for cards short
+ *          of VRAM", intro; "mbehr90/whisper-large-v3-turbo-nvfp4", section "What
+ *          is quantized"; run as a W4A16 GEMM -- same section).
+ *   Q4_0 / Q8_0  32-value blocks with one fp16 scale and signed 4-/8-bit codes
+ *          ("Run quantized Whisper on the fused Metal decode path", "Summary" and
+ *          "Why the policy").
+ * The exact rounding rules, the NF4 levels, the double-quant scheme and the packed
+ * tile layout are this library's own definitions (the pages leave them open) and
+ * are written out in the design doc of the source tree.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  libwq never
+ *     allocates, frees or synchronizes; work is enqueued on `stream` (a
+ *     hipStream_t; NULL = the default stream) and the call returns.
+ *   - Arguments are validated on the host before anything is enqueued.  A call
+ *     that returns a status other than WQ_OK has enqueued nothing.  There is no
+ *     fallback to a dense or unfused path and no silent format conversion.
+ *   - A HIP launch error maps to WQ_ERR_HIP.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *   - Shapes: n > 0 and n % 16 == 0; k > 0 and k % 128 == 0 (NF4, NVFP4, Q4_0)
+ *     or k % 64 == 0 (Q8_0); m >= 0 (m == 0 is a no-op that returns WQ_OK).
+ */
+#ifndef LIBWQ_WQ_H
+#define LIBWQ_WQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    WQ_OK = 0,
+    WQ_ERR_INVALID_ARG = 1,   /* NULL pointer, bad enum value, bad stride */
+    WQ_ERR_UNSUPPORTED = 2,   /* format/block/double-quant combination not offered */
+    WQ_ERR_SHAPE = 3,         /* n, k, m or split sizes violate the shape rules */
+    WQ_ERR_ALIGNMENT = 4,     /* a pointer or stride is not aligned as required */
+    WQ_ERR_MIXED_FORMAT = 5,  /* reserved: one descriptor always means one format */
+    WQ_ERR_WORKSPACE = 6,     /* non-NULL workspace smaller than wq_workspace_size */
+    WQ_ERR_HIP = 7            /* a HIP runtime call or kernel launch failed */
+} wq_status;
+
+typedef enum { WQ_NF4 = 1, WQ_NVFP4 = 2, WQ_Q4_0 = 3, WQ_Q8_0 = 4 } wq_format;
+
+typedef enum { WQ_BF16 = 1, WQ_F32 = 2 } wq_dtype;
+
+/* One quantized weight matrix W[n, k] (PyTorch Linear layout: [out, in]).
+ *   format   : wq_format
+ *   block    : 0 (= the format's block) or exactly 64 (NF4), 16 (NVFP4), 32 (Q4_0, Q8_0)
+ *   n, k     : matrix shape
+ *   dq_group : NF4 only: 0 = plain fp32 absmax per block, 256 = double quantization
+ *              (int8 absmax codes, one fp32 scale per 256 consecutive blocks in
+ *              row-major block order, one fp32 mean per matrix).  Must be 0 for
+ *              the other formats. */
+typedef struct {
+    int32_t format;
+    int32_t block;
+    int64_t n;
+    int64_t k;
+    int32_t dq_group;
+    int32_t reserved;   /* must be 0 */
+} wq_desc;
+
+/* The two device buffers holding a packed matrix; both 16-byte aligned. */
+typedef struct {
+    void* codes;
+    void* scales;
+} wq_packed;
+
+/* Human-readable name of a status. Never NULL. */
+const char* wq_status_str(wq_status s);
+
+/* Host-only.  Bytes of the two packed buffers for descriptor d:
+ *   codes : n*k/2 (4-bit formats) or n*k (Q8_0)
+ *   scales: NF4 4*n*k/64; NF4+DQ align16(n*k/64) + 4*ceil(n*k/64/256) + 4;
+ *           NVFP4 align16(n*k/16) + 4; Q4_0 and Q8_0 2*n*k/32. */
+wq_status wq_packed_size(const wq_desc* d, size_t* codes_bytes, size_t* scales_bytes);
+
+/* Quantize fp32 W[n,k] (row-major, leading dimension k, 16-byte aligned) into the
+ * packed buffers `out` (sizes from wq_packed_size, 16-byte aligned).  Bit-exact
+ * with the format definitions: codes and scales are a pure function of W.
+ * W must be finite.  Uses `out.codes` as temporary storage while it runs (no
+ * other scratch).  Passages: as for the formats above; NF4 quantizes one matrix
+ * at a time as the checkpoint streams in ("asr: add a 4-bit nf4 option for the
+ * Whisper engine", "Why NF4 and not the NVFP4 snapshot Parakeet ships"). */
+wq_status wq_quantize(const wq_desc* d, const float* w, wq_packed out, void* stream);
+
+/* Dequantize the packed matrix to fp32 W^[n,k] (row-major, leading dimension k,
+ * 16-byte aligned).  Bit-exact: W^ = the format's decode of every code/scale. */
+wq_status wq_dequantize(const wq_desc* d, wq_packed in, float* w_out, void* stream);
+
+/* Host-only.  Workspace bytes wq_matmul / wq_matmul_qkv can use for an
+ * m-row call with descriptor d (split-K partial sums and tile counters).
+ * 0 means the call never uses one.  A workspace lets small-N or long-K shapes
+ * spread over all compute units; without one (ws == NULL) the call runs a
+ * schedule with no K split, which gives results within the same bound.
+ * The workspace must be zero-filled by the caller before its first use; every
+ * call leaves it zero-filled again.  One workspace must not be shared by calls
+ * that may run concurrently (different streams). */
+wq_status wq_workspace_size(const wq_desc* d, int64_t m, size_t* bytes);
+
+/* Y = X * W^T + bias.
+ *   x    : bf16 [m, k], leading dimension ldx >= k, ldx % 8 == 0, 16-byte aligned
+ *   w    : packed matrix for d
+ *   bias : bf16 [n] or NULL (2-byte aligned)
+ *   y    : [m, n] of type ydt (WQ_BF16 or WQ_F32), leading dimension ldy >= n,
+ *          aligned to its element size.  Only the m x n window is written.
+ *   ws   : workspace (see wq_workspace_size) or NULL; ws_bytes its size
+ * Accumulation is fp32 over bf16 activations times bf16-rounded (or exact)
+ * dequantized weights; per element |y - y_ref| <= 4e-3 * sum_k |x_k * w^_k| + 1e-6
+ * against the fp32 reference (plus the final bf16 rounding for WQ_BF16 outputs).
+ * m <= 16 runs the split-K GEMV (decode: token-at-a-time, "asr: add a 4-bit nf4
+ * option for the Whisper engine", "Why NF4 and not the NVFP4 snapshot ..."),
+ * m >= 17 the MFMA GEMM (encoder frames, "mbehr90/whisper-large-v3-turbo-nvfp4",
+ * "Honest summary: on H100 this is not a win"). */
+wq_status wq_matmul(const wq_desc* d, int64_t m, const uint16_t* x, int64_t ldx, wq_packed w,
+                    const uint16_t* bias, void* y, int32_t ydt, int64_t ldy,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/* Fused projection over a row-concatenated weight W[n0 + n1 (+ n2), k] in ONE
+ * launch: columns [0, n0) go to y[0], [n0, n0+n1) to y[1], [n0+n1, n) to y[2],
+ * each with its own leading dimension ldy[i] >= split_n[i], so the destinations
+ * may be rows of a K/V cache slab; nothing outside each m x split_n[i] window is
+ * touched.  bias is bf16 [n] or NULL (use zeros where a split has none, e.g. the
+ * key projection).  nsplit is 2 (merged cross-attention K/V) or 3 (Q/K/V);
+ * split_n[i] > 0 and sum(split_n) == d->n.  Passages: "Run quantized Whisper on
+ * the fused Metal decode path", "Summary" (fused Q/K/V writing into slab rows
+ * with the bias applied on device) and "Test plan" (neighbouring rows
+ * untouched); "mbehr90/whisper-large-v3-turbo-nvfp4", "Why the encoder/decoder
+ * split matters" (two-way merged cross-attention K/V).  A projection whose
+ * parts use different formats cannot be described by one descriptor: callers
+ * fall back to separate wq_matmul calls. */
+wq_status wq_matmul_qkv(const wq_desc* d, int64_t m, const uint16_t* x, int64_t ldx, wq_packed w,
+                        const uint16_t* bias, int32_t nsplit, const int64_t* split_n,
+                        void* const* y, const int64_t* ldy, int32_t ydt,
+                        void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBWQ_WQ_H */

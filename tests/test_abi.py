@@ -1,0 +1,139 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, agrees with the oracle on packed sizes, and rejects bad
+arguments on the host before anything is enqueued."""
+import os
+import re
+
+import pytest
+
+from block_quantized_bit_amd import wq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wq.h")
+NF4, NVFP4, Q4_0, Q8_0 = 1, 2, 3, 4
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(wq_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(wq.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = wq.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = os.popen(f"nm -D --defined-only {wq.LIB_PATH}").read()
+    exported = set(re.findall(r" T (wq_[a-z_]+)", out))
+    assert set(_declared()) <= exported
+
+
+def test_status_strings():
+    for s, name in wq.STATUS_NAMES.items():
+        assert wq.wq_status_str(s) == name
+
+
+SHAPES = [(16, 128), (48, 384), (272, 640), (1536, 384), (3840, 1280), (1280, 5120)]
+
+
+@pytest.mark.parametrize("fmt,dq", [(NF4, False), (NF4, True), (NVFP4, False), (Q4_0, False), (Q8_0, False)])
+def test_packed_size_matches_oracle(orc, fmt, dq):
+    for n, k in SHAPES:
+        assert wq.wq_packed_size(wq.desc(fmt, n, k, dq)) == orc.packed_size(fmt, dq, n, k)
+    # q8_0 also accepts K % 64 == 0
+    if fmt == Q8_0:
+        assert wq.wq_packed_size(wq.desc(fmt, 32, 192)) == orc.packed_size(fmt, False, 32, 192)
+
+
+def _status(fn, *a):
+    try:
+        fn(*a)
+    except wq.WqError as e:
+        return e.status
+    return 0
+
+
+def test_descriptor_validation():
+    bad = [
+        (wq.wq_desc(9, 0, 16, 128, 0, 0), 1),           # unknown format
+        (wq.wq_desc(NF4, 32, 16, 128, 0, 0), 2),        # NF4 block must be 64
+        (wq.wq_desc(NVFP4, 0, 16, 128, 256, 0), 2),     # double-quant only for NF4
+        (wq.wq_desc(NF4, 0, 16, 128, 128, 0), 2),       # group must be 256
+        (wq.wq_desc(NF4, 0, 24, 128, 0, 0), 3),         # n % 16
+        (wq.wq_desc(Q4_0, 0, 16, 64, 0, 0), 3),         # k % 128 for 4-bit
+        (wq.wq_desc(Q8_0, 0, 16, 96, 0, 0), 3),         # k % 64 for q8_0
+        (wq.wq_desc(Q8_0, 0, 0, 64, 0, 0), 3),          # n > 0
+        (wq.wq_desc(NF4, 0, 16, 128, 0, 7), 1),         # reserved
+    ]
+    for d, want in bad:
+        assert _status(wq.wq_packed_size, d) == want
+        assert _status(wq.wq_workspace_size, d, 4) == want
+
+
+FAKE = 1 << 20   # a 16-aligned non-NULL address; every call below must fail before use
+
+
+def test_matmul_argument_validation_returns_before_launch():
+    d = wq.desc(NF4, 64, 256)
+    mm = lambda **kw: _status(wq.wq_matmul, kw.get("d", d), kw.get("m", 4), kw.get("x", FAKE),
+                              kw.get("ldx", 256), kw.get("codes", FAKE), kw.get("scales", FAKE),
+                              kw.get("bias", None), kw.get("y", FAKE), kw.get("ydt", wq.WQ_F32),
+                              kw.get("ldy", 64), kw.get("ws", None), kw.get("ws_bytes", 0), 0)
+    assert mm(m=-1) == 3
+    assert mm(x=None) == 1
+    assert mm(x=FAKE + 8) == 4
+    assert mm(ldx=200) == 1
+    assert mm(ldx=260) == 1             # ldx % 8
+    assert mm(codes=None) == 1
+    assert mm(scales=FAKE + 4) == 4
+    assert mm(bias=FAKE + 1) == 4
+    assert mm(y=None) == 1
+    assert mm(y=FAKE + 2) == 4          # fp32 output needs 4-byte alignment
+    assert mm(ydt=3) == 1
+    assert mm(ldy=32) == 1
+    assert mm(ws=FAKE + 8) == 4
+    assert mm(d=wq.desc(NF4, 24, 256)) == 3
+    # a workspace smaller than asked for is an error (only checked when a split is wanted)
+    dd = wq.desc(NF4, 1280, 5120)
+    need = wq.wq_workspace_size(dd, 1)
+    assert need > 0
+    assert mm(d=dd, m=1, ldx=5120, ldy=1280, ws=FAKE, ws_bytes=need - 1) == 6
+    # m == 0 is a no-op: validated, nothing enqueued
+    assert mm(m=0) == 0
+
+
+def test_qkv_argument_validation():
+    d = wq.desc(NF4, 96, 256)
+    def q(split, ys=None, ldys=None, **kw):
+        ys = ys if ys is not None else [FAKE] * len(split)
+        ldys = ldys if ldys is not None else [max(s, 1) for s in split]
+        return _status(wq.wq_matmul_qkv, kw.get("d", d), 2, FAKE, 256, FAKE, FAKE, None, split, ys, ldys,
+                       wq.WQ_BF16, None, 0, 0)
+    assert q([96]) == 1                         # nsplit must be 2 or 3
+    assert q([32, 32, 16, 16]) == 1
+    assert q([32, 32, 16]) == 3                 # does not sum to n
+    assert q([64, 0, 32]) == 3
+    assert q([32, 32, 32], ys=[FAKE, None, FAKE]) == 1
+    assert q([32, 32, 32], ys=[FAKE, FAKE + 1, FAKE]) == 4
+    assert q([32, 32, 32], ldys=[32, 16, 32]) == 1
+
+
+def test_quantize_argument_validation():
+    d = wq.desc(NVFP4, 32, 256)
+    assert _status(wq.wq_quantize, d, None, FAKE, FAKE, 0) == 1
+    assert _status(wq.wq_quantize, d, FAKE + 4, FAKE, FAKE, 0) == 4
+    assert _status(wq.wq_quantize, d, FAKE, None, FAKE, 0) == 1
+    assert _status(wq.wq_dequantize, d, FAKE, FAKE, FAKE + 8, 0) == 4
+    assert _status(wq.wq_dequantize, wq.desc(NVFP4, 32, 200), FAKE, FAKE, FAKE, 0) == 3
+
+
+def test_format_names():
+    assert wq.format_from_name("nf4") == wq.format_from_name("4bit") == wq.format_from_name("INT4") == NF4
+    assert wq.format_from_name("nvfp4") == NVFP4
+    assert wq.format_from_name("q4_0") == Q4_0 and wq.format_from_name("q8_0") == Q8_0
+    with pytest.raises(ValueError):
+        wq.format_from_name("fp8")
