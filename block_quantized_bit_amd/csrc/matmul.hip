@@ -136,232 +136,426 @@ __device__ inline f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
 }
 
 // ---------------------------------------------------------------------------
-// Output: scatter one value to its split, add bias, convert.
+// Output.  A lane's output column is fixed for a whole tile, so the split it
+// falls in, its base pointer and leading dimension are selected once per
+// column (constant-index kernel-argument reads, then selects) and the bias is
+// read once per column.
 // ---------------------------------------------------------------------------
-__device__ inline void store_out(const OutSplit& o, int64_t m, int64_t n, float v) {
-    int s = 0;
-    int64_t c0 = 0;
-    if (n >= o.end[0]) {
-        s = 1;
-        c0 = o.end[0];
-        if (n >= o.end[1]) { s = 2; c0 = o.end[1]; }
+struct ColOut {
+    char* p;       // address of element (row 0, this column)
+    int64_t ld;    // row stride in bytes
+    float bias;
+};
+
+__device__ inline ColOut col_out(const KArgs& a, int64_t col) {
+    const OutSplit& o = a.out;
+    const bool s1 = col >= o.end[0], s2 = col >= o.end[1];
+    char* const y0 = reinterpret_cast<char*>(o.y[0]);
+    char* const y1 = reinterpret_cast<char*>(o.y[1]);
+    char* const y2 = reinterpret_cast<char*>(o.y[2]);
+    char* const base = s2 ? y2 : (s1 ? y1 : y0);
+    const int64_t ld = s2 ? o.ldy[2] : (s1 ? o.ldy[1] : o.ldy[0]);
+    const int64_t c0 = s2 ? o.end[1] : (s1 ? o.end[0] : 0);
+    const int64_t es = o.f32 ? 4 : 2;
+    ColOut c;
+    c.p = base + (col - c0) * es;
+    c.ld = ld * es;
+    c.bias = a.bias ? bf16_value(a.bias[col]) : 0.0f;
+    return c;
+}
+
+// y = acc * g + bias, converted and stored at row m.
+__device__ inline void put_out(const KArgs& a, const ColOut& c, int64_t m, float v, float g) {
+    const float r = v * g + c.bias;
+    char* const p = c.p + m * c.ld;
+    if (a.out.f32) *reinterpret_cast<float*>(p) = r;
+    else *reinterpret_cast<uint16_t*>(p) = bf16_rne(r);
+}
+
+// Sum of the split-K partials of one output element in piece order 0, 1, ...
+__device__ inline float sum_partials(const float* p, int64_t stride, int ks) {
+    float v = 0.0f;
+    for (int s0 = 0; s0 < ks; s0 += 4) {
+        float t[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) t[u] = (s0 + u < ks) ? __builtin_nontemporal_load(p + (s0 + u) * stride) : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 4; u++) v += t[u];
     }
-    const int64_t off = m * o.ldy[s] + (n - c0);
-    if (o.f32) reinterpret_cast<float*>(o.y[s])[off] = v;
-    else reinterpret_cast<uint16_t*>(o.y[s])[off] = bf16_rne(v);
-}
-
-__device__ inline float finish(const KArgs& a, int64_t n, float v, float g) {
-    float r = v * g;
-    if (a.bias) r = r + bf16_value(a.bias[n]);
-    return r;
+    return v;
 }
 
 // ===========================================================================
-// GEMV, m <= 16.  Workgroup = 4 waves on one 16-row band and one K piece; wave w
-// takes tiles w, w+4, ... of the piece.  Lane l owns row (l & 15) of the band as
-// B operand and row (l & 15) of X as A operand; the 16x16 result tile has
-// D[4*(l>>4)+i][l&15] in lane l.
+// GEMV, m <= 16.  Work item = (16-row band, K piece).  Each wave owns whole
+// items (no cross-wave reduction); an item's tiles are fetched C at a time --
+// codes, scales and X operands of all C tiles are requested before any is
+// used -- so every wave keeps up to C KiB of weights in flight.  Lane l owns row
+// (l & 15) of the band as B operand and row (l & 15) of X as A operand; the
+// 16x16 result tile has D[4*(l>>4)+i][l&15] in lane l.
 // ===========================================================================
+template <int FMT>
+struct GemvTile {
+    uint4 code;             // this lane's 16 bytes of the tile
+    uint32_t sc[3];         // raw scale words (format dependent)
+    u32x4 A[tile_k(FMT) / 32];
+};
+
+template <int FMT, bool DQ>
+__device__ inline void gemv_load(GemvTile<FMT>& t, const KArgs& a, int64_t band, int64_t kt, int lane, int r,
+                                 bool mrow, const uint16_t* xrow, int64_t KT) {
+    constexpr int TK = tile_k(FMT);
+    const int64_t tile = band * KT + kt;
+    t.code = *reinterpret_cast<const uint4*>(a.codes + tile * kTileBytes + lane * 16);
+    if constexpr (FMT == kNF4) {
+        if constexpr (DQ) {
+            t.sc[0] = *reinterpret_cast<const uint16_t*>(a.scales + tile * 32 + r * 2);
+            const int64_t b0 = (band * 16 + r) * (a.k / 64) + kt * 2;
+            const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
+            t.sc[1] = __float_as_uint(dt[b0 >> 8]);
+            t.sc[2] = __float_as_uint(dt[(b0 + 1) >> 8]);
+        } else {
+            const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 32 + r * 2) * 4);
+            t.sc[0] = v.x;
+            t.sc[1] = v.y;
+        }
+    } else if constexpr (FMT == kQ4_0) {
+        const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 64 + r * 4) * 2);
+        t.sc[0] = v.x;
+        t.sc[1] = v.y;
+    } else if constexpr (FMT == kNVFP4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(a.scales + tile * 128 + r * 8);
+        t.sc[0] = v.x;
+        t.sc[1] = v.y;
+    } else {
+        t.sc[0] = *reinterpret_cast<const uint32_t*>(a.scales + (tile * 32 + r * 2) * 2);
+    }
+    // rows r >= m read row 0 (always valid); their products land in output rows that are never stored
+#pragma unroll
+    for (int j = 0; j < TK / 32; j++) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xrow + kt * TK + 32 * j);
+        t.A[j] = mrow ? u32x4{v.x, v.y, v.z, v.w} : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
 template <int FMT, bool DQ, int NI>
-__global__ __launch_bounds__(256, 2) void k_gemv(KArgs a) {
+__device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const uint32_t* lut, uint32_t lane4,
+                                    int h, float mu) {
+    const uint32_t uw[4] = {t.code.x, t.code.y, t.code.z, t.code.w};
+    if constexpr (FMT == kNF4) {
+        float s0, s1;
+        if constexpr (DQ) {
+            s0 = __fadd_rn(__fmul_rn((float)(int8_t)(t.sc[0] & 255u), __uint_as_float(t.sc[1])), mu);
+            s1 = __fadd_rn(__fmul_rn((float)(int8_t)((t.sc[0] >> 8) & 255u), __uint_as_float(t.sc[2])), mu);
+        } else {
+            s0 = __uint_as_float(t.sc[0]);
+            s1 = __uint_as_float(t.sc[1]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < 2; jj++) {
+                const int j = kb * 2 + jj;
+                u32x4 B;
+#pragma unroll
+                for (int q = 0; q < 4; q++) B[q] = lut_pair(lut, lane4, uw[j], q);
+                p = mfma(t.A[j], B, p);
+            }
+            const float s = kb ? s1 : s0;
+#pragma unroll
+            for (int i = 0; i < NI; i++) acc[i] += p[i] * s;
+        }
+    } else if constexpr (FMT == kQ4_0) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            u32x4 B;
+#pragma unroll
+            for (int q = 0; q < 4; q++) B[q] = lut_pair(lut, lane4, uw[j], q);
+            const f32x4 p = mfma(t.A[j], B, f32x4{0.f, 0.f, 0.f, 0.f});
+            const float s = f16_value((uint16_t)(t.sc[j >> 1] >> (16 * (j & 1))));
+#pragma unroll
+            for (int i = 0; i < NI; i++) acc[i] += p[i] * s;
+        }
+    } else if constexpr (FMT == kNVFP4) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int blk = 2 * j + (h >> 1);
+            const uint32_t sb = (t.sc[blk >> 2] >> (8 * (blk & 3))) & 255u;
+            const float s = e4m3_value(sb);
+            u32x4 B;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const uint32_t pr = lut_pair(lut, lane4, uw[j], q);
+                const float lo = lo_f(pr) * s, hi = hi_f(pr) * s;                    // exact
+                B[q] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+            }
+            acc = mfma(t.A[j], B, acc);
+        }
+    } else {  // kQ8_0: 16 x 64 tile, K slices j = 0, 1
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            u32x4 B;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const uint32_t wv = uw[2 * j + (q >> 1)];
+                const int sh = 16 * (q & 1);
+                const float f0 = (float)(int)(int8_t)(wv >> sh);
+                const float f1 = (float)(int)(int8_t)(wv >> (sh + 8));
+                B[q] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+            }
+            const f32x4 p = mfma(t.A[j], B, f32x4{0.f, 0.f, 0.f, 0.f});
+            const float s = f16_value((uint16_t)(t.sc[0] >> (16 * j)));
+#pragma unroll
+            for (int i = 0; i < NI; i++) acc[i] += p[i] * s;
+        }
+    }
+}
+
+constexpr int kGemvWaves = 8;   // waves per workgroup, all on one band, splitting its K range
+
+template <int FMT, bool DQ, int NI, int C>
+__global__ __launch_bounds__(64 * kGemvWaves, 1) void k_gemv(KArgs a) {
     __shared__ uint32_t lut[(FMT == kQ8_0) ? 1 : kLutWords];
-    __shared__ f32x4 red[4][64];
-    __shared__ int s_last;
+    __shared__ f32x4 red[kGemvWaves][64];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15;
     const int h = lane >> 4;
     const uint32_t lane4 = (uint32_t)lane << 2;
-    const int M = a.m;
-    const int64_t K = a.k;
-    constexpr int TK = tile_k(FMT);
-    const int64_t KT = K / TK;
+    const int64_t KT = a.k / tile_k(FMT);
     const int64_t nbands = a.n / 16;
-    const int64_t items = nbands * a.ksplit;
-
-    if constexpr (FMT != kQ8_0) build_lut<FMT>(lut);
-    __syncthreads();
 
     float g = 1.0f, mu = 0.0f;
     if constexpr (FMT == kNVFP4) g = *reinterpret_cast<const float*>(a.scales + a.L.g_off);
     if constexpr (FMT == kNF4 && DQ) mu = *reinterpret_cast<const float*>(a.scales + a.L.mu_off);
-
-    const bool mrow = r < M;
+    const bool mrow = r < a.m;
     const uint16_t* xrow = a.x + (int64_t)(mrow ? r : 0) * a.ldx + h * 8;
 
-    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-        const int64_t band = item / a.ksplit;
-        const int ks = (int)(item % a.ksplit);
-        const int64_t kt0 = ks * a.kt_per;
-        const int64_t kt1 = std::min<int64_t>(KT, kt0 + a.kt_per);
-        const int64_t row = band * 16 + r;
-
+    // wave w takes tiles w, w + W, w + 2W, ... of the band, C of them per round
+    const int64_t per_wave = (KT + kGemvWaves - 1) / kGemvWaves;
+    bool first = true;
+    for (int64_t band = blockIdx.x; band < nbands; band += gridDim.x) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int64_t kt = kt0 + wave; kt < kt1; kt += 4) {
-            const int64_t tile = band * KT + kt;
-            const uint4 u = *reinterpret_cast<const uint4*>(a.codes + tile * kTileBytes + lane * 16);
-            const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
-            // A operands: 8 consecutive bf16 of X row r at k = kt*TK + 32j + 8h
-            u32x4 A[TK / 32];
+        for (int64_t c0 = 0; c0 < per_wave; c0 += C) {
+            GemvTile<FMT> R[C];
 #pragma unroll
-            for (int j = 0; j < TK / 32; j++) {
-                if (mrow) {
-                    const uint4 t = *reinterpret_cast<const uint4*>(xrow + kt * TK + 32 * j);
-                    A[j] = u32x4{t.x, t.y, t.z, t.w};
-                } else {
-                    A[j] = u32x4{0u, 0u, 0u, 0u};
-                }
+            for (int s = 0; s < C; s++) {
+                const int64_t kt = std::min<int64_t>(wave + (c0 + s) * kGemvWaves, KT - 1);
+                gemv_load<FMT, DQ>(R[s], a, band, kt, lane, r, mrow, xrow, KT);
             }
-            if constexpr (FMT == kNF4) {
-                float s0, s1;
-                if constexpr (DQ) {
-                    const uint16_t qq = *reinterpret_cast<const uint16_t*>(a.scales + tile * 32 + r * 2);
-                    const int64_t b0 = row * (K / 64) + kt * 2;
-                    const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
-                    s0 = __fadd_rn(__fmul_rn((float)(int8_t)(qq & 255), dt[b0 >> 8]), mu);
-                    s1 = __fadd_rn(__fmul_rn((float)(int8_t)(qq >> 8), dt[(b0 + 1) >> 8]), mu);
-                } else {
-                    const float2 sc = *reinterpret_cast<const float2*>(a.scales + (tile * 32 + r * 2) * 4);
-                    s0 = sc.x;
-                    s1 = sc.y;
-                }
-#pragma unroll
-                for (int kb = 0; kb < 2; kb++) {
-                    f32x4 t = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int jj = 0; jj < 2; jj++) {
-                        const int j = kb * 2 + jj;
-                        u32x4 B;
-#pragma unroll
-                        for (int p = 0; p < 4; p++) B[p] = lut_pair(lut, lane4, uw[j], p);
-                        t = mfma(A[j], B, t);
-                    }
-                    const float s = kb ? s1 : s0;
-#pragma unroll
-                    for (int i = 0; i < NI; i++) acc[i] += t[i] * s;
-                }
-            } else if constexpr (FMT == kQ4_0) {
-                const uint2 sc = *reinterpret_cast<const uint2*>(a.scales + (tile * 64 + r * 4) * 2);
-                const uint32_t sw[2] = {sc.x, sc.y};
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    u32x4 B;
-#pragma unroll
-                    for (int p = 0; p < 4; p++) B[p] = lut_pair(lut, lane4, uw[j], p);
-                    const f32x4 t = mfma(A[j], B, f32x4{0.f, 0.f, 0.f, 0.f});
-                    const float s = f16_value((uint16_t)(sw[j >> 1] >> (16 * (j & 1))));
-#pragma unroll
-                    for (int i = 0; i < NI; i++) acc[i] += t[i] * s;
-                }
-            } else if constexpr (FMT == kNVFP4) {
-                const uint2 sc = *reinterpret_cast<const uint2*>(a.scales + tile * 128 + r * 8);
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const int blk = 2 * j + (h >> 1);
-                    const uint32_t sb = ((blk < 4 ? sc.x : sc.y) >> (8 * (blk & 3))) & 255u;
-                    const float s = e4m3_value(sb);
-                    u32x4 B;
-#pragma unroll
-                    for (int p = 0; p < 4; p++) {
-                        const uint32_t pr = lut_pair(lut, lane4, uw[j], p);
-                        const float lo = lo_f(pr) * s, hi = hi_f(pr) * s;                 // exact
-                        B[p] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-                    }
-                    acc = mfma(A[j], B, acc);
-                }
-            } else {  // kQ8_0: 16 x 64 tile, slices j = 0, 1
-                const uint32_t sc = *reinterpret_cast<const uint32_t*>(a.scales + (tile * 32 + r * 2) * 2);
-#pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    u32x4 B;
-#pragma unroll
-                    for (int p = 0; p < 4; p++) {
-                        const uint32_t wv = uw[2 * j + (p >> 1)];
-                        const int sh = 16 * (p & 1);
-                        const float f0 = (float)(int)(int8_t)(wv >> sh);
-                        const float f1 = (float)(int)(int8_t)(wv >> (sh + 8));
-                        B[p] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
-                    }
-                    const f32x4 t = mfma(A[j], B, f32x4{0.f, 0.f, 0.f, 0.f});
-                    const float s = f16_value((uint16_t)(sc >> (16 * j)));
-#pragma unroll
-                    for (int i = 0; i < NI; i++) acc[i] += t[i] * s;
-                }
+            if (first) {   // build the code table while the first tiles are in flight
+                if constexpr (FMT != kQ8_0) build_lut<FMT>(lut);
+                __syncthreads();
+                first = false;
             }
+#pragma unroll
+            for (int s = 0; s < C; s++)
+                if (wave + (c0 + s) * kGemvWaves < KT) gemv_consume<FMT, DQ, NI>(R[s], acc, lut, lane4, h, mu);
         }
-
-        // cross-wave reduction in a fixed order
+        if (first) {
+            if constexpr (FMT != kQ8_0) build_lut<FMT>(lut);
+            __syncthreads();
+            first = false;
+        }
+        // reduce the waves' partial tiles in a fixed order; wave 0 stores
         red[wave][lane] = acc;
         __syncthreads();
-        f32x4 sum = {0.f, 0.f, 0.f, 0.f};
         if (wave == 0) {
-            sum = red[0][lane];
+            f32x4 v = red[0][lane];
 #pragma unroll
-            for (int w = 1; w < 4; w++) sum += red[w][lane];
-        }
-        const int64_t col = band * 16 + r;
-        if (a.ksplit == 1) {
-            if (wave == 0) {
+            for (int w = 1; w < kGemvWaves; w++) v += red[w][lane];
+            const int64_t col = band * 16 + r;
+            const ColOut c = col_out(a, col);
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int mm = 4 * h + i;
-                    if (mm < M) store_out(a.out, mm, col, finish(a, col, sum[i], g));
-                }
-            }
-        } else {
-            if (wave == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int mm = 4 * h + i;
-                    if (mm < M) a.partial[((int64_t)ks * M + mm) * a.n + col] = sum[i];
-                }
-                __threadfence();
-                if (lane == 0) {
-                    const uint32_t old = atomicAdd(&a.counters[band], 1u);
-                    s_last = (old == (uint32_t)(a.ksplit - 1));
-                }
-            }
-            __syncthreads();
-            if (s_last && wave == 0) {
-                __threadfence();
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int mm = 4 * h + i;
-                    if (mm < M) {
-                        float v = 0.0f;
-                        for (int s2 = 0; s2 < a.ksplit; s2++)
-                            v += __builtin_nontemporal_load(&a.partial[((int64_t)s2 * M + mm) * a.n + col]);
-                        store_out(a.out, mm, col, finish(a, col, v, g));
-                    }
-                }
-                if (lane == 0) atomicExch(&a.counters[band], 0u);
+            for (int i = 0; i < 4; i++) {
+                const int mm = 4 * h + i;
+                if (mm < a.m) put_out(a, c, mm, v[i], g);
             }
         }
-        __syncthreads();   // red[] and s_last are reused by the next item
+        __syncthreads();
     }
 }
 
 // ===========================================================================
 // GEMM, m >= 17.  Workgroup tile 128 (M) x 256 (N), K step 128; wave w owns
 // columns [64w, 64w+64) (4 bands) for all 128 rows: 8 x 4 MFMA tiles of 16x16.
+// LDS: the fp32 code table at offset 0 (so a v_perm result is the address),
+// then the double-buffered X tile.  W codes/scales and X for step s+1 are
+// requested while step s is computed; those requests are unconditional (rows
+// past m and bands past n re-read valid rows; their results are never stored)
+// and alternate between two register sets, so nothing waits on them early.
 // ===========================================================================
 constexpr int BM = 128, BN = 256, BK = 128;
-constexpr int XS_STRIDE = BK + 8;          // bf16 elements per LDS row (272 B: conflict-free A reads)
+constexpr int kLutBytes = kLutWords * 4;
+constexpr int kXsBytes = BM * BK * 2;      // one X tile: 128 rows x 256 B, 16-byte chunks XOR-swizzled by row
+
+template <int FMT>
+struct GemmW {
+    uint4 code[tile_k(FMT) == 64 ? 2 : 1];
+    uint32_t sc[3];
+};
+
+template <int FMT, bool DQ>
+__device__ inline void gemm_load_w(GemmW<FMT>& w, const KArgs& a, int64_t band, int64_t st, int lane, int r, int64_t KT) {
+    if constexpr (FMT == kQ8_0) {
+#pragma unroll
+        for (int half = 0; half < 2; half++) {
+            const int64_t tile = band * KT + st * 2 + half;
+            w.code[half] = *reinterpret_cast<const uint4*>(a.codes + tile * kTileBytes + lane * 16);
+            w.sc[half] = *reinterpret_cast<const uint32_t*>(a.scales + (tile * 32 + r * 2) * 2);
+        }
+    } else {
+        const int64_t tile = band * KT + st;
+        w.code[0] = *reinterpret_cast<const uint4*>(a.codes + tile * kTileBytes + lane * 16);
+        if constexpr (FMT == kNF4) {
+            if constexpr (DQ) {
+                w.sc[0] = *reinterpret_cast<const uint16_t*>(a.scales + tile * 32 + r * 2);
+                const int64_t b0 = (band * 16 + r) * (a.k / 64) + st * 2;
+                const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
+                w.sc[1] = __float_as_uint(dt[b0 >> 8]);
+                w.sc[2] = __float_as_uint(dt[(b0 + 1) >> 8]);
+            } else {
+                const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 32 + r * 2) * 4);
+                w.sc[0] = v.x;
+                w.sc[1] = v.y;
+            }
+        } else if constexpr (FMT == kQ4_0) {
+            const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 64 + r * 4) * 2);
+            w.sc[0] = v.x;
+            w.sc[1] = v.y;
+        } else {  // NVFP4
+            const uint2 v = *reinterpret_cast<const uint2*>(a.scales + tile * 128 + r * 8);
+            w.sc[0] = v.x;
+            w.sc[1] = v.y;
+        }
+    }
+}
+
+// B operand (bf16 of w^, one rounding) for K slice j of one band.
+template <int FMT, bool DQ>
+__device__ inline u32x4 gemm_dequant(const GemmW<FMT>& w, int j, const uint32_t* lut, uint32_t lane8, int h, float mu) {
+    u32x4 B;
+    if constexpr (FMT == kQ8_0) {
+        const uint4 c = w.code[j >> 1];
+        const uint32_t uw[4] = {c.x, c.y, c.z, c.w};
+        const float d = f16_value((uint16_t)(w.sc[j >> 1] >> (16 * (j & 1))));
+        const float d128 = -128.0f * d;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const uint32_t wv = uw[2 * (j & 1) + (q >> 1)] ^ 0x80808080u;   // q + 128 as unsigned bytes
+            const int sh = 16 * (q & 1);
+            const float f0 = (float)((wv >> sh) & 255u);
+            const float f1 = (float)((wv >> (sh + 8)) & 255u);
+            // (q+128)*d - 128*d == q*d exactly (19 significant bits); one rounding to bf16
+            B[q] = pack_bf16_rne(__builtin_fmaf(f0, d, d128), __builtin_fmaf(f1, d, d128));
+        }
+    } else {
+        const uint32_t word = j == 0 ? w.code[0].x : j == 1 ? w.code[0].y : j == 2 ? w.code[0].z : w.code[0].w;
+        float s;
+        if constexpr (FMT == kNF4) {
+            const int kb = j >> 1;
+            if constexpr (DQ) {
+                s = __fadd_rn(__fmul_rn((float)(int8_t)((w.sc[0] >> (8 * kb)) & 255u), __uint_as_float(w.sc[1 + kb])), mu);
+            } else {
+                s = __uint_as_float(w.sc[kb]);
+            }
+        } else if constexpr (FMT == kQ4_0) {
+            s = f16_value((uint16_t)(w.sc[j >> 1] >> (16 * (j & 1))));
+        } else {  // NVFP4
+            const int blk = 2 * j + (h >> 1);
+            s = e4m3_value((w.sc[blk >> 2] >> (8 * (blk & 3))) & 255u);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            // w^ = fl(code * scale) exactly as the format defines it, then one RNE to bf16
+            const float2 pr = lut_pair_f32(lut, lane8, word, q);
+            B[q] = pack_bf16_rne(__fmul_rn(pr.x, s), __fmul_rn(pr.y, s));
+        }
+    }
+    return B;
+}
+
+template <int FMT, bool DQ>
+__device__ __forceinline__ void gemm_load_w4(GemmW<FMT> (&w)[4], const KArgs& a, const int64_t (&wband)[4], int64_t st,
+                                             int lane, int r, int64_t KT) {
+#pragma unroll
+    for (int nf = 0; nf < 4; nf++) gemm_load_w<FMT, DQ>(w[nf], a, wband[nf], st, lane, r, KT);
+}
+
+// X tile (128 x 128 bf16) global -> LDS without passing through registers.  In
+// LDS, chunk c (16 bytes = 8 k) of tile row t sits at position c ^ (t & 15) of
+// the row, so the 16 lanes of an A-fragment read (16 rows, one chunk) hit 16
+// different bank groups.  Wave w fills rows 32w .. 32w+31, four rows per
+// 64-lane instruction; rows past the matrix re-read its last row (their results
+// are never stored).
+__device__ __forceinline__ void gemm_load_x_lds(uint8_t* xs_buf, const uint16_t* x, int64_t ldx, int64_t m0, int64_t M,
+                                                int wave, int lane, int64_t st) {
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int t = wave * 32 + 4 * i + (lane >> 4);                  // tile row of this lane
+        const int c = (lane & 15) ^ (t & 15);                           // chunk it fetches
+        const int64_t row = std::min<int64_t>(m0 + t, M - 1);
+        const uint16_t* g = x + row * ldx + st * BK + c * 8;
+        __builtin_amdgcn_global_load_lds(g, xs_buf + (wave * 32 + 4 * i) * 256, 16, 0, 0);
+    }
+}
+
+// wait for this wave's outstanding global loads (including LDS-direct ones)
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+
+// One K step: request step st + 1 (clamped: the last step re-reads itself,
+// harmlessly) into wn / xnext, compute step st from wc / xcur, then swap.
+// A fragment (row 16*mf + r, chunk 4j + h) sits at position (4j + h) ^ r.
+template <int FMT, bool DQ>
+__device__ __forceinline__ void gemm_kstep(f32x4 (&acc)[8][4], GemmW<FMT> (&wc)[4], GemmW<FMT> (&wn)[4],
+                                           const KArgs& a, const int64_t (&wband)[4], const uint8_t* xcur,
+                                           uint8_t* xnext, const uint32_t* lut, int64_t st, int64_t s1, int64_t m0,
+                                           int64_t M, int64_t KT, int wave, int lane, int r, int h, uint32_t lane8,
+                                           float mu) {
+    const int64_t nx = std::min<int64_t>(st + 1, s1 - 1);
+    gemm_load_w4<FMT, DQ>(wn, a, wband, nx, lane, r, KT);
+    gemm_load_x_lds(xnext, a.x, a.ldx, m0, M, wave, lane, nx);
+    const uint32_t arow = (uint32_t)r * 256u;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        u32x4 B[4];
+#pragma unroll
+        for (int nf = 0; nf < 4; nf++) B[nf] = gemm_dequant<FMT, DQ>(wc[nf], j, lut, lane8, h, mu);
+        const uint32_t aoff = arow + ((uint32_t)((4 * j + h) ^ r) << 4);
+        u32x4 A[8];
+#pragma unroll
+        for (int mf = 0; mf < 8; mf++) {
+            const uint4 t = *reinterpret_cast<const uint4*>(xcur + mf * 4096 + aoff);
+            A[mf] = u32x4{t.x, t.y, t.z, t.w};
+        }
+#pragma unroll
+        for (int nf = 0; nf < 4; nf++)
+#pragma unroll
+            for (int mf = 0; mf < 8; mf++) acc[mf][nf] = mfma(A[mf], B[nf], acc[mf][nf]);
+        __builtin_amdgcn_sched_barrier(0);   // keep each K slice's operands short-lived
+    }
+#pragma unroll
+    for (int nf = 0; nf < 4; nf++) wc[nf] = wn[nf];
+    wait_vm();
+    __syncthreads();
+}
 
 template <int FMT, bool DQ>
 __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
-    __shared__ uint32_t lut[(FMT == kQ8_0) ? 1 : kLutWords];
-    __shared__ __attribute__((aligned(16))) uint16_t xs[2][BM * XS_STRIDE];
-    __shared__ int s_last;
+    // separate LDS objects for the code table and the two X buffers, so the
+    // LDS-direct loads into one X buffer are never mistaken for writes to the others
+    __shared__ __attribute__((aligned(16))) uint32_t lut_s[(FMT == kQ8_0) ? 4 : kLutWords];
+    __shared__ __attribute__((aligned(16))) uint8_t xs0[kXsBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t xs1[kXsBytes];
+    const uint32_t* lut = lut_s;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15;
     const int h = lane >> 4;
-    const uint32_t lane4 = (uint32_t)lane << 2;
+    const uint32_t lane8 = (uint32_t)(lane & 31) << 3;
     const int64_t M = a.m, N = a.n, K = a.k;
     constexpr int TK = tile_k(FMT);
     const int64_t KT = K / TK;
@@ -370,8 +564,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     // XCD-aware item order: consecutive items (same N tile, neighbouring M tiles
     // and K pieces) run on the same XCD and share its L2.
     const int64_t items = a.tiles_m * a.tiles_n * a.ksplit;
-    const int64_t grid = gridDim.x;
-    const int64_t per_xcd = grid / 8;
+    const int64_t per_xcd = (int64_t)gridDim.x / 8;
     const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (item >= items) return;
     const int ks = (int)(item % a.ksplit);
@@ -381,29 +574,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     const int64_t m0 = tm * BM, n0 = tn * BN;
     const int64_t s0 = ks * a.kt_per, s1 = std::min<int64_t>(nsteps_total, s0 + a.kt_per);  // in BK steps
 
-    if constexpr (FMT != kQ8_0) build_lut_f32<FMT>(lut);
-    const uint32_t lane8 = (uint32_t)(lane & 31) << 3;
+    const int64_t band0 = n0 / 16 + wave * 4;
+    const int64_t nbands = N / 16;
 
     float g = 1.0f, mu = 0.0f;
     if constexpr (FMT == kNVFP4) g = *reinterpret_cast<const float*>(a.scales + a.L.g_off);
     if constexpr (FMT == kNF4 && DQ) mu = *reinterpret_cast<const float*>(a.scales + a.L.mu_off);
 
-    // X tile loader: thread t copies rows (t>>4) + 16*i, 8 columns at (t & 15) * 8
-    const int xr0 = tid >> 4, xc = (tid & 15) * 8;
-    uint4 xreg[8];
-    auto load_x = [&](int64_t step) {
+    int64_t wband[4];
 #pragma unroll
-        for (int i = 0; i < 8; i++) {
-            const int64_t mm = m0 + xr0 + 16 * i;
-            if (mm < M) xreg[i] = *reinterpret_cast<const uint4*>(a.x + mm * a.ldx + step * BK + xc);
-            else xreg[i] = make_uint4(0, 0, 0, 0);
-        }
-    };
-    auto store_x = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 8; i++)
-            *reinterpret_cast<uint4*>(&xs[buf][(xr0 + 16 * i) * XS_STRIDE + xc]) = xreg[i];
-    };
+    for (int nf = 0; nf < 4; nf++) wband[nf] = std::min<int64_t>(band0 + nf, nbands - 1);
 
     f32x4 acc[8][4];
 #pragma unroll
@@ -411,128 +591,39 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int64_t band0 = n0 / 16 + wave * 4;
-    const int64_t nbands = N / 16;
-
-    if (s0 < s1) {
-        load_x(s0);
-        store_x(0);
-    }
+    // every K piece is non-empty (the schedule guarantees s0 < s1)
+    GemmW<FMT> wc[4], wn[4];
+    gemm_load_w4<FMT, DQ>(wc, a, wband, s0, lane, r, KT);
+    gemm_load_x_lds(xs0, a.x, a.ldx, m0, M, wave, lane, s0);
+    if constexpr (FMT != kQ8_0) build_lut_f32<FMT>(lut_s);
+    wait_vm();
     __syncthreads();
 
-    for (int64_t st = s0; st < s1; st++) {
-        const int buf = (int)((st - s0) & 1);
-        const bool more = st + 1 < s1;
-        if (more) load_x(st + 1);
-
-        // ---- dequantize this wave's 4 bands x 128 K into B operands, then MFMA ----
-#pragma unroll
-        for (int nf = 0; nf < 4; nf++) {
-            const int64_t band = band0 + nf;
-            const bool bval = band < nbands;
-            const int64_t rowW = band * 16 + r;
-            u32x4 Bq[4];   // 4 K-slices of 32
-            if (!bval) {
-#pragma unroll
-                for (int j = 0; j < 4; j++) Bq[j] = u32x4{0u, 0u, 0u, 0u};
-            } else if constexpr (FMT == kQ8_0) {
-#pragma unroll
-                for (int half = 0; half < 2; half++) {
-                    const int64_t tile = band * KT + st * 2 + half;
-                    const uint4 u = *reinterpret_cast<const uint4*>(a.codes + tile * kTileBytes + lane * 16);
-                    const uint32_t sc = *reinterpret_cast<const uint32_t*>(a.scales + (tile * 32 + r * 2) * 2);
-                    const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-                    for (int j = 0; j < 2; j++) {
-                        const float d = f16_value((uint16_t)(sc >> (16 * j)));
-                        const float d128 = -128.0f * d;
-#pragma unroll
-                        for (int p = 0; p < 4; p++) {
-                            const uint32_t wv = uw[2 * j + (p >> 1)] ^ 0x80808080u;   // q + 128
-                            const int sh = 16 * (p & 1);
-                            const float f0 = (float)((wv >> sh) & 255u);
-                            const float f1 = (float)((wv >> (sh + 8)) & 255u);
-                            // (q+128)*d - 128*d == q*d exactly (fits 19 bits); one rounding to bf16
-                            Bq[2 * half + j][p] = pack_bf16_rne(__builtin_fmaf(f0, d, d128), __builtin_fmaf(f1, d, d128));
-                        }
-                    }
-                }
-            } else {
-                const int64_t tile = band * KT + st;
-                const uint4 u = *reinterpret_cast<const uint4*>(a.codes + tile * kTileBytes + lane * 16);
-                const uint32_t uw[4] = {u.x, u.y, u.z, u.w};
-                float sj[4];
-                if constexpr (FMT == kNF4) {
-                    float s0_, s1_;
-                    if constexpr (DQ) {
-                        const uint16_t qq = *reinterpret_cast<const uint16_t*>(a.scales + tile * 32 + r * 2);
-                        const int64_t b0 = rowW * (K / 64) + st * 2;
-                        const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
-                        s0_ = __fadd_rn(__fmul_rn((float)(int8_t)(qq & 255), dt[b0 >> 8]), mu);
-                        s1_ = __fadd_rn(__fmul_rn((float)(int8_t)(qq >> 8), dt[(b0 + 1) >> 8]), mu);
-                    } else {
-                        const float2 sc = *reinterpret_cast<const float2*>(a.scales + (tile * 32 + r * 2) * 4);
-                        s0_ = sc.x;
-                        s1_ = sc.y;
-                    }
-                    sj[0] = sj[1] = s0_;
-                    sj[2] = sj[3] = s1_;
-                } else if constexpr (FMT == kQ4_0) {
-                    const uint2 sc = *reinterpret_cast<const uint2*>(a.scales + (tile * 64 + r * 4) * 2);
-                    sj[0] = f16_value((uint16_t)sc.x);
-                    sj[1] = f16_value((uint16_t)(sc.x >> 16));
-                    sj[2] = f16_value((uint16_t)sc.y);
-                    sj[3] = f16_value((uint16_t)(sc.y >> 16));
-                } else {  // NVFP4
-                    const uint2 sc = *reinterpret_cast<const uint2*>(a.scales + tile * 128 + r * 8);
-#pragma unroll
-                    for (int j = 0; j < 4; j++) {
-                        const int blk = 2 * j + (h >> 1);
-                        sj[j] = e4m3_value(((blk < 4 ? sc.x : sc.y) >> (8 * (blk & 3))) & 255u);
-                    }
-                }
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-#pragma unroll
-                    for (int p = 0; p < 4; p++) {
-                        // w^ = fl(code * scale) exactly as the format defines it, then one RNE to bf16
-                        const float2 pr = lut_pair_f32(lut, lane8, uw[j], p);
-                        Bq[j][p] = pack_bf16_rne(__fmul_rn(pr.x, sj[j]), __fmul_rn(pr.y, sj[j]));
-                    }
-                }
-            }
-            // MFMA over the 8 row fragments for this band
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-#pragma unroll
-                for (int mf = 0; mf < 8; mf++) {
-                    const uint4 t = *reinterpret_cast<const uint4*>(&xs[buf][(16 * mf + r) * XS_STRIDE + 32 * j + 8 * h]);
-                    acc[mf][nf] = mfma(u32x4{t.x, t.y, t.z, t.w}, Bq[j], acc[mf][nf]);
-                }
-            }
-        }
-
-        if (more) store_x(buf ^ 1);
-        __syncthreads();
+    // steps alternate X buffers: even steps read xs0 and fill xs1, odd steps the reverse
+    for (int64_t st = s0; st < s1; st += 2) {
+        gemm_kstep<FMT, DQ>(acc, wc, wn, a, wband, xs0, xs1, lut, st, s1, m0, M, KT, wave, lane, r, h, lane8, mu);
+        if (st + 1 < s1)
+            gemm_kstep<FMT, DQ>(acc, wc, wn, a, wband, xs1, xs0, lut, st + 1, s1, m0, M, KT, wave, lane, r, h, lane8, mu);
     }
 
     // ---- epilogue ----
-    const int64_t tile_id = tn * a.tiles_m + tm;
     if (a.ksplit == 1) {
 #pragma unroll
         for (int nf = 0; nf < 4; nf++) {
             const int64_t col = (band0 + nf) * 16 + r;
             if (col >= N) continue;
+            const ColOut c = col_out(a, col);
 #pragma unroll
             for (int mf = 0; mf < 8; mf++)
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
                     const int64_t mm = m0 + 16 * mf + 4 * h + i;
-                    if (mm < M) store_out(a.out, mm, col, finish(a, col, acc[mf][nf][i], g));
+                    if (mm < M) put_out(a, c, mm, acc[mf][nf][i], g);
                 }
         }
         return;
     }
+    // K split: deposit this piece's partial tile; k_splitk_reduce finishes the outputs
 #pragma unroll
     for (int nf = 0; nf < 4; nf++) {
         const int64_t col = (band0 + nf) * 16 + r;
@@ -545,33 +636,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
                 if (mm < M) a.partial[((int64_t)ks * M + mm) * N + col] = acc[mf][nf][i];
             }
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) {
-        const uint32_t old = atomicAdd(&a.counters[tile_id], 1u);
-        s_last = (old == (uint32_t)(a.ksplit - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __threadfence();
+}
+
+// Sum the K pieces' partials of each output in piece order, add the bias,
+// convert and store.  Thread = 4 consecutive columns of one row.  Runs after
+// k_gemm on the same stream, so every partial is complete and visible.
+__global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, int global_scale) {
+    const float g = global_scale ? *reinterpret_cast<const float*>(a.scales + a.L.g_off) : 1.0f;
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t nq = a.n / 4;
+    if (q >= (int64_t)a.m * nq) return;
+    const int64_t mm = q / nq, col0 = (q % nq) * 4;
+    const int64_t pstride = (int64_t)a.m * a.n;
+    const float* p = a.partial + mm * a.n + col0;
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < a.ksplit; s++) v += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + s * pstride));
 #pragma unroll
-    for (int nf = 0; nf < 4; nf++) {
-        const int64_t col = (band0 + nf) * 16 + r;
-        if (col >= N) continue;
-#pragma unroll
-        for (int mf = 0; mf < 8; mf++)
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int64_t mm = m0 + 16 * mf + 4 * h + i;
-                if (mm < M) {
-                    float v = 0.0f;
-                    for (int s2 = 0; s2 < a.ksplit; s2++)
-                        v += __builtin_nontemporal_load(&a.partial[((int64_t)s2 * M + mm) * N + col]);
-                    store_out(a.out, mm, col, finish(a, col, v, g));
-                }
-            }
-    }
-    if (tid == 0) atomicExch(&a.counters[tile_id], 0u);
+    for (int u = 0; u < 4; u++) put_out(a, col_out(a, col0 + u), mm, v[u], g);
 }
 
 // ---------------------------------------------------------------------------
@@ -582,66 +663,42 @@ constexpr int kNumCU = 256;
 struct Sched {
     int ksplit;
     int64_t kt_per;
-    int64_t counters;
     int64_t tiles_m, tiles_n;
     unsigned grid;
 };
 
-static Sched gemv_sched(int fmt, int64_t m, int64_t n, int64_t k, bool allow_split) {
-    Sched s{};
-    const int64_t KT = k / tile_k(fmt);
-    const int64_t nbands = n / 16;
-    int ks = 1;
-    if (allow_split) {
-        // split K until every CU has a workgroup, keeping >= one tile per wave per piece
-        while (nbands * ks < kNumCU && KT / (ks * 2) >= 4) ks *= 2;
-    }
-    s.ksplit = ks;
-    s.kt_per = (KT + ks - 1) / ks;
-    s.counters = nbands;
-    s.tiles_m = 1;
-    s.tiles_n = nbands;
-    const int64_t items = nbands * ks;
-    s.grid = (unsigned)std::min<int64_t>(items, 2 * kNumCU);
-    (void)m;
-    return s;
-}
-
-static Sched gemm_sched(int fmt, int64_t m, int64_t n, int64_t k, bool allow_split) {
-    (void)fmt;
+// GEMM: 128 x 256 tiles; K is split only when the tiles cannot fill half the
+// chip, and then only as far as every piece keeps >= 4 K steps.
+static Sched gemm_sched(int64_t m, int64_t n, int64_t k, bool allow_split) {
     Sched s{};
     s.tiles_m = (m + BM - 1) / BM;
     s.tiles_n = (n + BN - 1) / BN;
     const int64_t steps = k / BK;
     const int64_t tiles = s.tiles_m * s.tiles_n;
     int ks = 1;
-    if (allow_split) {
+    if (allow_split && tiles < kNumCU / 2) {
         while (tiles * ks < kNumCU && steps / (ks * 2) >= 4) ks *= 2;
     }
     s.ksplit = ks;
-    s.kt_per = (steps + ks - 1) / ks;
-    s.counters = tiles;
+    s.kt_per = (steps + ks - 1) / ks;     // every piece non-empty: (ks - 1) * kt_per < steps
     const int64_t items = tiles * ks;
     s.grid = (unsigned)(((items + 7) / 8) * 8);
     return s;
 }
 
-static size_t ws_bytes_for(const Sched& s, int64_t m, int64_t n) {
-    if (s.ksplit <= 1) return 0;
-    return (size_t)align16(256 + 4 * s.counters) + (size_t)s.ksplit * (size_t)m * (size_t)n * 4u;
+size_t gemv_workspace_bytes(int, int64_t, int64_t, int64_t) { return 0; }
+
+size_t gemm_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
+    (void)fmt;
+    const Sched s = gemm_sched(m, n, k, true);
+    return s.ksplit <= 1 ? 0 : (size_t)s.ksplit * (size_t)m * (size_t)n * 4u;
 }
 
-size_t gemv_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
-    return ws_bytes_for(gemv_sched(fmt, m, n, k, true), m, n);
-}
-size_t gemm_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
-    return ws_bytes_for(gemm_sched(fmt, m, n, k, true), m, n);
-}
 size_t matmul_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
     return m <= 16 ? gemv_workspace_bytes(fmt, m, n, k) : gemm_workspace_bytes(fmt, m, n, k);
 }
 
-static KArgs make_args(const MatmulProblem& p, const Sched& s) {
+static KArgs make_args(const MatmulProblem& p) {
     KArgs a{};
     a.x = p.x;
     a.ldx = p.ldx;
@@ -653,40 +710,35 @@ static KArgs make_args(const MatmulProblem& p, const Sched& s) {
     a.bias = p.bias;
     a.out = p.out;
     a.L = scale_layout(p.fmt, p.dq, p.n, p.k);
-    a.ksplit = s.ksplit;
-    a.kt_per = s.kt_per;
-    a.tiles_m = s.tiles_m;
-    a.tiles_n = s.tiles_n;
-    if (s.ksplit > 1) {
-        a.counters = reinterpret_cast<uint32_t*>(p.ws);
-        a.partial = reinterpret_cast<float*>(reinterpret_cast<char*>(p.ws) + align16(256 + 4 * s.counters));
-    }
+    a.ksplit = 1;
     return a;
 }
 
+constexpr int kGemvChunk = 8;   // tiles requested together per wave
+
 template <int FMT, bool DQ>
 static void gemv_dispatch_ni(const KArgs& a, unsigned grid, hipStream_t st) {
+    const dim3 block(64 * kGemvWaves);
     switch (a.m) {
-    case 1: hipLaunchKernelGGL((k_gemv<FMT, DQ, 1>), dim3(grid), dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_gemv<FMT, DQ, 2>), dim3(grid), dim3(256), 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_gemv<FMT, DQ, 3>), dim3(grid), dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((k_gemv<FMT, DQ, 4>), dim3(grid), dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((k_gemv<FMT, DQ, 1, kGemvChunk>), dim3(grid), block, 0, st, a); break;
+    case 2: hipLaunchKernelGGL((k_gemv<FMT, DQ, 2, kGemvChunk>), dim3(grid), block, 0, st, a); break;
+    case 3: hipLaunchKernelGGL((k_gemv<FMT, DQ, 3, kGemvChunk>), dim3(grid), block, 0, st, a); break;
+    default: hipLaunchKernelGGL((k_gemv<FMT, DQ, 4, kGemvChunk>), dim3(grid), block, 0, st, a); break;
     }
 }
 
 hipError_t launch_gemv(const MatmulProblem& p, hipStream_t st) {
-    const size_t need = gemv_workspace_bytes(p.fmt, p.m, p.n, p.k);
-    const bool split = p.ws != nullptr && need > 0 && p.ws_bytes >= need;
-    const Sched s = gemv_sched(p.fmt, p.m, p.n, p.k, split);
-    const KArgs a = make_args(p, s);
+    const KArgs a = make_args(p);
+    // one workgroup per band, at most one resident workgroup per CU (persistent beyond that)
+    const unsigned grid = (unsigned)std::min<int64_t>(p.n / 16, kNumCU);
     switch (p.fmt) {
     case kNF4:
-        if (p.dq) gemv_dispatch_ni<kNF4, true>(a, s.grid, st);
-        else gemv_dispatch_ni<kNF4, false>(a, s.grid, st);
+        if (p.dq) gemv_dispatch_ni<kNF4, true>(a, grid, st);
+        else gemv_dispatch_ni<kNF4, false>(a, grid, st);
         break;
-    case kNVFP4: gemv_dispatch_ni<kNVFP4, false>(a, s.grid, st); break;
-    case kQ4_0: gemv_dispatch_ni<kQ4_0, false>(a, s.grid, st); break;
-    case kQ8_0: gemv_dispatch_ni<kQ8_0, false>(a, s.grid, st); break;
+    case kNVFP4: gemv_dispatch_ni<kNVFP4, false>(a, grid, st); break;
+    case kQ4_0: gemv_dispatch_ni<kQ4_0, false>(a, grid, st); break;
+    case kQ8_0: gemv_dispatch_ni<kQ8_0, false>(a, grid, st); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -695,8 +747,13 @@ hipError_t launch_gemv(const MatmulProblem& p, hipStream_t st) {
 hipError_t launch_gemm(const MatmulProblem& p, hipStream_t st) {
     const size_t need = gemm_workspace_bytes(p.fmt, p.m, p.n, p.k);
     const bool split = p.ws != nullptr && need > 0 && p.ws_bytes >= need;
-    const Sched s = gemm_sched(p.fmt, p.m, p.n, p.k, split);
-    const KArgs a = make_args(p, s);
+    const Sched s = gemm_sched(p.m, p.n, p.k, split);
+    KArgs a = make_args(p);
+    a.ksplit = s.ksplit;
+    a.kt_per = s.kt_per;
+    a.tiles_m = s.tiles_m;
+    a.tiles_n = s.tiles_n;
+    if (s.ksplit > 1) a.partial = reinterpret_cast<float*>(p.ws);
     const dim3 grid(s.grid), block(256);
     switch (p.fmt) {
     case kNF4:
@@ -707,6 +764,11 @@ hipError_t launch_gemm(const MatmulProblem& p, hipStream_t st) {
     case kQ4_0: hipLaunchKernelGGL((k_gemm<kQ4_0, false>), grid, block, 0, st, a); break;
     case kQ8_0: hipLaunchKernelGGL((k_gemm<kQ8_0, false>), grid, block, 0, st, a); break;
     default: return hipErrorInvalidValue;
+    }
+    if (s.ksplit > 1) {
+        const int64_t nthreads = p.m * (p.n / 4);
+        hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, a,
+                           (int)(p.fmt == kNVFP4));
     }
     return hipGetLastError();
 }

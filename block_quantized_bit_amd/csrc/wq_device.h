@@ -43,9 +43,10 @@ __host__ __device__ inline int64_t align16(int64_t v) { return (v + 15) & ~int64
 
 // E4M3 (OCP, FN) value of a non-negative code (sign bit not used by scales).
 __device__ inline float e4m3_value(uint32_t b) {
-    uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    if (e == 0) return (float)m * 0.001953125f;               // m * 2^-9, exact
-    return __uint_as_float(((e + 120u) << 23) | (m << 20));   // (1+m/8) * 2^(e-7)
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    const float sub = (float)m * 0.001953125f;                       // m * 2^-9, exact
+    const float nrm = __uint_as_float(((e + 120u) << 23) | (m << 20)); // (1+m/8) * 2^(e-7)
+    return e == 0u ? sub : nrm;
 }
 
 // Round a non-negative float to E4M3 (nearest, ties to even code), saturating to

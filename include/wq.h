@@ -18,9 +18,22 @@
  *   Q4_0 / Q8_0  32-value blocks with one fp16 scale and signed 4-/8-bit codes
  *          ("Run quantized Whisper on the fused Metal decode path", "Summary" and
  *          "Why the policy").
- * The exact rounding rules, the NF4 levels, the double-quant scheme and the packed
- * tile layout are this library's own definitions (the pages leave them open) and
- * are written out in the design doc of the source tree.
+ * The pages leave the exact rounding rules, the NF4 levels, the double-quant
+ * scheme and the storage layout open; this library fixes them as follows.
+ *   NF4     levels: QLoRA's NormalFloat quantiles (binary64 construction, rounded
+ *           to binary32); code = nearest level to w/absmax (ties to the lower
+ *           level); double-quant: mean of the absmax values (binary64 sum in block
+ *           order), int8 symmetric codes of (absmax - mean) per 256 blocks.
+ *   NVFP4   global scale g = absmax(W)/2688, block scale = E4M3(block absmax /
+ *           (6g)) round-to-nearest-even saturating at 448, codes E2M1 of
+ *           w/(scale*g) nearest, ties to even; w^ = e2m1 * scale * g.
+ *   Q8_0    d = fp16(absmax/127), q = clamp(rint(w/d), -127, 127).
+ *   Q4_0    d = fp16(m/-8) with m the signed element of largest magnitude (first
+ *           on ties), q = clamp(rint(w/d), -8, 7) + 8.
+ *   Layout  codes in 1 KiB tiles of 16 rows x 128 K (64 K for Q8_0), ordered by
+ *           16-row band then K; 16-byte slot s of a tile holds row s%16, and its
+ *           32-bit word j holds k = 32j + 8(s/16) + 0..7 (Q8_0: 8-byte word j);
+ *           scales are grouped per tile in row-major (row, block) order.
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  libwq never
@@ -105,13 +118,12 @@ wq_status wq_quantize(const wq_desc* d, const float* w, wq_packed out, void* str
 wq_status wq_dequantize(const wq_desc* d, wq_packed in, float* w_out, void* stream);
 
 /* Host-only.  Workspace bytes wq_matmul / wq_matmul_qkv can use for an
- * m-row call with descriptor d (split-K partial sums and tile counters).
- * 0 means the call never uses one.  A workspace lets small-N or long-K shapes
- * spread over all compute units; without one (ws == NULL) the call runs a
- * schedule with no K split, which gives results within the same bound.
- * The workspace must be zero-filled by the caller before its first use; every
- * call leaves it zero-filled again.  One workspace must not be shared by calls
- * that may run concurrently (different streams). */
+ * m-row call with descriptor d: fp32 partial sums when the K dimension is split
+ * so that shapes with few output tiles (small n at m >= 17) still spread over
+ * all compute units.  0 means the call never uses one (every m <= 16 call).
+ * Without a workspace (ws == NULL) the call runs with no K split; the result
+ * meets the same bound.  The workspace needs no initialization; one workspace
+ * must not be used by calls that may run concurrently (different streams). */
 wq_status wq_workspace_size(const wq_desc* d, int64_t m, size_t* bytes);
 
 /* Y = X * W^T + bias.
@@ -124,7 +136,7 @@ wq_status wq_workspace_size(const wq_desc* d, int64_t m, size_t* bytes);
  * Accumulation is fp32 over bf16 activations times bf16-rounded (or exact)
  * dequantized weights; per element |y - y_ref| <= 4e-3 * sum_k |x_k * w^_k| + 1e-6
  * against the fp32 reference (plus the final bf16 rounding for WQ_BF16 outputs).
- * m <= 16 runs the split-K GEMV (decode: token-at-a-time, "asr: add a 4-bit nf4
+ * m <= 16 runs the GEMV, K split over the waves of a workgroup (decode: token-at-a-time, "asr: add a 4-bit nf4
  * option for the Whisper engine", "Why NF4 and not the NVFP4 snapshot ..."),
  * m >= 17 the MFMA GEMM (encoder frames, "mbehr90/whisper-large-v3-turbo-nvfp4",
  * "Honest summary: on H100 this is not a win"). */
@@ -132,8 +144,9 @@ wq_status wq_matmul(const wq_desc* d, int64_t m, const uint16_t* x, int64_t ldx,
                     const uint16_t* bias, void* y, int32_t ydt, int64_t ldy,
                     void* ws, size_t ws_bytes, void* stream);
 
-/* Fused projection over a row-concatenated weight W[n0 + n1 (+ n2), k] in ONE
- * launch: columns [0, n0) go to y[0], [n0, n0+n1) to y[1], [n0+n1, n) to y[2],
+/* Fused projection over a row-concatenated weight W[n0 + n1 (+ n2), k] in one
+ * pass over W (one kernel; a K-split GEMM adds one small reduction kernel):
+ * columns [0, n0) go to y[0], [n0, n0+n1) to y[1], [n0+n1, n) to y[2],
  * each with its own leading dimension ldy[i] >= split_n[i], so the destinations
  * may be rows of a K/V cache slab; nothing outside each m x split_n[i] window is
  * touched.  bias is bf16 [n] or NULL (use zeros where a split has none, e.g. the
