@@ -313,8 +313,55 @@ __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const ui
 
 constexpr int kGemvWaves = 8;   // waves per workgroup, all on one band, splitting its K range
 
+// Wave w of a workgroup owns tiles w, w + 8, w + 16, ... of its band's K range:
+// C of them, all requested before any is used.  A band is finished by summing
+// the 8 waves' 16x16 partial tiles in LDS in wave order.
+template <int FMT, bool DQ, int C>
+__device__ __forceinline__ void gemv_load_band(GemvTile<FMT> (&R)[C], const KArgs& a, int64_t band, int64_t c0,
+                                               int wave, int lane, int r, bool mrow, const uint16_t* xrow,
+                                               int64_t KT) {
+#pragma unroll
+    for (int s = 0; s < C; s++) {
+        const int64_t kt = std::min<int64_t>(wave + (c0 + s) * kGemvWaves, KT - 1);
+        gemv_load<FMT, DQ>(R[s], a, band, kt, lane, r, mrow, xrow, KT);
+    }
+}
+
 template <int FMT, bool DQ, int NI, int C>
-__global__ __launch_bounds__(64 * kGemvWaves, 1) void k_gemv(KArgs a) {
+__device__ __forceinline__ void gemv_consume_band(const GemvTile<FMT> (&R)[C], f32x4& acc, int64_t c0, int wave,
+                                                  int64_t KT, const uint32_t* lut, uint32_t lane4, int h, float mu) {
+#pragma unroll
+    for (int s = 0; s < C; s++)
+        if (wave + (c0 + s) * kGemvWaves < KT) gemv_consume<FMT, DQ, NI>(R[s], acc, lut, lane4, h, mu);
+}
+
+__device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kGemvWaves][64], const f32x4& acc,
+                                                 int64_t band, int wave, int lane, float g) {
+    const int r = lane & 15, h = lane >> 4;
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        f32x4 v = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < kGemvWaves; w++) v += red[w][lane];
+        const ColOut c = col_out(a, band * 16 + r);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int mm = 4 * h + i;
+            if (mm < a.m) put_out(a, c, mm, v[i], g);
+        }
+    }
+    __syncthreads();
+}
+
+// PIPE = false: every workgroup owns one band (grid == number of bands), its
+//   tiles come in rounds of C per wave (one round when K <= 8 * C tiles).
+// PIPE = true : workgroups loop over bands; each wave holds all its tiles of a
+//   band in one round (K <= 8 * C tiles) and requests the next band's tiles
+//   before using the current ones.  The prefetch index is clamped to the last
+//   band, so the requests are unconditional.
+template <int FMT, bool DQ, int NI, int C, bool PIPE>
+__global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArgs a) {
     __shared__ uint32_t lut[(FMT == kQ8_0) ? 1 : kLutWords];
     __shared__ f32x4 red[kGemvWaves][64];
 
@@ -331,49 +378,41 @@ __global__ __launch_bounds__(64 * kGemvWaves, 1) void k_gemv(KArgs a) {
     if constexpr (FMT == kNF4 && DQ) mu = *reinterpret_cast<const float*>(a.scales + a.L.mu_off);
     const bool mrow = r < a.m;
     const uint16_t* xrow = a.x + (int64_t)(mrow ? r : 0) * a.ldx + h * 8;
-
-    // wave w takes tiles w, w + W, w + 2W, ... of the band, C of them per round
     const int64_t per_wave = (KT + kGemvWaves - 1) / kGemvWaves;
-    bool first = true;
-    for (int64_t band = blockIdx.x; band < nbands; band += gridDim.x) {
+
+    if constexpr (!PIPE) {
+        const int64_t band = blockIdx.x;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int64_t c0 = 0; c0 < per_wave; c0 += C) {
             GemvTile<FMT> R[C];
-#pragma unroll
-            for (int s = 0; s < C; s++) {
-                const int64_t kt = std::min<int64_t>(wave + (c0 + s) * kGemvWaves, KT - 1);
-                gemv_load<FMT, DQ>(R[s], a, band, kt, lane, r, mrow, xrow, KT);
-            }
-            if (first) {   // build the code table while the first tiles are in flight
+            gemv_load_band<FMT, DQ, C>(R, a, band, c0, wave, lane, r, mrow, xrow, KT);
+            if (c0 == 0) {   // build the code table while the first tiles are in flight
                 if constexpr (FMT != kQ8_0) build_lut<FMT>(lut);
                 __syncthreads();
-                first = false;
             }
-#pragma unroll
-            for (int s = 0; s < C; s++)
-                if (wave + (c0 + s) * kGemvWaves < KT) gemv_consume<FMT, DQ, NI>(R[s], acc, lut, lane4, h, mu);
+            gemv_consume_band<FMT, DQ, NI, C>(R, acc, c0, wave, KT, lut, lane4, h, mu);
         }
-        if (first) {
-            if constexpr (FMT != kQ8_0) build_lut<FMT>(lut);
-            __syncthreads();
-            first = false;
-        }
-        // reduce the waves' partial tiles in a fixed order; wave 0 stores
-        red[wave][lane] = acc;
+        gemv_finish_band(a, red, acc, band, wave, lane, g);
+    } else {
+        const int64_t stride = gridDim.x;
+        GemvTile<FMT> R0[C], R1[C];
+        int64_t band = blockIdx.x;
+        gemv_load_band<FMT, DQ, C>(R0, a, band, 0, wave, lane, r, mrow, xrow, KT);
+        if constexpr (FMT != kQ8_0) build_lut<FMT>(lut);
         __syncthreads();
-        if (wave == 0) {
-            f32x4 v = red[0][lane];
-#pragma unroll
-            for (int w = 1; w < kGemvWaves; w++) v += red[w][lane];
-            const int64_t col = band * 16 + r;
-            const ColOut c = col_out(a, col);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int mm = 4 * h + i;
-                if (mm < a.m) put_out(a, c, mm, v[i], g);
-            }
+        for (; band < nbands; band += 2 * stride) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            gemv_load_band<FMT, DQ, C>(R1, a, std::min<int64_t>(band + stride, nbands - 1), 0, wave, lane, r, mrow,
+                                      xrow, KT);
+            gemv_consume_band<FMT, DQ, NI, C>(R0, acc, 0, wave, KT, lut, lane4, h, mu);
+            gemv_finish_band(a, red, acc, band, wave, lane, g);
+            if (band + stride >= nbands) break;
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            gemv_load_band<FMT, DQ, C>(R0, a, std::min<int64_t>(band + 2 * stride, nbands - 1), 0, wave, lane, r,
+                                      mrow, xrow, KT);
+            gemv_consume_band<FMT, DQ, NI, C>(R1, acc, 0, wave, KT, lut, lane4, h, mu);
+            gemv_finish_band(a, red, acc, band + stride, wave, lane, g);
         }
-        __syncthreads();
     }
 }
 
@@ -714,31 +753,57 @@ static KArgs make_args(const MatmulProblem& p) {
     return a;
 }
 
-constexpr int kGemvChunk = 8;   // tiles requested together per wave
+// Tiles per wave per round: the smallest offered count covering the band's K
+// range in one round (K <= 64 tiles), else rounds of 8.
+static int gemv_chunk(int64_t KT) {
+    const int64_t pw = (KT + kGemvWaves - 1) / kGemvWaves;
+    return pw <= 1 ? 1 : pw <= 2 ? 2 : pw <= 4 ? 4 : pw <= 5 ? 5 : 8;
+}
+
+template <int FMT, bool DQ, int NI, int C>
+static void gemv_launch_c(const KArgs& a, int64_t nbands, int64_t KT, hipStream_t st) {
+    const dim3 block(64 * kGemvWaves);
+    // band pipelining only where its two register sets fit without spilling (C <= 2)
+    if constexpr (C <= 2) {
+        const int64_t resident = kNumCU;
+        if (nbands > resident && (KT + kGemvWaves - 1) / kGemvWaves <= C) {
+            hipLaunchKernelGGL((k_gemv<FMT, DQ, NI, C, true>), dim3((unsigned)resident), block, 0, st, a);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((k_gemv<FMT, DQ, NI, C, false>), dim3((unsigned)nbands), block, 0, st, a);
+}
+
+template <int FMT, bool DQ, int NI>
+static void gemv_launch_ni(const KArgs& a, hipStream_t st) {
+    const int64_t KT = a.k / tile_k(FMT);
+    const int64_t nbands = a.n / 16;
+    switch (gemv_chunk(KT)) {
+    case 1: gemv_launch_c<FMT, DQ, NI, 1>(a, nbands, KT, st); break;
+    case 2: gemv_launch_c<FMT, DQ, NI, 2>(a, nbands, KT, st); break;
+    case 4: gemv_launch_c<FMT, DQ, NI, 4>(a, nbands, KT, st); break;
+    case 5: gemv_launch_c<FMT, DQ, NI, 5>(a, nbands, KT, st); break;
+    default: gemv_launch_c<FMT, DQ, NI, 8>(a, nbands, KT, st); break;
+    }
+}
 
 template <int FMT, bool DQ>
-static void gemv_dispatch_ni(const KArgs& a, unsigned grid, hipStream_t st) {
-    const dim3 block(64 * kGemvWaves);
-    switch (a.m) {
-    case 1: hipLaunchKernelGGL((k_gemv<FMT, DQ, 1, kGemvChunk>), dim3(grid), block, 0, st, a); break;
-    case 2: hipLaunchKernelGGL((k_gemv<FMT, DQ, 2, kGemvChunk>), dim3(grid), block, 0, st, a); break;
-    case 3: hipLaunchKernelGGL((k_gemv<FMT, DQ, 3, kGemvChunk>), dim3(grid), block, 0, st, a); break;
-    default: hipLaunchKernelGGL((k_gemv<FMT, DQ, 4, kGemvChunk>), dim3(grid), block, 0, st, a); break;
-    }
+static void gemv_dispatch_ni(const KArgs& a, hipStream_t st) {
+    // one token updates one accumulator row per lane; more tokens update all four
+    if (a.m == 1) gemv_launch_ni<FMT, DQ, 1>(a, st);
+    else gemv_launch_ni<FMT, DQ, 4>(a, st);
 }
 
 hipError_t launch_gemv(const MatmulProblem& p, hipStream_t st) {
     const KArgs a = make_args(p);
-    // one workgroup per band, at most one resident workgroup per CU (persistent beyond that)
-    const unsigned grid = (unsigned)std::min<int64_t>(p.n / 16, kNumCU);
     switch (p.fmt) {
     case kNF4:
-        if (p.dq) gemv_dispatch_ni<kNF4, true>(a, grid, st);
-        else gemv_dispatch_ni<kNF4, false>(a, grid, st);
+        if (p.dq) gemv_dispatch_ni<kNF4, true>(a, st);
+        else gemv_dispatch_ni<kNF4, false>(a, st);
         break;
-    case kNVFP4: gemv_dispatch_ni<kNVFP4, false>(a, grid, st); break;
-    case kQ4_0: gemv_dispatch_ni<kQ4_0, false>(a, grid, st); break;
-    case kQ8_0: gemv_dispatch_ni<kQ8_0, false>(a, grid, st); break;
+    case kNVFP4: gemv_dispatch_ni<kNVFP4, false>(a, st); break;
+    case kQ4_0: gemv_dispatch_ni<kQ4_0, false>(a, st); break;
+    case kQ8_0: gemv_dispatch_ni<kQ8_0, false>(a, st); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
