@@ -164,6 +164,23 @@ __device__ inline ColOut col_out(const KArgs& a, int64_t col) {
     return c;
 }
 
+__device__ inline ColOut col_out_nobias(const KArgs& a, int64_t col) {
+    const OutSplit& o = a.out;
+    const bool s1 = col >= o.end[0], s2 = col >= o.end[1];
+    char* const y0 = reinterpret_cast<char*>(o.y[0]);
+    char* const y1 = reinterpret_cast<char*>(o.y[1]);
+    char* const y2 = reinterpret_cast<char*>(o.y[2]);
+    char* const base = s2 ? y2 : (s1 ? y1 : y0);
+    const int64_t ld = s2 ? o.ldy[2] : (s1 ? o.ldy[1] : o.ldy[0]);
+    const int64_t c0 = s2 ? o.end[1] : (s1 ? o.end[0] : 0);
+    const int64_t es = o.f32 ? 4 : 2;
+    ColOut c;
+    c.p = base + (col - c0) * es;
+    c.ld = ld * es;
+    c.bias = 0.0f;
+    return c;
+}
+
 // y = acc * g + bias, converted and stored at row m.
 __device__ inline void put_out(const KArgs& a, const ColOut& c, int64_t m, float v, float g) {
     const float r = v * g + c.bias;
@@ -413,6 +430,159 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
             gemv_consume_band<FMT, DQ, NI, C>(R1, acc, 0, wave, KT, lut, lane4, h, mu);
             gemv_finish_band(a, red, acc, band + stride, wave, lane, g);
         }
+    }
+}
+
+// ===========================================================================
+// Streaming GEMV (many more bands than workgroups, short K, small X): each wave
+// owns whole bands, so there is no cross-wave reduction and no barrier in the
+// loop.  A band's T tiles are requested one band ahead into the other of two
+// register sets.  Loads are buffer loads whose base is the band's first tile
+// (wave-uniform, scalar arithmetic) with a per-lane offset fixed for the whole
+// kernel, so addressing costs no vector instructions; the descriptor covers
+// exactly the band's K tiles, so slots s >= K/tile_k read zeros (the buffer
+// range check) and take their A operand from a zero row.  X is staged once per
+// workgroup in LDS and read there as the MFMA A operand; the double-quant
+// group scales of a lane's row are fetched once per band (a row of <= 10 tiles
+// spans at most two 256-block groups).
+// ===========================================================================
+constexpr int kStreamXMax = 8192 - 128;   // bf16 elements of X staged in LDS (m * k), then 128 zeros
+constexpr int kBufWord3 = 0x00020000;   // buffer descriptor word 3: raw, untyped access
+
+typedef __amdgpu_buffer_rsrc_t BufRes;
+
+__device__ inline BufRes buf_res(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+
+// Scale bytes per tile and per lane (one row of the tile) in the packed layout.
+template <int FMT, bool DQ>
+__device__ constexpr int tile_scale_bytes() {
+    return FMT == kQ8_0 ? 64 : (FMT == kNF4 && DQ) ? 32 : 128;
+}
+
+struct StreamTile {
+    u32x4 code;
+    uint32_t sc[2];
+};
+
+struct StreamBand {
+    uint32_t braw;     // bias (bf16 bits) of this lane's column
+    float dA, dB;      // double quant: group scales of the first / last block of the lane's row
+    int32_t jt;        // double quant: blocks of the row that belong to group A
+};
+
+template <int FMT, bool DQ, int T>
+__device__ __forceinline__ void stream_load_band(StreamTile (&R)[T], StreamBand& B, const KArgs& a, int64_t band,
+                                                 int lane, int r, int64_t KT) {
+    constexpr int SB = tile_scale_bytes<FMT, DQ>();
+    const BufRes rc = buf_res(a.codes + band * KT * kTileBytes, (uint32_t)(KT * kTileBytes));
+    const BufRes rs = buf_res(a.scales + band * KT * SB, (uint32_t)(KT * SB));
+#pragma unroll
+    for (int s = 0; s < T; s++) {
+        R[s].code = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16 + s * kTileBytes, 0, 0));
+        if constexpr (FMT == kNF4 && DQ) {
+            R[s].sc[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, r * 2 + s * SB, 0, 0);
+        } else if constexpr (FMT == kQ8_0) {
+            R[s].sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, r * 4 + s * SB, 0, 0);
+        } else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, r * 8 + s * SB, 0, 0);
+            R[s].sc[0] = v[0];
+            R[s].sc[1] = v[1];
+        }
+    }
+    const int64_t col = band * 16 + r;
+    B.braw = a.bias ? (uint32_t)a.bias[col] : 0u;
+    if constexpr (FMT == kNF4 && DQ) {
+        const int64_t nbr = a.k / 64;                 // blocks per row
+        const int64_t b0 = col * nbr;                 // first block of the row
+        const int64_t gA = b0 >> 8, gB = (b0 + nbr - 1) >> 8;
+        const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
+        B.dA = dt[gA];
+        B.dB = dt[gB];
+        B.jt = (int32_t)((gA + 1) * 256 - b0);
+    }
+}
+
+template <int FMT, bool DQ, int NI, int T>
+__device__ __forceinline__ void stream_band(const StreamTile (&R)[T], const StreamBand& B, const KArgs& a,
+                                            int64_t band, const uint16_t* xrow, const uint16_t* xzero, int h,
+                                            uint32_t lane4, const uint32_t* lut, float mu, float g, int64_t KT) {
+    constexpr int TK = tile_k(FMT);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < T; s++) {
+        {
+            GemvTile<FMT> t;
+            t.code = make_uint4(R[s].code[0], R[s].code[1], R[s].code[2], R[s].code[3]);
+            t.sc[0] = R[s].sc[0];
+            t.sc[1] = R[s].sc[1];
+            if constexpr (FMT == kNF4 && DQ) {
+                t.sc[1] = __float_as_uint(2 * s < B.jt ? B.dA : B.dB);
+                t.sc[2] = __float_as_uint(2 * s + 1 < B.jt ? B.dA : B.dB);
+            }
+            // rows r >= m read row 0: their products only reach output rows that are never stored
+            const uint16_t* xp = s < KT ? xrow + s * TK : xzero;
+#pragma unroll
+            for (int j = 0; j < TK / 32; j++) {
+                const uint4 v = *reinterpret_cast<const uint4*>(xp + 32 * j);
+                t.A[j] = u32x4{v.x, v.y, v.z, v.w};
+            }
+            gemv_consume<FMT, DQ, NI>(t, acc, lut, lane4, h, mu);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep tiles in order: bounded register use
+    }
+    // lane (h, r) holds rows 4h .. 4h+3 of column band * 16 + r
+    ColOut c = col_out_nobias(a, band * 16 + (__lane_id() & 15));
+    c.bias = bf16_value((uint16_t)B.braw);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int mm = 4 * h + i;
+        if (mm < a.m) put_out(a, c, mm, acc[i], g);
+    }
+}
+
+template <int FMT, bool DQ, int NI, int T>
+__global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
+    __shared__ uint32_t lut[(FMT == kQ8_0) ? 1 : kLutWords];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kStreamXMax + 128];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15;
+    const int h = lane >> 4;
+    const uint32_t lane4 = (uint32_t)lane << 2;
+    const int64_t KT = a.k / tile_k(FMT);
+    const int64_t nbands = a.n / 16;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+
+    float g = 1.0f, mu = 0.0f;
+    if constexpr (FMT == kNVFP4) g = *reinterpret_cast<const float*>(a.scales + a.L.g_off);
+    if constexpr (FMT == kNF4 && DQ) mu = *reinterpret_cast<const float*>(a.scales + a.L.mu_off);
+
+    int64_t band = (int64_t)blockIdx.x * 4 + wave;
+    StreamTile R0[T], R1[T];
+    StreamBand B0, B1;
+    stream_load_band<FMT, DQ, T>(R0, B0, a, std::min<int64_t>(band, nbands - 1), lane, r, KT);
+    // stage X (m rows of k bf16, rows contiguous in LDS) and the zero row
+    if (tid < 16) *reinterpret_cast<uint4*>(xs + kStreamXMax + tid * 8) = make_uint4(0u, 0u, 0u, 0u);
+    const int64_t nx = (int64_t)a.m * a.k;
+    for (int64_t i = (int64_t)tid * 8; i < nx; i += 256 * 8) {
+        const int64_t row = i / a.k, col = i - row * a.k;
+        *reinterpret_cast<uint4*>(xs + i) = *reinterpret_cast<const uint4*>(a.x + row * a.ldx + col);
+    }
+    if constexpr (FMT != kQ8_0) build_lut<FMT>(lut);
+    __syncthreads();
+    const uint16_t* xrow = xs + (r < a.m ? r : 0) * a.k + h * 8;
+    const uint16_t* xzero = xs + kStreamXMax + h * 8;
+
+    for (; band < nbands; band += 2 * stride) {
+        stream_load_band<FMT, DQ, T>(R1, B1, a, std::min<int64_t>(band + stride, nbands - 1), lane, r, KT);
+        stream_band<FMT, DQ, NI, T>(R0, B0, a, band, xrow, xzero, h, lane4, lut, mu, g, KT);
+        if (band + stride >= nbands) break;
+        stream_load_band<FMT, DQ, T>(R0, B0, a, std::min<int64_t>(band + 2 * stride, nbands - 1), lane, r, KT);
+        stream_band<FMT, DQ, NI, T>(R1, B1, a, band + stride, xrow, xzero, h, lane4, lut, mu, g, KT);
     }
 }
 
@@ -698,6 +868,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, int global_scale
 // Schedules and launchers.
 // ---------------------------------------------------------------------------
 constexpr int kNumCU = 256;
+constexpr int64_t kStreamMinBands = 4 * 2 * 4 * kNumCU;   // bands per wave x waves
 
 struct Sched {
     int ksplit;
@@ -778,6 +949,14 @@ template <int FMT, bool DQ, int NI>
 static void gemv_launch_ni(const KArgs& a, hipStream_t st) {
     const int64_t KT = a.k / tile_k(FMT);
     const int64_t nbands = a.n / 16;
+    // Many more bands than resident waves, K <= 10 tiles, X fits in LDS: the
+    // streaming kernel (two workgroups of 4 waves per CU, each wave >= 4 bands).
+    if (nbands >= kStreamMinBands && (int64_t)a.m * a.k <= kStreamXMax && KT <= 10) {
+        const unsigned grid = 2 * kNumCU;
+        if (KT <= 4) hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 4>), dim3(grid), dim3(256), 0, st, a);
+        else hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 10>), dim3(grid), dim3(256), 0, st, a);
+        return;
+    }
     switch (gemv_chunk(KT)) {
     case 1: gemv_launch_c<FMT, DQ, NI, 1>(a, nbands, KT, st); break;
     case 2: gemv_launch_c<FMT, DQ, NI, 2>(a, nbands, KT, st); break;

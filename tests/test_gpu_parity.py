@@ -7,7 +7,7 @@ import pytest
 import torch
 
 from block_quantized_bit_amd import wq
-from block_quantized_bit_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits, linear_case
+from block_quantized_bit_amd.inputs import bf16_bits_to_f32, f32_to_bf16_bits, gen_x, linear_case
 
 from gpu_helpers import (abs_dot, check_bound, dev_bf16, gpu_dequantize, gpu_matmul, gpu_quantize,
                          require_gpu, say, workspace, DEV, NAMES)
@@ -134,6 +134,62 @@ def test_decoder_gemv_set_full(orc, m):
         say("decoder gemv", n, k, m)
         y = gpu_matmul(d, codes, scales, x, b)
         check_bound(y, orc.matmul(x, ref["w_hat"], b), abs_dot(x, ref["w_hat"]), what=f"dec {n}x{k} m={m}")
+
+
+# N = 131072 is 8192 16-row bands: enough that each of the 2048 resident waves
+# owns >= 4 bands, which selects the many-band streaming GEMV (same kernel and
+# grid as the 655360-row streaming measurement).  Every output is checked.
+STREAM_N = 131072
+
+
+@pytest.mark.parametrize("fmt,dq,k,m,use_bias,ydt", [
+    (NF4, True, 1280, 1, True, wq.WQ_F32),       # fc1 geometry, K = 10 tiles
+    (NVFP4, False, 384, 3, True, wq.WQ_BF16),    # K = 3 tiles (the 4-tile variant: slot 3 reads zeros)
+    (Q8_0, False, 256, 2, False, wq.WQ_F32),     # K = 4 tiles of 64
+    (Q4_0, False, 640, 5, True, wq.WQ_F32),      # K = 5 tiles (the 10-tile variant)
+    (NF4, False, 512, 15, True, wq.WQ_F32),      # m * k = 7680, near the most X the kernel stages
+    (NF4, False, 384, 16, True, wq.WQ_BF16),     # all 16 rows, K = 3 tiles
+], ids=["nf4dq-k1280-m1", "nvfp4-k384-m3", "q8_0-k256-m2", "q4_0-k640-m5", "nf4-k512-m15", "nf4-k384-m16"])
+def test_streaming_gemv_many_bands(orc, fmt, dq, k, m, use_bias, ydt):
+    d, codes, scales, ref, b = quantized(orc, fmt, dq, 6000 + k, STREAM_N, k, outlier_frac=0.001)
+    x = gen_x(np.random.default_rng(6100 + k), m, k)
+    b = b if use_bias else None
+    say("streaming gemv", NAMES[fmt], "dq" if dq else "", STREAM_N, k, m)
+    y = gpu_matmul(d, codes, scales, x, b, ydt=ydt, ldy_pad=16)
+    check_bound(y, orc.matmul(x, ref["w_hat"], b), abs_dot(x, ref["w_hat"]), bf16_out=ydt == wq.WQ_BF16,
+                what=f"stream {NAMES[fmt]} k={k} m={m}")
+
+
+def test_streaming_gemv_qkv_split(orc):
+    """The streaming kernel's per-column split selection: three strided windows,
+    each equal to the single-output call's columns, nothing else written."""
+    k, m = 1280, 1
+    d, codes, scales, ref, b = quantized(orc, NF4, True, 6000 + k, STREAM_N, k, outlier_frac=0.001)
+    x = gen_x(np.random.default_rng(6100 + k), m, k)
+    splits = [65536, 32768, 32768]
+    X, B = dev_bf16(x), dev_bf16(b)
+    canary = 0x7BAD
+    slabs, ys, ldys = [], [], []
+    for i, s in enumerate(splits):
+        ld = s + 64
+        slab = torch.full((m + 2, ld), canary, dtype=torch.int16, device=DEV)
+        slabs.append(slab)
+        ys.append(slab[1:].data_ptr() + 2 * 16)
+        ldys.append(ld)
+    say("streaming qkv", splits)
+    wq.wq_matmul_qkv(d, m, X, k, codes, scales, B, splits, ys, ldys, wq.WQ_BF16, None, 0)
+    Y = torch.empty((m, STREAM_N), dtype=torch.int16, device=DEV)
+    wq.wq_matmul(d, m, X, k, codes, scales, B, Y, wq.WQ_BF16, STREAM_N, None, 0)
+    torch.cuda.synchronize()
+    yfull = Y.cpu().numpy()
+    c0 = 0
+    for i, s in enumerate(splits):
+        sl = slabs[i].cpu().numpy()
+        assert np.array_equal(sl[1:1 + m, 16:16 + s], yfull[:, c0:c0 + s]), f"split {i} differs"
+        mask = np.ones_like(sl, bool)
+        mask[1:1 + m, 16:16 + s] = False
+        assert np.all(sl[mask] == canary), f"split {i}: writes outside its window"
+        c0 += s
 
 
 def _sample_rows(m, seed):
