@@ -56,11 +56,29 @@ struct KArgs {
     int64_t tiles_m, tiles_n;
 };
 
+// NF4 level of code c as a 16-way select over literals.  Table fills use these
+// rather than indexing the level arrays: a per-lane index would turn into a
+// vector memory load, and waiting for it would also wait for every weight load
+// already in flight.
+__device__ inline uint32_t nf4_level_bf16_sel(uint32_t c) {
+    uint32_t v = kNf4LevelBf16[0];
+#pragma unroll
+    for (uint32_t i = 1; i < 16; i++) v = ((c & 15u) == i) ? (uint32_t)kNf4LevelBf16[i] : v;
+    return v;
+}
+
+__device__ inline float nf4_level_sel(uint32_t c) {
+    uint32_t v = kNf4LevelBits[0];
+#pragma unroll
+    for (uint32_t i = 1; i < 16; i++) v = ((c & 15u) == i) ? kNf4LevelBits[i] : v;
+    return __uint_as_float(v);
+}
+
 // bf16 image of a 4-bit code's value (before any block scale).
 template <int FMT>
 __device__ inline uint32_t code_bf16(uint32_t c) {
     if constexpr (FMT == kNF4) {
-        return kNf4LevelBf16[c & 15u];
+        return nf4_level_bf16_sel(c);
     } else if constexpr (FMT == kQ4_0) {
         return __float_as_uint((float)((int)(c & 15u) - 8)) >> 16;          // exact
     } else {  // NVFP4
@@ -70,16 +88,25 @@ __device__ inline uint32_t code_bf16(uint32_t c) {
     }
 }
 
-// Fill the replicated byte table: word (e * 64 + slot) = bf16(lo nibble) | bf16(hi nibble) << 16.
-template <int FMT>
+// Fill the replicated byte table: word (e * 64 + slot) = bf16(lo nibble) | bf16(hi nibble) << 16,
+// e = 16 * hi + lo.  Thread t (of NT = 256 or 512) owns 4 slots of entries with
+// lo = (t >> 4) & 15 and hi = t >> 8 (mod NT / 256): the lo value is looked up
+// once, the hi value is the same for a whole wave.
+template <int FMT, int NT>
 __device__ inline void build_lut(uint32_t* lut) {
-    const int t = threadIdx.x;             // 256 threads
+    static_assert(NT == 256 || NT == 512, "table fill for blocks of 256 or 512 threads");
+    const int t = threadIdx.x;
     const int slot4 = (t & 15) * 4;
-#pragma unroll 4
-    for (int e0 = 0; e0 < 256; e0 += 16) {
-        const int e = e0 + (t >> 4);
-        const uint32_t v = code_bf16<FMT>(e & 15) | (code_bf16<FMT>(e >> 4) << 16);
-        *reinterpret_cast<uint4*>(lut + e * 64 + slot4) = make_uint4(v, v, v, v);
+    const uint32_t lo = (t >> 4) & 15;
+    const uint32_t vlo = code_bf16<FMT>(lo);
+    const uint32_t hsub = __builtin_amdgcn_readfirstlane(t >> 8);
+#pragma unroll
+    for (uint32_t h0 = 0; h0 < 16; h0 += NT / 256) {
+        const uint32_t hi = h0 + hsub;
+        uint32_t vhi = code_bf16<FMT>(h0);
+        if constexpr (NT == 512) vhi = hsub ? code_bf16<FMT>(h0 + 1) : vhi;
+        const uint32_t v = vlo | (vhi << 16);
+        *reinterpret_cast<uint4*>(lut + (hi * 16 + lo) * 64 + slot4) = make_uint4(v, v, v, v);
     }
 }
 
@@ -94,7 +121,7 @@ __device__ inline uint32_t lut_pair(const uint32_t* lut, uint32_t lane4, uint32_
 template <int FMT>
 __device__ inline float code_f32(uint32_t c) {
     if constexpr (FMT == kNF4) {
-        return nf4_level(c);
+        return nf4_level_sel(c);
     } else if constexpr (FMT == kQ4_0) {
         return (float)((int)(c & 15u) - 8);
     } else {  // NVFP4
@@ -107,13 +134,13 @@ __device__ inline float code_f32(uint32_t c) {
 // lane copies: pair (e, slot) at byte offset e * 256 + slot * 8.
 template <int FMT>
 __device__ inline void build_lut_f32(uint32_t* lut) {
-    const int t = threadIdx.x;             // 256 threads
+    const int t = threadIdx.x;             // 256 threads: entry 16 * hi + lo with lo = t >> 4
     const int slot = (t & 15) * 2;
-#pragma unroll 4
-    for (int e0 = 0; e0 < 256; e0 += 16) {
-        const int e = e0 + (t >> 4);
-        const uint32_t lo = __float_as_uint(code_f32<FMT>(e & 15)), hi = __float_as_uint(code_f32<FMT>(e >> 4));
-        *reinterpret_cast<uint4*>(lut + e * 64 + slot * 2) = make_uint4(lo, hi, lo, hi);
+    const uint32_t lo = __float_as_uint(code_f32<FMT>((uint32_t)t >> 4));
+#pragma unroll
+    for (uint32_t e0 = 0; e0 < 256; e0 += 16) {
+        const uint32_t hi = __float_as_uint(code_f32<FMT>(e0 >> 4));
+        *reinterpret_cast<uint4*>(lut + (e0 + (t >> 4)) * 64 + slot * 2) = make_uint4(lo, hi, lo, hi);
     }
 }
 
@@ -219,7 +246,7 @@ struct GemvTile {
 
 template <int FMT, bool DQ>
 __device__ inline void gemv_load(GemvTile<FMT>& t, const KArgs& a, int64_t band, int64_t kt, int lane, int r,
-                                 bool mrow, const uint16_t* xrow, int64_t KT) {
+                                 const uint16_t* xrow, int64_t KT) {
     constexpr int TK = tile_k(FMT);
     const int64_t tile = band * KT + kt;
     t.code = *reinterpret_cast<const uint4*>(a.codes + tile * kTileBytes + lane * 16);
@@ -246,11 +273,11 @@ __device__ inline void gemv_load(GemvTile<FMT>& t, const KArgs& a, int64_t band,
     } else {
         t.sc[0] = *reinterpret_cast<const uint32_t*>(a.scales + (tile * 32 + r * 2) * 2);
     }
-    // rows r >= m read row 0 (always valid); their products land in output rows that are never stored
+    // rows r >= m read row 0 (always valid); their products only reach output rows that are never stored
 #pragma unroll
     for (int j = 0; j < TK / 32; j++) {
         const uint4 v = *reinterpret_cast<const uint4*>(xrow + kt * TK + 32 * j);
-        t.A[j] = mrow ? u32x4{v.x, v.y, v.z, v.w} : u32x4{0u, 0u, 0u, 0u};
+        t.A[j] = u32x4{v.x, v.y, v.z, v.w};
     }
 }
 
@@ -335,12 +362,12 @@ constexpr int kGemvWaves = 8;   // waves per workgroup, all on one band, splitti
 // the 8 waves' 16x16 partial tiles in LDS in wave order.
 template <int FMT, bool DQ, int C>
 __device__ __forceinline__ void gemv_load_band(GemvTile<FMT> (&R)[C], const KArgs& a, int64_t band, int64_t c0,
-                                               int wave, int lane, int r, bool mrow, const uint16_t* xrow,
+                                               int wave, int lane, int r, const uint16_t* xrow,
                                                int64_t KT) {
 #pragma unroll
     for (int s = 0; s < C; s++) {
         const int64_t kt = std::min<int64_t>(wave + (c0 + s) * kGemvWaves, KT - 1);
-        gemv_load<FMT, DQ>(R[s], a, band, kt, lane, r, mrow, xrow, KT);
+        gemv_load<FMT, DQ>(R[s], a, band, kt, lane, r, xrow, KT);
     }
 }
 
@@ -393,8 +420,7 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
     float g = 1.0f, mu = 0.0f;
     if constexpr (FMT == kNVFP4) g = *reinterpret_cast<const float*>(a.scales + a.L.g_off);
     if constexpr (FMT == kNF4 && DQ) mu = *reinterpret_cast<const float*>(a.scales + a.L.mu_off);
-    const bool mrow = r < a.m;
-    const uint16_t* xrow = a.x + (int64_t)(mrow ? r : 0) * a.ldx + h * 8;
+    const uint16_t* xrow = a.x + (int64_t)(r < a.m ? r : 0) * a.ldx + h * 8;
     const int64_t per_wave = (KT + kGemvWaves - 1) / kGemvWaves;
 
     if constexpr (!PIPE) {
@@ -402,9 +428,9 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int64_t c0 = 0; c0 < per_wave; c0 += C) {
             GemvTile<FMT> R[C];
-            gemv_load_band<FMT, DQ, C>(R, a, band, c0, wave, lane, r, mrow, xrow, KT);
+            gemv_load_band<FMT, DQ, C>(R, a, band, c0, wave, lane, r, xrow, KT);
             if (c0 == 0) {   // build the code table while the first tiles are in flight
-                if constexpr (FMT != kQ8_0) build_lut<FMT>(lut);
+                if constexpr (FMT != kQ8_0) build_lut<FMT, 64 * kGemvWaves>(lut);
                 __syncthreads();
             }
             gemv_consume_band<FMT, DQ, NI, C>(R, acc, c0, wave, KT, lut, lane4, h, mu);
@@ -414,19 +440,19 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
         const int64_t stride = gridDim.x;
         GemvTile<FMT> R0[C], R1[C];
         int64_t band = blockIdx.x;
-        gemv_load_band<FMT, DQ, C>(R0, a, band, 0, wave, lane, r, mrow, xrow, KT);
-        if constexpr (FMT != kQ8_0) build_lut<FMT>(lut);
+        gemv_load_band<FMT, DQ, C>(R0, a, band, 0, wave, lane, r, xrow, KT);
+        if constexpr (FMT != kQ8_0) build_lut<FMT, 64 * kGemvWaves>(lut);
         __syncthreads();
         for (; band < nbands; band += 2 * stride) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            gemv_load_band<FMT, DQ, C>(R1, a, std::min<int64_t>(band + stride, nbands - 1), 0, wave, lane, r, mrow,
-                                      xrow, KT);
+            gemv_load_band<FMT, DQ, C>(R1, a, std::min<int64_t>(band + stride, nbands - 1), 0, wave, lane, r, xrow,
+                                      KT);
             gemv_consume_band<FMT, DQ, NI, C>(R0, acc, 0, wave, KT, lut, lane4, h, mu);
             gemv_finish_band(a, red, acc, band, wave, lane, g);
             if (band + stride >= nbands) break;
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
             gemv_load_band<FMT, DQ, C>(R0, a, std::min<int64_t>(band + 2 * stride, nbands - 1), 0, wave, lane, r,
-                                      mrow, xrow, KT);
+                                      xrow, KT);
             gemv_consume_band<FMT, DQ, NI, C>(R1, acc, 0, wave, KT, lut, lane4, h, mu);
             gemv_finish_band(a, red, acc, band + stride, wave, lane, g);
         }
@@ -572,7 +598,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
         const int64_t row = i / a.k, col = i - row * a.k;
         *reinterpret_cast<uint4*>(xs + i) = *reinterpret_cast<const uint4*>(a.x + row * a.ldx + col);
     }
-    if constexpr (FMT != kQ8_0) build_lut<FMT>(lut);
+    if constexpr (FMT != kQ8_0) build_lut<FMT, 256>(lut);
     __syncthreads();
     const uint16_t* xrow = xs + (r < a.m ? r : 0) * a.k + h * 8;
     const uint16_t* xzero = xs + kStreamXMax + h * 8;
