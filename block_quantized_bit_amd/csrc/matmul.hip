@@ -481,6 +481,17 @@ __device__ inline BufRes buf_res(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
 }
 
+// The same for a base and size that are equal in every lane but that the
+// compiler cannot prove so (results of 64-bit division, values held in
+// arrays): read them from the first active lane.
+__device__ inline uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline BufRes buf_res_uni(const void* base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t u = (uint64_t)uni((uint32_t)b) | ((uint64_t)uni((uint32_t)(b >> 32)) << 32);
+    return buf_res(reinterpret_cast<const void*>(u), uni(bytes));
+}
+
 // Scale bytes per tile and per lane (one row of the tile) in the packed layout.
 template <int FMT, bool DQ>
 __device__ constexpr int tile_scale_bytes() {
@@ -615,15 +626,22 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
 // ===========================================================================
 // GEMM, m >= 17.  Workgroup tile 128 (M) x 256 (N), K step 128; wave w owns
 // columns [64w, 64w+64) (4 bands) for all 128 rows: 8 x 4 MFMA tiles of 16x16.
-// LDS: the fp32 code table at offset 0 (so a v_perm result is the address),
-// then the double-buffered X tile.  W codes/scales and X for step s+1 are
-// requested while step s is computed; those requests are unconditional (rows
-// past m and bands past n re-read valid rows; their results are never stored)
-// and alternate between two register sets, so nothing waits on them early.
+// Three-stage pipeline: X tiles (LDS, filled by LDS-direct loads) and W codes/
+// scales (registers) for step s+2 are requested while step s is computed, so
+// two steps of compute cover the load latency.  Requests are unconditional
+// (rows past m and bands past n re-read valid rows, steps past the end re-read
+// the last step; none of those results is stored).  Within a step the four
+// 32-wide K slices are software-pipelined: the A fragments and dequantized B
+// fragments of slice j+1 are produced while the MFMAs of slice j run, and the
+// schedule interleaves MFMA, VALU and LDS instructions explicitly.
+// LDS: the fp32 code table (NF4, Q4_0), then three X tiles.
 // ===========================================================================
 constexpr int BM = 128, BN = 256, BK = 128;
 constexpr int kLutBytes = kLutWords * 4;
 constexpr int kXsBytes = BM * BK * 2;      // one X tile: 128 rows x 256 B, 16-byte chunks XOR-swizzled by row
+
+template <int FMT>
+__device__ constexpr bool gemm_uses_lut() { return FMT == kNF4 || FMT == kQ4_0; }
 
 template <int FMT>
 struct GemmW {
@@ -631,45 +649,56 @@ struct GemmW {
     uint32_t sc[3];
 };
 
+// Buffer descriptors of one workgroup's loads: per band of the wave (its
+// tiles, its scales), the double-quant group scales, and X from row m0 on.
+// All wave-uniform, so every offset that changes with the K step is scalar.
+struct GemmSrc {
+    const uint8_t* code[4];     // first tile of each band
+    const uint8_t* scale[4];    // scales of that tile
+    uint32_t wbytes, sbytes;    // one band's codes / scales
+    const uint8_t* dt;          // double-quant group scales
+    uint32_t dtbytes;
+    const uint8_t* x;           // X row m0
+    uint32_t xbytes;
+};
+
+// Vector memory instructions gemm_load_w issues per band (the pipeline waits count them).
 template <int FMT, bool DQ>
-__device__ inline void gemm_load_w(GemmW<FMT>& w, const KArgs& a, int64_t band, int64_t st, int lane, int r, int64_t KT) {
+__device__ constexpr int gemm_w_loads() { return FMT == kQ8_0 ? 4 : (FMT == kNF4 && DQ) ? 4 : 2; }
+
+// Codes and scales of K step st (one 16 x 128 tile, two 16 x 64 tiles for Q8_0) of band nf.
+// rowblk: index of the first 64-value block of the lane's row (double quant only).
+template <int FMT, bool DQ>
+__device__ __forceinline__ void gemm_load_w(GemmW<FMT>& w, const GemmSrc& S, int nf, int64_t rowblk, int st,
+                                            int lane, int r) {
     if constexpr (FMT == kQ8_0) {
 #pragma unroll
         for (int half = 0; half < 2; half++) {
-            const int64_t tile = band * KT + st * 2 + half;
-            w.code[half] = *reinterpret_cast<const uint4*>(a.codes + tile * kTileBytes + lane * 16);
-            w.sc[half] = *reinterpret_cast<const uint32_t*>(a.scales + (tile * 32 + r * 2) * 2);
+            const int t = 2 * st + half;
+            w.code[half] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buf_res_uni(S.code[nf], S.wbytes), lane * 16, uni(t * kTileBytes), 0));
+            w.sc[half] = __builtin_amdgcn_raw_buffer_load_b32(buf_res_uni(S.scale[nf], S.sbytes), r * 4, uni(t * 64), 0);
         }
     } else {
-        const int64_t tile = band * KT + st;
-        w.code[0] = *reinterpret_cast<const uint4*>(a.codes + tile * kTileBytes + lane * 16);
-        if constexpr (FMT == kNF4) {
-            if constexpr (DQ) {
-                w.sc[0] = *reinterpret_cast<const uint16_t*>(a.scales + tile * 32 + r * 2);
-                const int64_t b0 = (band * 16 + r) * (a.k / 64) + st * 2;
-                const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
-                w.sc[1] = __float_as_uint(dt[b0 >> 8]);
-                w.sc[2] = __float_as_uint(dt[(b0 + 1) >> 8]);
-            } else {
-                const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 32 + r * 2) * 4);
-                w.sc[0] = v.x;
-                w.sc[1] = v.y;
-            }
-        } else if constexpr (FMT == kQ4_0) {
-            const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 64 + r * 4) * 2);
-            w.sc[0] = v.x;
-            w.sc[1] = v.y;
-        } else {  // NVFP4
-            const uint2 v = *reinterpret_cast<const uint2*>(a.scales + tile * 128 + r * 8);
-            w.sc[0] = v.x;
-            w.sc[1] = v.y;
+        w.code[0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buf_res_uni(S.code[nf], S.wbytes), lane * 16, uni(st * kTileBytes), 0));
+        if constexpr (FMT == kNF4 && DQ) {
+            w.sc[0] = __builtin_amdgcn_raw_buffer_load_b16(buf_res_uni(S.scale[nf], S.sbytes), r * 2, uni(st * 32), 0);
+            const int64_t b0 = rowblk + 2 * st;
+            w.sc[1] = __builtin_amdgcn_raw_buffer_load_b32(buf_res_uni(S.dt, S.dtbytes), (uint32_t)(b0 >> 8) * 4u, 0, 0);
+            w.sc[2] = __builtin_amdgcn_raw_buffer_load_b32(buf_res_uni(S.dt, S.dtbytes), (uint32_t)((b0 + 1) >> 8) * 4u, 0, 0);
+        } else {   // NF4 (fp32 pair), Q4_0 (4 x fp16), NVFP4 (8 x E4M3): 8 bytes per row and tile
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(buf_res_uni(S.scale[nf], S.sbytes), r * 8, uni(st * 128), 0);
+            w.sc[0] = v[0];
+            w.sc[1] = v[1];
         }
     }
 }
 
-// B operand (bf16 of w^, one rounding) for K slice j of one band.
+// B operand (bf16 of w^, one rounding) for K slice j of one band.  `hs` is
+// 8 * (h >> 1): NVFP4 lanes of the upper half of a 32-wide slice use the
+// second 16-value block's scale.
 template <int FMT, bool DQ>
-__device__ inline u32x4 gemm_dequant(const GemmW<FMT>& w, int j, const uint32_t* lut, uint32_t lane8, int h, float mu) {
+__device__ __forceinline__ u32x4 gemm_dequant(const GemmW<FMT>& w, int j, const uint32_t* lut, uint32_t lane8,
+                                              uint32_t hs, float mu) {
     u32x4 B;
     if constexpr (FMT == kQ8_0) {
         const uint4 c = w.code[j >> 1];
@@ -685,6 +714,21 @@ __device__ inline u32x4 gemm_dequant(const GemmW<FMT>& w, int j, const uint32_t*
             // (q+128)*d - 128*d == q*d exactly (19 significant bits); one rounding to bf16
             B[q] = pack_bf16_rne(__builtin_fmaf(f0, d, d128), __builtin_fmaf(f1, d, d128));
         }
+    } else if constexpr (FMT == kNVFP4) {
+        // block 2j + (h >> 1) of the tile row: byte (2j & 3) of the scale word shifted by hs
+        const uint32_t sw = (j < 2 ? w.sc[0] : w.sc[1]) >> hs;
+        const float s = (j & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)sw, 2) : __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
+        const uint32_t word = j == 0 ? w.code[0].x : j == 1 ? w.code[0].y : j == 2 ? w.code[0].z : w.code[0].w;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            // e2m1 pair of byte q (low nibble first), times the E4M3 scale: exact, so the bf16 rounding is exact too
+            f32x2 v;
+            if (q == 0) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
+            else if (q == 1) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
+            else if (q == 2) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2);
+            else v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
+            B[q] = pack_bf16_rne(__fmul_rn(v[0], s), __fmul_rn(v[1], s));
+        }
     } else {
         const uint32_t word = j == 0 ? w.code[0].x : j == 1 ? w.code[0].y : j == 2 ? w.code[0].z : w.code[0].w;
         float s;
@@ -695,11 +739,8 @@ __device__ inline u32x4 gemm_dequant(const GemmW<FMT>& w, int j, const uint32_t*
             } else {
                 s = __uint_as_float(w.sc[kb]);
             }
-        } else if constexpr (FMT == kQ4_0) {
+        } else {  // Q4_0
             s = f16_value((uint16_t)(w.sc[j >> 1] >> (16 * (j & 1))));
-        } else {  // NVFP4
-            const int blk = 2 * j + (h >> 1);
-            s = e4m3_value((w.sc[blk >> 2] >> (8 * (blk & 3))) & 255u);
         }
 #pragma unroll
         for (int q = 0; q < 4; q++) {
@@ -712,77 +753,103 @@ __device__ inline u32x4 gemm_dequant(const GemmW<FMT>& w, int j, const uint32_t*
 }
 
 template <int FMT, bool DQ>
-__device__ __forceinline__ void gemm_load_w4(GemmW<FMT> (&w)[4], const KArgs& a, const int64_t (&wband)[4], int64_t st,
-                                             int lane, int r, int64_t KT) {
+__device__ __forceinline__ void gemm_load_w4(GemmW<FMT> (&w)[4], const GemmSrc& S, const int64_t (&rowblk)[4], int st,
+                                             int lane, int r) {
 #pragma unroll
-    for (int nf = 0; nf < 4; nf++) gemm_load_w<FMT, DQ>(w[nf], a, wband[nf], st, lane, r, KT);
+    for (int nf = 0; nf < 4; nf++) gemm_load_w<FMT, DQ>(w[nf], S, nf, rowblk[nf], st, lane, r);
 }
 
 // X tile (128 x 128 bf16) global -> LDS without passing through registers.  In
 // LDS, chunk c (16 bytes = 8 k) of tile row t sits at position c ^ (t & 15) of
 // the row, so the 16 lanes of an A-fragment read (16 rows, one chunk) hit 16
 // different bank groups.  Wave w fills rows 32w .. 32w+31, four rows per
-// 64-lane instruction; rows past the matrix re-read its last row (their results
-// are never stored).
-__device__ __forceinline__ void gemm_load_x_lds(uint8_t* xs_buf, const uint16_t* x, int64_t ldx, int64_t m0, int64_t M,
-                                                int wave, int lane, int64_t st) {
+// 64-lane instruction (8 instructions); xoff[i] is the lane's byte offset of
+// its (row, chunk) at K step 0 -- rows past the matrix re-read its last row,
+// whose results are never stored.
+constexpr int kXLoads = 8;
+__device__ __forceinline__ void gemm_load_x_lds(uint8_t* xs_buf, const GemmSrc& S, const uint32_t (&xoff)[kXLoads],
+                                                int wave, int st) {
 #pragma unroll
-    for (int i = 0; i < 8; i++) {
-        const int t = wave * 32 + 4 * i + (lane >> 4);                  // tile row of this lane
-        const int c = (lane & 15) ^ (t & 15);                           // chunk it fetches
-        const int64_t row = std::min<int64_t>(m0 + t, M - 1);
-        const uint16_t* g = x + row * ldx + st * BK + c * 8;
-        __builtin_amdgcn_global_load_lds(g, xs_buf + (wave * 32 + 4 * i) * 256, 16, 0, 0);
-    }
+    for (int i = 0; i < kXLoads; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_res_uni(S.x, S.xbytes), (__attribute__((address_space(3))) void*)(xs_buf + (wave * 32 + 4 * i) * 256),
+                                                 16, xoff[i], uni(st * (BK * 2)), 0, 0);
 }
 
-// wait for this wave's outstanding global loads (including LDS-direct ones)
-__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }   // vmcnt(0)
+// s_waitcnt vmcnt(N) with lgkmcnt and expcnt left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
-// One K step: request step st + 1 (clamped: the last step re-reads itself,
-// harmlessly) into wn / xnext, compute step st from wc / xcur, then swap.
-// A fragment (row 16*mf + r, chunk 4j + h) sits at position (4j + h) ^ r.
 template <int FMT, bool DQ>
-__device__ __forceinline__ void gemm_kstep(f32x4 (&acc)[8][4], GemmW<FMT> (&wc)[4], GemmW<FMT> (&wn)[4],
-                                           const KArgs& a, const int64_t (&wband)[4], const uint8_t* xcur,
-                                           uint8_t* xnext, const uint32_t* lut, int64_t st, int64_t s1, int64_t m0,
-                                           int64_t M, int64_t KT, int wave, int lane, int r, int h, uint32_t lane8,
-                                           float mu) {
-    const int64_t nx = std::min<int64_t>(st + 1, s1 - 1);
-    gemm_load_w4<FMT, DQ>(wn, a, wband, nx, lane, r, KT);
-    gemm_load_x_lds(xnext, a.x, a.ldx, m0, M, wave, lane, nx);
+__device__ constexpr int gemm_step_loads() { return kXLoads + 4 * gemm_w_loads<FMT, DQ>(); }
+
+// A fragment of K slice j for rows 16 * mf + r: chunk 4j + h, stored at position (4j + h) ^ r.
+__device__ __forceinline__ u32x4 gemm_load_a(const uint8_t* xcur, uint32_t arow, int mf, int j, int h, int r) {
+    const uint4 t = *reinterpret_cast<const uint4*>(xcur + mf * 4096 + arow + ((uint32_t)((4 * j + h) ^ r) << 4));
+    return u32x4{t.x, t.y, t.z, t.w};
+}
+
+template <int FMT, bool DQ>
+__device__ __forceinline__ void gemm_dequant4(u32x4 (&B)[4], const GemmW<FMT> (&w)[4], int j, const uint32_t* lut,
+                                              uint32_t lane8, uint32_t hs, float mu) {
+#pragma unroll
+    for (int nf = 0; nf < 4; nf++) B[nf] = gemm_dequant<FMT, DQ>(w[nf], j, lut, lane8, hs, mu);
+}
+
+// One K step: request step nx into (wn, xnext), compute the step held in
+// (wc, xcur), then wait until the step after this one has landed (the
+// requests just made may stay in flight) and synchronize the workgroup.
+// On entry B holds slice 0 of wc dequantized; on exit, slice 0 of wf (the
+// W set of the following step).  Slice j's 32 MFMAs run in row-fragment order
+// (one A fragment live at a time) interleaved with the next slice's dequant.
+template <int FMT, bool DQ>
+__device__ __forceinline__ void gemm_kstep(f32x4 (&acc)[8][4], u32x4 (&B)[4], const GemmW<FMT> (&wc)[4],
+                                           GemmW<FMT> (&wn)[4], const GemmW<FMT> (&wf)[4], const GemmSrc& S,
+                                           const int64_t (&rowblk)[4], const uint32_t (&xoff)[kXLoads],
+                                           const uint8_t* xcur, uint8_t* xnext, const uint32_t* lut, int nx, bool more,
+                                           int wave, int lane, int r, int h, uint32_t lane8, uint32_t hs, float mu) {
+    gemm_load_w4<FMT, DQ>(wn, S, rowblk, nx, lane, r);
+    gemm_load_x_lds(xnext, S, xoff, wave, nx);
     const uint32_t arow = (uint32_t)r * 256u;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        u32x4 B[4];
-#pragma unroll
-        for (int nf = 0; nf < 4; nf++) B[nf] = gemm_dequant<FMT, DQ>(wc[nf], j, lut, lane8, h, mu);
-        const uint32_t aoff = arow + ((uint32_t)((4 * j + h) ^ r) << 4);
-        u32x4 A[8];
+        u32x4 Bn[4];
+        if (j < 3) gemm_dequant4<FMT, DQ>(Bn, wc, j + 1, lut, lane8, hs, mu);
+        else if (more) gemm_dequant4<FMT, DQ>(Bn, wf, 0, lut, lane8, hs, mu);
 #pragma unroll
         for (int mf = 0; mf < 8; mf++) {
-            const uint4 t = *reinterpret_cast<const uint4*>(xcur + mf * 4096 + aoff);
-            A[mf] = u32x4{t.x, t.y, t.z, t.w};
+            const u32x4 A = gemm_load_a(xcur, arow, mf, j, h, r);
+#pragma unroll
+            for (int nf = 0; nf < 4; nf++) acc[mf][nf] = mfma(A, B[nf], acc[mf][nf]);
         }
+        // the slice's A reads first, then 32 MFMAs each followed by a share of the next slice's
+        // dequant; in the first slice the next step's loads are spread over the MFMAs too
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-        for (int nf = 0; nf < 4; nf++)
+        for (int i = 0; i < 32; i++) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            if (j == 0 && i < gemm_step_loads<FMT, DQ>()) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int mf = 0; mf < 8; mf++) acc[mf][nf] = mfma(A[mf], B[nf], acc[mf][nf]);
-        __builtin_amdgcn_sched_barrier(0);   // keep each K slice's operands short-lived
+        for (int nf = 0; nf < 4; nf++) B[nf] = Bn[nf];
     }
-#pragma unroll
-    for (int nf = 0; nf < 4; nf++) wc[nf] = wn[nf];
-    wait_vm();
+    wait_vm<gemm_step_loads<FMT, DQ>()>();
     __syncthreads();
 }
 
 template <int FMT, bool DQ>
 __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
-    // separate LDS objects for the code table and the two X buffers, so the
+    // separate LDS objects for the code table and the X buffers, so the
     // LDS-direct loads into one X buffer are never mistaken for writes to the others
-    __shared__ __attribute__((aligned(16))) uint32_t lut_s[(FMT == kQ8_0) ? 4 : kLutWords];
+    __shared__ __attribute__((aligned(16))) uint32_t lut_s[gemm_uses_lut<FMT>() ? kLutWords : 4];
     __shared__ __attribute__((aligned(16))) uint8_t xs0[kXsBytes];
     __shared__ __attribute__((aligned(16))) uint8_t xs1[kXsBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t xs2[kXsBytes];
     const uint32_t* lut = lut_s;
 
     const int tid = threadIdx.x;
@@ -791,6 +858,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     const int r = lane & 15;
     const int h = lane >> 4;
     const uint32_t lane8 = (uint32_t)(lane & 31) << 3;
+    const uint32_t hs = 8u * (uint32_t)(h >> 1);
     const int64_t M = a.m, N = a.n, K = a.k;
     constexpr int TK = tile_k(FMT);
     const int64_t KT = K / TK;
@@ -816,9 +884,34 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     if constexpr (FMT == kNVFP4) g = *reinterpret_cast<const float*>(a.scales + a.L.g_off);
     if constexpr (FMT == kNF4 && DQ) mu = *reinterpret_cast<const float*>(a.scales + a.L.mu_off);
 
-    int64_t wband[4];
+    // descriptors: band tiles of this wave (bands past n re-read the last band), X rows m0 ..
+    GemmSrc S;
+    int64_t rowblk[4];
+    constexpr int SB = (FMT == kNF4 && DQ) ? 32 : (FMT == kQ8_0) ? 64 : 128;   // scale bytes per tile
 #pragma unroll
-    for (int nf = 0; nf < 4; nf++) wband[nf] = std::min<int64_t>(band0 + nf, nbands - 1);
+    for (int nf = 0; nf < 4; nf++) {
+        const int64_t band = std::min<int64_t>(band0 + nf, nbands - 1);
+        S.code[nf] = a.codes + band * KT * kTileBytes;
+        S.scale[nf] = a.scales + band * KT * SB;
+        rowblk[nf] = (band * 16 + r) * (K / 64);
+    }
+    S.wbytes = (uint32_t)(KT * kTileBytes);
+    S.sbytes = (uint32_t)(KT * SB);
+    S.dt = a.scales + a.L.d_off;
+    S.dtbytes = (uint32_t)(a.L.ng * 4);
+    {
+        const int64_t xbytes = (M - m0) * a.ldx * 2;
+        S.x = reinterpret_cast<const uint8_t*>(a.x + m0 * a.ldx);
+        S.xbytes = xbytes > 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)xbytes;
+    }
+    uint32_t xoff[kXLoads];
+#pragma unroll
+    for (int i = 0; i < kXLoads; i++) {
+        const int t = wave * 32 + 4 * i + (lane >> 4);                  // tile row of this lane
+        const int c = (lane & 15) ^ (t & 15);                           // chunk it fetches
+        const int64_t row = std::min<int64_t>(t, M - 1 - m0);
+        xoff[i] = (uint32_t)(row * a.ldx * 2 + c * 16);
+    }
 
     f32x4 acc[8][4];
 #pragma unroll
@@ -827,34 +920,75 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
         for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // every K piece is non-empty (the schedule guarantees s0 < s1)
-    GemmW<FMT> wc[4], wn[4];
-    gemm_load_w4<FMT, DQ>(wc, a, wband, s0, lane, r, KT);
-    gemm_load_x_lds(xs0, a.x, a.ldx, m0, M, wave, lane, s0);
-    if constexpr (FMT != kQ8_0) build_lut_f32<FMT>(lut_s);
-    wait_vm();
+    const int first = (int)s0, last = (int)s1 - 1, end = (int)s1;
+    GemmW<FMT> w0[4], w1[4], w2[4];
+    gemm_load_w4<FMT, DQ>(w0, S, rowblk, first, lane, r);
+    gemm_load_x_lds(xs0, S, xoff, wave, first);
+    gemm_load_w4<FMT, DQ>(w1, S, rowblk, std::min(first + 1, last), lane, r);
+    gemm_load_x_lds(xs1, S, xoff, wave, std::min(first + 1, last));
+    if constexpr (gemm_uses_lut<FMT>()) build_lut_f32<FMT>(lut_s);
+    wait_vm<gemm_step_loads<FMT, DQ>()>();
     __syncthreads();
+    u32x4 B[4];
+    gemm_dequant4<FMT, DQ>(B, w0, 0, lut, lane8, hs, mu);
 
-    // steps alternate X buffers: even steps read xs0 and fill xs1, odd steps the reverse
-    for (int64_t st = s0; st < s1; st += 2) {
-        gemm_kstep<FMT, DQ>(acc, wc, wn, a, wband, xs0, xs1, lut, st, s1, m0, M, KT, wave, lane, r, h, lane8, mu);
-        if (st + 1 < s1)
-            gemm_kstep<FMT, DQ>(acc, wc, wn, a, wband, xs1, xs0, lut, st + 1, s1, m0, M, KT, wave, lane, r, h, lane8, mu);
+    // buffers rotate with period 3: step s reads (w[s%3], xs[s%3]) and fills (w[(s+2)%3], xs[(s+2)%3]).
+    // Whole groups of three steps run in a loop with a single exit; the last
+    // one or two steps follow it.
+    int st = first;
+    for (; st + 3 <= end; st += 3) {
+        gemm_kstep<FMT, DQ>(acc, B, w0, w2, w1, S, rowblk, xoff, xs0, xs2, lut, std::min(st + 2, last), true,
+                            wave, lane, r, h, lane8, hs, mu);
+        gemm_kstep<FMT, DQ>(acc, B, w1, w0, w2, S, rowblk, xoff, xs1, xs0, lut, std::min(st + 3, last), true,
+                            wave, lane, r, h, lane8, hs, mu);
+        gemm_kstep<FMT, DQ>(acc, B, w2, w1, w0, S, rowblk, xoff, xs2, xs1, lut, std::min(st + 4, last), st + 3 < end,
+                            wave, lane, r, h, lane8, hs, mu);
     }
+    if (st < end) {
+        gemm_kstep<FMT, DQ>(acc, B, w0, w2, w1, S, rowblk, xoff, xs0, xs2, lut, std::min(st + 2, last), st + 1 < end,
+                            wave, lane, r, h, lane8, hs, mu);
+        if (st + 1 < end)
+            gemm_kstep<FMT, DQ>(acc, B, w1, w0, w2, S, rowblk, xoff, xs1, xs0, lut, std::min(st + 3, last), false,
+                                wave, lane, r, h, lane8, hs, mu);
+    }
+    wait_vm<0>();   // the last requests (re-reads of the last step) land before the workgroup ends
 
     // ---- epilogue ----
     if (a.ksplit == 1) {
+        const bool full = m0 + BM <= M;     // every row of the tile exists (all but the last row tile)
 #pragma unroll
         for (int nf = 0; nf < 4; nf++) {
-            const int64_t col = (band0 + nf) * 16 + r;
-            if (col >= N) continue;
-            const ColOut c = col_out(a, col);
+            if (band0 + nf >= nbands) continue;     // same for the whole wave
+            const ColOut c = col_out(a, (band0 + nf) * 16 + r);
+            if (full) {
+                // lane (h, r) owns rows 16 mf + 4h + i of its column: step through them by the row stride
+                char* p = c.p + (m0 + 4 * h) * c.ld;
 #pragma unroll
-            for (int mf = 0; mf < 8; mf++)
+                for (int mf = 0; mf < 8; mf++) {
+                    float v[4];
 #pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int64_t mm = m0 + 16 * mf + 4 * h + i;
-                    if (mm < M) put_out(a, c, mm, acc[mf][nf][i], g);
+                    for (int i = 0; i < 4; i++) v[i] = acc[mf][nf][i] * g + c.bias;
+                    if (a.out.f32) {
+#pragma unroll
+                        for (int i = 0; i < 4; i++) *reinterpret_cast<float*>(p + i * c.ld) = v[i];
+                    } else {
+                        const uint32_t b01 = pack_bf16_rne(v[0], v[1]), b23 = pack_bf16_rne(v[2], v[3]);
+                        *reinterpret_cast<uint16_t*>(p) = (uint16_t)b01;
+                        *reinterpret_cast<uint16_t*>(p + c.ld) = (uint16_t)(b01 >> 16);
+                        *reinterpret_cast<uint16_t*>(p + 2 * c.ld) = (uint16_t)b23;
+                        *reinterpret_cast<uint16_t*>(p + 3 * c.ld) = (uint16_t)(b23 >> 16);
+                    }
+                    p += 16 * c.ld;
                 }
+            } else {
+#pragma unroll
+                for (int mf = 0; mf < 8; mf++)
+#pragma unroll
+                    for (int i = 0; i < 4; i++) {
+                        const int64_t mm = m0 + 16 * mf + 4 * h + i;
+                        if (mm < M) put_out(a, c, mm, acc[mf][nf][i], g);
+                    }
+            }
         }
         return;
     }
