@@ -54,6 +54,7 @@ struct KArgs {
     float* partial;      // [ksplit][m][n] when ksplit > 1
     uint32_t* counters;  // one per output tile when ksplit > 1
     int64_t tiles_m, tiles_n;
+    int out_vec;         // every output split allows 4-column vector stores (alignment, split ends % 4)
 };
 
 // NF4 level of code c as a 16-way select over literals.  Table fills use these
@@ -214,6 +215,27 @@ __device__ inline void put_out(const KArgs& a, const ColOut& c, int64_t m, float
     char* const p = c.p + m * c.ld;
     if (a.out.f32) *reinterpret_cast<float*>(p) = r;
     else *reinterpret_cast<uint16_t*>(p) = bf16_rne(r);
+}
+
+// 4 x 4 transpose inside each quad of lanes (t = lane & 3): on entry v[i] is
+// element (row i, column t) of the quad's block, on exit v[j] is (row t, column j).
+// Two exchange stages, with lane t ^ 1 and then lane t ^ 2.
+__device__ __forceinline__ float dpp_xor1(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+}
+__device__ __forceinline__ void quad_transpose(float (&v)[4], int t) {
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) p[i] = dpp_xor1(v[i ^ 1]);
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = ((i ^ t) & 1) ? p[i] : v[i];
+#pragma unroll
+    for (int i = 0; i < 4; i++) p[i] = dpp_xor2(v[i ^ 2]);
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = ((i ^ t) & 2) ? p[i] : v[i];
 }
 
 // Sum of the split-K partials of one output element in piece order 0, 1, ...
@@ -814,24 +836,32 @@ __device__ __forceinline__ void gemm_kstep(f32x4 (&acc)[8][4], u32x4 (&B)[4], co
     gemm_load_w4<FMT, DQ>(wn, S, rowblk, nx, lane, r);
     gemm_load_x_lds(xnext, S, xoff, wave, nx);
     const uint32_t arow = (uint32_t)r * 256u;
+    // A fragments double-buffered across slices: slice j+1's are read while slice j's MFMAs run
+    u32x4 A[2][8];
+#pragma unroll
+    for (int mf = 0; mf < 8; mf++) A[0][mf] = gemm_load_a(xcur, arow, mf, 0, h, r);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
+        const int c = j & 1;
         u32x4 Bn[4];
-        if (j < 3) gemm_dequant4<FMT, DQ>(Bn, wc, j + 1, lut, lane8, hs, mu);
-        else if (more) gemm_dequant4<FMT, DQ>(Bn, wf, 0, lut, lane8, hs, mu);
+        if (j < 3) {
 #pragma unroll
-        for (int mf = 0; mf < 8; mf++) {
-            const u32x4 A = gemm_load_a(xcur, arow, mf, j, h, r);
-#pragma unroll
-            for (int nf = 0; nf < 4; nf++) acc[mf][nf] = mfma(A, B[nf], acc[mf][nf]);
+            for (int mf = 0; mf < 8; mf++) A[c ^ 1][mf] = gemm_load_a(xcur, arow, mf, j + 1, h, r);
+            gemm_dequant4<FMT, DQ>(Bn, wc, j + 1, lut, lane8, hs, mu);
+        } else if (more) {
+            gemm_dequant4<FMT, DQ>(Bn, wf, 0, lut, lane8, hs, mu);
         }
-        // the slice's A reads first, then 32 MFMAs each followed by a share of the next slice's
-        // dequant; in the first slice the next step's loads are spread over the MFMAs too
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+        for (int mf = 0; mf < 8; mf++)
+#pragma unroll
+            for (int nf = 0; nf < 4; nf++) acc[mf][nf] = mfma(A[c][mf], B[nf], acc[mf][nf]);
+        // 32 MFMAs, each followed by a share of the next slice's dequant; the next slice's A
+        // reads (and, in the first slice, the next step's loads) are spread over them too
 #pragma unroll
         for (int i = 0; i < 32; i++) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            if (j < 3 && (i & 3) == 0) __builtin_amdgcn_sched_group_barrier(0x100, gemm_uses_lut<FMT>() ? 3 : 1, 0);
             if (j == 0 && i < gemm_step_loads<FMT, DQ>()) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -993,17 +1023,33 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
         return;
     }
     // K split: deposit this piece's partial tile; k_splitk_reduce finishes the outputs
+    // (full row tiles: quad-transposed 16-byte stores; the workspace is 16-byte aligned and N % 16 == 0)
+    const bool full = m0 + BM <= M;
+    const int t = r & 3;
 #pragma unroll
     for (int nf = 0; nf < 4; nf++) {
+        if (band0 + nf >= nbands) continue;     // same for the whole wave
         const int64_t col = (band0 + nf) * 16 + r;
-        if (col >= N) continue;
+        if (full) {
+            float* p = a.partial + ((int64_t)ks * M + m0 + 4 * h + t) * N + (col - t);
 #pragma unroll
-        for (int mf = 0; mf < 8; mf++)
+            for (int mf = 0; mf < 8; mf++) {
+                float v[4];
 #pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int64_t mm = m0 + 16 * mf + 4 * h + i;
-                if (mm < M) a.partial[((int64_t)ks * M + mm) * N + col] = acc[mf][nf][i];
+                for (int i = 0; i < 4; i++) v[i] = acc[mf][nf][i];
+                quad_transpose(v, t);
+                *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
+                p += 16 * N;
             }
+        } else {
+#pragma unroll
+            for (int mf = 0; mf < 8; mf++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int64_t mm = m0 + 16 * mf + 4 * h + i;
+                    if (mm < M) a.partial[((int64_t)ks * M + mm) * N + col] = acc[mf][nf][i];
+                }
+        }
     }
 }
 
@@ -1020,6 +1066,18 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, int global_scale
     const float* p = a.partial + mm * a.n + col0;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < a.ksplit; s++) v += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + s * pstride));
+    if (a.out_vec) {
+        // the 4 columns lie in one output split and can be written with one store
+        const ColOut c = col_out(a, col0);
+        float o[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) o[u] = v[u] * g + (a.bias ? bf16_value(a.bias[col0 + u]) : 0.0f);
+        char* q = c.p + mm * c.ld;
+        if (a.out.f32) *reinterpret_cast<f32x4*>(q) = f32x4{o[0], o[1], o[2], o[3]};
+        else *reinterpret_cast<uint2*>(q) = make_uint2((uint32_t)bf16_rne(o[0]) | ((uint32_t)bf16_rne(o[1]) << 16),
+                                                      (uint32_t)bf16_rne(o[2]) | ((uint32_t)bf16_rne(o[3]) << 16));
+        return;
+    }
 #pragma unroll
     for (int u = 0; u < 4; u++) put_out(a, col_out(a, col0 + u), mm, v[u], g);
 }
@@ -1081,6 +1139,12 @@ static KArgs make_args(const MatmulProblem& p) {
     a.out = p.out;
     a.L = scale_layout(p.fmt, p.dq, p.n, p.k);
     a.ksplit = 1;
+    const uintptr_t align = p.out.f32 ? 16 : 8;
+    a.out_vec = 1;
+    for (int i = 0; i < p.out.nsplit; i++) {
+        if (reinterpret_cast<uintptr_t>(p.out.y[i]) % align != 0 || p.out.ldy[i] % 4 != 0 || p.out.end[i] % 4 != 0)
+            a.out_vec = 0;
+    }
     return a;
 }
 

@@ -122,6 +122,27 @@ def test_matmul_ragged(orc, fmt, dq, m):
         check_bound(y, y_ref, ad, what=f"{NAMES[fmt]} m={m} ws={use_ws}")
     y = gpu_matmul(d, codes, scales, x, None, ydt=wq.WQ_BF16)
     check_bound(y, orc.matmul(x, ref["w_hat"], None), ad, bf16_out=True, what="bf16 out, no bias")
+    # an odd output stride rules out the 4-column vector stores: the per-element store path
+    y = gpu_matmul(d, codes, scales, x, b, ydt=wq.WQ_BF16, ldy_pad=3)
+    check_bound(y, y_ref, ad, bf16_out=True, what="bf16 out, odd ldy")
+
+
+@pytest.mark.parametrize("fmt,dq", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("ydt,ldy_pad", [(wq.WQ_F32, 0), (wq.WQ_BF16, 0), (wq.WQ_BF16, 1), (wq.WQ_F32, 3)],
+                         ids=["f32", "bf16", "bf16-odd-ldy", "f32-odd-ldy"])
+def test_gemm_split_k_full_tiles(orc, fmt, dq, ydt, ldy_pad):
+    """Few output tiles (N = 512) with several full 128-row tiles (M = 300) and long K:
+    the GEMM splits K, deposits full-tile partials with vector stores and reduces
+    them in a second kernel (vector or per-element stores, by output alignment)."""
+    n, k, m = 512, 2560, 300
+    d, codes, scales, ref, b = quantized(orc, fmt, dq, 4200, n, k)
+    x = linear_case(4200, n, k, m)[2]
+    assert wq.wq_workspace_size(d, m) > 0
+    say("split-K gemm", NAMES[fmt], m, n, k, ydt, ldy_pad)
+    y = gpu_matmul(d, codes, scales, x, b, ydt=ydt, ldy_pad=ldy_pad)
+    rows = _sample_rows(m, 5)
+    check_bound(y[rows], orc.matmul(x, ref["w_hat"], b, rows=rows), abs_dot(x, ref["w_hat"], rows=rows),
+                bf16_out=ydt == wq.WQ_BF16, what=f"split-K {NAMES[fmt]} ydt={ydt} pad={ldy_pad}")
 
 
 @pytest.mark.parametrize("m", [1, 4, 16])
