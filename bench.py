@@ -46,6 +46,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=104)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-extras", action="store_true", help="only the decode set (for profiling)")
+    ap.add_argument("--encoder-only", action="store_true",
+                    help="only the encoder GEMMs (NVFP4, M=1500), for MFMA counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -78,45 +80,6 @@ def main():
     cal2 = torch.empty_like(cal)
     cal2.copy_(cal)
     torch.cuda.synchronize()
-
-    # ---------------- decode set: NF4 + double-quant, pool of weight copies ----------------
-    t0 = time.time()
-    base = []
-    for i, (name, n, k) in enumerate(DECODER):
-        w, b, x16 = linear_case(2000 + i, n, k, 16, outlier_frac=0.001)
-        if name == "qkv":
-            b = b.copy()
-            b[1280:2560] = 0                      # key projection has no bias
-        d, codes, scales = quantize_dev(wq.WQ_NF4, torch.from_numpy(w).to(dev), True)
-        base.append(dict(name=name, n=n, k=k, d=d, codes=codes, scales=scales, bias=bf16_dev(b),
-                         x16=bf16_dev(x16), w=w, b=b, xbits=x16))
-    set_bytes = sum(e["codes"].numel() + e["scales"].numel() for e in base)
-    pool_n = max(1, -(-(1 << 30) // set_bytes))               # >= 1 GiB of weights
-    pool = [[(e["codes"].clone(), e["scales"].clone()) for e in base] for _ in range(pool_n)]
-    torch.cuda.synchronize()
-    log(f"[bench] decode set {set_bytes / 1e6:.3f} MB of packed weights, pool of {pool_n} copies "
-        f"({pool_n * set_bytes / 2**30:.2f} GiB), built in {time.time() - t0:.1f}s")
-
-    def decode_buffers(m):
-        outs, wss = [], []
-        for e in base:
-            outs.append(torch.empty((m, e["n"]), dtype=torch.int16, device=dev))
-            nb = wq.wq_workspace_size(e["d"], m)
-            wss.append((torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev), nb))
-        return outs, wss
-
-    def enqueue_decode_step(m, slot, outs, wss, st):
-        for j, e in enumerate(base):
-            codes, scales = pool[slot][j]
-            y = outs[j]
-            ws, nb = wss[j]
-            if e["name"] == "qkv":
-                ys = [y.data_ptr(), y.data_ptr() + 2 * 1280, y.data_ptr() + 2 * 2560]
-                wq.wq_matmul_qkv(e["d"], m, e["x16"], e["k"], codes, scales, e["bias"], [1280, 1280, 1280],
-                                 ys, [e["n"]] * 3, wq.WQ_BF16, ws if nb else None, nb, stream=st)
-            else:
-                wq.wq_matmul(e["d"], m, e["x16"], e["k"], codes, scales, e["bias"], y, wq.WQ_BF16, e["n"],
-                             ws if nb else None, nb, stream=st)
 
     def run_graph_steps(enqueue, n_slots, steps, warmup):
         """Capture one graph over all slots, replay it; returns seconds for `steps` steps."""
@@ -156,6 +119,82 @@ def main():
             ev1.record(stream)
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / 1e3
+
+    def enc_step(s_, st, layers, m):
+        for e in layers:
+            wq.wq_matmul(e["d"], m, e["x"], e["k"], e["c"], e["s"], e["b"], e["y"], wq.WQ_BF16, e["n"],
+                         e["ws"] if e["nb"] else None, e["nb"], stream=st)
+
+    def encoder_part():
+        # ---- encoder GEMM, NVFP4, M = 1500: fc1 + fc2 ----
+        enc = []
+        for i, (n, k) in enumerate([(ENC_FFN, ENC_D), (ENC_D, ENC_FFN)]):
+            w, b, x = linear_case(3000 + i, n, k, ENC_M, row_lognormal_sigma=0.3)
+            d, c, s = quantize_dev(wq.WQ_NVFP4, torch.from_numpy(w).to(dev), False)
+            nb = wq.wq_workspace_size(d, ENC_M)
+            enc.append(dict(d=d, c=c, s=s, b=bf16_dev(b), x=bf16_dev(x), n=n, k=k,
+                            y=torch.empty((ENC_M, n), dtype=torch.int16, device=dev),
+                            ws=torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev), nb=nb))
+
+        reps = 50
+        te = run_graph_steps(lambda s_, st: enc_step(s_, st, enc, ENC_M), 1, reps, 5)
+        flops = sum(2.0 * ENC_M * e["n"] * e["k"] for e in enc)
+        tflops = flops * reps / te / 1e12
+        encoder = {
+            "metric": "encoder TFLOP/s (M=1500)",
+            "value": round(tflops, 2),
+            "unit": "TFLOP/s",
+            "config": {"workload": "encoder fc1 1280->5120 and fc2 5120->1280, NVFP4 W4A16, X[1500,1280] bf16"},
+            "us_per_step": round(te * 1e6 / reps, 2),
+            "roofline": {"kernel": "k_gemm<NVFP4>", "bound": "mfma", "achieved": round(tflops, 2),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None},
+        }
+        log(f"[bench] encoder NVFP4 M=1500: {encoder['us_per_step']} us, {tflops:.1f} TFLOP/s")
+        return encoder
+
+    if args.encoder_only:
+        print(json.dumps({"encoder": encoder_part()}), flush=True)
+        return
+
+    # ---------------- decode set: NF4 + double-quant, pool of weight copies ----------------
+    t0 = time.time()
+    base = []
+    for i, (name, n, k) in enumerate(DECODER):
+        w, b, x16 = linear_case(2000 + i, n, k, 16, outlier_frac=0.001)
+        if name == "qkv":
+            b = b.copy()
+            b[1280:2560] = 0                      # key projection has no bias
+        d, codes, scales = quantize_dev(wq.WQ_NF4, torch.from_numpy(w).to(dev), True)
+        base.append(dict(name=name, n=n, k=k, d=d, codes=codes, scales=scales, bias=bf16_dev(b),
+                         x16=bf16_dev(x16), w=w, b=b, xbits=x16))
+    set_bytes = sum(e["codes"].numel() + e["scales"].numel() for e in base)
+    pool_n = max(1, -(-(1 << 30) // set_bytes))               # >= 1 GiB of weights
+    pool = [[(e["codes"].clone(), e["scales"].clone()) for e in base] for _ in range(pool_n)]
+    torch.cuda.synchronize()
+    log(f"[bench] decode set {set_bytes / 1e6:.3f} MB of packed weights, pool of {pool_n} copies "
+        f"({pool_n * set_bytes / 2**30:.2f} GiB), built in {time.time() - t0:.1f}s")
+
+    def decode_buffers(m):
+        outs, wss = [], []
+        for e in base:
+            outs.append(torch.empty((m, e["n"]), dtype=torch.int16, device=dev))
+            nb = wq.wq_workspace_size(e["d"], m)
+            wss.append((torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev), nb))
+        return outs, wss
+
+    def enqueue_decode_step(m, slot, outs, wss, st):
+        for j, e in enumerate(base):
+            codes, scales = pool[slot][j]
+            y = outs[j]
+            ws, nb = wss[j]
+            if e["name"] == "qkv":
+                ys = [y.data_ptr(), y.data_ptr() + 2 * 1280, y.data_ptr() + 2 * 2560]
+                wq.wq_matmul_qkv(e["d"], m, e["x16"], e["k"], codes, scales, e["bias"], [1280, 1280, 1280],
+                                 ys, [e["n"]] * 3, wq.WQ_BF16, ws if nb else None, nb, stream=st)
+            else:
+                wq.wq_matmul(e["d"], m, e["x16"], e["k"], codes, scales, e["bias"], y, wq.WQ_BF16, e["n"],
+                             ws if nb else None, nb, stream=st)
 
     def decode_bytes(m):
         """algorithmic bytes of one step: packed weights + X + Y (bf16) + bias"""
@@ -242,36 +281,7 @@ def main():
         del c_s, s_s
         torch.cuda.empty_cache()
 
-        # ---- encoder GEMM, NVFP4, M = 1500: fc1 + fc2 ----
-        enc = []
-        for i, (n, k) in enumerate([(ENC_FFN, ENC_D), (ENC_D, ENC_FFN)]):
-            w, b, x = linear_case(3000 + i, n, k, ENC_M, row_lognormal_sigma=0.3)
-            d, c, s = quantize_dev(wq.WQ_NVFP4, torch.from_numpy(w).to(dev), False)
-            nb = wq.wq_workspace_size(d, ENC_M)
-            enc.append(dict(d=d, c=c, s=s, b=bf16_dev(b), x=bf16_dev(x), n=n, k=k,
-                            y=torch.empty((ENC_M, n), dtype=torch.int16, device=dev),
-                            ws=torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev), nb=nb))
-
-        def enc_step(s_, st, layers=enc, m=ENC_M):
-            for e in layers:
-                wq.wq_matmul(e["d"], m, e["x"], e["k"], e["c"], e["s"], e["b"], e["y"], wq.WQ_BF16, e["n"],
-                             e["ws"] if e["nb"] else None, e["nb"], stream=st)
-
-        reps = 50
-        te = run_graph_steps(enc_step, 1, reps, 5)
-        flops = sum(2.0 * ENC_M * e["n"] * e["k"] for e in enc)
-        tflops = flops * reps / te / 1e12
-        encoder = {
-            "metric": "encoder TFLOP/s (M=1500)",
-            "value": round(tflops, 2),
-            "unit": "TFLOP/s",
-            "config": {"workload": "encoder fc1 1280->5120 and fc2 5120->1280, NVFP4 W4A16, X[1500,1280] bf16"},
-            "us_per_step": round(te * 1e6 / reps, 2),
-            "roofline": {"kernel": "k_gemm<NVFP4>", "bound": "mfma", "achieved": round(tflops, 2),
-                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None},
-        }
-        log(f"[bench] encoder NVFP4 M=1500: {encoder['us_per_step']} us, {tflops:.1f} TFLOP/s")
+        encoder = encoder_part()
 
         # ---- one encoder layer at batch 4 (M = 6000), q8_0 and q4_0 on identical weights ----
         layer_shapes = [(ENC_D, ENC_D)] * 4 + [(ENC_FFN, ENC_D), (ENC_D, ENC_FFN)]

@@ -1064,8 +1064,18 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, int global_scale
     const int64_t mm = q / nq, col0 = (q % nq) * 4;
     const int64_t pstride = (int64_t)a.m * a.n;
     const float* p = a.partial + mm * a.n + col0;
+    // pieces are summed in order 0, 1, ...; their loads are issued four at a time (indices
+    // past the last piece re-read it and are dropped)
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < a.ksplit; s++) v += __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + s * pstride));
+    for (int s0 = 0; s0 < a.ksplit; s0 += 4) {
+        f32x4 t[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            t[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + std::min(s0 + u, a.ksplit - 1) * pstride));
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            if (s0 + u < a.ksplit) v += t[u];
+    }
     if (a.out_vec) {
         // the 4 columns lie in one output split and can be written with one store
         const ColOut c = col_out(a, col0);
@@ -1158,9 +1168,10 @@ static int gemv_chunk(int64_t KT) {
 template <int FMT, bool DQ, int NI, int C>
 static void gemv_launch_c(const KArgs& a, int64_t nbands, int64_t KT, hipStream_t st) {
     const dim3 block(64 * kGemvWaves);
-    // band pipelining only where its two register sets fit without spilling (C <= 2)
+    // band pipelining only where its two register sets fit without spilling (C <= 2), and only
+    // when the bands outnumber the workgroups that fit at once (two of 8 waves per CU)
     if constexpr (C <= 2) {
-        const int64_t resident = kNumCU;
+        const int64_t resident = 2 * (int64_t)kNumCU;
         if (nbands > resident && (KT + kGemvWaves - 1) / kGemvWaves <= C) {
             hipLaunchKernelGGL((k_gemv<FMT, DQ, NI, C, true>), dim3((unsigned)resident), block, 0, st, a);
             return;
