@@ -55,6 +55,7 @@ struct KArgs {
     uint32_t* counters;  // one per output tile when ksplit > 1
     int64_t tiles_m, tiles_n;
     int out_vec;         // every output split allows 4-column vector stores (alignment, split ends % 4)
+    int rparts;          // GEMV: workgroups sharing one 16-row band, each owning 16 / rparts rows
 };
 
 // NF4 level of code c as a 16-way select over literals.  Table fills use these
@@ -251,6 +252,29 @@ __device__ inline float sum_partials(const float* p, int64_t stride, int ks) {
     return v;
 }
 
+// Workgroup barrier for data written to LDS by this workgroup's LDS-direct loads
+// and LDS stores, when the N most recent vector-memory requests (register
+// loads) may stay in flight: s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier.
+// __syncthreads() would wait for every outstanding load here, because its fence
+// cannot tell the LDS-direct loads from the later register loads.  The compiler
+// is kept from moving memory accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void lds_barrier_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// s_waitcnt vmcnt(N) with lgkmcnt and expcnt left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 // ===========================================================================
 // GEMV, m <= 16.  Work item = (16-row band, K piece).  Each wave owns whole
 // items (no cross-wave reduction); an item's tiles are fetched C at a time --
@@ -266,7 +290,13 @@ struct GemvTile {
     u32x4 A[tile_k(FMT) / 32];
 };
 
+constexpr int kGemvWaves = 8;   // waves per workgroup, all on one band, splitting its K range
+
+// Vector memory instructions gemv_load issues for a tile's codes and scales (X excluded).
 template <int FMT, bool DQ>
+__device__ constexpr int gemv_w_loads() { return (FMT == kNF4 && DQ) ? 4 : 2; }
+
+template <int FMT, bool DQ, bool XL = false>
 __device__ inline void gemv_load(GemvTile<FMT>& t, const KArgs& a, int64_t band, int64_t kt, int lane, int r,
                                  const uint16_t* xrow, int64_t KT) {
     constexpr int TK = tile_k(FMT);
@@ -296,10 +326,26 @@ __device__ inline void gemv_load(GemvTile<FMT>& t, const KArgs& a, int64_t band,
         t.sc[0] = *reinterpret_cast<const uint32_t*>(a.scales + (tile * 32 + r * 2) * 2);
     }
     // rows r >= m read row 0 (always valid); their products only reach output rows that are never stored
+    if constexpr (!XL) {
 #pragma unroll
-    for (int j = 0; j < TK / 32; j++) {
-        const uint4 v = *reinterpret_cast<const uint4*>(xrow + kt * TK + 32 * j);
-        t.A[j] = u32x4{v.x, v.y, v.z, v.w};
+        for (int j = 0; j < TK / 32; j++) {
+            const uint4 v = *reinterpret_cast<const uint4*>(xrow + kt * TK + 32 * j);
+            t.A[j] = u32x4{v.x, v.y, v.z, v.w};
+        }
+    }
+}
+
+// X (m rows of k bf16) copied once into LDS, rows packed with stride k, by LDS-direct loads
+// of 16 bytes per lane: chunk i (8 elements) of the copy lands at byte 16 i.
+__device__ __forceinline__ void gemv_stage_x(uint16_t* xs, const KArgs& a, int wave, int lane) {
+    const int64_t per_row = a.k / 8;
+    const int64_t nchunks = (int64_t)a.m * per_row;
+    for (int64_t c0 = (int64_t)wave * 64; c0 < nchunks; c0 += 64 * kGemvWaves) {
+        const int64_t i = c0 + lane;
+        if (i < nchunks) {
+            const int64_t row = i / per_row, col = (i - row * per_row) * 8;
+            __builtin_amdgcn_global_load_lds(a.x + row * a.ldx + col, xs + c0 * 8, 16, 0, 0);
+        }
     }
 }
 
@@ -377,32 +423,44 @@ __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const ui
     }
 }
 
-constexpr int kGemvWaves = 8;   // waves per workgroup, all on one band, splitting its K range
-
 // Wave w of a workgroup owns tiles w, w + 8, w + 16, ... of its band's K range:
 // C of them, all requested before any is used.  A band is finished by summing
 // the 8 waves' 16x16 partial tiles in LDS in wave order.
-template <int FMT, bool DQ, int C>
+template <int FMT, bool DQ, int C, bool XL>
 __device__ __forceinline__ void gemv_load_band(GemvTile<FMT> (&R)[C], const KArgs& a, int64_t band, int64_t c0,
                                                int wave, int lane, int r, const uint16_t* xrow,
                                                int64_t KT) {
 #pragma unroll
     for (int s = 0; s < C; s++) {
         const int64_t kt = std::min<int64_t>(wave + (c0 + s) * kGemvWaves, KT - 1);
-        gemv_load<FMT, DQ>(R[s], a, band, kt, lane, r, xrow, KT);
+        gemv_load<FMT, DQ, XL>(R[s], a, band, kt, lane, r, xrow, KT);
     }
 }
 
-template <int FMT, bool DQ, int NI, int C>
-__device__ __forceinline__ void gemv_consume_band(const GemvTile<FMT> (&R)[C], f32x4& acc, int64_t c0, int wave,
-                                                  int64_t KT, const uint32_t* lut, uint32_t lane4, int h, float mu) {
+// XL: the A operands come from the LDS copy of X (xl = this lane's row, chunk h), read here.
+template <int FMT, bool DQ, int NI, int C, bool XL>
+__device__ __forceinline__ void gemv_consume_band(GemvTile<FMT> (&R)[C], f32x4& acc, int64_t c0, int wave,
+                                                  int64_t KT, const uint32_t* lut, uint32_t lane4, int h, float mu,
+                                                  const uint16_t* xl) {
+    constexpr int TK = tile_k(FMT);
 #pragma unroll
-    for (int s = 0; s < C; s++)
-        if (wave + (c0 + s) * kGemvWaves < KT) gemv_consume<FMT, DQ, NI>(R[s], acc, lut, lane4, h, mu);
+    for (int s = 0; s < C; s++) {
+        const int64_t kt = wave + (c0 + s) * kGemvWaves;
+        if (kt < KT) {
+            if constexpr (XL) {
+#pragma unroll
+                for (int j = 0; j < TK / 32; j++) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(xl + kt * TK + 32 * j);
+                    R[s].A[j] = u32x4{v.x, v.y, v.z, v.w};
+                }
+            }
+            gemv_consume<FMT, DQ, NI>(R[s], acc, lut, lane4, h, mu);
+        }
+    }
 }
 
 __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kGemvWaves][64], const f32x4& acc,
-                                                 int64_t band, int wave, int lane, float g) {
+                                                 int64_t band, int wave, int lane, float g, bool own = true) {
     const int r = lane & 15, h = lane >> 4;
     red[wave][lane] = acc;
     __syncthreads();
@@ -414,22 +472,32 @@ __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kG
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int mm = 4 * h + i;
-            if (mm < a.m) put_out(a, c, mm, v[i], g);
+            if (mm < a.m && own) put_out(a, c, mm, v[i], g);
         }
     }
     __syncthreads();
 }
 
-// PIPE = false: every workgroup owns one band (grid == number of bands), its
-//   tiles come in rounds of C per wave (one round when K <= 8 * C tiles).
+// PIPE = false: every workgroup owns one band, or 16 / rparts of its rows
+//   (rparts > 1 spreads few bands over more CUs; the parts of a band run on one
+//   XCD), its tiles come in rounds of C per wave (one round when K <= 8 * C tiles).
+//   A workgroup owning part of a band loads only its rows: every lane of the
+//   wave points at the slot of one of those rows, so no other row's bytes are
+//   fetched, and only the lanes of its own rows store.
 // PIPE = true : workgroups loop over bands; each wave holds all its tiles of a
 //   band in one round (K <= 8 * C tiles) and requests the next band's tiles
 //   before using the current ones.  The prefetch index is clamped to the last
 //   band, so the requests are unconditional.
-template <int FMT, bool DQ, int NI, int C, bool PIPE>
+// XL: X is copied once into (dynamic) LDS at the start -- a few LDS-direct loads
+//   per workgroup instead of four 64-lane loads per tile and wave -- and the A
+//   operands are read from there; used when m * k is small (decode).  The copy
+//   is requested before the weights, so waiting for it (vmcnt = the weight loads
+//   issued after it) never waits for a weight load.
+template <int FMT, bool DQ, int NI, int C, bool PIPE, bool XL>
 __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArgs a) {
     __shared__ uint32_t lut[(FMT == kQ8_0) ? 1 : kLutWords];
     __shared__ f32x4 red[kGemvWaves][64];
+    extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -443,39 +511,69 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
     if constexpr (FMT == kNVFP4) g = *reinterpret_cast<const float*>(a.scales + a.L.g_off);
     if constexpr (FMT == kNF4 && DQ) mu = *reinterpret_cast<const float*>(a.scales + a.L.mu_off);
     const uint16_t* xrow = a.x + (int64_t)(r < a.m ? r : 0) * a.ldx + h * 8;
+    const uint16_t* xl = xs_dyn + (int64_t)(r < a.m ? r : 0) * a.k + h * 8;
     const int64_t per_wave = (KT + kGemvWaves - 1) / kGemvWaves;
 
     if constexpr (!PIPE) {
-        const int64_t band = blockIdx.x;
+        const int P = a.rparts;
+        int64_t band = blockIdx.x;
+        int part = 0;
+        if (P > 1) {   // workgroup b runs on XCD b % 8: give the parts of a band the same b % 8
+            const int64_t q = blockIdx.x / 8;
+            part = (int)(q % P);
+            band = (q / P) * 8 + blockIdx.x % 8;
+            if (band >= nbands) return;     // the whole workgroup, before any barrier
+        }
+        const int rows = 16 / P;
+        const int rs = part * rows + (r & (rows - 1));     // row whose data this lane loads
+        // With XL the code table is filled first: LDS writes issued while the LDS-direct X copy
+        // is in flight would have to wait for every load.  Otherwise it is filled while the first
+        // tiles are in flight.
+        if constexpr (XL) {
+            if constexpr (FMT != kQ8_0) build_lut<FMT, 64 * kGemvWaves>(lut);
+            gemv_stage_x(xs_dyn, a, wave, lane);
+        }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int64_t c0 = 0; c0 < per_wave; c0 += C) {
             GemvTile<FMT> R[C];
-            gemv_load_band<FMT, DQ, C>(R, a, band, c0, wave, lane, r, xrow, KT);
-            if (c0 == 0) {   // build the code table while the first tiles are in flight
-                if constexpr (FMT != kQ8_0) build_lut<FMT, 64 * kGemvWaves>(lut);
-                __syncthreads();
+            gemv_load_band<FMT, DQ, C, XL>(R, a, band, c0, wave, rs + 16 * h, rs, xrow, KT);
+            if (c0 == 0) {
+                if constexpr (XL) {
+                    lds_barrier_vm<C * gemv_w_loads<FMT, DQ>()>();
+                } else {
+                    if constexpr (FMT != kQ8_0) build_lut<FMT, 64 * kGemvWaves>(lut);
+                    __syncthreads();
+                }
             }
-            gemv_consume_band<FMT, DQ, NI, C>(R, acc, c0, wave, KT, lut, lane4, h, mu);
+            gemv_consume_band<FMT, DQ, NI, C, XL>(R, acc, c0, wave, KT, lut, lane4, h, mu, xl);
         }
-        gemv_finish_band(a, red, acc, band, wave, lane, g);
+        gemv_finish_band(a, red, acc, band, wave, lane, g, rs == r);
     } else {
         const int64_t stride = gridDim.x;
         GemvTile<FMT> R0[C], R1[C];
         int64_t band = blockIdx.x;
-        gemv_load_band<FMT, DQ, C>(R0, a, band, 0, wave, lane, r, xrow, KT);
-        if constexpr (FMT != kQ8_0) build_lut<FMT, 64 * kGemvWaves>(lut);
-        __syncthreads();
+        if constexpr (XL) {
+            if constexpr (FMT != kQ8_0) build_lut<FMT, 64 * kGemvWaves>(lut);
+            gemv_stage_x(xs_dyn, a, wave, lane);
+        }
+        gemv_load_band<FMT, DQ, C, XL>(R0, a, band, 0, wave, lane, r, xrow, KT);
+        if constexpr (XL) {
+            lds_barrier_vm<C * gemv_w_loads<FMT, DQ>()>();
+        } else {
+            if constexpr (FMT != kQ8_0) build_lut<FMT, 64 * kGemvWaves>(lut);
+            __syncthreads();
+        }
         for (; band < nbands; band += 2 * stride) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            gemv_load_band<FMT, DQ, C>(R1, a, std::min<int64_t>(band + stride, nbands - 1), 0, wave, lane, r, xrow,
-                                      KT);
-            gemv_consume_band<FMT, DQ, NI, C>(R0, acc, 0, wave, KT, lut, lane4, h, mu);
+            gemv_load_band<FMT, DQ, C, XL>(R1, a, std::min<int64_t>(band + stride, nbands - 1), 0, wave, lane, r,
+                                          xrow, KT);
+            gemv_consume_band<FMT, DQ, NI, C, XL>(R0, acc, 0, wave, KT, lut, lane4, h, mu, xl);
             gemv_finish_band(a, red, acc, band, wave, lane, g);
             if (band + stride >= nbands) break;
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
-            gemv_load_band<FMT, DQ, C>(R0, a, std::min<int64_t>(band + 2 * stride, nbands - 1), 0, wave, lane, r,
-                                      xrow, KT);
-            gemv_consume_band<FMT, DQ, NI, C>(R1, acc, 0, wave, KT, lut, lane4, h, mu);
+            gemv_load_band<FMT, DQ, C, XL>(R0, a, std::min<int64_t>(band + 2 * stride, nbands - 1), 0, wave, lane, r,
+                                          xrow, KT);
+            gemv_consume_band<FMT, DQ, NI, C, XL>(R1, acc, 0, wave, KT, lut, lane4, h, mu, xl);
             gemv_finish_band(a, red, acc, band + stride, wave, lane, g);
         }
     }
@@ -795,14 +893,6 @@ __device__ __forceinline__ void gemm_load_x_lds(uint8_t* xs_buf, const GemmSrc& 
     for (int i = 0; i < kXLoads; i++)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(buf_res_uni(S.x, S.xbytes), (__attribute__((address_space(3))) void*)(xs_buf + (wave * 32 + 4 * i) * 256),
                                                  16, xoff[i], uni(st * (BK * 2)), 0, 0);
-}
-
-// s_waitcnt vmcnt(N) with lgkmcnt and expcnt left alone (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
 template <int FMT, bool DQ>
@@ -1149,6 +1239,7 @@ static KArgs make_args(const MatmulProblem& p) {
     a.out = p.out;
     a.L = scale_layout(p.fmt, p.dq, p.n, p.k);
     a.ksplit = 1;
+    a.rparts = 1;
     const uintptr_t align = p.out.f32 ? 16 : 8;
     a.out_vec = 1;
     for (int i = 0; i < p.out.nsplit; i++) {
@@ -1165,19 +1256,37 @@ static int gemv_chunk(int64_t KT) {
     return pw <= 1 ? 1 : pw <= 2 ? 2 : pw <= 4 ? 4 : pw <= 5 ? 5 : 8;
 }
 
-template <int FMT, bool DQ, int NI, int C>
-static void gemv_launch_c(const KArgs& a, int64_t nbands, int64_t KT, hipStream_t st) {
+constexpr int64_t kGemvXlMax = 32768;   // bf16 elements of X (m * k) copied to LDS by the decode GEMV
+
+template <int FMT, bool DQ, int NI, int C, bool XL>
+static void gemv_launch_cx(const KArgs& a, int64_t nbands, int64_t KT, hipStream_t st) {
     const dim3 block(64 * kGemvWaves);
+    const size_t xbytes = XL ? (size_t)a.m * (size_t)a.k * 2 : 0;
+    // two workgroups per CU fit when the X copy leaves room for two code tables
+    const int64_t per_cu = (C <= 2 && xbytes <= 8192) ? 2 : 1;
     // band pipelining only where its two register sets fit without spilling (C <= 2), and only
-    // when the bands outnumber the workgroups that fit at once (two of 8 waves per CU)
+    // when the bands outnumber the workgroups that fit at once
     if constexpr (C <= 2) {
-        const int64_t resident = 2 * (int64_t)kNumCU;
+        const int64_t resident = per_cu * (int64_t)kNumCU;
         if (nbands > resident && (KT + kGemvWaves - 1) / kGemvWaves <= C) {
-            hipLaunchKernelGGL((k_gemv<FMT, DQ, NI, C, true>), dim3((unsigned)resident), block, 0, st, a);
+            hipLaunchKernelGGL((k_gemv<FMT, DQ, NI, C, true, XL>), dim3((unsigned)resident), block, xbytes, st, a);
             return;
         }
     }
-    hipLaunchKernelGGL((k_gemv<FMT, DQ, NI, C, false>), dim3((unsigned)nbands), block, 0, st, a);
+    // few bands: split each band's rows over 2 or 4 workgroups so that more CUs pull weights
+    KArgs b = a;
+    b.rparts = nbands * 4 <= kNumCU ? 4 : nbands * 2 <= kNumCU ? 2 : 1;
+    const int64_t grid = b.rparts == 1 ? nbands : (nbands + 7) / 8 * 8 * b.rparts;
+    hipLaunchKernelGGL((k_gemv<FMT, DQ, NI, C, false, XL>), dim3((unsigned)grid), block, xbytes, st, b);
+}
+
+// The LDS copy of X is used when it is small enough, and when it either keeps two workgroups
+// per CU (<= 8 KiB) or the bands fit one workgroup per CU anyway.
+template <int FMT, bool DQ, int NI, int C>
+static void gemv_launch_c(const KArgs& a, int64_t nbands, int64_t KT, hipStream_t st) {
+    const int64_t mk = (int64_t)a.m * a.k;
+    if (mk <= kGemvXlMax && (mk * 2 <= 8192 || nbands <= kNumCU)) gemv_launch_cx<FMT, DQ, NI, C, true>(a, nbands, KT, st);
+    else gemv_launch_cx<FMT, DQ, NI, C, false>(a, nbands, KT, st);
 }
 
 template <int FMT, bool DQ, int NI>
