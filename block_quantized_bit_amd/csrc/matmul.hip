@@ -55,7 +55,6 @@ struct KArgs {
     uint32_t* counters;  // one per output tile when ksplit > 1
     int64_t tiles_m, tiles_n;
     int out_vec;         // every output split allows 4-column vector stores (alignment, split ends % 4)
-    int rparts;          // GEMV: workgroups sharing one 16-row band, each owning 16 / rparts rows
 };
 
 // NF4 level of code c as a 16-way select over literals.  Table fills use these
@@ -292,23 +291,45 @@ struct GemvTile {
 
 constexpr int kGemvWaves = 8;   // waves per workgroup, all on one band, splitting its K range
 
-// Vector memory instructions gemv_load issues for a tile's codes and scales (X excluded).
+// Vector memory instructions gemv_load issues for a tile's codes and scales (X excluded; for
+// double quant with k <= 16384, plus two per band for the row's group scales -- a wait for at
+// most this many per tile outstanding can only wait longer than needed).
 template <int FMT, bool DQ>
-__device__ constexpr int gemv_w_loads() { return (FMT == kNF4 && DQ) ? 4 : 2; }
+__device__ constexpr int gemv_w_loads() { return 2; }
 
+// Double-quant group scales of one row, when the row holds <= 256 blocks (k <= 16384) and so
+// spans at most two 256-block groups: blocks j < jt of the row are in the first.
+struct DqRow {
+    float dA, dB;
+    int32_t jt;
+};
+
+__device__ inline DqRow dq_row(const KArgs& a, int64_t row) {
+    const int64_t nbr = a.k / 64, b0 = row * nbr;
+    const int64_t gA = b0 >> 8, gB = (b0 + nbr - 1) >> 8;
+    const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
+    return DqRow{dt[gA], dt[gB], (int32_t)((gA + 1) * 256 - b0)};
+}
+
+// dq: non-null when the double-quant group scales come from the row's pair (DqRow) instead of
+// being gathered per tile.
 template <int FMT, bool DQ, bool XL = false>
 __device__ inline void gemv_load(GemvTile<FMT>& t, const KArgs& a, int64_t band, int64_t kt, int lane, int r,
-                                 const uint16_t* xrow, int64_t KT) {
+                                 const uint16_t* xrow, int64_t KT, const DqRow* dq = nullptr) {
     constexpr int TK = tile_k(FMT);
     const int64_t tile = band * KT + kt;
     t.code = *reinterpret_cast<const uint4*>(a.codes + tile * kTileBytes + lane * 16);
     if constexpr (FMT == kNF4) {
         if constexpr (DQ) {
             t.sc[0] = *reinterpret_cast<const uint16_t*>(a.scales + tile * 32 + r * 2);
-            const int64_t b0 = (band * 16 + r) * (a.k / 64) + kt * 2;
-            const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
-            t.sc[1] = __float_as_uint(dt[b0 >> 8]);
-            t.sc[2] = __float_as_uint(dt[(b0 + 1) >> 8]);
+            if (dq) {
+                // group scales: taken from the row's pair at use time (gemv_dq_scales)
+            } else {
+                const int64_t b0 = (band * 16 + r) * (a.k / 64) + kt * 2;
+                const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
+                t.sc[1] = __float_as_uint(dt[b0 >> 8]);
+                t.sc[2] = __float_as_uint(dt[(b0 + 1) >> 8]);
+            }
         } else {
             const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 32 + r * 2) * 4);
             t.sc[0] = v.x;
@@ -426,27 +447,38 @@ __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const ui
 // Wave w of a workgroup owns tiles w, w + 8, w + 16, ... of its band's K range:
 // C of them, all requested before any is used.  A band is finished by summing
 // the 8 waves' 16x16 partial tiles in LDS in wave order.
+// Double quant with fewer than 8 tiles per wave (k <= 5120 here) takes the row's two group
+// scales once per band (DqRow) instead of two gathers per tile.
+template <int FMT, bool DQ, int C>
+__device__ constexpr bool gemv_dq_rows() { return FMT == kNF4 && DQ && C < 8; }
+
 template <int FMT, bool DQ, int C, bool XL>
-__device__ __forceinline__ void gemv_load_band(GemvTile<FMT> (&R)[C], const KArgs& a, int64_t band, int64_t c0,
-                                               int wave, int lane, int r, const uint16_t* xrow,
+__device__ __forceinline__ void gemv_load_band(GemvTile<FMT> (&R)[C], DqRow& dq, const KArgs& a, int64_t band,
+                                               int64_t c0, int wave, int lane, int r, const uint16_t* xrow,
                                                int64_t KT) {
+    constexpr bool DR = gemv_dq_rows<FMT, DQ, C>();
+    if constexpr (DR) dq = dq_row(a, band * 16 + r);
 #pragma unroll
     for (int s = 0; s < C; s++) {
         const int64_t kt = std::min<int64_t>(wave + (c0 + s) * kGemvWaves, KT - 1);
-        gemv_load<FMT, DQ, XL>(R[s], a, band, kt, lane, r, xrow, KT);
+        gemv_load<FMT, DQ, XL>(R[s], a, band, kt, lane, r, xrow, KT, DR ? &dq : nullptr);
     }
 }
 
 // XL: the A operands come from the LDS copy of X (xl = this lane's row, chunk h), read here.
 template <int FMT, bool DQ, int NI, int C, bool XL>
-__device__ __forceinline__ void gemv_consume_band(GemvTile<FMT> (&R)[C], f32x4& acc, int64_t c0, int wave,
-                                                  int64_t KT, const uint32_t* lut, uint32_t lane4, int h, float mu,
-                                                  const uint16_t* xl) {
+__device__ __forceinline__ void gemv_consume_band(GemvTile<FMT> (&R)[C], const DqRow& dq, f32x4& acc, int64_t c0,
+                                                  int wave, int64_t KT, const uint32_t* lut, uint32_t lane4, int h,
+                                                  float mu, const uint16_t* xl) {
     constexpr int TK = tile_k(FMT);
 #pragma unroll
     for (int s = 0; s < C; s++) {
         const int64_t kt = wave + (c0 + s) * kGemvWaves;
         if (kt < KT) {
+            if constexpr (gemv_dq_rows<FMT, DQ, C>()) {
+                R[s].sc[1] = __float_as_uint(2 * kt < dq.jt ? dq.dA : dq.dB);
+                R[s].sc[2] = __float_as_uint(2 * kt + 1 < dq.jt ? dq.dA : dq.dB);
+            }
             if constexpr (XL) {
 #pragma unroll
                 for (int j = 0; j < TK / 32; j++) {
@@ -460,7 +492,7 @@ __device__ __forceinline__ void gemv_consume_band(GemvTile<FMT> (&R)[C], f32x4& 
 }
 
 __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kGemvWaves][64], const f32x4& acc,
-                                                 int64_t band, int wave, int lane, float g, bool own = true) {
+                                                 int64_t band, int wave, int lane, float g) {
     const int r = lane & 15, h = lane >> 4;
     red[wave][lane] = acc;
     __syncthreads();
@@ -472,18 +504,14 @@ __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kG
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int mm = 4 * h + i;
-            if (mm < a.m && own) put_out(a, c, mm, v[i], g);
+            if (mm < a.m) put_out(a, c, mm, v[i], g);
         }
     }
     __syncthreads();
 }
 
-// PIPE = false: every workgroup owns one band, or 16 / rparts of its rows
-//   (rparts > 1 spreads few bands over more CUs; the parts of a band run on one
-//   XCD), its tiles come in rounds of C per wave (one round when K <= 8 * C tiles).
-//   A workgroup owning part of a band loads only its rows: every lane of the
-//   wave points at the slot of one of those rows, so no other row's bytes are
-//   fetched, and only the lanes of its own rows store.
+// PIPE = false: every workgroup owns one band (grid == number of bands), its
+//   tiles come in rounds of C per wave (one round when K <= 8 * C tiles).
 // PIPE = true : workgroups loop over bands; each wave holds all its tiles of a
 //   band in one round (K <= 8 * C tiles) and requests the next band's tiles
 //   before using the current ones.  The prefetch index is clamped to the last
@@ -515,17 +543,7 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
     const int64_t per_wave = (KT + kGemvWaves - 1) / kGemvWaves;
 
     if constexpr (!PIPE) {
-        const int P = a.rparts;
-        int64_t band = blockIdx.x;
-        int part = 0;
-        if (P > 1) {   // workgroup b runs on XCD b % 8: give the parts of a band the same b % 8
-            const int64_t q = blockIdx.x / 8;
-            part = (int)(q % P);
-            band = (q / P) * 8 + blockIdx.x % 8;
-            if (band >= nbands) return;     // the whole workgroup, before any barrier
-        }
-        const int rows = 16 / P;
-        const int rs = part * rows + (r & (rows - 1));     // row whose data this lane loads
+        const int64_t band = blockIdx.x;
         // With XL the code table is filled first: LDS writes issued while the LDS-direct X copy
         // is in flight would have to wait for every load.  Otherwise it is filled while the first
         // tiles are in flight.
@@ -536,7 +554,8 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int64_t c0 = 0; c0 < per_wave; c0 += C) {
             GemvTile<FMT> R[C];
-            gemv_load_band<FMT, DQ, C, XL>(R, a, band, c0, wave, rs + 16 * h, rs, xrow, KT);
+            DqRow dq;
+            gemv_load_band<FMT, DQ, C, XL>(R, dq, a, band, c0, wave, lane, r, xrow, KT);
             if (c0 == 0) {
                 if constexpr (XL) {
                     lds_barrier_vm<C * gemv_w_loads<FMT, DQ>()>();
@@ -545,18 +564,19 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
                     __syncthreads();
                 }
             }
-            gemv_consume_band<FMT, DQ, NI, C, XL>(R, acc, c0, wave, KT, lut, lane4, h, mu, xl);
+            gemv_consume_band<FMT, DQ, NI, C, XL>(R, dq, acc, c0, wave, KT, lut, lane4, h, mu, xl);
         }
-        gemv_finish_band(a, red, acc, band, wave, lane, g, rs == r);
+        gemv_finish_band(a, red, acc, band, wave, lane, g);
     } else {
         const int64_t stride = gridDim.x;
         GemvTile<FMT> R0[C], R1[C];
+        DqRow dq0, dq1;
         int64_t band = blockIdx.x;
         if constexpr (XL) {
             if constexpr (FMT != kQ8_0) build_lut<FMT, 64 * kGemvWaves>(lut);
             gemv_stage_x(xs_dyn, a, wave, lane);
         }
-        gemv_load_band<FMT, DQ, C, XL>(R0, a, band, 0, wave, lane, r, xrow, KT);
+        gemv_load_band<FMT, DQ, C, XL>(R0, dq0, a, band, 0, wave, lane, r, xrow, KT);
         if constexpr (XL) {
             lds_barrier_vm<C * gemv_w_loads<FMT, DQ>()>();
         } else {
@@ -565,15 +585,15 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
         }
         for (; band < nbands; band += 2 * stride) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            gemv_load_band<FMT, DQ, C, XL>(R1, a, std::min<int64_t>(band + stride, nbands - 1), 0, wave, lane, r,
-                                          xrow, KT);
-            gemv_consume_band<FMT, DQ, NI, C, XL>(R0, acc, 0, wave, KT, lut, lane4, h, mu, xl);
+            gemv_load_band<FMT, DQ, C, XL>(R1, dq1, a, std::min<int64_t>(band + stride, nbands - 1), 0, wave, lane,
+                                          r, xrow, KT);
+            gemv_consume_band<FMT, DQ, NI, C, XL>(R0, dq0, acc, 0, wave, KT, lut, lane4, h, mu, xl);
             gemv_finish_band(a, red, acc, band, wave, lane, g);
             if (band + stride >= nbands) break;
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
-            gemv_load_band<FMT, DQ, C, XL>(R0, a, std::min<int64_t>(band + 2 * stride, nbands - 1), 0, wave, lane, r,
-                                          xrow, KT);
-            gemv_consume_band<FMT, DQ, NI, C, XL>(R1, acc, 0, wave, KT, lut, lane4, h, mu, xl);
+            gemv_load_band<FMT, DQ, C, XL>(R0, dq0, a, std::min<int64_t>(band + 2 * stride, nbands - 1), 0, wave,
+                                          lane, r, xrow, KT);
+            gemv_consume_band<FMT, DQ, NI, C, XL>(R1, dq1, acc, 0, wave, KT, lut, lane4, h, mu, xl);
             gemv_finish_band(a, red, acc, band + stride, wave, lane, g);
         }
     }
@@ -1239,7 +1259,6 @@ static KArgs make_args(const MatmulProblem& p) {
     a.out = p.out;
     a.L = scale_layout(p.fmt, p.dq, p.n, p.k);
     a.ksplit = 1;
-    a.rparts = 1;
     const uintptr_t align = p.out.f32 ? 16 : 8;
     a.out_vec = 1;
     for (int i = 0; i < p.out.nsplit; i++) {
@@ -1273,19 +1292,17 @@ static void gemv_launch_cx(const KArgs& a, int64_t nbands, int64_t KT, hipStream
             return;
         }
     }
-    // few bands: split each band's rows over 2 or 4 workgroups so that more CUs pull weights
-    KArgs b = a;
-    b.rparts = nbands * 4 <= kNumCU ? 4 : nbands * 2 <= kNumCU ? 2 : 1;
-    const int64_t grid = b.rparts == 1 ? nbands : (nbands + 7) / 8 * 8 * b.rparts;
-    hipLaunchKernelGGL((k_gemv<FMT, DQ, NI, C, false, XL>), dim3((unsigned)grid), block, xbytes, st, b);
+    hipLaunchKernelGGL((k_gemv<FMT, DQ, NI, C, false, XL>), dim3((unsigned)nbands), block, xbytes, st, a);
 }
 
-// The LDS copy of X is used when it is small enough, and when it either keeps two workgroups
-// per CU (<= 8 KiB) or the bands fit one workgroup per CU anyway.
+// The LDS copy of X is used when it is small enough, when every band gets its own workgroup
+// (no band pipelining: its per-band barriers would wait for the prefetched band's loads), and
+// when it either keeps two workgroups per CU (<= 8 KiB) or the bands fit one per CU anyway.
 template <int FMT, bool DQ, int NI, int C>
 static void gemv_launch_c(const KArgs& a, int64_t nbands, int64_t KT, hipStream_t st) {
     const int64_t mk = (int64_t)a.m * a.k;
-    if (mk <= kGemvXlMax && (mk * 2 <= 8192 || nbands <= kNumCU)) gemv_launch_cx<FMT, DQ, NI, C, true>(a, nbands, KT, st);
+    const bool xl = mk <= kGemvXlMax && nbands <= 2 * kNumCU && (mk * 2 <= 8192 || nbands <= kNumCU);
+    if (xl) gemv_launch_cx<FMT, DQ, NI, C, true>(a, nbands, KT, st);
     else gemv_launch_cx<FMT, DQ, NI, C, false>(a, nbands, KT, st);
 }
 
