@@ -55,6 +55,7 @@ struct KArgs {
     uint32_t* counters;  // one per output tile when ksplit > 1
     int64_t tiles_m, tiles_n;
     int out_vec;         // every output split allows 4-column vector stores (alignment, split ends % 4)
+    int out_v16;         // bf16 output whose splits allow 8-column (16-byte) stores
 };
 
 // NF4 level of code c as a 16-way select over literals.  Table fills use these
@@ -1094,6 +1095,46 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     wait_vm<0>();   // the last requests (re-reads of the last step) land before the workgroup ends
 
     // ---- epilogue ----
+    if (a.ksplit == 1 && a.out_v16) {
+        // The tile's bf16 results go through LDS (the X buffers are free once every
+        // wave's loads have landed), so that each output row is written in whole
+        // 128-byte pieces by 16-byte stores rather than in 32-byte fragments.
+        // Wave w stages its 128 x 64 block (16 KiB, rows of 128 bytes whose 16-byte
+        // chunks are XOR-swizzled by row) and writes it back itself.
+        __syncthreads();
+        uint8_t* stg = (wave < 2 ? xs0 : xs1) + (wave & 1) * 16384;
+        const int t = r & 3, q = r >> 2;
+#pragma unroll
+        for (int nf = 0; nf < 4; nf++) {
+            if (band0 + nf >= nbands) continue;     // same for the whole wave
+            const float bias = a.bias ? bf16_value(a.bias[(band0 + nf) * 16 + r]) : 0.0f;
+#pragma unroll
+            for (int mf = 0; mf < 8; mf++) {
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; i++) v[i] = acc[mf][nf][i] * g + bias;
+                quad_transpose(v, t);   // now row 16 mf + 4h + t, columns 16 nf + 4q .. 4q + 3
+                const int row = 16 * mf + 4 * h + t;
+                const int ch = (2 * nf + (q >> 1)) ^ (row & 7);
+                *reinterpret_cast<uint2*>(stg + row * 128 + ch * 16 + (q & 1) * 8) =
+                    make_uint2(pack_bf16_rne(v[0], v[1]), pack_bf16_rne(v[2], v[3]));
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        const int c = lane & 7;
+        const int64_t col = band0 * 16 + 8 * c;
+        if (col < N) {
+            const ColOut o = col_out_nobias(a, col);
+#pragma unroll
+            for (int it = 0; it < 16; it++) {
+                const int row = 8 * it + (lane >> 3);
+                const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 128 + ((c ^ (row & 7)) << 4));
+                if (m0 + row < M) *reinterpret_cast<uint4*>(o.p + (m0 + row) * o.ld) = v;
+            }
+        }
+        return;
+    }
     if (a.ksplit == 1) {
         const bool full = m0 + BM <= M;     // every row of the tile exists (all but the last row tile)
 #pragma unroll
@@ -1261,9 +1302,11 @@ static KArgs make_args(const MatmulProblem& p) {
     a.ksplit = 1;
     const uintptr_t align = p.out.f32 ? 16 : 8;
     a.out_vec = 1;
+    a.out_v16 = p.out.f32 ? 0 : 1;
     for (int i = 0; i < p.out.nsplit; i++) {
-        if (reinterpret_cast<uintptr_t>(p.out.y[i]) % align != 0 || p.out.ldy[i] % 4 != 0 || p.out.end[i] % 4 != 0)
-            a.out_vec = 0;
+        const uintptr_t y = reinterpret_cast<uintptr_t>(p.out.y[i]);
+        if (y % align != 0 || p.out.ldy[i] % 4 != 0 || p.out.end[i] % 4 != 0) a.out_vec = 0;
+        if (y % 16 != 0 || p.out.ldy[i] % 8 != 0 || p.out.end[i] % 8 != 0) a.out_v16 = 0;
     }
     return a;
 }
