@@ -1173,34 +1173,44 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
         }
         return;
     }
-    // K split: deposit this piece's partial tile; k_splitk_reduce finishes the outputs
-    // (full row tiles: quad-transposed 16-byte stores; the workspace is 16-byte aligned and N % 16 == 0)
-    const bool full = m0 + BM <= M;
-    const int t = r & 3;
+    // K split: deposit this piece's partial tile; k_splitk_reduce finishes the outputs.
+    // Staged through LDS like the bf16 output: wave w writes its 128 x 64 fp32 block in
+    // two halves of 64 rows (16 KiB each, rows of 256 bytes with 16-byte chunks
+    // XOR-swizzled by row), each row then leaving as one 256-byte piece.  The workspace
+    // is 16-byte aligned and N % 16 == 0.
+    __syncthreads();
+    uint8_t* stg = (wave < 2 ? xs0 : xs1) + (wave & 1) * 16384;
+    const int t = r & 3, q = r >> 2;
+    const int c = lane & 15;
+    const bool colok = band0 + (c >> 2) < nbands;
+    float* const pbase = a.partial + ((int64_t)ks * M + m0) * N + band0 * 16 + 4 * c;
 #pragma unroll
-    for (int nf = 0; nf < 4; nf++) {
-        if (band0 + nf >= nbands) continue;     // same for the whole wave
-        const int64_t col = (band0 + nf) * 16 + r;
-        if (full) {
-            float* p = a.partial + ((int64_t)ks * M + m0 + 4 * h + t) * N + (col - t);
+    for (int half = 0; half < 2; half++) {
 #pragma unroll
-            for (int mf = 0; mf < 8; mf++) {
+        for (int nf = 0; nf < 4; nf++) {
+#pragma unroll
+            for (int mh = 0; mh < 4; mh++) {
+                const int mf = 4 * half + mh;
                 float v[4];
 #pragma unroll
                 for (int i = 0; i < 4; i++) v[i] = acc[mf][nf][i];
-                quad_transpose(v, t);
-                *reinterpret_cast<f32x4*>(p) = f32x4{v[0], v[1], v[2], v[3]};
-                p += 16 * N;
+                quad_transpose(v, t);   // now row 16 mf + 4h + t, columns 16 nf + 4q .. 4q + 3
+                const int row = 16 * mh + 4 * h + t;
+                *reinterpret_cast<f32x4*>(stg + row * 256 + (((4 * nf + q) ^ (row & 15)) << 4)) =
+                    f32x4{v[0], v[1], v[2], v[3]};
             }
-        } else {
-#pragma unroll
-            for (int mf = 0; mf < 8; mf++)
-#pragma unroll
-                for (int i = 0; i < 4; i++) {
-                    const int64_t mm = m0 + 16 * mf + 4 * h + i;
-                    if (mm < M) a.partial[((int64_t)ks * M + mm) * N + col] = acc[mf][nf][i];
-                }
         }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int it = 0; it < 16; it++) {
+            const int row = 4 * it + (lane >> 4);
+            const f32x4 v = *reinterpret_cast<const f32x4*>(stg + row * 256 + ((c ^ (row & 15)) << 4));
+            const int64_t mrow = 64 * half + row;
+            if (colok && m0 + mrow < M) *reinterpret_cast<f32x4*>(pbase + mrow * N) = v;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        __builtin_amdgcn_wave_barrier();
     }
 }
 
