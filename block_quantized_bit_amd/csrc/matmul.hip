@@ -1005,16 +1005,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     const int64_t KT = K / TK;
     const int64_t nsteps_total = K / BK;
 
-    // XCD-aware item order: consecutive items (same N tile, neighbouring M tiles
-    // and K pieces) run on the same XCD and share its L2.
-    const int64_t items = a.tiles_m * a.tiles_n * a.ksplit;
+    // XCD-aware item order.  Workgroups are dealt to the 8 XCDs in turn, so XCD x
+    // gets the consecutive items [x * per_xcd, (x + 1) * per_xcd).  Items run K piece
+    // by K piece, and within a piece in groups of kGroupM row tiles by all column
+    // tiles, column-major inside the group: the items an XCD runs at one time cover
+    // a compact block of row and column tiles, whose X rows and W bands its L2 holds.
+    constexpr int64_t kGroupM = 6;
+    const int64_t tiles = a.tiles_m * a.tiles_n;
+    const int64_t items = tiles * a.ksplit;
     const int64_t per_xcd = (int64_t)gridDim.x / 8;
     const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (item >= items) return;
-    const int ks = (int)(item % a.ksplit);
-    const int64_t tmn = item / a.ksplit;
-    const int64_t tm = tmn % a.tiles_m;
-    const int64_t tn = tmn / a.tiles_m;
+    const int ks = (int)(item / tiles);
+    const int64_t ti = item - (int64_t)ks * tiles;
+    const int64_t grp = ti / (kGroupM * a.tiles_n);
+    const int64_t gm = std::min<int64_t>(kGroupM, a.tiles_m - grp * kGroupM);
+    const int64_t within = ti - grp * kGroupM * a.tiles_n;
+    const int64_t tm = grp * kGroupM + within % gm;
+    const int64_t tn = within / gm;
     const int64_t m0 = tm * BM, n0 = tn * BN;
     const int64_t s0 = ks * a.kt_per, s1 = std::min<int64_t>(nsteps_total, s0 + a.kt_per);  // in BK steps
 
