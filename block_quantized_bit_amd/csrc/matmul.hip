@@ -775,14 +775,14 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
 // 32-wide K slices are software-pipelined: the A fragments and dequantized B
 // fragments of slice j+1 are produced while the MFMAs of slice j run, and the
 // schedule interleaves MFMA, VALU and LDS instructions explicitly.
-// LDS: the fp32 code table (NF4, Q4_0), then three X tiles.
+// LDS: the fp32 code table (NF4), then three X tiles.
 // ===========================================================================
 constexpr int BM = 128, BN = 256, BK = 128;
 constexpr int kLutBytes = kLutWords * 4;
 constexpr int kXsBytes = BM * BK * 2;      // one X tile: 128 rows x 256 B, 16-byte chunks XOR-swizzled by row
 
 template <int FMT>
-__device__ constexpr bool gemm_uses_lut() { return FMT == kNF4 || FMT == kQ4_0; }
+__device__ constexpr bool gemm_uses_lut() { return FMT == kNF4; }
 
 template <int FMT>
 struct GemmW {
@@ -870,18 +870,30 @@ __device__ __forceinline__ u32x4 gemm_dequant(const GemmW<FMT>& w, int j, const 
             else v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
             B[q] = pack_bf16_rne(__fmul_rn(v[0], s), __fmul_rn(v[1], s));
         }
-    } else {
+    } else if constexpr (FMT == kQ4_0) {
+        // nibble c as a float, then c*d - 8d: both products are exact in fp32 (c has 4
+        // significant bits, d 11), so this is (c - 8)*d exactly; one RNE to bf16
         const uint32_t word = j == 0 ? w.code[0].x : j == 1 ? w.code[0].y : j == 2 ? w.code[0].z : w.code[0].w;
+        const float d = f16_value((uint16_t)(w.sc[j >> 1] >> (16 * (j & 1))));
+        const float d8 = -8.0f * d;
+        uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+        // opaque to the optimizer, so that each byte converts with one v_cvt_f32_ubyteN
+        // instead of a bit-field extract followed by a conversion
+        asm("" : "+v"(lo), "+v"(hi));
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const float c0 = (float)((lo >> (8 * q)) & 255u);
+            const float c1 = (float)((hi >> (8 * q)) & 255u);
+            B[q] = pack_bf16_rne(__builtin_fmaf(c0, d, d8), __builtin_fmaf(c1, d, d8));
+        }
+    } else {   // NF4: code values from the LDS table
+        const uint32_t word = j == 0 ? w.code[0].x : j == 1 ? w.code[0].y : j == 2 ? w.code[0].z : w.code[0].w;
+        const int kb = j >> 1;
         float s;
-        if constexpr (FMT == kNF4) {
-            const int kb = j >> 1;
-            if constexpr (DQ) {
-                s = __fadd_rn(__fmul_rn((float)(int8_t)((w.sc[0] >> (8 * kb)) & 255u), __uint_as_float(w.sc[1 + kb])), mu);
-            } else {
-                s = __uint_as_float(w.sc[kb]);
-            }
-        } else {  // Q4_0
-            s = f16_value((uint16_t)(w.sc[j >> 1] >> (16 * (j & 1))));
+        if constexpr (DQ) {
+            s = __fadd_rn(__fmul_rn((float)(int8_t)((w.sc[0] >> (8 * kb)) & 255u), __uint_as_float(w.sc[1 + kb])), mu);
+        } else {
+            s = __uint_as_float(w.sc[kb]);
         }
 #pragma unroll
         for (int q = 0; q < 4; q++) {
