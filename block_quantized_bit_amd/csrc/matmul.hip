@@ -767,15 +767,16 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
 // ===========================================================================
 // GEMM, m >= 17.  Workgroup tile 128 (M) x 256 (N), K step 128; wave w owns
 // columns [64w, 64w+64) (4 bands) for all 128 rows: 8 x 4 MFMA tiles of 16x16.
-// Three-stage pipeline: X tiles (LDS, filled by LDS-direct loads) and W codes/
-// scales (registers) for step s+2 are requested while step s is computed, so
-// two steps of compute cover the load latency.  Requests are unconditional
-// (rows past m and bands past n re-read valid rows, steps past the end re-read
-// the last step; none of those results is stored).  Within a step the four
-// 32-wide K slices are software-pipelined: the A fragments and dequantized B
-// fragments of slice j+1 are produced while the MFMAs of slice j run, and the
-// schedule interleaves MFMA, VALU and LDS instructions explicitly.
-// LDS: the fp32 code table (NF4), then three X tiles.
+// Two-stage pipeline: the X tile (LDS, filled by LDS-direct loads) and W codes/
+// scales (registers) of step s+1 are requested at the start of step s and are
+// waited for at the one workgroup synchronization of step s, after three of its
+// four 32-wide K slices.  Requests are unconditional (rows past m and bands past
+// n re-read valid rows, steps past the end re-read the last step; none of those
+// results is stored).  The K slices are software-pipelined across steps: the A
+// fragments and dequantized B fragments of the next slice (in the last slice,
+// the next step's first) are produced while the MFMAs of the current slice run,
+// and the schedule interleaves MFMA, VALU and LDS instructions explicitly.
+// LDS: the fp32 code table (NF4), then two X tiles.
 // ===========================================================================
 constexpr int BM = 128, BN = 256, BK = 128;
 constexpr int kLutBytes = kLutWords * 4;
@@ -945,54 +946,57 @@ __device__ __forceinline__ void gemm_dequant4(u32x4 (&B)[4], const GemmW<FMT> (&
 }
 
 // One K step: request step nx into (wn, xnext), compute the step held in
-// (wc, xcur), then wait until the step after this one has landed (the
-// requests just made may stay in flight) and synchronize the workgroup.
-// On entry B holds slice 0 of wc dequantized; on exit, slice 0 of wf (the
-// W set of the following step).  Slice j's 32 MFMAs run in row-fragment order
-// (one A fragment live at a time) interleaved with the next slice's dequant.
-template <int FMT, bool DQ>
-__device__ __forceinline__ void gemm_kstep(f32x4 (&acc)[8][4], u32x4 (&B)[4], const GemmW<FMT> (&wc)[4],
-                                           GemmW<FMT> (&wn)[4], const GemmW<FMT> (&wf)[4], const GemmSrc& S,
-                                           const int64_t (&rowblk)[4], const uint32_t (&xoff)[kXLoads],
-                                           const uint8_t* xcur, uint8_t* xnext, const uint32_t* lut, int nx, bool more,
-                                           int wave, int lane, int r, int h, uint32_t lane8, uint32_t hs, float mu) {
+// (wc, xcur).  On entry A holds the A fragments of K slice 0 and B slice 0 of wc
+// dequantized.  Slice j's 32 MFMAs run in row-fragment order; as soon as the four
+// MFMAs of row fragment mf have issued, its register set is refilled with the
+// next slice's fragment mf (8 A fragments live, not 16), and the next slice's B
+// fragments are dequantized in between.
+// The workgroup synchronizes once per step, after slice 2: by then every wave has
+// read all of xcur (slice 3's fragments are read during slice 2), and waiting for
+// all but the newest requests makes the following step's X tile (xfol) and W set
+// (wf) complete.  Slice 3 then reads the following step's slice-0 A fragments and
+// dequantizes its slice-0 B fragments (when `more`), so the next step starts
+// with its operands in registers.  The next step's requests overwrite xcur's
+// buffer only after this synchronization.
+template <int FMT, bool DQ, int NWAIT>
+__device__ __forceinline__ void gemm_kstep(f32x4 (&acc)[8][4], u32x4 (&A)[8], u32x4 (&B)[4],
+                                           const GemmW<FMT> (&wc)[4], GemmW<FMT> (&wn)[4], const GemmW<FMT> (&wf)[4],
+                                           const GemmSrc& S, const int64_t (&rowblk)[4], const uint32_t (&xoff)[kXLoads],
+                                           const uint8_t* xcur, uint8_t* xnext, const uint8_t* xfol, const uint32_t* lut,
+                                           int nx, bool more, int wave, int lane, int r, int h, uint32_t lane8,
+                                           uint32_t hs, float mu) {
     gemm_load_w4<FMT, DQ>(wn, S, rowblk, nx, lane, r);
     gemm_load_x_lds(xnext, S, xoff, wave, nx);
     const uint32_t arow = (uint32_t)r * 256u;
-    // A fragments double-buffered across slices: slice j+1's are read while slice j's MFMAs run
-    u32x4 A[2][8];
-#pragma unroll
-    for (int mf = 0; mf < 8; mf++) A[0][mf] = gemm_load_a(xcur, arow, mf, 0, h, r);
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        const int c = j & 1;
+        const bool refill = j < 3 || more;
+        const uint8_t* asrc = j < 3 ? xcur : xfol;
+        const int aslice = j < 3 ? j + 1 : 0;
         u32x4 Bn[4];
-        if (j < 3) {
+        if (j < 3) gemm_dequant4<FMT, DQ>(Bn, wc, j + 1, lut, lane8, hs, mu);
+        else if (more) gemm_dequant4<FMT, DQ>(Bn, wf, 0, lut, lane8, hs, mu);
 #pragma unroll
-            for (int mf = 0; mf < 8; mf++) A[c ^ 1][mf] = gemm_load_a(xcur, arow, mf, j + 1, h, r);
-            gemm_dequant4<FMT, DQ>(Bn, wc, j + 1, lut, lane8, hs, mu);
-        } else if (more) {
-            gemm_dequant4<FMT, DQ>(Bn, wf, 0, lut, lane8, hs, mu);
+        for (int mf = 0; mf < 8; mf++) {
+#pragma unroll
+            for (int nf = 0; nf < 4; nf++) acc[mf][nf] = mfma(A[mf], B[nf], acc[mf][nf]);
+            if (refill) A[mf] = gemm_load_a(asrc, arow, mf, aslice, h, r);
         }
-#pragma unroll
-        for (int mf = 0; mf < 8; mf++)
-#pragma unroll
-            for (int nf = 0; nf < 4; nf++) acc[mf][nf] = mfma(A[c][mf], B[nf], acc[mf][nf]);
-        // 32 MFMAs, each followed by a share of the next slice's dequant; the next slice's A
-        // reads (and, in the first slice, the next step's loads) are spread over them too
+        // 32 MFMAs, each followed by a share of the next slice's dequant; the A
+        // refills follow the fourth MFMA of each row fragment, and in the first
+        // slice the next step's loads are spread over the MFMAs too
 #pragma unroll
         for (int i = 0; i < 32; i++) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-            if (j < 3 && (i & 3) == 0) __builtin_amdgcn_sched_group_barrier(0x100, gemm_uses_lut<FMT>() ? 3 : 1, 0);
+            if (refill && (i & 3) == 3) __builtin_amdgcn_sched_group_barrier(0x100, gemm_uses_lut<FMT>() ? 3 : 1, 0);
             if (j == 0 && i < gemm_step_loads<FMT, DQ>()) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int nf = 0; nf < 4; nf++) B[nf] = Bn[nf];
+        if (j == 2) lds_barrier_vm<NWAIT>();
     }
-    wait_vm<gemm_step_loads<FMT, DQ>()>();
-    __syncthreads();
 }
 
 template <int FMT, bool DQ>
@@ -1002,7 +1006,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     __shared__ __attribute__((aligned(16))) uint32_t lut_s[gemm_uses_lut<FMT>() ? kLutWords : 4];
     __shared__ __attribute__((aligned(16))) uint8_t xs0[kXsBytes];
     __shared__ __attribute__((aligned(16))) uint8_t xs1[kXsBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t xs2[kXsBytes];
     const uint32_t* lut = lut_s;
 
     const int tid = threadIdx.x;
@@ -1082,36 +1085,31 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
 
     // every K piece is non-empty (the schedule guarantees s0 < s1)
     const int first = (int)s0, last = (int)s1 - 1, end = (int)s1;
-    GemmW<FMT> w0[4], w1[4], w2[4];
+    GemmW<FMT> w0[4], w1[4];
     gemm_load_w4<FMT, DQ>(w0, S, rowblk, first, lane, r);
     gemm_load_x_lds(xs0, S, xoff, wave, first);
-    gemm_load_w4<FMT, DQ>(w1, S, rowblk, std::min(first + 1, last), lane, r);
-    gemm_load_x_lds(xs1, S, xoff, wave, std::min(first + 1, last));
     if constexpr (gemm_uses_lut<FMT>()) build_lut_f32<FMT>(lut_s);
-    wait_vm<gemm_step_loads<FMT, DQ>()>();
+    wait_vm<0>();
     __syncthreads();
-    u32x4 B[4];
+    u32x4 A[8], B[4];
+#pragma unroll
+    for (int mf = 0; mf < 8; mf++) A[mf] = gemm_load_a(xs0, (uint32_t)r * 256u, mf, 0, h, r);
     gemm_dequant4<FMT, DQ>(B, w0, 0, lut, lane8, hs, mu);
 
-    // buffers rotate with period 3: step s reads (w[s%3], xs[s%3]) and fills (w[(s+2)%3], xs[(s+2)%3]).
-    // Whole groups of three steps run in a loop with a single exit; the last
-    // one or two steps follow it.
+    // two buffer sets: step s reads (w[s%2], xs[s%2]) and requests step s + 1 into
+    // the other set, whose previous contents were last read before the previous
+    // step's synchronization.  Pairs of steps run in a loop with a single exit;
+    // an odd last step follows it.
     int st = first;
-    for (; st + 3 <= end; st += 3) {
-        gemm_kstep<FMT, DQ>(acc, B, w0, w2, w1, S, rowblk, xoff, xs0, xs2, lut, std::min(st + 2, last), true,
-                            wave, lane, r, h, lane8, hs, mu);
-        gemm_kstep<FMT, DQ>(acc, B, w1, w0, w2, S, rowblk, xoff, xs1, xs0, lut, std::min(st + 3, last), true,
-                            wave, lane, r, h, lane8, hs, mu);
-        gemm_kstep<FMT, DQ>(acc, B, w2, w1, w0, S, rowblk, xoff, xs2, xs1, lut, std::min(st + 4, last), st + 3 < end,
-                            wave, lane, r, h, lane8, hs, mu);
+    for (; st + 2 <= end; st += 2) {
+        gemm_kstep<FMT, DQ, 0>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, std::min(st + 1, last), true,
+                               wave, lane, r, h, lane8, hs, mu);
+        gemm_kstep<FMT, DQ, 0>(acc, A, B, w1, w0, w0, S, rowblk, xoff, xs1, xs0, xs0, lut, std::min(st + 2, last),
+                               st + 2 < end, wave, lane, r, h, lane8, hs, mu);
     }
-    if (st < end) {
-        gemm_kstep<FMT, DQ>(acc, B, w0, w2, w1, S, rowblk, xoff, xs0, xs2, lut, std::min(st + 2, last), st + 1 < end,
-                            wave, lane, r, h, lane8, hs, mu);
-        if (st + 1 < end)
-            gemm_kstep<FMT, DQ>(acc, B, w1, w0, w2, S, rowblk, xoff, xs1, xs0, lut, std::min(st + 3, last), false,
-                                wave, lane, r, h, lane8, hs, mu);
-    }
+    if (st < end)
+        gemm_kstep<FMT, DQ, 0>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, last, false,
+                               wave, lane, r, h, lane8, hs, mu);
     wait_vm<0>();   // the last requests (re-reads of the last step) land before the workgroup ends
 
     // ---- epilogue ----
@@ -1286,8 +1284,9 @@ struct Sched {
     unsigned grid;
 };
 
-// GEMM: 128 x 256 tiles; K is split only when the tiles cannot fill half the
-// chip, and then only as far as every piece keeps >= 4 K steps.
+// GEMM: 128 x 256 tiles, one workgroup per CU.  K is split only when the tiles
+// cannot fill half the chip, and then doubled only while all pieces still run in
+// one round on the CUs and every piece keeps >= 4 K steps.
 static Sched gemm_sched(int64_t m, int64_t n, int64_t k, bool allow_split) {
     Sched s{};
     s.tiles_m = (m + BM - 1) / BM;
@@ -1296,7 +1295,7 @@ static Sched gemm_sched(int64_t m, int64_t n, int64_t k, bool allow_split) {
     const int64_t tiles = s.tiles_m * s.tiles_n;
     int ks = 1;
     if (allow_split && tiles < kNumCU / 2) {
-        while (tiles * ks < kNumCU && steps / (ks * 2) >= 4) ks *= 2;
+        while (tiles * ks * 2 <= kNumCU && steps / (ks * 2) >= 4) ks *= 2;
     }
     s.ksplit = ks;
     s.kt_per = (steps + ks - 1) / ks;     // every piece non-empty: (ks - 1) * kt_per < steps
