@@ -375,6 +375,11 @@ __device__ __forceinline__ void gemv_stage_x(uint16_t* xs, const KArgs& a, int w
     }
 }
 
+// NF4 and Q4_0 codes become bf16 pairs through the LDS table; NVFP4 and Q8_0
+// convert in registers.
+template <int FMT>
+__device__ constexpr bool gemv_uses_lut() { return FMT == kNF4 || FMT == kQ4_0; }
+
 template <int FMT, bool DQ, int NI>
 __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const uint32_t* lut, uint32_t lane4,
                                     int h, float mu) {
@@ -415,17 +420,23 @@ __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const ui
             for (int i = 0; i < NI; i++) acc[i] += p[i] * s;
         }
     } else if constexpr (FMT == kNVFP4) {
+        // block 2j + (h >> 1) of the row: byte 2 (j & 1) + (h >> 1) of scale word j >> 1
+        const uint32_t hs = 8u * (uint32_t)(h >> 1);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            const int blk = 2 * j + (h >> 1);
-            const uint32_t sb = (t.sc[blk >> 2] >> (8 * (blk & 3))) & 255u;
-            const float s = e4m3_value(sb);
+            const uint32_t sw = t.sc[j >> 1] >> hs;
+            const float s = (j & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)sw, 2) : __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
             u32x4 B;
 #pragma unroll
             for (int q = 0; q < 4; q++) {
-                const uint32_t pr = lut_pair(lut, lane4, uw[j], q);
-                const float lo = lo_f(pr) * s, hi = hi_f(pr) * s;                    // exact
-                B[q] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+                // e2m1 pair of byte q (low nibble first) times the E4M3 scale: exact, so keeping
+                // the upper halves of the fp32 products is the exact bf16 value
+                f32x2 v;
+                if (q == 0) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(uw[j], 1.0f, 0);
+                else if (q == 1) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(uw[j], 1.0f, 1);
+                else if (q == 2) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(uw[j], 1.0f, 2);
+                else v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(uw[j], 1.0f, 3);
+                B[q] = __builtin_amdgcn_perm(__float_as_uint(v[1] * s), __float_as_uint(v[0] * s), 0x07060302u);
             }
             acc = mfma(t.A[j], B, acc);
         }
@@ -528,7 +539,7 @@ __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kG
 //   issued after it) never waits for a weight load.
 template <int FMT, bool DQ, int NI, int C, bool PIPE, bool XL>
 __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArgs a) {
-    __shared__ uint32_t lut[(FMT == kQ8_0) ? 1 : kLutWords];
+    __shared__ uint32_t lut[gemv_uses_lut<FMT>() ? kLutWords : 1];
     __shared__ f32x4 red[kGemvWaves][64];
     extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
 
@@ -553,7 +564,7 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
         // is in flight would have to wait for every load.  Otherwise it is filled while the first
         // tiles are in flight.
         if constexpr (XL) {
-            if constexpr (FMT != kQ8_0) build_lut<FMT, 64 * kGemvWaves>(lut);
+            if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
             gemv_stage_x(xs_dyn, a, wave, lane);
         }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -565,7 +576,7 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
                 if constexpr (XL) {
                     lds_barrier_vm<C * gemv_w_loads<FMT, DQ>()>();
                 } else {
-                    if constexpr (FMT != kQ8_0) build_lut<FMT, 64 * kGemvWaves>(lut);
+                    if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
                     __syncthreads();
                 }
             }
@@ -578,14 +589,14 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
         DqRow dq0, dq1;
         int64_t band = blockIdx.x;
         if constexpr (XL) {
-            if constexpr (FMT != kQ8_0) build_lut<FMT, 64 * kGemvWaves>(lut);
+            if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
             gemv_stage_x(xs_dyn, a, wave, lane);
         }
         gemv_load_band<FMT, DQ, C, XL>(R0, dq0, a, band, 0, wave, lane, r, xrow, KT);
         if constexpr (XL) {
             lds_barrier_vm<C * gemv_w_loads<FMT, DQ>()>();
         } else {
-            if constexpr (FMT != kQ8_0) build_lut<FMT, 64 * kGemvWaves>(lut);
+            if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
             __syncthreads();
         }
         for (; band < nbands; band += 2 * stride) {
@@ -731,7 +742,7 @@ __device__ __forceinline__ void stream_band(const StreamTile (&R)[T], const Stre
 
 template <int FMT, bool DQ, int NI, int T>
 __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
-    __shared__ uint32_t lut[(FMT == kQ8_0) ? 1 : kLutWords];
+    __shared__ uint32_t lut[gemv_uses_lut<FMT>() ? kLutWords : 1];
     __shared__ __attribute__((aligned(16))) uint16_t xs[kStreamXMax + 128];
 
     const int tid = threadIdx.x;
@@ -759,7 +770,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
         const int64_t row = i / a.k, col = i - row * a.k;
         *reinterpret_cast<uint4*>(xs + i) = *reinterpret_cast<const uint4*>(a.x + row * a.ldx + col);
     }
-    if constexpr (FMT != kQ8_0) build_lut<FMT, 256>(lut);
+    if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 256>(lut);
     __syncthreads();
     const uint16_t* xrow = xs + (r < a.m ? r : 0) * a.k + h * 8;
     const uint16_t* xzero = xs + kStreamXMax + h * 8;
