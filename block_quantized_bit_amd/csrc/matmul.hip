@@ -1176,7 +1176,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
             for (int it = 0; it < 16; it++) {
                 const int row = 8 * it + (lane >> 3);
                 const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 128 + ((c ^ (row & 7)) << 4));
-                if (m0 + row < M) *reinterpret_cast<uint4*>(o.p + (m0 + row) * o.ld) = v;
+                // written once and not read again here: non-temporal
+                if (m0 + row < M) __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(o.p + (m0 + row) * o.ld));
             }
         }
         return;
@@ -1253,7 +1254,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
             const int row = 4 * it + (lane >> 4);
             const f32x4 v = *reinterpret_cast<const f32x4*>(stg + row * 256 + ((c ^ (row & 15)) << 4));
             const int64_t mrow = 64 * half + row;
-            if (colok && m0 + mrow < M) *reinterpret_cast<f32x4*>(pbase + mrow * N) = v;
+            if (colok && m0 + mrow < M) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(pbase + mrow * N));
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         __builtin_amdgcn_wave_barrier();
