@@ -145,16 +145,19 @@ def test_gemm_split_k_full_tiles(orc, fmt, dq, ydt, ldy_pad):
                 bf16_out=ydt == wq.WQ_BF16, what=f"split-K {NAMES[fmt]} ydt={ydt} pad={ldy_pad}")
 
 
+@pytest.mark.parametrize("ydt", [wq.WQ_F32, wq.WQ_BF16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("m", [1, 4, 16])
-def test_decoder_gemv_set_full(orc, m):
+def test_decoder_gemv_set_full(orc, m, ydt):
     """Decoder GEMV set, NF4 + double-quant: QKV 1280->3840, out 1280->1280,
-    fc1 1280->5120, fc2 5120->1280; W ~N(0,0.02) with 0.1% outliers x8; X ~N(0,1)."""
+    fc1 1280->5120, fc2 5120->1280; W ~N(0,0.02) with 0.1% outliers x8; X ~N(0,1).
+    bf16 output is the configuration the decode step is timed in."""
     for i, (n, k) in enumerate([(3840, 1280), (1280, 1280), (5120, 1280), (1280, 5120)]):
         d, codes, scales, ref, b = quantized(orc, NF4, True, 2000 + i, n, k, outlier_frac=0.001)
         x = linear_case(2000 + i, n, k, 16, outlier_frac=0.001)[2][:m]
-        say("decoder gemv", n, k, m)
-        y = gpu_matmul(d, codes, scales, x, b)
-        check_bound(y, orc.matmul(x, ref["w_hat"], b), abs_dot(x, ref["w_hat"]), what=f"dec {n}x{k} m={m}")
+        say("decoder gemv", n, k, m, "bf16" if ydt == wq.WQ_BF16 else "f32")
+        y = gpu_matmul(d, codes, scales, x, b, ydt=ydt)
+        check_bound(y, orc.matmul(x, ref["w_hat"], b), abs_dot(x, ref["w_hat"]), bf16_out=ydt == wq.WQ_BF16,
+                    what=f"dec {n}x{k} m={m}")
 
 
 # N = 131072 is 8192 16-row bands: enough that each of the 2048 resident waves
@@ -223,16 +226,22 @@ def _sample_rows(m, seed):
     (NVFP4, 1500, [(5120, 1280), (1280, 5120)], dict(row_lognormal_sigma=0.3)),
     (Q8_0, 6000, [(1280, 1280), (5120, 1280), (1280, 5120)], {}),
     (Q4_0, 6000, [(1280, 1280), (5120, 1280), (1280, 5120)], {}),
-], ids=["encoder-nvfp4-1500", "layer-q8_0-6000", "layer-q4_0-6000"])
-def test_encoder_gemm_sampled_rows(orc, fmt, m, shapes, kw):
+    # the linear sweep's encoder layers: q8_0 at 1500 frames (the 1280-wide outputs take the K split)
+    (Q8_0, 1500, [(1280, 1280), (5120, 1280), (1280, 5120)], {}),
+], ids=["encoder-nvfp4-1500", "layer-q8_0-6000", "layer-q4_0-6000", "sweep-q8_0-1500"])
+@pytest.mark.parametrize("ydt", [wq.WQ_F32, wq.WQ_BF16], ids=["f32", "bf16"])
+def test_encoder_gemm_sampled_rows(orc, fmt, m, shapes, kw, ydt):
+    """Full-size encoder GEMMs (bf16 output is the timed configuration); 64 sampled
+    rows, first and last included, are checked against the oracle."""
     for i, (n, k) in enumerate(shapes):
         d, codes, scales, ref, b = quantized(orc, fmt, False, 3000 + i, n, k, **kw)
         x = linear_case(3000 + i, n, k, m, **kw)[2]
-        say("encoder gemm", NAMES[fmt], m, n, k)
-        y = gpu_matmul(d, codes, scales, x, b)
+        say("encoder gemm", NAMES[fmt], m, n, k, "bf16" if ydt == wq.WQ_BF16 else "f32")
+        y = gpu_matmul(d, codes, scales, x, b, ydt=ydt)
         rows = _sample_rows(m, i)
         y_ref = orc.matmul(x, ref["w_hat"], b, rows=rows)
-        check_bound(y[rows], y_ref, abs_dot(x, ref["w_hat"], rows=rows), what=f"{NAMES[fmt]} {n}x{k} m={m}")
+        check_bound(y[rows], y_ref, abs_dot(x, ref["w_hat"], rows=rows), bf16_out=ydt == wq.WQ_BF16,
+                    what=f"{NAMES[fmt]} {n}x{k} m={m}")
         assert np.all(np.isfinite(y))
 
 
