@@ -81,8 +81,10 @@ def main():
     cal2.copy_(cal)
     torch.cuda.synchronize()
 
-    def run_graph_steps(enqueue, n_slots, steps, warmup):
-        """Capture one graph over all slots, replay it; returns seconds for `steps` steps."""
+    def run_graph_steps(enqueue, n_slots, steps, warmup, per_graph=None):
+        """Capture one graph over `per_graph` consecutive steps (default: one per slot;
+        step s uses slot s % n_slots), replay it; returns seconds for `steps` steps."""
+        per = per_graph or n_slots
         graphs = {}
 
         def graph_for(count):
@@ -98,9 +100,9 @@ def main():
             return graphs[count]
 
         def replay(total):
-            full, rest = divmod(total, n_slots)
+            full, rest = divmod(total, per)
             for _ in range(full):
-                graph_for(n_slots).replay()
+                graph_for(per).replay()
             if rest:
                 graph_for(rest).replay()
 
@@ -109,9 +111,9 @@ def main():
         torch.cuda.synchronize()
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
-        graph_for(n_slots)
-        if steps % n_slots:
-            graph_for(steps % n_slots)
+        graph_for(per)
+        if steps % per:
+            graph_for(steps % per)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             ev0.record(stream)
@@ -137,7 +139,8 @@ def main():
                             ws=torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev), nb=nb))
 
         reps = 50
-        te = run_graph_steps(lambda s_, st: enc_step(s_, st, enc, ENC_M), 1, reps, 5)
+        # ten steps per captured graph, so that graph launches do not count against the kernels
+        te = run_graph_steps(lambda s_, st: enc_step(s_, st, enc, ENC_M), 1, reps, 10, per_graph=10)
         flops = sum(2.0 * ENC_M * e["n"] * e["k"] for e in enc)
         tflops = flops * reps / te / 1e12
         encoder = {
@@ -272,7 +275,7 @@ def main():
         sbytes = c_s.numel() + s_s.numel()
         reps = 20
         ts = run_graph_steps(lambda s, st: wq.wq_matmul(d_s, 1, xs, ks, c_s, s_s, None, ys, wq.WQ_BF16, ns,
-                                                        wss_ if nbs else None, nbs, stream=st), 1, reps, 3)
+                                                        wss_ if nbs else None, nbs, stream=st), 1, reps, 5, per_graph=5)
         extras["streaming_gemv"] = {"shape": f"M=1 N={ns} K={ks} NF4+DQ", "bytes": sbytes,
                                     "us": round(ts * 1e6 / reps, 2),
                                     "GBps": round(sbytes * reps / ts / 1e9, 1),
@@ -296,7 +299,7 @@ def main():
                                 y=torch.empty((mb4, n), dtype=torch.int16, device=dev),
                                 ws=torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev), nb=nb))
             reps = 10
-            tl = run_graph_steps(lambda s_, st: enc_step(s_, st, lay, mb4), 1, reps, 2)
+            tl = run_graph_steps(lambda s_, st: enc_step(s_, st, lay, mb4), 1, reps, 5, per_graph=5)
             fl = sum(2.0 * mb4 * n * k for n, k in layer_shapes)
             extras[f"encoder_layer_b4_{fmt_name}"] = {"us_per_layer": round(tl * 1e6 / reps, 1),
                                                       "TFLOPs": round(fl * reps / tl / 1e12, 2),
