@@ -151,7 +151,11 @@ def main():
             "us_per_step": round(te * 1e6 / reps, 2),
             "roofline": {"kernel": "k_gemm<NVFP4>", "bound": "mfma", "achieved": round(tflops, 2),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None},
+                         "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("encoder_nvfp4_m1500", "traffic_bytes_per_step"),
+                         "traffic_per": "step (fc1 + fc2 + K-split reduce)",
+                         "algorithmic_bytes_per_step": sum(e["c"].numel() + e["s"].numel() + 2 * ENC_M * (e["k"] + e["n"])
+                                                           + 2 * e["n"] for e in enc)},
         }
         log(f"[bench] encoder NVFP4 M=1500: {encoder['us_per_step']} us, {tflops:.1f} TFLOP/s")
         return encoder
@@ -317,9 +321,9 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def measured_traffic(key):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, or None when
-    the kernel source changed since those counters were taken."""
+def measured_traffic(key, field="traffic_bytes_per_launch"):
+    """HBM bytes (per launch, or per step for the encoder) from the committed rocprofv3
+    counter runs, or None when the kernel source changed since those counters were taken."""
     import hashlib
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[key]
@@ -328,7 +332,7 @@ def measured_traffic(key):
         return None
     if hashlib.sha256(src).hexdigest() != rec.get("matmul_hip_sha256"):
         return None
-    return rec["traffic_bytes_per_launch"]
+    return rec[field]
 
 
 def cpu_baseline(base, set_bytes):
