@@ -239,19 +239,6 @@ __device__ __forceinline__ void quad_transpose(float (&v)[4], int t) {
     for (int i = 0; i < 4; i++) v[i] = ((i ^ t) & 2) ? p[i] : v[i];
 }
 
-// Sum of the split-K partials of one output element in piece order 0, 1, ...
-__device__ inline float sum_partials(const float* p, int64_t stride, int ks) {
-    float v = 0.0f;
-    for (int s0 = 0; s0 < ks; s0 += 4) {
-        float t[4];
-#pragma unroll
-        for (int u = 0; u < 4; u++) t[u] = (s0 + u < ks) ? __builtin_nontemporal_load(p + (s0 + u) * stride) : 0.0f;
-#pragma unroll
-        for (int u = 0; u < 4; u++) v += t[u];
-    }
-    return v;
-}
-
 // Workgroup barrier for data written to LDS by this workgroup's LDS-direct loads
 // and LDS stores, when the N most recent vector-memory requests (register
 // loads) may stay in flight: s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier.
@@ -1261,43 +1248,60 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     }
 }
 
-// Sum the K pieces' partials of each output in piece order, add the bias,
-// convert and store.  Thread = 4 consecutive columns of one row.  Runs after
-// k_gemm on the same stream, so every partial is complete and visible.
-__global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, int global_scale) {
-    const float g = global_scale ? *reinterpret_cast<const float*>(a.scales + a.L.g_off) : 1.0f;
-    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+// y = v * g + bias for quad q (4 consecutive columns of one row), converted and stored.
+__device__ inline void reduce_store(const KArgs& a, int64_t q, const f32x4& v, float g) {
     const int64_t nq = a.n / 4;
-    if (q >= (int64_t)a.m * nq) return;
-    const int64_t mm = q / nq, col0 = (q % nq) * 4;
-    const int64_t pstride = (int64_t)a.m * a.n;
-    const float* p = a.partial + mm * a.n + col0;
-    // pieces are summed in order 0, 1, ...; their loads are issued four at a time (indices
-    // past the last piece re-read it and are dropped)
-    f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < a.ksplit; s0 += 4) {
-        f32x4 t[4];
-#pragma unroll
-        for (int u = 0; u < 4; u++)
-            t[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + std::min(s0 + u, a.ksplit - 1) * pstride));
-#pragma unroll
-        for (int u = 0; u < 4; u++)
-            if (s0 + u < a.ksplit) v += t[u];
-    }
+    const int64_t mm = q / nq, col0 = (q - mm * nq) * 4;
     if (a.out_vec) {
         // the 4 columns lie in one output split and can be written with one store
         const ColOut c = col_out(a, col0);
         float o[4];
 #pragma unroll
         for (int u = 0; u < 4; u++) o[u] = v[u] * g + (a.bias ? bf16_value(a.bias[col0 + u]) : 0.0f);
-        char* q = c.p + mm * c.ld;
-        if (a.out.f32) *reinterpret_cast<f32x4*>(q) = f32x4{o[0], o[1], o[2], o[3]};
-        else *reinterpret_cast<uint2*>(q) = make_uint2((uint32_t)bf16_rne(o[0]) | ((uint32_t)bf16_rne(o[1]) << 16),
+        char* p = c.p + mm * c.ld;
+        if (a.out.f32) *reinterpret_cast<f32x4*>(p) = f32x4{o[0], o[1], o[2], o[3]};
+        else *reinterpret_cast<uint2*>(p) = make_uint2((uint32_t)bf16_rne(o[0]) | ((uint32_t)bf16_rne(o[1]) << 16),
                                                       (uint32_t)bf16_rne(o[2]) | ((uint32_t)bf16_rne(o[3]) << 16));
         return;
     }
 #pragma unroll
     for (int u = 0; u < 4; u++) put_out(a, col_out(a, col0 + u), mm, v[u], g);
+}
+
+// Sum the K pieces' partials of each output in piece order, add the bias,
+// convert and store.  A thread owns two quads (4 consecutive columns of one
+// row each) 256 quads apart, so eight 16-byte loads are in flight per thread.
+// Runs after k_gemm on the same stream, so every partial is complete and visible.
+__global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, int global_scale) {
+    const float g = global_scale ? *reinterpret_cast<const float*>(a.scales + a.L.g_off) : 1.0f;
+    const int64_t total = (int64_t)a.m * (a.n / 4);
+    const int64_t qa = (int64_t)blockIdx.x * 512 + threadIdx.x, qb = qa + 256;
+    if (qa >= total) return;
+    const bool hb = qb < total;
+    const int64_t pstride = (int64_t)a.m * a.n;
+    // the partials are [ksplit][m][n] row-major with n % 4 == 0: quad q starts at element 4q
+    const float* pa = a.partial + qa * 4;
+    const float* pb = a.partial + (hb ? qb : qa) * 4;
+    // pieces are summed in order 0, 1, ...; their loads are issued four at a time (indices
+    // past the last piece re-read it and are dropped)
+    f32x4 va = {0.f, 0.f, 0.f, 0.f}, vb = {0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < a.ksplit; s0 += 4) {
+        f32x4 ta[4], tb[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int64_t off = std::min(s0 + u, a.ksplit - 1) * pstride;
+            ta[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(pa + off));
+            tb[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(pb + off));
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++)
+            if (s0 + u < a.ksplit) {
+                va += ta[u];
+                vb += tb[u];
+            }
+    }
+    reduce_store(a, qa, va, g);
+    if (hb) reduce_store(a, qb, vb, g);
 }
 
 // ---------------------------------------------------------------------------
@@ -1472,8 +1476,8 @@ hipError_t launch_gemm(const MatmulProblem& p, hipStream_t st) {
     default: return hipErrorInvalidValue;
     }
     if (s.ksplit > 1) {
-        const int64_t nthreads = p.m * (p.n / 4);
-        hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((nthreads + 255) / 256)), dim3(256), 0, st, a,
+        const int64_t nquads = p.m * (p.n / 4);
+        hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a,
                            (int)(p.fmt == kNVFP4));
     }
     return hipGetLastError();
