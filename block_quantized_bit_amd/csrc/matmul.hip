@@ -9,21 +9,24 @@
 // so a wave turns one 1 KiB tile load (64 lanes x 16 B, fully coalesced) into
 // four MFMA B operands without any data exchange.
 //
-// 4-bit codes are decoded through byte-indexed tables in LDS (one entry per code
-// byte, i.e. two values per lookup), replicated per lane so that concurrent
-// lookups of different bytes hit different banks; the LDS address is built with
-// one v_perm_b32.  The GEMV table holds bf16 values (fed straight to the MFMA),
-// the GEMM table fp32 values (scaled exactly, then rounded once to bf16).
+// NF4 codes (and q4_0 codes in the GEMV) are decoded through byte-indexed tables
+// in LDS (one entry per code byte, i.e. two values per lookup), replicated per
+// lane so that concurrent lookups of different bytes hit different banks; the LDS
+// address is built with one v_perm_b32.  The GEMV table holds bf16 values (fed
+// straight to the MFMA), the GEMM table fp32 values (scaled exactly, then rounded
+// once to bf16).  NVFP4 codes and scales are decoded with the gfx950 fp4 / fp8
+// conversion instructions; q8_0 bytes (and q4_0 nibbles in the GEMM) are
+// converted to floats in registers.
 //
 // GEMV (m <= 16, decode): B = raw code values (NF4 level, q4_0 q-8, q8_0 q),
 //   the per-block scale is applied to the MFMA partial sum of each block; for
 //   NVFP4 (16-value blocks, two per 32-K slice) B = e2m1*scale (exact in bf16).
-//   Split-K over the waves of a workgroup (reduced in LDS) and, with a
-//   workspace, across workgroups (last-arriving workgroup reduces).
+//   K is split over the waves of a workgroup and reduced in LDS.
 // GEMM (m >= 17, encoder): each wave dequantizes 64 columns x 128 K of W per
 //   step to bf16(w^) -- w^ computed exactly as the format defines it, then one
 //   round-to-nearest-even -- straight into MFMA B registers; the X tile
-//   (128 x 128 bf16) is shared through LDS.
+//   (128 x 128 bf16) is shared through LDS.  Few output tiles split K across
+//   workgroups into an fp32 workspace, summed in order by a second kernel.
 #include "wq_device.h"
 #include "wq_launch.h"
 
@@ -52,7 +55,6 @@ struct KArgs {
     int ksplit;          // K pieces per output tile
     int64_t kt_per;      // K tiles (of tile_k) per piece
     float* partial;      // [ksplit][m][n] when ksplit > 1
-    uint32_t* counters;  // one per output tile when ksplit > 1
     int64_t tiles_m, tiles_n;
     int out_vec;         // every output split allows 4-column vector stores (alignment, split ends % 4)
     int out_v16;         // bf16 output whose splits allow 8-column (16-byte) stores
