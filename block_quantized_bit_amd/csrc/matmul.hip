@@ -1112,6 +1112,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     // loop with a single exit; the last one or two steps follow it (whether a
     // step prefetches its successor is a compile-time property of each copy).
     int st = first;
+    if constexpr (FMT == kQ8_0) {
+        // q8_0 runs faster with four steps per iteration (measured); the others spill
+        for (; st + 5 <= end; st += 4) {
+            gemm_kstep<FMT, DQ, 0, true>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, st + 1,
+                                         wave, lane, r, h, lane8, hs, mu);
+            gemm_kstep<FMT, DQ, 0, true>(acc, A, B, w1, w0, w0, S, rowblk, xoff, xs1, xs0, xs0, lut, st + 2,
+                                         wave, lane, r, h, lane8, hs, mu);
+            gemm_kstep<FMT, DQ, 0, true>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, st + 3,
+                                         wave, lane, r, h, lane8, hs, mu);
+            gemm_kstep<FMT, DQ, 0, true>(acc, A, B, w1, w0, w0, S, rowblk, xoff, xs1, xs0, xs0, lut, st + 4,
+                                         wave, lane, r, h, lane8, hs, mu);
+        }
+    }
     for (; st + 3 <= end; st += 2) {
         gemm_kstep<FMT, DQ, 0, true>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, st + 1,
                                      wave, lane, r, h, lane8, hs, mu);
