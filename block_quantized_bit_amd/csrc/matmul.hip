@@ -998,7 +998,8 @@ __device__ __forceinline__ void gemm_kstep(f32x4 (&acc)[8][4], u32x4 (&A)[8], u3
 #pragma unroll
         for (int i = 0; i < 32; i++) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            // VALU share per MFMA: 2 for the byte-converting formats, 3 for NVFP4 / NF4 (measured)
+            __builtin_amdgcn_sched_group_barrier(0x002, (FMT == kQ8_0 || FMT == kQ4_0) ? 2 : 3, 0);
             if (refill && (i & 3) == 3) __builtin_amdgcn_sched_group_barrier(0x100, gemm_uses_lut<FMT>() ? 3 : 1, 0);
             if (j == 0 && i < gemm_step_loads<FMT, DQ>()) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
