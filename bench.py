@@ -14,7 +14,9 @@ slots are captured once in a HIP graph and replayed.  `value` is weight bytes
 Also reported (same JSON line): the encoder GEMM at M=1500 in NVFP4 (fc1 + fc2,
 TFLOP/s), one encoder layer at batch 4 (M=6000) in q8_0 and q4_0, the decode
 set at M=4 and M=16, a 433 MB streaming GEMV (NF4+DQ, M=1), the dominant
-kernels' roofline fractions, and the CPU oracle timed on a bounded sample.
+kernels' roofline fractions, an unfused ablation (dequantize, cast, library
+GEMM) and a dense bf16 GEMM at the encoder and decode shapes, and the CPU
+oracle timed on a bounded sample.
 """
 from __future__ import annotations
 
@@ -158,6 +160,7 @@ def main():
                                                            + 2 * e["n"] for e in enc)},
         }
         log(f"[bench] encoder NVFP4 M=1500: {encoder['us_per_step']} us, {tflops:.1f} TFLOP/s")
+        encoder_part.layers = enc
         return encoder
 
     if args.encoder_only:
@@ -207,6 +210,72 @@ def main():
         """algorithmic bytes of one step: packed weights + X + Y (bf16) + bias"""
         return sum(e["codes"].numel() + e["scales"].numel() + 2 * m * e["k"] + 2 * m * e["n"] + 2 * e["n"]
                    for e in base)
+
+    def ablation_part(enc, fused_enc_us, fused_dec_us):
+        """The same Linears without fusion, for comparison (bench only, not part of the library):
+        unfused = wq_dequantize to fp32, cast to bf16, then torch's GEMM (hipBLASLt);
+        dense = torch's GEMM on the unquantized weights cast to bf16."""
+        import torch.nn.functional as F
+        out = {"how": "unfused: wq_dequantize -> fp32, cast to bf16, F.linear (hipBLASLt); "
+                      "dense: F.linear on bf16 weights (no quantization); HIP graph replay"}
+        # encoder, NVFP4, M = 1500
+        for e in enc:
+            e["w32"] = torch.empty((e["n"], e["k"]), dtype=torch.float32, device=dev)
+            e["wq"] = torch.empty((e["n"], e["k"]), dtype=torch.bfloat16, device=dev)
+            w, _, _ = linear_case(3000 + enc.index(e), e["n"], e["k"], ENC_M, row_lognormal_sigma=0.3)
+            e["wd"] = torch.from_numpy(w).to(dev).to(torch.bfloat16)
+
+        def enc_unfused(s_, st):
+            for e in enc:
+                wq.wq_dequantize(e["d"], e["c"], e["s"], e["w32"], stream=st)
+                e["wq"].copy_(e["w32"])
+                F.linear(e["x"].view(torch.bfloat16), e["wq"], e["b"].view(torch.bfloat16))
+
+        def enc_dense(s_, st):
+            for e in enc:
+                F.linear(e["x"].view(torch.bfloat16), e["wd"], e["b"].view(torch.bfloat16))
+
+        reps = 50
+        tu = run_graph_steps(enc_unfused, 1, reps, 10, per_graph=10) * 1e6 / reps
+        td = run_graph_steps(enc_dense, 1, reps, 10, per_graph=10) * 1e6 / reps
+        out["encoder_nvfp4_m1500_fc1_fc2"] = {"fused_us": fused_enc_us, "unfused_us": round(tu, 2),
+                                              "dense_bf16_us": round(td, 2),
+                                              "unfused_over_fused": round(tu / fused_enc_us, 3),
+                                              "fused_over_dense": round(fused_enc_us / td, 3)}
+        for e in enc:
+            del e["w32"], e["wq"], e["wd"]
+        # decode set, NF4 + double-quant, M = 1: packed weights cycled over the >= 1 GiB pool as in the
+        # fused step; the dense bf16 weights cycled over their own >= 1 GiB pool
+        w32 = [torch.empty((e["n"], e["k"]), dtype=torch.float32, device=dev) for e in base]
+        wqb = [torch.empty((e["n"], e["k"]), dtype=torch.bfloat16, device=dev) for e in base]
+        x1 = [e["x16"][:1].view(torch.bfloat16) for e in base]
+        bb = [e["bias"].view(torch.bfloat16) for e in base]
+
+        def dec_unfused(slot, st):
+            for j, e in enumerate(base):
+                codes, scales = pool[slot][j]
+                wq.wq_dequantize(e["d"], codes, scales, w32[j], stream=st)
+                wqb[j].copy_(w32[j])
+                F.linear(x1[j], wqb[j], bb[j])
+
+        dense_bytes = sum(2 * e["n"] * e["k"] for e in base)
+        dpool_n = max(1, -(-(1 << 30) // dense_bytes))
+        dpool = [[torch.from_numpy(e["w"]).to(dev).to(torch.bfloat16) for e in base] for _ in range(dpool_n)]
+
+        def dec_dense(slot, st):
+            for j, e in enumerate(base):
+                F.linear(x1[j], dpool[slot][j], bb[j])
+
+        tu = run_graph_steps(dec_unfused, pool_n, pool_n * 2, pool_n) * 1e6 / (pool_n * 2)
+        td = run_graph_steps(dec_dense, dpool_n, dpool_n * 4, dpool_n) * 1e6 / (dpool_n * 4)
+        out["decode_nf4dq_m1_step"] = {"fused_us": round(fused_dec_us, 3), "unfused_us": round(tu, 2),
+                                       "dense_bf16_us": round(td, 2),
+                                       "unfused_over_fused": round(tu / fused_dec_us, 3),
+                                       "fused_over_dense": round(fused_dec_us / td, 3)}
+        del w32, wqb, dpool
+        torch.cuda.empty_cache()
+        log(f"[bench] unfused ablation: {out}")
+        return out
 
     outs1, wss1 = decode_buffers(1)
     t = run_graph_steps(lambda s, st: enqueue_decode_step(1, s, outs1, wss1, st), pool_n, args.steps, args.warmup)
@@ -289,6 +358,8 @@ def main():
         torch.cuda.empty_cache()
 
         encoder = encoder_part()
+        extras["unfused_ablation"] = ablation_part(encoder_part.layers, encoder["us_per_step"], ms_per_step * 1e3)
+        encoder_part.layers = None
 
         # ---- one encoder layer at batch 4 (M = 6000), q8_0 and q4_0 on identical weights ----
         layer_shapes = [(ENC_D, ENC_D)] * 4 + [(ENC_FFN, ENC_D), (ENC_D, ENC_FFN)]

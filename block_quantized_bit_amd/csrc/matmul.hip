@@ -787,7 +787,9 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
 // and the schedule interleaves MFMA, VALU and LDS instructions explicitly.
 // LDS: the fp32 code table (NF4), then two X tiles.
 // ===========================================================================
-constexpr int BM = 128, BN = 256, BK = 128;
+// A tile is BM rows by 64 * NB columns: wave w owns bands NB w .. NB w + NB - 1 (NB = 4: 128 x 256
+// tiles; NB = 2: 128 x 128 tiles for shapes whose wide tiles cannot fill the chip).
+constexpr int BM = 128, BK = 128;
 constexpr int kLutBytes = kLutWords * 4;
 constexpr int kXsBytes = BM * BK * 2;      // one X tile: 128 rows x 256 B, 16-byte chunks XOR-swizzled by row
 
@@ -915,11 +917,11 @@ __device__ __forceinline__ u32x4 gemm_dequant(const GemmW<FMT>& w, int j, const 
     return B;
 }
 
-template <int FMT, bool DQ>
-__device__ __forceinline__ void gemm_load_w4(GemmW<FMT> (&w)[4], const GemmSrc& S, const int64_t (&rowblk)[4], int st,
+template <int FMT, bool DQ, int NB>
+__device__ __forceinline__ void gemm_load_w4(GemmW<FMT> (&w)[NB], const GemmSrc& S, const int64_t (&rowblk)[NB], int st,
                                              int lane, int r) {
 #pragma unroll
-    for (int nf = 0; nf < 4; nf++) gemm_load_w<FMT, DQ>(w[nf], S, nf, rowblk[nf], st, lane, r);
+    for (int nf = 0; nf < NB; nf++) gemm_load_w<FMT, DQ>(w[nf], S, nf, rowblk[nf], st, lane, r);
 }
 
 // X tile (128 x 128 bf16) global -> LDS without passing through registers.  In
@@ -938,8 +940,8 @@ __device__ __forceinline__ void gemm_load_x_lds(uint8_t* xs_buf, const GemmSrc& 
                                                  16, xoff[i], uni(st * (BK * 2)), 0, 0);
 }
 
-template <int FMT, bool DQ>
-__device__ constexpr int gemm_step_loads() { return kXLoads + 4 * gemm_w_loads<FMT, DQ>(); }
+template <int FMT, bool DQ, int NB>
+__device__ constexpr int gemm_step_loads() { return kXLoads + NB * gemm_w_loads<FMT, DQ>(); }
 
 // A fragment of K slice j for rows 16 * mf + r: chunk 4j + h, stored at position (4j + h) ^ r.
 __device__ __forceinline__ u32x4 gemm_load_a(const uint8_t* xcur, uint32_t arow, int mf, int j, int h, int r) {
@@ -947,11 +949,11 @@ __device__ __forceinline__ u32x4 gemm_load_a(const uint8_t* xcur, uint32_t arow,
     return u32x4{t.x, t.y, t.z, t.w};
 }
 
-template <int FMT, bool DQ>
-__device__ __forceinline__ void gemm_dequant4(u32x4 (&B)[4], const GemmW<FMT> (&w)[4], int j, const uint32_t* lut,
+template <int FMT, bool DQ, int NB>
+__device__ __forceinline__ void gemm_dequant4(u32x4 (&B)[NB], const GemmW<FMT> (&w)[NB], int j, const uint32_t* lut,
                                               uint32_t lane8, uint32_t hs, float mu) {
 #pragma unroll
-    for (int nf = 0; nf < 4; nf++) B[nf] = gemm_dequant<FMT, DQ>(w[nf], j, lut, lane8, hs, mu);
+    for (int nf = 0; nf < NB; nf++) B[nf] = gemm_dequant<FMT, DQ>(w[nf], j, lut, lane8, hs, mu);
 }
 
 // One K step: request step nx into (wn, xnext), compute the step held in
@@ -967,14 +969,14 @@ __device__ __forceinline__ void gemm_dequant4(u32x4 (&B)[4], const GemmW<FMT> (&
 // dequantizes its slice-0 B fragments (when `more`), so the next step starts
 // with its operands in registers.  The next step's requests overwrite xcur's
 // buffer only after this synchronization.
-template <int FMT, bool DQ, int NWAIT, bool MORE>
-__device__ __forceinline__ void gemm_kstep(f32x4 (&acc)[8][4], u32x4 (&A)[8], u32x4 (&B)[4],
-                                           const GemmW<FMT> (&wc)[4], GemmW<FMT> (&wn)[4], const GemmW<FMT> (&wf)[4],
-                                           const GemmSrc& S, const int64_t (&rowblk)[4], const uint32_t (&xoff)[kXLoads],
+template <int FMT, bool DQ, int NB, int NWAIT, bool MORE>
+__device__ __forceinline__ void gemm_kstep(f32x4 (&acc)[8][NB], u32x4 (&A)[8], u32x4 (&B)[NB],
+                                           const GemmW<FMT> (&wc)[NB], GemmW<FMT> (&wn)[NB], const GemmW<FMT> (&wf)[NB],
+                                           const GemmSrc& S, const int64_t (&rowblk)[NB], const uint32_t (&xoff)[kXLoads],
                                            const uint8_t* xcur, uint8_t* xnext, const uint8_t* xfol, const uint32_t* lut,
                                            int nx, int wave, int lane, int r, int h, uint32_t lane8,
                                            uint32_t hs, float mu) {
-    gemm_load_w4<FMT, DQ>(wn, S, rowblk, nx, lane, r);
+    gemm_load_w4<FMT, DQ, NB>(wn, S, rowblk, nx, lane, r);
     gemm_load_x_lds(xnext, S, xoff, wave, nx);
     const uint32_t arow = (uint32_t)r * 256u;
 #pragma unroll
@@ -983,35 +985,37 @@ __device__ __forceinline__ void gemm_kstep(f32x4 (&acc)[8][4], u32x4 (&A)[8], u3
         const bool refill = j < 3 || more;
         const uint8_t* asrc = j < 3 ? xcur : xfol;
         const int aslice = j < 3 ? j + 1 : 0;
-        u32x4 Bn[4];
-        if (j < 3) gemm_dequant4<FMT, DQ>(Bn, wc, j + 1, lut, lane8, hs, mu);
-        else if (more) gemm_dequant4<FMT, DQ>(Bn, wf, 0, lut, lane8, hs, mu);
+        u32x4 Bn[NB];
+        if (j < 3) gemm_dequant4<FMT, DQ, NB>(Bn, wc, j + 1, lut, lane8, hs, mu);
+        else if (more) gemm_dequant4<FMT, DQ, NB>(Bn, wf, 0, lut, lane8, hs, mu);
 #pragma unroll
         for (int mf = 0; mf < 8; mf++) {
 #pragma unroll
-            for (int nf = 0; nf < 4; nf++) acc[mf][nf] = mfma(A[mf], B[nf], acc[mf][nf]);
+            for (int nf = 0; nf < NB; nf++) acc[mf][nf] = mfma(A[mf], B[nf], acc[mf][nf]);
             if (refill) A[mf] = gemm_load_a(asrc, arow, mf, aslice, h, r);
         }
-        // 32 MFMAs, each followed by a share of the next slice's dequant; the A
-        // refills follow the fourth MFMA of each row fragment, and in the first
+        // 8 NB MFMAs, each followed by a share of the next slice's dequant; the A
+        // refills follow the last MFMA of each row fragment, and in the first
         // slice the next step's loads are spread over the MFMAs too
+        static_assert(gemm_step_loads<FMT, DQ, NB>() <= 8 * NB, "step loads spread one per MFMA");
 #pragma unroll
-        for (int i = 0; i < 32; i++) {
+        for (int i = 0; i < 8 * NB; i++) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             // VALU share per MFMA: 2 for the byte-converting formats, 3 for NVFP4 / NF4 (measured)
             __builtin_amdgcn_sched_group_barrier(0x002, (FMT == kQ8_0 || FMT == kQ4_0) ? 2 : 3, 0);
-            if (refill && (i & 3) == 3) __builtin_amdgcn_sched_group_barrier(0x100, gemm_uses_lut<FMT>() ? 3 : 1, 0);
-            if (j == 0 && i < gemm_step_loads<FMT, DQ>()) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            if (refill && (i % NB) == NB - 1) __builtin_amdgcn_sched_group_barrier(0x100, gemm_uses_lut<FMT>() ? 3 : 1, 0);
+            if (j == 0 && i < gemm_step_loads<FMT, DQ, NB>()) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int nf = 0; nf < 4; nf++) B[nf] = Bn[nf];
+        for (int nf = 0; nf < NB; nf++) B[nf] = Bn[nf];
         if (j == 2) lds_barrier_vm<NWAIT>();
     }
 }
 
-template <int FMT, bool DQ>
+template <int FMT, bool DQ, int NB>
 __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
+    constexpr int BN = 64 * NB;
     // separate LDS objects for the code table and the X buffers, so the
     // LDS-direct loads into one X buffer are never mistaken for writes to the others
     __shared__ __attribute__((aligned(16))) uint32_t lut_s[gemm_uses_lut<FMT>() ? kLutWords : 4];
@@ -1052,7 +1056,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     const int64_t m0 = tm * BM, n0 = tn * BN;
     const int64_t s0 = ks * a.kt_per, s1 = std::min<int64_t>(nsteps_total, s0 + a.kt_per);  // in BK steps
 
-    const int64_t band0 = n0 / 16 + wave * 4;
+    const int64_t band0 = n0 / 16 + wave * NB;
     const int64_t nbands = N / 16;
 
     float g = 1.0f, mu = 0.0f;
@@ -1061,10 +1065,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
 
     // descriptors: band tiles of this wave (bands past n re-read the last band), X rows m0 ..
     GemmSrc S;
-    int64_t rowblk[4];
+    int64_t rowblk[NB];
     constexpr int SB = (FMT == kNF4 && DQ) ? 32 : (FMT == kQ8_0) ? 64 : 128;   // scale bytes per tile
 #pragma unroll
-    for (int nf = 0; nf < 4; nf++) {
+    for (int nf = 0; nf < NB; nf++) {
         const int64_t band = std::min<int64_t>(band0 + nf, nbands - 1);
         S.code[nf] = a.codes + band * KT * kTileBytes;
         S.scale[nf] = a.scales + band * KT * SB;
@@ -1088,24 +1092,24 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
         xoff[i] = (uint32_t)(row * a.ldx * 2 + c * 16);
     }
 
-    f32x4 acc[8][4];
+    f32x4 acc[8][NB];
 #pragma unroll
     for (int i = 0; i < 8; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NB; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // every K piece is non-empty (the schedule guarantees s0 < s1)
     const int first = (int)s0, last = (int)s1 - 1, end = (int)s1;
-    GemmW<FMT> w0[4], w1[4];
-    gemm_load_w4<FMT, DQ>(w0, S, rowblk, first, lane, r);
+    GemmW<FMT> w0[NB], w1[NB];
+    gemm_load_w4<FMT, DQ, NB>(w0, S, rowblk, first, lane, r);
     gemm_load_x_lds(xs0, S, xoff, wave, first);
     if constexpr (gemm_uses_lut<FMT>()) build_lut_f32<FMT>(lut_s);
     wait_vm<0>();
     __syncthreads();
-    u32x4 A[8], B[4];
+    u32x4 A[8], B[NB];
 #pragma unroll
     for (int mf = 0; mf < 8; mf++) A[mf] = gemm_load_a(xs0, (uint32_t)r * 256u, mf, 0, h, r);
-    gemm_dequant4<FMT, DQ>(B, w0, 0, lut, lane8, hs, mu);
+    gemm_dequant4<FMT, DQ, NB>(B, w0, 0, lut, lane8, hs, mu);
 
     // two buffer sets: step s reads (w[s%2], xs[s%2]) and requests step s + 1 into
     // the other set, whose previous contents were last read before the previous
@@ -1116,29 +1120,29 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     if constexpr (FMT == kQ8_0) {
         // q8_0 runs faster with four steps per iteration (measured); the others spill
         for (; st + 5 <= end; st += 4) {
-            gemm_kstep<FMT, DQ, 0, true>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, st + 1,
+            gemm_kstep<FMT, DQ, NB, 0, true>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, st + 1,
                                          wave, lane, r, h, lane8, hs, mu);
-            gemm_kstep<FMT, DQ, 0, true>(acc, A, B, w1, w0, w0, S, rowblk, xoff, xs1, xs0, xs0, lut, st + 2,
+            gemm_kstep<FMT, DQ, NB, 0, true>(acc, A, B, w1, w0, w0, S, rowblk, xoff, xs1, xs0, xs0, lut, st + 2,
                                          wave, lane, r, h, lane8, hs, mu);
-            gemm_kstep<FMT, DQ, 0, true>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, st + 3,
+            gemm_kstep<FMT, DQ, NB, 0, true>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, st + 3,
                                          wave, lane, r, h, lane8, hs, mu);
-            gemm_kstep<FMT, DQ, 0, true>(acc, A, B, w1, w0, w0, S, rowblk, xoff, xs1, xs0, xs0, lut, st + 4,
+            gemm_kstep<FMT, DQ, NB, 0, true>(acc, A, B, w1, w0, w0, S, rowblk, xoff, xs1, xs0, xs0, lut, st + 4,
                                          wave, lane, r, h, lane8, hs, mu);
         }
     }
     for (; st + 3 <= end; st += 2) {
-        gemm_kstep<FMT, DQ, 0, true>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, st + 1,
+        gemm_kstep<FMT, DQ, NB, 0, true>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, st + 1,
                                      wave, lane, r, h, lane8, hs, mu);
-        gemm_kstep<FMT, DQ, 0, true>(acc, A, B, w1, w0, w0, S, rowblk, xoff, xs1, xs0, xs0, lut, st + 2,
+        gemm_kstep<FMT, DQ, NB, 0, true>(acc, A, B, w1, w0, w0, S, rowblk, xoff, xs1, xs0, xs0, lut, st + 2,
                                      wave, lane, r, h, lane8, hs, mu);
     }
     if (st + 2 == end) {
-        gemm_kstep<FMT, DQ, 0, true>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, last,
+        gemm_kstep<FMT, DQ, NB, 0, true>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, last,
                                      wave, lane, r, h, lane8, hs, mu);
-        gemm_kstep<FMT, DQ, 0, false>(acc, A, B, w1, w0, w0, S, rowblk, xoff, xs1, xs0, xs0, lut, last,
+        gemm_kstep<FMT, DQ, NB, 0, false>(acc, A, B, w1, w0, w0, S, rowblk, xoff, xs1, xs0, xs0, lut, last,
                                       wave, lane, r, h, lane8, hs, mu);
     } else {
-        gemm_kstep<FMT, DQ, 0, false>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, last,
+        gemm_kstep<FMT, DQ, NB, 0, false>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, last,
                                       wave, lane, r, h, lane8, hs, mu);
     }
     wait_vm<0>();   // the last requests (re-reads of the last step) land before the workgroup ends
@@ -1148,13 +1152,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
         // The tile's bf16 results go through LDS (the X buffers are free once every
         // wave's loads have landed), so that each output row is written in whole
         // 128-byte pieces by 16-byte stores rather than in 32-byte fragments.
-        // Wave w stages its 128 x 64 block (16 KiB, rows of 128 bytes whose 16-byte
-        // chunks are XOR-swizzled by row) and writes it back itself.
+        // Wave w stages its 128 x 16 NB block (rows of RB bytes whose 16-byte chunks
+        // are XOR-swizzled by row) and writes it back itself.
+        constexpr int RB = 32 * NB, CH = 2 * NB;      // row bytes, 16-byte chunks per row
         __syncthreads();
         uint8_t* stg = (wave < 2 ? xs0 : xs1) + (wave & 1) * 16384;
         const int t = r & 3, q = r >> 2;
 #pragma unroll
-        for (int nf = 0; nf < 4; nf++) {
+        for (int nf = 0; nf < NB; nf++) {
             if (band0 + nf >= nbands) continue;     // same for the whole wave
             const float bias = a.bias ? bf16_value(a.bias[(band0 + nf) * 16 + r]) : 0.0f;
 #pragma unroll
@@ -1164,21 +1169,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
                 for (int i = 0; i < 4; i++) v[i] = acc[mf][nf][i] * g + bias;
                 quad_transpose(v, t);   // now row 16 mf + 4h + t, columns 16 nf + 4q .. 4q + 3
                 const int row = 16 * mf + 4 * h + t;
-                const int ch = (2 * nf + (q >> 1)) ^ (row & 7);
-                *reinterpret_cast<uint2*>(stg + row * 128 + ch * 16 + (q & 1) * 8) =
+                const int ch = (2 * nf + (q >> 1)) ^ (row & (CH - 1));
+                *reinterpret_cast<uint2*>(stg + row * RB + ch * 16 + (q & 1) * 8) =
                     make_uint2(pack_bf16_rne(v[0], v[1]), pack_bf16_rne(v[2], v[3]));
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         __builtin_amdgcn_wave_barrier();
-        const int c = lane & 7;
+        const int c = lane & (CH - 1);
         const int64_t col = band0 * 16 + 8 * c;
         if (col < N) {
             const ColOut o = col_out_nobias(a, col);
 #pragma unroll
-            for (int it = 0; it < 16; it++) {
-                const int row = 8 * it + (lane >> 3);
-                const uint4 v = *reinterpret_cast<const uint4*>(stg + row * 128 + ((c ^ (row & 7)) << 4));
+            for (int it = 0; it < 2 * CH; it++) {
+                const int row = (64 / CH) * it + lane / CH;
+                const uint4 v = *reinterpret_cast<const uint4*>(stg + row * RB + ((c ^ (row & (CH - 1))) << 4));
                 // written once and not read again here: non-temporal
                 if (m0 + row < M) __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(o.p + (m0 + row) * o.ld));
             }
@@ -1188,7 +1193,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     if (a.ksplit == 1) {
         const bool full = m0 + BM <= M;     // every row of the tile exists (all but the last row tile)
 #pragma unroll
-        for (int nf = 0; nf < 4; nf++) {
+        for (int nf = 0; nf < NB; nf++) {
             if (band0 + nf >= nbands) continue;     // same for the whole wave
             const ColOut c = col_out(a, (band0 + nf) * 16 + r);
             if (full) {
@@ -1224,20 +1229,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
         return;
     }
     // K split: deposit this piece's partial tile; k_splitk_reduce finishes the outputs.
-    // Staged through LDS like the bf16 output: wave w writes its 128 x 64 fp32 block in
-    // two halves of 64 rows (16 KiB each, rows of 256 bytes with 16-byte chunks
-    // XOR-swizzled by row), each row then leaving as one 256-byte piece.  The workspace
-    // is 16-byte aligned and N % 16 == 0.
+    // Staged through LDS like the bf16 output: wave w writes its 128 x 16 NB fp32 block in
+    // two halves of 64 rows (rows of RB bytes with 16-byte chunks XOR-swizzled by row),
+    // each row then leaving as one RB-byte piece.  The workspace is 16-byte aligned and
+    // N % 16 == 0.
+    constexpr int RB = 64 * NB, CH = 4 * NB;      // row bytes, 16-byte chunks per row
     __syncthreads();
     uint8_t* stg = (wave < 2 ? xs0 : xs1) + (wave & 1) * 16384;
     const int t = r & 3, q = r >> 2;
-    const int c = lane & 15;
+    const int c = lane & (CH - 1);
     const bool colok = band0 + (c >> 2) < nbands;
     float* const pbase = a.partial + ((int64_t)ks * M + m0) * N + band0 * 16 + 4 * c;
 #pragma unroll
     for (int half = 0; half < 2; half++) {
 #pragma unroll
-        for (int nf = 0; nf < 4; nf++) {
+        for (int nf = 0; nf < NB; nf++) {
 #pragma unroll
             for (int mh = 0; mh < 4; mh++) {
                 const int mf = 4 * half + mh;
@@ -1246,16 +1252,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
                 for (int i = 0; i < 4; i++) v[i] = acc[mf][nf][i];
                 quad_transpose(v, t);   // now row 16 mf + 4h + t, columns 16 nf + 4q .. 4q + 3
                 const int row = 16 * mh + 4 * h + t;
-                *reinterpret_cast<f32x4*>(stg + row * 256 + (((4 * nf + q) ^ (row & 15)) << 4)) =
+                *reinterpret_cast<f32x4*>(stg + row * RB + (((4 * nf + q) ^ (row & (CH - 1))) << 4)) =
                     f32x4{v[0], v[1], v[2], v[3]};
             }
         }
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
-        for (int it = 0; it < 16; it++) {
-            const int row = 4 * it + (lane >> 4);
-            const f32x4 v = *reinterpret_cast<const f32x4*>(stg + row * 256 + ((c ^ (row & 15)) << 4));
+        for (int it = 0; it < CH; it++) {
+            const int row = (64 / CH) * it + lane / CH;
+            const f32x4 v = *reinterpret_cast<const f32x4*>(stg + row * RB + ((c ^ (row & (CH - 1))) << 4));
             const int64_t mrow = 64 * half + row;
             if (colok && m0 + mrow < M) __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(pbase + mrow * N));
         }
@@ -1327,24 +1333,32 @@ constexpr int kNumCU = 256;
 constexpr int64_t kStreamMinBands = 4 * 2 * 4 * kNumCU;   // bands per wave x waves
 
 struct Sched {
+    int nb;              // bands per wave: tiles are 128 x (64 nb)
     int ksplit;
     int64_t kt_per;
     int64_t tiles_m, tiles_n;
     unsigned grid;
 };
 
-// GEMM: 128 x 256 tiles, one workgroup per CU.  K is split only when the tiles
+// GEMM: one workgroup per CU.  Tiles are 128 x 256, or 128 x 128 when the wide
+// tiles cannot fill half the chip.  K is split only when even then the tiles
 // cannot fill half the chip, and then doubled only while all pieces still run in
-// one round on the CUs and every piece keeps >= 4 K steps.
+// one round on the CUs and every piece keeps >= kMinPieceSteps K steps: a split
+// costs the fp32 partials' round trip through memory and a second launch, about
+// as much as 11 K steps of a 128 x 128 tile (measured on MI355X at M = 1500).
+constexpr int64_t kMinPieceSteps = 12;
+
 static Sched gemm_sched(int64_t m, int64_t n, int64_t k, bool allow_split) {
     Sched s{};
     s.tiles_m = (m + BM - 1) / BM;
-    s.tiles_n = (n + BN - 1) / BN;
+    s.nb = s.tiles_m * ((n + 255) / 256) < kNumCU / 2 ? 2 : 4;
+    const int64_t bn = 64 * s.nb;
+    s.tiles_n = (n + bn - 1) / bn;
     const int64_t steps = k / BK;
     const int64_t tiles = s.tiles_m * s.tiles_n;
     int ks = 1;
     if (allow_split && tiles < kNumCU / 2) {
-        while (tiles * ks * 2 <= kNumCU && steps / (ks * 2) >= 4) ks *= 2;
+        while (tiles * ks * 2 <= kNumCU && steps / (ks * 2) >= kMinPieceSteps) ks *= 2;
     }
     s.ksplit = ks;
     s.kt_per = (steps + ks - 1) / ks;     // every piece non-empty: (ks - 1) * kt_per < steps
@@ -1470,6 +1484,12 @@ hipError_t launch_gemv(const MatmulProblem& p, hipStream_t st) {
     return hipGetLastError();
 }
 
+template <int FMT, bool DQ>
+static void gemm_launch(int nb, dim3 grid, const KArgs& a, hipStream_t st) {
+    if (nb == 2) hipLaunchKernelGGL((k_gemm<FMT, DQ, 2>), grid, dim3(256), 0, st, a);
+    else hipLaunchKernelGGL((k_gemm<FMT, DQ, 4>), grid, dim3(256), 0, st, a);
+}
+
 hipError_t launch_gemm(const MatmulProblem& p, hipStream_t st) {
     const size_t need = gemm_workspace_bytes(p.fmt, p.m, p.n, p.k);
     const bool split = p.ws != nullptr && need > 0 && p.ws_bytes >= need;
@@ -1483,12 +1503,12 @@ hipError_t launch_gemm(const MatmulProblem& p, hipStream_t st) {
     const dim3 grid(s.grid), block(256);
     switch (p.fmt) {
     case kNF4:
-        if (p.dq) hipLaunchKernelGGL((k_gemm<kNF4, true>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((k_gemm<kNF4, false>), grid, block, 0, st, a);
+        if (p.dq) gemm_launch<kNF4, true>(s.nb, grid, a, st);
+        else gemm_launch<kNF4, false>(s.nb, grid, a, st);
         break;
-    case kNVFP4: hipLaunchKernelGGL((k_gemm<kNVFP4, false>), grid, block, 0, st, a); break;
-    case kQ4_0: hipLaunchKernelGGL((k_gemm<kQ4_0, false>), grid, block, 0, st, a); break;
-    case kQ8_0: hipLaunchKernelGGL((k_gemm<kQ8_0, false>), grid, block, 0, st, a); break;
+    case kNVFP4: gemm_launch<kNVFP4, false>(s.nb, grid, a, st); break;
+    case kQ4_0: gemm_launch<kQ4_0, false>(s.nb, grid, a, st); break;
+    case kQ8_0: gemm_launch<kQ8_0, false>(s.nb, grid, a, st); break;
     default: return hipErrorInvalidValue;
     }
     if (s.ksplit > 1) {

@@ -100,7 +100,7 @@ def test_matmul_argument_validation_returns_before_launch():
     # a workspace smaller than asked for is an error (only checked when a split is wanted)
     dd = wq.desc(NF4, 1280, 5120)
     assert wq.wq_workspace_size(dd, 1) == 0          # decode GEMV never splits across workgroups
-    need = wq.wq_workspace_size(dd, 20)              # 5 output tiles: the GEMM splits K
+    need = wq.wq_workspace_size(dd, 20)              # 10 output tiles, 40 K steps: the GEMM splits K
     assert need > 0
     assert mm(d=dd, m=20, ldx=5120, ldy=1280, ws=FAKE, ws_bytes=need - 1) == 6
     # m == 0 is a no-op: validated, nothing enqueued

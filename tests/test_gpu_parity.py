@@ -130,11 +130,13 @@ def test_matmul_ragged(orc, fmt, dq, m):
 @pytest.mark.parametrize("fmt,dq", FORMATS, ids=FMT_IDS)
 @pytest.mark.parametrize("ydt,ldy_pad", [(wq.WQ_F32, 0), (wq.WQ_BF16, 0), (wq.WQ_BF16, 1), (wq.WQ_F32, 3)],
                          ids=["f32", "bf16", "bf16-odd-ldy", "f32-odd-ldy"])
-def test_gemm_split_k_full_tiles(orc, fmt, dq, ydt, ldy_pad):
+@pytest.mark.parametrize("k", [5120, 6144], ids=["2pieces", "4pieces"])
+def test_gemm_split_k_full_tiles(orc, fmt, dq, ydt, ldy_pad, k):
     """Few output tiles (N = 512) with several full 128-row tiles (M = 300) and long K:
-    the GEMM splits K, deposits full-tile partials with vector stores and reduces
-    them in a second kernel (vector or per-element stores, by output alignment)."""
-    n, k, m = 512, 2560, 300
+    the GEMM splits K (in 2 pieces at K = 5120, 4 at K = 6144), deposits full-tile
+    partials with vector stores and reduces them in a second kernel (vector or
+    per-element stores, by output alignment)."""
+    n, m = 512, 300
     d, codes, scales, ref, b = quantized(orc, fmt, dq, 4200, n, k)
     x = linear_case(4200, n, k, m)[2]
     assert wq.wq_workspace_size(d, m) > 0
