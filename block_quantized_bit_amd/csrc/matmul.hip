@@ -1326,6 +1326,35 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, int global_scale
     if (hb) reduce_store(a, qb, vb, g);
 }
 
+// The same for exactly KS pieces (2 or 4): each thread owns 8 / KS quads, spaced 256
+// apart, and issues all 8 of its partial loads before adding any (pieces in order).
+template <int KS>
+__global__ __launch_bounds__(256) void k_splitk_reduce_n(KArgs a, int global_scale) {
+    constexpr int Q = 8 / KS;
+    const float g = global_scale ? *reinterpret_cast<const float*>(a.scales + a.L.g_off) : 1.0f;
+    const int64_t total = (int64_t)a.m * (a.n / 4);
+    const int64_t q0 = (int64_t)blockIdx.x * (256 * Q) + threadIdx.x;
+    if (q0 >= total) return;
+    const int64_t pstride = (int64_t)a.m * a.n;
+    f32x4 t[KS][Q];
+#pragma unroll
+    for (int i = 0; i < Q; i++) {
+        // quads past the end re-read the first one and are dropped
+        const int64_t q = q0 + 256 * i < total ? q0 + 256 * i : q0;
+#pragma unroll
+        for (int s = 0; s < KS; s++)
+            t[s][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.partial + s * pstride + q * 4));
+    }
+#pragma unroll
+    for (int i = 0; i < Q; i++) {
+        if (q0 + 256 * i >= total) break;
+        f32x4 v = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < KS; s++) v += t[s][i];
+        reduce_store(a, q0 + 256 * i, v, g);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Schedules and launchers.
 // ---------------------------------------------------------------------------
@@ -1513,8 +1542,13 @@ hipError_t launch_gemm(const MatmulProblem& p, hipStream_t st) {
     }
     if (s.ksplit > 1) {
         const int64_t nquads = p.m * (p.n / 4);
-        hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a,
-                           (int)(p.fmt == kNVFP4));
+        const int gs = (int)(p.fmt == kNVFP4);
+        if (s.ksplit == 2)
+            hipLaunchKernelGGL(k_splitk_reduce_n<2>, dim3((unsigned)((nquads + 1023) / 1024)), dim3(256), 0, st, a, gs);
+        else if (s.ksplit == 4)
+            hipLaunchKernelGGL(k_splitk_reduce_n<4>, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a, gs);
+        else
+            hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a, gs);
     }
     return hipGetLastError();
 }

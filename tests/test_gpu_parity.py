@@ -130,10 +130,10 @@ def test_matmul_ragged(orc, fmt, dq, m):
 @pytest.mark.parametrize("fmt,dq", FORMATS, ids=FMT_IDS)
 @pytest.mark.parametrize("ydt,ldy_pad", [(wq.WQ_F32, 0), (wq.WQ_BF16, 0), (wq.WQ_BF16, 1), (wq.WQ_F32, 3)],
                          ids=["f32", "bf16", "bf16-odd-ldy", "f32-odd-ldy"])
-@pytest.mark.parametrize("k", [5120, 6144], ids=["2pieces", "4pieces"])
+@pytest.mark.parametrize("k", [5120, 6144, 12288], ids=["2pieces", "4pieces", "8pieces"])
 def test_gemm_split_k_full_tiles(orc, fmt, dq, ydt, ldy_pad, k):
     """Few output tiles (N = 512) with several full 128-row tiles (M = 300) and long K:
-    the GEMM splits K (in 2 pieces at K = 5120, 4 at K = 6144), deposits full-tile
+    the GEMM splits K (in 2 pieces at K = 5120, 4 at K = 6144, 8 at K = 12288), deposits full-tile
     partials with vector stores and reduces them in a second kernel (vector or
     per-element stores, by output alignment)."""
     n, m = 512, 300
