@@ -277,6 +277,85 @@ def main():
         log(f"[bench] unfused ablation: {out}")
         return out
 
+    def sweep_part():
+        """large-v3-turbo's Linears as a decoder and an encoder call them.
+        Decoder step: 4 layers x {self-attn Q/K/V (one wq_matmul_qkv), self O, cross Q, cross O,
+        fc1, fc2} = 24 launches, NF4 + double-quant, at M = 1 and 16, cycled over a >= 1 GiB pool
+        (cross-attention K/V is computed once per utterance and is not part of a token's step).
+        Encoder: 32 layers x {Q, K, V, O, fc1, fc2} = 192 launches, q8_0, M = 1500.  Weights are
+        drawn on the device from a seeded generator (only their shapes matter for timing)."""
+        out = {}
+        gen = torch.Generator(device=dev).manual_seed(5000)
+        dec_shapes = [("qkv", 3840, 1280), ("self_o", 1280, 1280), ("cross_q", 1280, 1280),
+                      ("cross_o", 1280, 1280), ("fc1", 5120, 1280), ("fc2", 1280, 5120)]
+        layers = []
+        for _ in range(4):
+            for name, n, k in dec_shapes:
+                w = torch.randn((n, k), device=dev, generator=gen, dtype=torch.float32) * 0.02
+                d, c, s_ = quantize_dev(wq.WQ_NF4, w, True)
+                layers.append(dict(name=name, n=n, k=k, d=d, c=c, s=s_,
+                                   bias=(torch.randn(n, device=dev, generator=gen) * 0.01).to(torch.bfloat16)))
+        step_bytes = sum(e["c"].numel() + e["s"].numel() for e in layers)
+        spool_n = max(1, -(-(1 << 30) // step_bytes))
+        spool = [[(e["c"].clone(), e["s"].clone()) for e in layers] for _ in range(spool_n)]
+        xk = {k: torch.randn((16, k), device=dev, generator=gen).to(torch.bfloat16) for k in (1280, 5120)}
+        torch.cuda.synchronize()
+        for m in (1, 16):
+            ys = {n: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for n in (1280, 3840, 5120)}
+
+            def dec_step(slot, st, m=m, ys=ys):
+                for j, e in enumerate(layers):
+                    c, s_ = spool[slot][j]
+                    y = ys[e["n"]]
+                    if e["name"] == "qkv":
+                        p0 = y.data_ptr()
+                        wq.wq_matmul_qkv(e["d"], m, xk[e["k"]], e["k"], c, s_, e["bias"], [1280, 1280, 1280],
+                                         [p0, p0 + 2 * 1280, p0 + 2 * 2560], [3840] * 3, wq.WQ_BF16, stream=st)
+                    else:
+                        wq.wq_matmul(e["d"], m, xk[e["k"]], e["k"], c, s_, e["bias"], y, wq.WQ_BF16, e["n"],
+                                     stream=st)
+
+            t = run_graph_steps(dec_step, spool_n, spool_n * 2, spool_n) / (spool_n * 2)
+            alg = step_bytes + sum(2 * m * (e["k"] + e["n"]) + 2 * e["n"] for e in layers)
+            out[f"decoder_step_m{m}"] = {"launches": len(layers), "us_per_step": round(t * 1e6, 2),
+                                         "weight_bytes": step_bytes, "weight_GBps": round(step_bytes / t / 1e9, 1),
+                                         "algorithmic_GBps": round(alg / t / 1e9, 1),
+                                         "us_per_launch": round(t * 1e6 / len(layers), 3)}
+            log(f"[bench] decoder step M={m}: {out[f'decoder_step_m{m}']}")
+        del spool, layers
+        torch.cuda.empty_cache()
+        # encoder sweep, q8_0, M = 1500
+        enc_shapes = [(1280, 1280)] * 4 + [(5120, 1280), (1280, 5120)]
+        xs = {k: torch.randn((ENC_M, k), device=dev, generator=gen).to(torch.bfloat16) for k in (1280, 5120)}
+        ys = {n: torch.empty((ENC_M, n), dtype=torch.bfloat16, device=dev) for n in (1280, 5120)}
+        lin = []
+        for _ in range(32):
+            for n, k in enc_shapes:
+                w = torch.randn((n, k), device=dev, generator=gen, dtype=torch.float32) * 0.02
+                d, c, s_ = quantize_dev(wq.WQ_Q8_0, w, False)
+                nb = wq.wq_workspace_size(d, ENC_M)
+                lin.append(dict(d=d, c=c, s=s_, n=n, k=k, nb=nb, bias=torch.zeros(n, dtype=torch.bfloat16, device=dev)))
+        wsz = max(e["nb"] for e in lin)
+        wsb = torch.zeros(max(wsz, 16), dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+        def enc_sweep(s_, st):
+            for e in lin:
+                wq.wq_matmul(e["d"], ENC_M, xs[e["k"]], e["k"], e["c"], e["s"], e["bias"], ys[e["n"]], wq.WQ_BF16,
+                             e["n"], wsb if e["nb"] else None, e["nb"], stream=st)
+
+        reps = 3
+        t = run_graph_steps(enc_sweep, 1, reps, 1, per_graph=1) / reps
+        fl = sum(2.0 * ENC_M * e["n"] * e["k"] for e in lin)
+        out["encoder_sweep_q8_0_m1500"] = {"launches": len(lin), "us": round(t * 1e6, 1),
+                                           "weight_bytes": sum(e["c"].numel() + e["s"].numel() for e in lin),
+                                           "TFLOPs": round(fl / t / 1e12, 2),
+                                           "frac_mfma": round(fl / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        log(f"[bench] encoder sweep q8_0: {out['encoder_sweep_q8_0_m1500']}")
+        del lin
+        torch.cuda.empty_cache()
+        return out
+
     outs1, wss1 = decode_buffers(1)
     t = run_graph_steps(lambda s, st: enqueue_decode_step(1, s, outs1, wss1, st), pool_n, args.steps, args.warmup)
     ms_per_step = t * 1e3 / args.steps
@@ -360,6 +439,9 @@ def main():
         encoder = encoder_part()
         extras["unfused_ablation"] = ablation_part(encoder_part.layers, encoder["us_per_step"], ms_per_step * 1e3)
         encoder_part.layers = None
+
+        # ---- large-v3-turbo sweep: the whole per-token decoder step and the q8_0 encoder ----
+        extras.update(sweep_part())
 
         # ---- one encoder layer at batch 4 (M = 6000), q8_0 and q4_0 on identical weights ----
         layer_shapes = [(ENC_D, ENC_D)] * 4 + [(ENC_FFN, ENC_D), (ENC_D, ENC_FFN)]
