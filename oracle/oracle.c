@@ -20,7 +20,9 @@
  *     short of VRAM", intro; "mbehr90/whisper-large-v3-turbo-nvfp4", section
  *     "What is quantized".
  *   - q8_0 / q4_0 block formats: "Run quantized Whisper on the fused Metal
- *     decode path", sections "Summary" and "Why the policy".
+ *     decode path", sections "Summary" and "Why the policy"; q4_1 is named
+ *     there too (section "Why the policy") as a format that decodes correctly
+ *     but lacks fast kernels.
  *   - Host reference path for quantized linears used to rule out kernel bugs:
  *     same page, section "Why the policy".
  * Everything the pages leave open (codebook values, rounding, tie-breaks,
@@ -40,6 +42,7 @@
 #define OR_NVFP4 2
 #define OR_Q4_0 3
 #define OR_Q8_0 4
+#define OR_Q4_1 5
 
 /* ------------------------------------------------------------------------ */
 /* Scalar codecs                                                              */
@@ -425,9 +428,62 @@ void or_q4_0_dequantize(int64_t n, int64_t k, const uint8_t* codes, const uint16
 }
 
 /* ------------------------------------------------------------------------ */
+/* q4_1: blocks of 32 with an fp16 scale d and an fp16 minimum m, unsigned      */
+/* codes.  The page only names the format; reading (as for q4_0): the codes are  */
+/* chosen against the stored fp16 values, rounding to nearest even.             */
+/*   lo = min(w), hi = max(w) over the block (exact);                            */
+/*   d = fp16(fl(fl(hi - lo) / 15)), m = fp16(lo); delta = float(d), mu = float(m) */
+/*   q = 0 if delta == 0 else clamp(rint(fl(fl(w - mu) / delta)), 0, 15);        */
+/*   w^ = fl(q * delta + mu), one rounding (q * delta has <= 15 significant bits */
+/*   and is exact).                                                               */
+/* scales: [n][k/32][2] fp16, d first.                                           */
+/* ------------------------------------------------------------------------ */
+void or_q4_1_quantize(int64_t n, int64_t k, const float* w, uint8_t* codes, uint16_t* scales) {
+    const int64_t nbk = k / 32;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t b = 0; b < nbk; b++) {
+            const float* src = w + r * k + b * 32;
+            float lo = src[0], hi = src[0];
+            for (int i = 1; i < 32; i++) {
+                if (src[i] < lo) lo = src[i];
+                if (src[i] > hi) hi = src[i];
+            }
+            const float range = hi - lo;
+            const uint16_t d = or_fp16_encode(range / 15.0f);
+            const uint16_t m = or_fp16_encode(lo);
+            scales[(r * nbk + b) * 2] = d;
+            scales[(r * nbk + b) * 2 + 1] = m;
+            const float delta = or_fp16_decode(d), mu = or_fp16_decode(m);
+            for (int i = 0; i < 32; i++) {
+                uint8_t q = 0;
+                if (delta != 0.0f) {
+                    const float t = src[i] - mu;
+                    float v = rintf(t / delta);
+                    if (v > 15.0f) v = 15.0f;
+                    if (v < 0.0f) v = 0.0f;
+                    q = (uint8_t)v;
+                }
+                codes[r * k + b * 32 + i] = q;
+            }
+        }
+}
+
+void or_q4_1_dequantize(int64_t n, int64_t k, const uint8_t* codes, const uint16_t* scales, float* out) {
+    const int64_t nbk = k / 32;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t i = 0; i < k; i++) {
+            const int64_t b = r * nbk + i / 32;
+            const float delta = or_fp16_decode(scales[2 * b]), mu = or_fp16_decode(scales[2 * b + 1]);
+            const float qd = (float)codes[r * k + i] * delta;      /* exact */
+            out[r * k + i] = qd + mu;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Packed layout (the library's storage format; the pages give none).          */
 /*                                                                              */
-/* 4-bit codes (NF4, NVFP4, q4_0): the matrix is cut into tiles of 16 rows x    */
+/* 4-bit codes (NF4, NVFP4, q4_0, q4_1): the matrix is cut into tiles of 16     */
+/* rows x                                                                        */
 /* 128 K = 1024 bytes, ordered band-major (band = 16 rows), K-fastest.  Inside  */
 /* a tile, 64 slots of 16 bytes; slot s holds row (s mod 16) and K-chunk        */
 /* h = s div 16; byte 4j + i/2 of the slot (j = 0..3, i = 0..7) holds          */
@@ -441,6 +497,7 @@ void or_q4_0_dequantize(int64_t n, int64_t k, const uint8_t* codes, const uint16
 /*   NF4+DQ  int8 q,      2 per row, then at align16(nb): fp32 d[ng], then mu  */
 /*   NVFP4   E4M3 byte,   8 per row  (128 per tile), then at align16(nb): g    */
 /*   q4_0    fp16,        4 per row  (64 per tile)                              */
+/*   q4_1    fp16 pair (d, m), 4 per row  (64 pairs = 256 bytes per tile)       */
 /*   q8_0    fp16,        2 per row  (32 per 16x64 tile)                        */
 /* ------------------------------------------------------------------------ */
 static int64_t align16(int64_t v) { return (v + 15) & ~(int64_t)15; }
@@ -465,6 +522,11 @@ int or_packed_size(int fmt, int dq, int64_t n, int64_t k, int64_t* codes_bytes, 
         if (k % 128) return -1;
         *codes_bytes = n * k / 2;
         *scales_bytes = 2 * (n * k / 32);
+        return 0;
+    case OR_Q4_1:
+        if (k % 128) return -1;
+        *codes_bytes = n * k / 2;
+        *scales_bytes = 4 * (n * k / 32);
         return 0;
     case OR_Q8_0:
         if (k % 64) return -1;
@@ -593,6 +655,15 @@ int or_quantize_packed(int fmt, int dq, int64_t n, int64_t k, const float* w,
         or_pack_codes4(n, k, codes_logical, codes_packed);
         or_pack_scales(n, k, 32, 128, 2, s, scales_packed);
         or_q4_0_dequantize(n, k, codes_logical, s, w_hat);
+        free(s);
+        return 0;
+    }
+    if (fmt == OR_Q4_1) {
+        uint16_t* s = (uint16_t*)malloc(4 * (n * k / 32));
+        or_q4_1_quantize(n, k, w, codes_logical, s);
+        or_pack_codes4(n, k, codes_logical, codes_packed);
+        or_pack_scales(n, k, 32, 128, 4, s, scales_packed);
+        or_q4_1_dequantize(n, k, codes_logical, s, w_hat);
         free(s);
         return 0;
     }

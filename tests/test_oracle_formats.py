@@ -307,3 +307,82 @@ def test_q4_0_extreme_exact_negative_zero_and_ties(orc):
     assert codes[1, 41] == 15 and w_hat[1, 41] == np.float32(7 * 0.0625)
     # an all-zero block: delta = 0, every code 8
     assert np.all(codes[2] == 8) and np.all(w_hat[2] == 0)
+
+
+# ----------------------------------------------------------------- q4_1 ----
+# q4_1 is only named ("Run quantized Whisper on the fused Metal decode path",
+# "Why the policy"); the reading: d = fp16((max - min) / 15), m = fp16(min),
+# codes = the nearest of the 16 levels q*d + m, chosen against the stored fp16
+# values, w^ = q*d + m.
+
+def _f16(x):
+    return np.array([x], np.float32).astype(np.float16)
+
+
+def test_q4_1_brute_force(orc):
+    """Scales follow from the block's extremes; every code is the nearest level
+    found by exhaustive search in exact arithmetic (near-ties excepted)."""
+    rng = np.random.default_rng(15)
+    w = (rng.standard_normal((16, 128)) * 0.02).astype(np.float32)
+    w[3, 40] = 0.1                                         # an outlier in one block
+    codes, sc = orc.q4_1_quantize(w)
+    assert codes.max() <= 15
+    for r in range(16):
+        for b in range(4):
+            blk = w[r, 32 * b:32 * b + 32]
+            lo, hi = blk.min(), blk.max()
+            want_d = _f16(_f32(_f32(hi - lo) / _f32(15))).view(np.uint16)[0]
+            want_m = _f16(lo).view(np.uint16)[0]
+            assert sc[r * 4 + b, 0] == want_d and sc[r * 4 + b, 1] == want_m
+            delta = Fraction(float(np.uint16(want_d).view(np.float16)))
+            mu = Fraction(float(np.uint16(want_m).view(np.float16)))
+            for i in range(32):
+                t = Fraction(float(blk[i]))
+                dist = [abs(t - (q * delta + mu)) for q in range(16)]
+                qb = dist.index(min(dist))
+                qi = int(codes[r, 32 * b + i])
+                if qi != qb:                                   # only a near-tie may differ
+                    assert abs(dist[qi] - dist[qb]) <= delta / 2 ** 16
+
+
+def test_q4_1_round_trip_constant_blocks_and_positions(orc):
+    w = np.zeros((16, 128), np.float32)
+    # block of exactly representable levels: m = -0.25, d = 0.03125 (both fp16-exact, (hi - lo) / 15 exact)
+    q = np.arange(32) % 16
+    w[0, :32] = (np.float32(-0.25) + q.astype(np.float32) * np.float32(0.03125)).astype(np.float32)
+    w[1, 32:64] = np.float32(0.375)                        # constant block: d = 0, codes 0, w^ = m
+    w[2, 64:96] = np.float32(-1.5)
+    codes, sc = orc.q4_1_quantize(w)
+    w_hat = orc.q4_1_dequantize(codes, sc)
+    assert np.array_equal(codes[0, :32], q) and np.array_equal(w_hat[0, :32], w[0, :32])
+    assert sc[1 * 4 + 1, 0] == 0 and np.all(codes[1, 32:64] == 0) and np.all(w_hat[1, 32:64] == np.float32(0.375))
+    assert np.all(w_hat[2, 64:96] == np.float32(-1.5))
+    # an all-zero block: d = 0, m = +0, w^ = 0
+    assert np.all(codes[3] == 0) and np.all(w_hat[3] == 0)
+    # packed scales: block b of row r at byte 256 * tile + 16 * (r % 16) + 4 * (b % 4), d first
+    res = orc.quantize(5, w)
+    sp = res["scales"].view(np.uint16)
+    for r, b in [(0, 0), (1, 1), (2, 2), (15, 3)]:
+        off = (256 * (b // 4) + 16 * r + 4 * (b % 4)) // 2
+        assert sp[off] == sc[r * 4 + b, 0] and sp[off + 1] == sc[r * 4 + b, 1]
+    assert np.array_equal(res["w_hat"], w_hat)
+    # 0.625 bytes per weight: 4-bit codes plus two fp16 per 32 values
+    assert orc.packed_size(5, False, 16, 128) == (1024, 256)
+
+
+def test_q4_1_error_bound(orc):
+    """Every w^ lies within half a level (plus the fp16 rounding of the minimum)
+    of w, and the block minimum decodes to m exactly."""
+    rng = np.random.default_rng(16)
+    w = (rng.standard_normal((32, 256)) * 0.02).astype(np.float32)
+    codes, sc = orc.q4_1_quantize(w)
+    w_hat = orc.q4_1_dequantize(codes, sc)
+    for r in range(32):
+        for b in range(8):
+            blk = w[r, 32 * b:32 * b + 32]
+            d = float(np.uint16(sc[r * 8 + b, 0]).view(np.float16))
+            m = float(np.uint16(sc[r * 8 + b, 1]).view(np.float16))
+            err = np.abs(w_hat[r, 32 * b:32 * b + 32].astype(np.float64) - blk)
+            assert err.max() <= d / 2 + abs(m - float(blk.min())) + 1e-9
+            j = int(np.argmin(blk))
+            assert codes[r, 32 * b + j] == 0 and w_hat[r, 32 * b + j] == np.float32(m)
