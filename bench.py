@@ -277,6 +277,38 @@ def main():
         log(f"[bench] unfused ablation: {out}")
         return out
 
+    def decode_by_format():
+        """The decode set (QKV as one wq_matmul_qkv, out, fc1, fc2; M = 1) quantized from the
+        same fp32 weights in each format, each cycled over its own >= 1 GiB pool."""
+        out = {}
+        x1 = [e["x16"] for e in base]
+        ys = [torch.empty((1, e["n"]), dtype=torch.int16, device=dev) for e in base]
+        for name, fmt, dq in (("nf4", wq.WQ_NF4, False), ("nvfp4", wq.WQ_NVFP4, False),
+                              ("q4_0", wq.WQ_Q4_0, False), ("q4_1", wq.WQ_Q4_1, False), ("q8_0", wq.WQ_Q8_0, False)):
+            mats = [quantize_dev(fmt, torch.from_numpy(e["w"]).to(dev), dq) for e in base]
+            nbytes = sum(c.numel() + s_.numel() for _, c, s_ in mats)
+            pn = max(1, -(-(1 << 30) // nbytes))
+            fpool = [[(c.clone(), s_.clone()) for _, c, s_ in mats] for _ in range(pn)]
+
+            def step(slot, st, mats=mats, fpool=fpool):
+                for j, e in enumerate(base):
+                    d = mats[j][0]
+                    c, s_ = fpool[slot][j]
+                    if e["name"] == "qkv":
+                        p0 = ys[j].data_ptr()
+                        wq.wq_matmul_qkv(d, 1, x1[j], e["k"], c, s_, e["bias"], [1280, 1280, 1280],
+                                         [p0, p0 + 2 * 1280, p0 + 2 * 2560], [e["n"]] * 3, wq.WQ_BF16, stream=st)
+                    else:
+                        wq.wq_matmul(d, 1, x1[j], e["k"], c, s_, e["bias"], ys[j], wq.WQ_BF16, e["n"], stream=st)
+
+            t = run_graph_steps(step, pn, pn * 2, pn) / (pn * 2)
+            out[name] = {"us_per_step": round(t * 1e6, 2), "weight_bytes": nbytes,
+                         "weight_GBps": round(nbytes / t / 1e9, 1)}
+            del fpool, mats
+            torch.cuda.empty_cache()
+        log(f"[bench] decode M=1 by format: {out}")
+        return out
+
     def sweep_part():
         """large-v3-turbo's Linears as a decoder and an encoder call them.
         Decoder step: 4 layers x {self-attn Q/K/V (one wq_matmul_qkv), self O, cross Q, cross O,
@@ -440,13 +472,16 @@ def main():
         extras["unfused_ablation"] = ablation_part(encoder_part.layers, encoder["us_per_step"], ms_per_step * 1e3)
         encoder_part.layers = None
 
+        # ---- the decode set (M = 1) in every format, same weights ----
+        extras["decode_m1_by_format"] = decode_by_format()
+
         # ---- large-v3-turbo sweep: the whole per-token decoder step and the q8_0 encoder ----
         extras.update(sweep_part())
 
         # ---- one encoder layer at batch 4 (M = 6000), q8_0 and q4_0 on identical weights ----
         layer_shapes = [(ENC_D, ENC_D)] * 4 + [(ENC_FFN, ENC_D), (ENC_D, ENC_FFN)]
         mb4 = 4 * ENC_M
-        for fmt_name, fmt in (("q8_0", wq.WQ_Q8_0), ("q4_0", wq.WQ_Q4_0)):
+        for fmt_name, fmt in (("q8_0", wq.WQ_Q8_0), ("q4_0", wq.WQ_Q4_0), ("q4_1", wq.WQ_Q4_1)):
             lay = []
             for i, (n, k) in enumerate(layer_shapes):
                 w, b, x = linear_case(4000 + i, n, k, mb4)

@@ -15,12 +15,13 @@
 // address is built with one v_perm_b32.  The GEMV table holds bf16 values (fed
 // straight to the MFMA), the GEMM table fp32 values (scaled exactly, then rounded
 // once to bf16).  NVFP4 codes and scales are decoded with the gfx950 fp4 / fp8
-// conversion instructions; q8_0 bytes (and q4_0 nibbles in the GEMM) are
-// converted to floats in registers.
+// conversion instructions; q8_0 bytes, q4_1 nibbles (and q4_0 nibbles in the
+// GEMM) are converted to floats in registers.
 //
 // GEMV (m <= 16, decode): B = raw code values (NF4 level, q4_0 q-8, q8_0 q),
 //   the per-block scale is applied to the MFMA partial sum of each block; for
-//   NVFP4 (16-value blocks, two per 32-K slice) B = e2m1*scale (exact in bf16).
+//   NVFP4 (16-value blocks, two per 32-K slice) B = e2m1*scale (exact in bf16);
+//   for q4_1 (scale and minimum) B = bf16(w^) as in the GEMM.
 //   K is split over the waves of a workgroup and reduced in LDS.
 // GEMM (m >= 17, encoder): each wave dequantizes 64 columns x 128 K of W per
 //   step to bf16(w^) -- w^ computed exactly as the format defines it, then one
@@ -162,6 +163,24 @@ __device__ inline uint32_t pack_bf16_rne(float a, float b) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// q4_1 B operand for one 32-wide K slice: the slice's code word (nibble i = k 8h + i)
+// and its block's fp16 pair dm = d | m << 16.  w^ = fl(c * d + m) with c * d exact (4 + 11
+// significant bits), so one fma is the format's w^; then one RNE to bf16.
+__device__ __forceinline__ u32x4 q4_1_operand(uint32_t word, uint32_t dm) {
+    const float d = f16_value((uint16_t)(dm & 0xFFFFu)), m = f16_value((uint16_t)(dm >> 16));
+    uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+    // opaque to the optimizer, so that each byte converts with one v_cvt_f32_ubyteN
+    asm("" : "+v"(lo), "+v"(hi));
+    u32x4 B;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const float c0 = (float)((lo >> (8 * q)) & 255u);
+        const float c1 = (float)((hi >> (8 * q)) & 255u);
+        B[q] = pack_bf16_rne(__builtin_fmaf(c0, d, m), __builtin_fmaf(c1, d, m));
+    }
+    return B;
+}
+
 __device__ inline f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
@@ -275,7 +294,7 @@ __device__ __forceinline__ void wait_vm() {
 template <int FMT>
 struct GemvTile {
     uint4 code;             // this lane's 16 bytes of the tile
-    uint32_t sc[3];         // raw scale words (format dependent)
+    uint32_t sc[4];         // raw scale words (format dependent)
     u32x4 A[tile_k(FMT) / 32];
 };
 
@@ -333,6 +352,13 @@ __device__ inline void gemv_load(GemvTile<FMT>& t, const KArgs& a, int64_t band,
         const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 64 + r * 4) * 2);
         t.sc[0] = v.x;
         t.sc[1] = v.y;
+    } else if constexpr (FMT == kQ4_1) {
+        // the row's four (d, m) pairs of the tile: 16 bytes
+        const uint4 v = *reinterpret_cast<const uint4*>(a.scales + tile * 256 + r * 16);
+        t.sc[0] = v.x;
+        t.sc[1] = v.y;
+        t.sc[2] = v.z;
+        t.sc[3] = v.w;
     } else if constexpr (FMT == kNVFP4) {
         const uint2 v = *reinterpret_cast<const uint2*>(a.scales + tile * 128 + r * 8);
         t.sc[0] = v.x;
@@ -408,6 +434,10 @@ __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const ui
 #pragma unroll
             for (int i = 0; i < NI; i++) acc[i] += p[i] * s;
         }
+    } else if constexpr (FMT == kQ4_1) {
+        // B = bf16(w^), block j of the row for K slice j
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc = mfma(t.A[j], q4_1_operand(uw[j], t.sc[j]), acc);
     } else if constexpr (FMT == kNVFP4) {
         // block 2j + (h >> 1) of the row: byte 2 (j & 1) + (h >> 1) of scale word j >> 1
         const uint32_t hs = 8u * (uint32_t)(h >> 1);
@@ -799,7 +829,7 @@ __device__ constexpr bool gemm_uses_lut() { return FMT == kNF4; }
 template <int FMT>
 struct GemmW {
     uint4 code[tile_k(FMT) == 64 ? 2 : 1];
-    uint32_t sc[3];
+    uint32_t sc[4];
 };
 
 // Buffer descriptors of one workgroup's loads: per band of the wave (its
@@ -838,6 +868,12 @@ __device__ __forceinline__ void gemm_load_w(GemmW<FMT>& w, const GemmSrc& S, int
             const int64_t b0 = rowblk + 2 * st;
             w.sc[1] = __builtin_amdgcn_raw_buffer_load_b32(buf_res_uni(S.dt, S.dtbytes), (uint32_t)(b0 >> 8) * 4u, 0, 0);
             w.sc[2] = __builtin_amdgcn_raw_buffer_load_b32(buf_res_uni(S.dt, S.dtbytes), (uint32_t)((b0 + 1) >> 8) * 4u, 0, 0);
+        } else if constexpr (FMT == kQ4_1) {   // 4 x (fp16 d, fp16 m): 16 bytes per row and tile
+            const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buf_res_uni(S.scale[nf], S.sbytes), r * 16, uni(st * 256), 0));
+            w.sc[0] = v.x;
+            w.sc[1] = v.y;
+            w.sc[2] = v.z;
+            w.sc[3] = v.w;
         } else {   // NF4 (fp32 pair), Q4_0 (4 x fp16), NVFP4 (8 x E4M3): 8 bytes per row and tile
             const auto v = __builtin_amdgcn_raw_buffer_load_b64(buf_res_uni(S.scale[nf], S.sbytes), r * 8, uni(st * 128), 0);
             w.sc[0] = v[0];
@@ -882,6 +918,9 @@ __device__ __forceinline__ u32x4 gemm_dequant(const GemmW<FMT>& w, int j, const 
             else v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
             B[q] = pack_bf16_rne(__fmul_rn(v[0], s), __fmul_rn(v[1], s));
         }
+    } else if constexpr (FMT == kQ4_1) {
+        const uint32_t word = j == 0 ? w.code[0].x : j == 1 ? w.code[0].y : j == 2 ? w.code[0].z : w.code[0].w;
+        B = q4_1_operand(word, w.sc[j]);
     } else if constexpr (FMT == kQ4_0) {
         // nibble c as a float, then c*d - 8d: both products are exact in fp32 (c has 4
         // significant bits, d 11), so this is (c - 8)*d exactly; one RNE to bf16
@@ -1002,7 +1041,7 @@ __device__ __forceinline__ void gemm_kstep(f32x4 (&acc)[8][NB], u32x4 (&A)[8], u
         for (int i = 0; i < 8 * NB; i++) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             // VALU share per MFMA: 2 for the byte-converting formats, 3 for NVFP4 / NF4 (measured)
-            __builtin_amdgcn_sched_group_barrier(0x002, (FMT == kQ8_0 || FMT == kQ4_0) ? 2 : 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, (FMT == kQ8_0 || FMT == kQ4_0 || FMT == kQ4_1) ? 2 : 3, 0);
             if (refill && (i % NB) == NB - 1) __builtin_amdgcn_sched_group_barrier(0x100, gemm_uses_lut<FMT>() ? 3 : 1, 0);
             if (j == 0 && i < gemm_step_loads<FMT, DQ, NB>()) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         }
@@ -1066,7 +1105,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     // descriptors: band tiles of this wave (bands past n re-read the last band), X rows m0 ..
     GemmSrc S;
     int64_t rowblk[NB];
-    constexpr int SB = (FMT == kNF4 && DQ) ? 32 : (FMT == kQ8_0) ? 64 : 128;   // scale bytes per tile
+    constexpr int SB = (FMT == kNF4 && DQ) ? 32 : (FMT == kQ8_0) ? 64 : (FMT == kQ4_1) ? 256 : 128;   // scale bytes per tile
 #pragma unroll
     for (int nf = 0; nf < NB; nf++) {
         const int64_t band = std::min<int64_t>(band0 + nf, nbands - 1);
@@ -1476,11 +1515,15 @@ static void gemv_launch_ni(const KArgs& a, hipStream_t st) {
     const int64_t nbands = a.n / 16;
     // Many more bands than resident waves, K <= 10 tiles, X fits in LDS: the
     // streaming kernel (two workgroups of 4 waves per CU, each wave >= 4 bands).
-    if (nbands >= kStreamMinBands && (int64_t)a.m * a.k <= kStreamXMax && KT <= 10) {
-        const unsigned grid = 2 * kNumCU;
-        if (KT <= 4) hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 4>), dim3(grid), dim3(256), 0, st, a);
-        else hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 10>), dim3(grid), dim3(256), 0, st, a);
-        return;
+    // (q4_1 has no streaming variant: its 16 bytes of scales per row and tile take the
+    // general kernel)
+    if constexpr (FMT != kQ4_1) {
+        if (nbands >= kStreamMinBands && (int64_t)a.m * a.k <= kStreamXMax && KT <= 10) {
+            const unsigned grid = 2 * kNumCU;
+            if (KT <= 4) hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 4>), dim3(grid), dim3(256), 0, st, a);
+            else hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 10>), dim3(grid), dim3(256), 0, st, a);
+            return;
+        }
     }
     switch (gemv_chunk(KT)) {
     case 1: gemv_launch_c<FMT, DQ, NI, 1>(a, nbands, KT, st); break;
@@ -1507,6 +1550,7 @@ hipError_t launch_gemv(const MatmulProblem& p, hipStream_t st) {
         break;
     case kNVFP4: gemv_dispatch_ni<kNVFP4, false>(a, st); break;
     case kQ4_0: gemv_dispatch_ni<kQ4_0, false>(a, st); break;
+    case kQ4_1: gemv_dispatch_ni<kQ4_1, false>(a, st); break;
     case kQ8_0: gemv_dispatch_ni<kQ8_0, false>(a, st); break;
     default: return hipErrorInvalidValue;
     }
@@ -1537,6 +1581,7 @@ hipError_t launch_gemm(const MatmulProblem& p, hipStream_t st) {
         break;
     case kNVFP4: gemm_launch<kNVFP4, false>(s.nb, grid, a, st); break;
     case kQ4_0: gemm_launch<kQ4_0, false>(s.nb, grid, a, st); break;
+    case kQ4_1: gemm_launch<kQ4_1, false>(s.nb, grid, a, st); break;
     case kQ8_0: gemm_launch<kQ8_0, false>(s.nb, grid, a, st); break;
     default: return hipErrorInvalidValue;
     }

@@ -7,7 +7,7 @@
 // for the Whisper engine", "What's here"); NVFP4 ("asr: add a 4-bit nvfp4 option
 // for cards short of VRAM", intro; "mbehr90/whisper-large-v3-turbo-nvfp4", "What
 // is quantized"); q4_0 / q8_0 ("Run quantized Whisper on the fused Metal decode
-// path", "Summary").  One matrix at a time, as the checkpoint streams in ("asr:
+// path", "Summary"); q4_1 (same page, "Why the policy").  One matrix at a time, as the checkpoint streams in ("asr:
 // add a 4-bit nf4 option for the Whisper engine", "Why NF4 and not the NVFP4
 // snapshot Parakeet ships"); the only temporary storage is the codes buffer.
 #include "wq_device.h"
@@ -32,6 +32,9 @@ ScaleLayout scale_layout(int fmt, bool dq, int64_t n, int64_t k) {
     case kNVFP4:
         L.g_off = align16(L.nb);
         L.bytes = L.g_off + 4;
+        break;
+    case kQ4_1:
+        L.bytes = 4 * L.nb;      // fp16 pair (d, m) per block
         break;
     default:
         L.bytes = 2 * L.nb;
@@ -169,6 +172,37 @@ __global__ __launch_bounds__(256) void k_quant_chunks(const float* __restrict__ 
         }
         *reinterpret_cast<uint2*>(codes + word_off8(n, k0, K)) = make_uint2(lo, hi);
         if ((k0 & 31) == 0) reinterpret_cast<uint16_t*>(scales)[scale_slot<kQ8_0>(n, k0 >> 5, K)] = d;
+    } else if constexpr (FMT == kQ4_1) {
+        // block minimum and maximum, each the first such element in ascending k (so the
+        // sign of a zero minimum is that of its first occurrence)
+        float lo = v[0], hi = v[0];
+        int lo_k = (int)(k0 & 31), hi_k = lo_k;
+#pragma unroll
+        for (int i = 1; i < 8; i++) {
+            if (v[i] < lo) { lo = v[i]; lo_k = (int)(k0 & 31) + i; }
+            if (v[i] > hi) { hi = v[i]; hi_k = (int)(k0 & 31) + i; }
+        }
+#pragma unroll
+        for (int s = 1; s <= 2; s <<= 1) {
+            const float pl = __shfl_xor(lo, s, 4), ph = __shfl_xor(hi, s, 4);
+            const int plk = __shfl_xor(lo_k, s, 4), phk = __shfl_xor(hi_k, s, 4);
+            if (pl < lo || (pl == lo && plk < lo_k)) { lo = pl; lo_k = plk; }
+            if (ph > hi || (ph == hi && phk < hi_k)) { hi = ph; hi_k = phk; }
+        }
+        if (!valid) return;
+        const uint16_t d = f16_sat_bits((hi - lo) / 15.0f);
+        const uint16_t m = f16_sat_bits(lo);
+        const float delta = f16_value(d), mu = f16_value(m);
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            uint32_t q = 0;
+            if (delta != 0.0f) q = (uint32_t)fminf(fmaxf(rintf((v[i] - mu) / delta), 0.0f), 15.0f);
+            word |= q << (4 * i);
+        }
+        *reinterpret_cast<uint32_t*>(codes + word_off4(n, k0, K)) = word;
+        if ((k0 & 31) == 0)
+            reinterpret_cast<uint32_t*>(scales)[scale_slot<kQ4_1>(n, k0 >> 5, K)] = (uint32_t)d | ((uint32_t)m << 16);
     } else {  // kQ4_0
         // signed element of largest magnitude; first index (ascending k) on ties
         float best_a = -1.0f, best_v = 0.0f;
@@ -320,6 +354,12 @@ __global__ __launch_bounds__(256) void k_dequant_chunks(const uint8_t* __restric
                 if (cd & 8u) v = -v;
                 o[i] = __fmul_rn(__fmul_rn(v, s), g);
             }
+        } else if constexpr (FMT == kQ4_1) {
+            const uint32_t dm = reinterpret_cast<const uint32_t*>(scales)[scale_slot<kQ4_1>(n, k0 >> 5, K)];
+            const float delta = f16_value((uint16_t)(dm & 0xFFFFu)), mu = f16_value((uint16_t)(dm >> 16));
+            // q * delta is exact (4 + 11 significant bits): one rounding, in the add
+#pragma unroll
+            for (int i = 0; i < 8; i++) o[i] = __fadd_rn(__fmul_rn((float)((word >> (4 * i)) & 15u), delta), mu);
         } else {  // kQ4_0
             const float delta = f16_value(reinterpret_cast<const uint16_t*>(scales)[scale_slot<kQ4_0>(n, k0 >> 5, K)]);
 #pragma unroll
@@ -361,6 +401,9 @@ hipError_t launch_quantize(int fmt, bool dq, int64_t n, int64_t k, const float* 
     case kQ4_0:
         hipLaunchKernelGGL((k_quant_chunks<kQ4_0, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
         break;
+    case kQ4_1:
+        hipLaunchKernelGGL((k_quant_chunks<kQ4_1, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
+        break;
     case kQ8_0:
         hipLaunchKernelGGL((k_quant_chunks<kQ8_0, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
         break;
@@ -384,6 +427,9 @@ hipError_t launch_dequantize(int fmt, bool dq, int64_t n, int64_t k, const uint8
         break;
     case kQ4_0:
         hipLaunchKernelGGL((k_dequant_chunks<kQ4_0, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);
+        break;
+    case kQ4_1:
+        hipLaunchKernelGGL((k_dequant_chunks<kQ4_1, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);
         break;
     case kQ8_0:
         hipLaunchKernelGGL((k_dequant_chunks<kQ8_0, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);
