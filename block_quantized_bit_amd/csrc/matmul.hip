@@ -61,6 +61,16 @@ struct KArgs {
     int out_v16;         // bf16 output whose splits allow 8-column (16-byte) stores
 };
 
+// One fp32 value at a uniform address (the NVFP4 global scale, the double-quant mean),
+// read with a vector buffer load.  A plain read of a uniform address becomes a scalar
+// load, and scalar loads share one wait counter with the kernel-argument loads: the
+// kernel's first wait for an argument would then also wait for this value's trip to
+// memory, before any weight load is issued.
+__device__ inline float load_f32_vmem(const uint8_t* p) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, 4, 0x00020000);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
+}
+
 // NF4 level of code c as a 16-way select over literals.  Table fills use these
 // rather than indexing the level arrays: a per-lane index would turn into a
 // vector memory load, and waiting for it would also wait for every weight load
@@ -571,8 +581,8 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
     const int64_t nbands = a.n / 16;
 
     float g = 1.0f, mu = 0.0f;
-    if constexpr (FMT == kNVFP4) g = *reinterpret_cast<const float*>(a.scales + a.L.g_off);
-    if constexpr (FMT == kNF4 && DQ) mu = *reinterpret_cast<const float*>(a.scales + a.L.mu_off);
+    if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.scales + a.L.g_off);
+    if constexpr (FMT == kNF4 && DQ) mu = load_f32_vmem(a.scales + a.L.mu_off);
     const uint16_t* xrow = a.x + (int64_t)(r < a.m ? r : 0) * a.ldx + h * 8;
     const uint16_t* xl = xs_dyn + (int64_t)(r < a.m ? r : 0) * a.k + h * 8;
     const int64_t per_wave = (KT + kGemvWaves - 1) / kGemvWaves;
@@ -775,8 +785,8 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
     const int64_t stride = (int64_t)gridDim.x * 4;
 
     float g = 1.0f, mu = 0.0f;
-    if constexpr (FMT == kNVFP4) g = *reinterpret_cast<const float*>(a.scales + a.L.g_off);
-    if constexpr (FMT == kNF4 && DQ) mu = *reinterpret_cast<const float*>(a.scales + a.L.mu_off);
+    if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.scales + a.L.g_off);
+    if constexpr (FMT == kNF4 && DQ) mu = load_f32_vmem(a.scales + a.L.mu_off);
 
     int64_t band = (int64_t)blockIdx.x * 4 + wave;
     StreamTile R0[T], R1[T];
@@ -1099,8 +1109,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     const int64_t nbands = N / 16;
 
     float g = 1.0f, mu = 0.0f;
-    if constexpr (FMT == kNVFP4) g = *reinterpret_cast<const float*>(a.scales + a.L.g_off);
-    if constexpr (FMT == kNF4 && DQ) mu = *reinterpret_cast<const float*>(a.scales + a.L.mu_off);
+    if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.scales + a.L.g_off);
+    if constexpr (FMT == kNF4 && DQ) mu = load_f32_vmem(a.scales + a.L.mu_off);
 
     // descriptors: band tiles of this wave (bands past n re-read the last band), X rows m0 ..
     GemmSrc S;
