@@ -386,16 +386,21 @@ __device__ inline void gemv_load(GemvTile<FMT>& t, const KArgs& a, int64_t band,
     }
 }
 
-// X (m rows of k bf16) copied once into LDS, rows packed with stride k, by LDS-direct loads
-// of 16 bytes per lane: chunk i (8 elements) of the copy lands at byte 16 i.
+// X (m rows of k bf16) copied once into LDS by LDS-direct loads of 16 bytes per lane,
+// chunk-major: chunk c (elements 8c .. 8c+7) of row r lands at byte 16 (c m + r).  The
+// 16 lanes that read one K chunk for 16 different rows (an A-operand read at m = 16)
+// then touch 256 contiguous bytes; row-major rows k * 2 bytes apart would all fall on
+// the same banks.  An LDS-direct load writes its lanes' chunks contiguously, and here
+// lane i of the copy fetches destination chunk i, so only the source addresses move.
 __device__ __forceinline__ void gemv_stage_x(uint16_t* xs, const KArgs& a, int wave, int lane) {
-    const int64_t per_row = a.k / 8;
-    const int64_t nchunks = (int64_t)a.m * per_row;
-    for (int64_t c0 = (int64_t)wave * 64; c0 < nchunks; c0 += 64 * kGemvWaves) {
-        const int64_t i = c0 + lane;
+    // the copy is used for m * k <= 32768 elements, so chunk indices fit 32 bits
+    const uint32_t m = (uint32_t)a.m;
+    const uint32_t nchunks = m * (uint32_t)(a.k / 8);
+    for (uint32_t c0 = (uint32_t)wave * 64; c0 < nchunks; c0 += 64 * kGemvWaves) {
+        const uint32_t i = c0 + (uint32_t)lane;
         if (i < nchunks) {
-            const int64_t row = i / per_row, col = (i - row * per_row) * 8;
-            __builtin_amdgcn_global_load_lds(a.x + row * a.ldx + col, xs + c0 * 8, 16, 0, 0);
+            const uint32_t c = m == 1 ? i : i / m, row = i - c * m;
+            __builtin_amdgcn_global_load_lds(a.x + (int64_t)row * a.ldx + (int64_t)c * 8, xs + c0 * 8, 16, 0, 0);
         }
     }
 }
@@ -514,7 +519,7 @@ __device__ __forceinline__ void gemv_load_band(GemvTile<FMT> (&R)[C], DqRow& dq,
 template <int FMT, bool DQ, int NI, int C, bool XL>
 __device__ __forceinline__ void gemv_consume_band(GemvTile<FMT> (&R)[C], const DqRow& dq, f32x4& acc, int64_t c0,
                                                   int wave, int64_t KT, const uint32_t* lut, uint32_t lane4, int h,
-                                                  float mu, const uint16_t* xl) {
+                                                  float mu, const uint16_t* xl, int64_t xm8) {
     constexpr int TK = tile_k(FMT);
 #pragma unroll
     for (int s = 0; s < C; s++) {
@@ -527,7 +532,8 @@ __device__ __forceinline__ void gemv_consume_band(GemvTile<FMT> (&R)[C], const D
             if constexpr (XL) {
 #pragma unroll
                 for (int j = 0; j < TK / 32; j++) {
-                    const uint4 v = *reinterpret_cast<const uint4*>(xl + kt * TK + 32 * j);
+                    // chunk kt TK / 8 + 4 j + h of this lane's row, chunk-major (gemv_stage_x)
+                    const uint4 v = *reinterpret_cast<const uint4*>(xl + (kt * (TK / 8) + 4 * j) * xm8);
                     R[s].A[j] = u32x4{v.x, v.y, v.z, v.w};
                 }
             }
@@ -584,7 +590,11 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
     if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.scales + a.L.g_off);
     if constexpr (FMT == kNF4 && DQ) mu = load_f32_vmem(a.scales + a.L.mu_off);
     const uint16_t* xrow = a.x + (int64_t)(r < a.m ? r : 0) * a.ldx + h * 8;
-    const uint16_t* xl = xs_dyn + (int64_t)(r < a.m ? r : 0) * a.k + h * 8;
+    // the LDS copy of X is chunk-major: chunk c of row r at element 8 (c m + r); the
+    // one-token instantiation (NI = 1 is only launched for m = 1) gets a constant stride,
+    // so its reads keep immediate offsets
+    const int64_t xm8 = NI == 1 ? 8 : (int64_t)a.m * 8;
+    const uint16_t* xl = xs_dyn + (int64_t)h * xm8 + (int64_t)(r < a.m ? r : 0) * 8;
     const int64_t per_wave = (KT + kGemvWaves - 1) / kGemvWaves;
 
     if constexpr (!PIPE) {
@@ -609,7 +619,7 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
                     __syncthreads();
                 }
             }
-            gemv_consume_band<FMT, DQ, NI, C, XL>(R, dq, acc, c0, wave, KT, lut, lane4, h, mu, xl);
+            gemv_consume_band<FMT, DQ, NI, C, XL>(R, dq, acc, c0, wave, KT, lut, lane4, h, mu, xl, xm8);
         }
         gemv_finish_band(a, red, acc, band, wave, lane, g);
     } else {
@@ -632,13 +642,13 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             gemv_load_band<FMT, DQ, C, XL>(R1, dq1, a, std::min<int64_t>(band + stride, nbands - 1), 0, wave, lane,
                                           r, xrow, KT);
-            gemv_consume_band<FMT, DQ, NI, C, XL>(R0, dq0, acc, 0, wave, KT, lut, lane4, h, mu, xl);
+            gemv_consume_band<FMT, DQ, NI, C, XL>(R0, dq0, acc, 0, wave, KT, lut, lane4, h, mu, xl, xm8);
             gemv_finish_band(a, red, acc, band, wave, lane, g);
             if (band + stride >= nbands) break;
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
             gemv_load_band<FMT, DQ, C, XL>(R0, dq0, a, std::min<int64_t>(band + 2 * stride, nbands - 1), 0, wave,
                                           lane, r, xrow, KT);
-            gemv_consume_band<FMT, DQ, NI, C, XL>(R1, dq1, acc, 0, wave, KT, lut, lane4, h, mu, xl);
+            gemv_consume_band<FMT, DQ, NI, C, XL>(R1, dq1, acc, 0, wave, KT, lut, lane4, h, mu, xl, xm8);
             gemv_finish_band(a, red, acc, band + stride, wave, lane, g);
         }
     }
