@@ -20,9 +20,9 @@
  *     short of VRAM", intro; "mbehr90/whisper-large-v3-turbo-nvfp4", section
  *     "What is quantized".
  *   - q8_0 / q4_0 block formats: "Run quantized Whisper on the fused Metal
- *     decode path", sections "Summary" and "Why the policy"; q4_1 is named
- *     there too (section "Why the policy") as a format that decodes correctly
- *     but lacks fast kernels.
+ *     decode path", sections "Summary" and "Why the policy"; q4_1 and q5_0
+ *     are named there too (section "Why the policy") as formats that decode
+ *     correctly but lack fast kernels.
  *   - Host reference path for quantized linears used to rule out kernel bugs:
  *     same page, section "Why the policy".
  * Everything the pages leave open (codebook values, rounding, tie-breaks,
@@ -43,6 +43,7 @@
 #define OR_Q4_0 3
 #define OR_Q8_0 4
 #define OR_Q4_1 5
+#define OR_Q5_0 6
 
 /* ------------------------------------------------------------------------ */
 /* Scalar codecs                                                              */
@@ -480,6 +481,48 @@ void or_q4_1_dequantize(int64_t n, int64_t k, const uint8_t* codes, const uint16
 }
 
 /* ------------------------------------------------------------------------ */
+/* q5_0: blocks of 32, one fp16 scale, signed 5-bit codes.  The page only names */
+/* the format; reading, as for q4_0 with one more bit:                          */
+/*   m = the signed element of largest magnitude (first in ascending k on a    */
+/*   tie); d = fp16(fl(m / -16)); delta = float(d);                             */
+/*   q = 16 if delta == 0 else clamp(rint(fl(w / delta)), -16, 15) + 16 (0..31), */
+/*   w^ = fl((q - 16) * delta) (exact: 5 + 11 significant bits).                 */
+/* codes: [n][k] one 5-bit code per byte; scales: [n][k/32] fp16.              */
+/* ------------------------------------------------------------------------ */
+void or_q5_0_quantize(int64_t n, int64_t k, const float* w, uint8_t* codes, uint16_t* scales) {
+    const int64_t nbk = k / 32;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t b = 0; b < nbk; b++) {
+            const float* src = w + r * k + b * 32;
+            float amax = 0.0f, m = src[0];
+            for (int i = 0; i < 32; i++) {
+                float t = fabsf(src[i]);
+                if (t > amax) { amax = t; m = src[i]; }
+            }
+            uint16_t d = or_fp16_encode(m / -16.0f);
+            scales[r * nbk + b] = d;
+            float delta = or_fp16_decode(d);
+            for (int i = 0; i < 32; i++) {
+                uint8_t q = 16;
+                if (delta != 0.0f) {
+                    float v = rintf(src[i] / delta);
+                    if (v > 15.0f) v = 15.0f;
+                    if (v < -16.0f) v = -16.0f;
+                    q = (uint8_t)((int)v + 16);
+                }
+                codes[r * k + b * 32 + i] = q;
+            }
+        }
+}
+
+void or_q5_0_dequantize(int64_t n, int64_t k, const uint8_t* codes, const uint16_t* scales, float* out) {
+    const int64_t nbk = k / 32;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t i = 0; i < k; i++)
+            out[r * k + i] = (float)((int)codes[r * k + i] - 16) * or_fp16_decode(scales[r * nbk + i / 32]);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Packed layout (the library's storage format; the pages give none).          */
 /*                                                                              */
 /* 4-bit codes (NF4, NVFP4, q4_0, q4_1): the matrix is cut into tiles of 16     */
@@ -498,6 +541,10 @@ void or_q4_1_dequantize(int64_t n, int64_t k, const uint8_t* codes, const uint16
 /*   NVFP4   E4M3 byte,   8 per row  (128 per tile), then at align16(nb): g    */
 /*   q4_0    fp16,        4 per row  (64 per tile)                              */
 /*   q4_1    fp16 pair (d, m), 4 per row  (64 pairs = 256 bytes per tile)       */
+/*   q5_0    fp16 d, 4 per row (like q4_0); then at align16(2 nb) a second     */
+/*           plane of one 32-bit word per block, same order (16 bytes per row   */
+/*           and tile): bit i holds bit 4 of the code of element i of the block; */
+/*           the codes' low 4 bits are the 4-bit codes above.                    */
 /*   q8_0    fp16,        2 per row  (32 per 16x64 tile)                        */
 /* ------------------------------------------------------------------------ */
 static int64_t align16(int64_t v) { return (v + 15) & ~(int64_t)15; }
@@ -527,6 +574,11 @@ int or_packed_size(int fmt, int dq, int64_t n, int64_t k, int64_t* codes_bytes, 
         if (k % 128) return -1;
         *codes_bytes = n * k / 2;
         *scales_bytes = 4 * (n * k / 32);
+        return 0;
+    case OR_Q5_0:
+        if (k % 128) return -1;
+        *codes_bytes = n * k / 2;
+        *scales_bytes = align16(2 * (n * k / 32)) + 4 * (n * k / 32);
         return 0;
     case OR_Q8_0:
         if (k % 64) return -1;
@@ -665,6 +717,25 @@ int or_quantize_packed(int fmt, int dq, int64_t n, int64_t k, const float* w,
         or_pack_scales(n, k, 32, 128, 4, s, scales_packed);
         or_q4_1_dequantize(n, k, codes_logical, s, w_hat);
         free(s);
+        return 0;
+    }
+    if (fmt == OR_Q5_0) {
+        const int64_t nb = n * k / 32;
+        uint16_t* s = (uint16_t*)malloc(2 * nb);
+        uint32_t* hb = (uint32_t*)calloc((size_t)nb, 4);
+        uint8_t* lo = (uint8_t*)malloc((size_t)(n * k));
+        or_q5_0_quantize(n, k, w, codes_logical, s);
+        for (int64_t r = 0; r < n; r++)
+            for (int64_t i = 0; i < k; i++) {
+                const uint8_t q = codes_logical[r * k + i];
+                lo[r * k + i] = q & 15;
+                if (q & 16) hb[r * (k / 32) + i / 32] |= 1u << (i % 32);
+            }
+        or_pack_codes4(n, k, lo, codes_packed);
+        or_pack_scales(n, k, 32, 128, 2, s, scales_packed);
+        or_pack_scales(n, k, 32, 128, 4, hb, scales_packed + align16(2 * nb));
+        or_q5_0_dequantize(n, k, codes_logical, s, w_hat);
+        free(s); free(hb); free(lo);
         return 0;
     }
     if (fmt == OR_Q8_0) {

@@ -5,7 +5,7 @@ CPU-baseline leg of the bench, never by the library.  It shares no code with
 the HIP path; it only receives the same seeded inputs.
 
 Format numbers match the library's public enum values so a test can pass one
-number to both sides: NF4 = 1, NVFP4 = 2, Q4_0 = 3, Q8_0 = 4, Q4_1 = 5.
+number to both sides: NF4 = 1, NVFP4 = 2, Q4_0 = 3, Q8_0 = 4, Q4_1 = 5, Q5_0 = 6.
 """
 from __future__ import annotations
 
@@ -15,7 +15,7 @@ import subprocess
 
 import numpy as np
 
-NF4, NVFP4, Q4_0, Q8_0, Q4_1 = 1, 2, 3, 4, 5
+NF4, NVFP4, Q4_0, Q8_0, Q4_1, Q5_0 = 1, 2, 3, 4, 5, 6
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -71,6 +71,8 @@ def lib():
         L.or_q4_0_dequantize.argtypes = [i64, i64, P, P, P]
         L.or_q4_1_quantize.argtypes = [i64, i64, P, P, P]
         L.or_q4_1_dequantize.argtypes = [i64, i64, P, P, P]
+        L.or_q5_0_quantize.argtypes = [i64, i64, P, P, P]
+        L.or_q5_0_dequantize.argtypes = [i64, i64, P, P, P]
         L.or_packed_size.restype = ctypes.c_int
         L.or_packed_size.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64,
                                      ctypes.POINTER(i64), ctypes.POINTER(i64)]
@@ -231,6 +233,25 @@ def q4_1_dequantize(codes, scales):
     n, k = codes.shape
     out = np.zeros((n, k), np.float32)
     lib().or_q4_1_dequantize(n, k, _p(codes), _p(scales), _p(out))
+    return out
+
+
+def q5_0_quantize(w: np.ndarray):
+    """Logical 5-bit codes [n,k] (0..31) and fp16 scales [n*k/32]."""
+    w = np.ascontiguousarray(w, np.float32)
+    n, k = w.shape
+    codes = np.zeros((n, k), np.uint8)
+    s = np.zeros(n * k // 32, np.uint16)
+    lib().or_q5_0_quantize(n, k, _p(w), _p(codes), _p(s))
+    return codes, s
+
+
+def q5_0_dequantize(codes, scales):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint16)
+    n, k = codes.shape
+    out = np.zeros((n, k), np.float32)
+    lib().or_q5_0_dequantize(n, k, _p(codes), _p(scales), _p(out))
     return out
 
 

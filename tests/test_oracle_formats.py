@@ -386,3 +386,55 @@ def test_q4_1_error_bound(orc):
             assert err.max() <= d / 2 + abs(m - float(blk.min())) + 1e-9
             j = int(np.argmin(blk))
             assert codes[r, 32 * b + j] == 0 and w_hat[r, 32 * b + j] == np.float32(m)
+
+
+# ----------------------------------------------------------------- q5_0 ----
+# q5_0 is only named ("Run quantized Whisper on the fused Metal decode path",
+# "Why the policy"); the reading: as q4_0 with 5-bit codes, d = fp16(m / -16),
+# q = clamp(rint(w / d), -16, 15) + 16, w^ = (q - 16) d.
+
+def test_q5_0_brute_force(orc):
+    rng = np.random.default_rng(17)
+    w = (rng.standard_normal((16, 128)) * 0.02).astype(np.float32)
+    codes, sc = orc.q5_0_quantize(w)
+    assert codes.max() <= 31
+    for r in range(16):
+        for b in range(4):
+            blk = w[r, 32 * b:32 * b + 32]
+            j = int(np.argmax(np.abs(blk)))                   # first index on ties
+            want_d = _f16(_f32(blk[j]) / _f32(-16)).view(np.uint16)[0]
+            assert sc[r * 4 + b] == want_d
+            delta = np.uint16(want_d).view(np.float16).astype(np.float32)
+            assert codes[r, 32 * b + j] == 0                   # the extreme maps to -16
+            for i in range(32):
+                qb = _q_brute(blk[i], delta, -16, 15) + 16
+                qi = int(codes[r, 32 * b + i])
+                if qi != qb:
+                    t = Fraction(float(blk[i])) / Fraction(float(delta))
+                    assert abs(abs(t - (qi - 16)) - Fraction(1, 2)) < Fraction(1, 2 ** 18)
+
+
+def test_q5_0_extreme_exact_zero_block_and_packing(orc):
+    w = np.zeros((16, 128), np.float32)
+    w[0, :32] = np.linspace(-0.5, 0.5, 32, dtype=np.float32)
+    w[0, 5] = 0.75                     # m = 0.75 -> d = -0.046875 (fp16 exact)
+    w[0, 6] = 0.0
+    w[1, 32:64] = (np.arange(32, dtype=np.float32) - 16) * np.float32(0.125)   # -2 .. 1.875: exact levels
+    codes, sc = orc.q5_0_quantize(w)
+    w_hat = orc.q5_0_dequantize(codes, sc)
+    assert w_hat[0, 5] == np.float32(0.75) and codes[0, 5] == 0
+    assert w_hat[0, 6] == 0 and np.signbit(w_hat[0, 6])       # (16-16) * negative delta = -0.0
+    assert np.array_equal(w_hat[1, 32:64], w[1, 32:64])         # m = -2 -> d = 0.125, every level exact
+    assert np.array_equal(codes[1, 32:64], np.arange(32))
+    assert np.all(codes[2] == 16) and np.all(w_hat[2] == 0)     # all-zero block
+    # packed: low nibbles in the 4-bit tiles, bit 4 of each code in the block's 32-bit word
+    res = orc.quantize(6, w)
+    assert orc.packed_size(6, False, 16, 128) == (1024, 128 + 256)
+    assert np.array_equal(orc.unpack_codes4(res["codes"], 16, 128), codes & 15)
+    hb = res["scales"][128:].view(np.uint32)
+    for r in range(16):
+        for b in range(4):
+            word = int(hb[r * 4 + b])                           # one tile: slot = 4 r + b
+            want = sum(1 << i for i in range(32) if codes[r, 32 * b + i] & 16)
+            assert word == want
+    assert np.array_equal(res["scales"][:128].view(np.uint16), sc.reshape(16, 4).reshape(-1))
