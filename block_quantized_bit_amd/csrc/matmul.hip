@@ -15,13 +15,13 @@
 // address is built with one v_perm_b32.  The GEMV table holds bf16 values (fed
 // straight to the MFMA), the GEMM table fp32 values (scaled exactly, then rounded
 // once to bf16).  NVFP4 codes and scales are decoded with the gfx950 fp4 / fp8
-// conversion instructions; q8_0 bytes, q4_1 nibbles (and q4_0 nibbles in the
-// GEMM) are converted to floats in registers.
+// conversion instructions; q8_0 bytes, q4_1 and q5_0 codes (and q4_0 nibbles in
+// the GEMM) are converted to floats in registers.
 //
 // GEMV (m <= 16, decode): B = raw code values (NF4 level, q4_0 q-8, q8_0 q),
 //   the per-block scale is applied to the MFMA partial sum of each block; for
 //   NVFP4 (16-value blocks, two per 32-K slice) B = e2m1*scale (exact in bf16);
-//   for q4_1 (scale and minimum) B = bf16(w^) as in the GEMM.
+//   for q4_1 (scale and minimum) and q5_0 (fifth bits) B = bf16(w^) as in the GEMM.
 //   K is split over the waves of a workgroup and reduced in LDS.
 // GEMM (m >= 17, encoder): each wave dequantizes 64 columns x 128 K of W per
 //   step to bf16(w^) -- w^ computed exactly as the format defines it, then one
@@ -191,6 +191,32 @@ __device__ __forceinline__ u32x4 q4_1_operand(uint32_t word, uint32_t dm) {
     return B;
 }
 
+// q5_0 B operand for one 32-wide K slice: the slice's code word (low 4 bits, nibble i =
+// k 8h + i), the 8 fifth bits of those k (bit i) and the block's fp16 scale.  The fifth
+// bits move to bit 4 of the byte their nibble lands in with one 24-bit multiply per
+// parity: in e = bits & 0x55 (bits 2p), e * 0x410410 puts bit 2p at 8p + 4 (the shifts
+// 4, 10, 16, 22 add 6p + 4 for term p; every other term lands on a different even bit and
+// any carry stops at the odd bit above it), then & 0x10101010 keeps bits 8p + 4.
+// c = q + 16 (0..31) as a float; w^ = (c - 16) * d = fl(c * d - 16 d) exactly (both products
+// fit 16 significant bits), one fma; then one RNE to bf16.
+__device__ __forceinline__ u32x4 q5_0_operand(uint32_t word, uint32_t high8, uint16_t dbits) {
+    const float d = f16_value(dbits);
+    const float d16 = -16.0f * d;
+    uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+    lo |= __umul24(high8 & 0x55u, 0x410410u) & 0x10101010u;
+    hi |= __umul24((high8 >> 1) & 0x55u, 0x410410u) & 0x10101010u;
+    // opaque to the optimizer, so that each byte converts with one v_cvt_f32_ubyteN
+    asm("" : "+v"(lo), "+v"(hi));
+    u32x4 B;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const float c0 = (float)((lo >> (8 * q)) & 255u);
+        const float c1 = (float)((hi >> (8 * q)) & 255u);
+        B[q] = pack_bf16_rne(__builtin_fmaf(c0, d, d16), __builtin_fmaf(c1, d, d16));
+    }
+    return B;
+}
+
 __device__ inline f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
@@ -304,7 +330,7 @@ __device__ __forceinline__ void wait_vm() {
 template <int FMT>
 struct GemvTile {
     uint4 code;             // this lane's 16 bytes of the tile
-    uint32_t sc[4];         // raw scale words (format dependent)
+    uint32_t sc[6];         // raw scale words (format dependent)
     u32x4 A[tile_k(FMT) / 32];
 };
 
@@ -314,7 +340,7 @@ constexpr int kGemvWaves = 8;   // waves per workgroup, all on one band, splitti
 // double quant with k <= 16384, plus two per band for the row's group scales -- a wait for at
 // most this many per tile outstanding can only wait longer than needed).
 template <int FMT, bool DQ>
-__device__ constexpr int gemv_w_loads() { return 2; }
+__device__ constexpr int gemv_w_loads() { return FMT == kQ5_0 ? 3 : 2; }
 
 // Double-quant group scales of one row, when the row holds <= 256 blocks (k <= 16384) and so
 // spans at most two 256-block groups: blocks j < jt of the row are in the first.
@@ -362,6 +388,16 @@ __device__ inline void gemv_load(GemvTile<FMT>& t, const KArgs& a, int64_t band,
         const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 64 + r * 4) * 2);
         t.sc[0] = v.x;
         t.sc[1] = v.y;
+    } else if constexpr (FMT == kQ5_0) {
+        // the row's four fp16 scales (8 bytes), then its four fifth-bit words (16 bytes)
+        const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 64 + r * 4) * 2);
+        t.sc[0] = v.x;
+        t.sc[1] = v.y;
+        const uint4 hb = *reinterpret_cast<const uint4*>(a.scales + a.L.hb_off + tile * 256 + r * 16);
+        t.sc[2] = hb.x;
+        t.sc[3] = hb.y;
+        t.sc[4] = hb.z;
+        t.sc[5] = hb.w;
     } else if constexpr (FMT == kQ4_1) {
         // the row's four (d, m) pairs of the tile: 16 bytes
         const uint4 v = *reinterpret_cast<const uint4*>(a.scales + tile * 256 + r * 16);
@@ -453,6 +489,14 @@ __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const ui
         // B = bf16(w^), block j of the row for K slice j
 #pragma unroll
         for (int j = 0; j < 4; j++) acc = mfma(t.A[j], q4_1_operand(uw[j], t.sc[j]), acc);
+    } else if constexpr (FMT == kQ5_0) {
+        // B = bf16(w^), block j of the row for K slice j; this lane's k are bits 8h .. 8h+7
+        // of the block's fifth-bit word
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint16_t db = (uint16_t)(t.sc[j >> 1] >> (16 * (j & 1)));
+            acc = mfma(t.A[j], q5_0_operand(uw[j], (t.sc[2 + j] >> (8 * h)) & 255u, db), acc);
+        }
     } else if constexpr (FMT == kNVFP4) {
         // block 2j + (h >> 1) of the row: byte 2 (j & 1) + (h >> 1) of scale word j >> 1
         const uint32_t hs = 8u * (uint32_t)(h >> 1);
@@ -849,7 +893,7 @@ __device__ constexpr bool gemm_uses_lut() { return FMT == kNF4; }
 template <int FMT>
 struct GemmW {
     uint4 code[tile_k(FMT) == 64 ? 2 : 1];
-    uint32_t sc[4];
+    uint32_t sc[6];
 };
 
 // Buffer descriptors of one workgroup's loads: per band of the wave (its
@@ -861,13 +905,15 @@ struct GemmSrc {
     uint32_t wbytes, sbytes;    // one band's codes / scales
     const uint8_t* dt;          // double-quant group scales
     uint32_t dtbytes;
+    const uint8_t* hb[4];       // q5_0: fifth-bit words of the band's first tile
+    uint32_t hbbytes;
     const uint8_t* x;           // X row m0
     uint32_t xbytes;
 };
 
 // Vector memory instructions gemm_load_w issues per band (the pipeline waits count them).
 template <int FMT, bool DQ>
-__device__ constexpr int gemm_w_loads() { return FMT == kQ8_0 ? 4 : (FMT == kNF4 && DQ) ? 4 : 2; }
+__device__ constexpr int gemm_w_loads() { return FMT == kQ8_0 ? 4 : (FMT == kNF4 && DQ) ? 4 : FMT == kQ5_0 ? 3 : 2; }
 
 // Codes and scales of K step st (one 16 x 128 tile, two 16 x 64 tiles for Q8_0) of band nf.
 // rowblk: index of the first 64-value block of the lane's row (double quant only).
@@ -888,6 +934,15 @@ __device__ __forceinline__ void gemm_load_w(GemmW<FMT>& w, const GemmSrc& S, int
             const int64_t b0 = rowblk + 2 * st;
             w.sc[1] = __builtin_amdgcn_raw_buffer_load_b32(buf_res_uni(S.dt, S.dtbytes), (uint32_t)(b0 >> 8) * 4u, 0, 0);
             w.sc[2] = __builtin_amdgcn_raw_buffer_load_b32(buf_res_uni(S.dt, S.dtbytes), (uint32_t)((b0 + 1) >> 8) * 4u, 0, 0);
+        } else if constexpr (FMT == kQ5_0) {   // 4 x fp16 d (8 bytes), 4 fifth-bit words (16 bytes)
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(buf_res_uni(S.scale[nf], S.sbytes), r * 8, uni(st * 128), 0);
+            w.sc[0] = v[0];
+            w.sc[1] = v[1];
+            const uint4 hb = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buf_res_uni(S.hb[nf], S.hbbytes), r * 16, uni(st * 256), 0));
+            w.sc[2] = hb.x;
+            w.sc[3] = hb.y;
+            w.sc[4] = hb.z;
+            w.sc[5] = hb.w;
         } else if constexpr (FMT == kQ4_1) {   // 4 x (fp16 d, fp16 m): 16 bytes per row and tile
             const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buf_res_uni(S.scale[nf], S.sbytes), r * 16, uni(st * 256), 0));
             w.sc[0] = v.x;
@@ -941,6 +996,10 @@ __device__ __forceinline__ u32x4 gemm_dequant(const GemmW<FMT>& w, int j, const 
     } else if constexpr (FMT == kQ4_1) {
         const uint32_t word = j == 0 ? w.code[0].x : j == 1 ? w.code[0].y : j == 2 ? w.code[0].z : w.code[0].w;
         B = q4_1_operand(word, w.sc[j]);
+    } else if constexpr (FMT == kQ5_0) {
+        // hs = 8 h for q5_0: this lane's k are bits 8h .. 8h+7 of block j's fifth-bit word
+        const uint32_t word = j == 0 ? w.code[0].x : j == 1 ? w.code[0].y : j == 2 ? w.code[0].z : w.code[0].w;
+        B = q5_0_operand(word, (w.sc[2 + j] >> hs) & 255u, (uint16_t)(w.sc[j >> 1] >> (16 * (j & 1))));
     } else if constexpr (FMT == kQ4_0) {
         // nibble c as a float, then c*d - 8d: both products are exact in fp32 (c has 4
         // significant bits, d 11), so this is (c - 8)*d exactly; one RNE to bf16
@@ -1088,7 +1147,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     const int r = lane & 15;
     const int h = lane >> 4;
     const uint32_t lane8 = (uint32_t)(lane & 31) << 3;
-    const uint32_t hs = 8u * (uint32_t)(h >> 1);
+    // NVFP4: byte of the scale word for this lane's 16-value block; q5_0: byte of the
+    // fifth-bit word for this lane's 8 k
+    const uint32_t hs = FMT == kQ5_0 ? 8u * (uint32_t)h : 8u * (uint32_t)(h >> 1);
     const int64_t M = a.m, N = a.n, K = a.k;
     constexpr int TK = tile_k(FMT);
     const int64_t KT = K / TK;
@@ -1132,7 +1193,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
         S.code[nf] = a.codes + band * KT * kTileBytes;
         S.scale[nf] = a.scales + band * KT * SB;
         rowblk[nf] = (band * 16 + r) * (K / 64);
+        if constexpr (FMT == kQ5_0) S.hb[nf] = a.scales + a.L.hb_off + band * KT * 256;
     }
+    S.hbbytes = (uint32_t)(KT * 256);
     S.wbytes = (uint32_t)(KT * kTileBytes);
     S.sbytes = (uint32_t)(KT * SB);
     S.dt = a.scales + a.L.d_off;
@@ -1535,9 +1598,9 @@ static void gemv_launch_ni(const KArgs& a, hipStream_t st) {
     const int64_t nbands = a.n / 16;
     // Many more bands than resident waves, K <= 10 tiles, X fits in LDS: the
     // streaming kernel (two workgroups of 4 waves per CU, each wave >= 4 bands).
-    // (q4_1 has no streaming variant: its 16 bytes of scales per row and tile take the
-    // general kernel)
-    if constexpr (FMT != kQ4_1) {
+    // (q4_1 and q5_0 have no streaming variant: their 16 more bytes of scales per row and
+    // tile take the general kernel)
+    if constexpr (FMT != kQ4_1 && FMT != kQ5_0) {
         if (nbands >= kStreamMinBands && (int64_t)a.m * a.k <= kStreamXMax && KT <= 10) {
             const unsigned grid = 2 * kNumCU;
             if (KT <= 4) hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 4>), dim3(grid), dim3(256), 0, st, a);
@@ -1571,6 +1634,7 @@ hipError_t launch_gemv(const MatmulProblem& p, hipStream_t st) {
     case kNVFP4: gemv_dispatch_ni<kNVFP4, false>(a, st); break;
     case kQ4_0: gemv_dispatch_ni<kQ4_0, false>(a, st); break;
     case kQ4_1: gemv_dispatch_ni<kQ4_1, false>(a, st); break;
+    case kQ5_0: gemv_dispatch_ni<kQ5_0, false>(a, st); break;
     case kQ8_0: gemv_dispatch_ni<kQ8_0, false>(a, st); break;
     default: return hipErrorInvalidValue;
     }
@@ -1602,6 +1666,7 @@ hipError_t launch_gemm(const MatmulProblem& p, hipStream_t st) {
     case kNVFP4: gemm_launch<kNVFP4, false>(s.nb, grid, a, st); break;
     case kQ4_0: gemm_launch<kQ4_0, false>(s.nb, grid, a, st); break;
     case kQ4_1: gemm_launch<kQ4_1, false>(s.nb, grid, a, st); break;
+    case kQ5_0: gemm_launch<kQ5_0, false>(s.nb, grid, a, st); break;
     case kQ8_0: gemm_launch<kQ8_0, false>(s.nb, grid, a, st); break;
     default: return hipErrorInvalidValue;
     }

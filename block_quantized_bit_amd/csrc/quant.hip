@@ -7,7 +7,7 @@
 // for the Whisper engine", "What's here"); NVFP4 ("asr: add a 4-bit nvfp4 option
 // for cards short of VRAM", intro; "mbehr90/whisper-large-v3-turbo-nvfp4", "What
 // is quantized"); q4_0 / q8_0 ("Run quantized Whisper on the fused Metal decode
-// path", "Summary"); q4_1 (same page, "Why the policy").  One matrix at a time, as the checkpoint streams in ("asr:
+// path", "Summary"); q4_1 and q5_0 (same page, "Why the policy").  One matrix at a time, as the checkpoint streams in ("asr:
 // add a 4-bit nf4 option for the Whisper engine", "Why NF4 and not the NVFP4
 // snapshot Parakeet ships"); the only temporary storage is the codes buffer.
 #include "wq_device.h"
@@ -35,6 +35,10 @@ ScaleLayout scale_layout(int fmt, bool dq, int64_t n, int64_t k) {
         break;
     case kQ4_1:
         L.bytes = 4 * L.nb;      // fp16 pair (d, m) per block
+        break;
+    case kQ5_0:
+        L.hb_off = align16(2 * L.nb);    // fp16 d per block, then one 32-bit fifth-bit word per block
+        L.bytes = L.hb_off + 4 * L.nb;
         break;
     default:
         L.bytes = 2 * L.nb;
@@ -203,6 +207,38 @@ __global__ __launch_bounds__(256) void k_quant_chunks(const float* __restrict__ 
         *reinterpret_cast<uint32_t*>(codes + word_off4(n, k0, K)) = word;
         if ((k0 & 31) == 0)
             reinterpret_cast<uint32_t*>(scales)[scale_slot<kQ4_1>(n, k0 >> 5, K)] = (uint32_t)d | ((uint32_t)m << 16);
+    } else if constexpr (FMT == kQ5_0) {
+        // signed element of largest magnitude; first index (ascending k) on ties
+        float best_a = -1.0f, best_v = 0.0f;
+        int best_k = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float t = fabsf(v[i]);
+            if (t > best_a) { best_a = t; best_v = v[i]; best_k = (int)(k0 & 31) + i; }
+        }
+#pragma unroll
+        for (int s = 1; s <= 2; s <<= 1) {
+            const float pa = __shfl_xor(best_a, s, 4);
+            const float pv = __shfl_xor(best_v, s, 4);
+            const int pk = __shfl_xor(best_k, s, 4);
+            if (pa > best_a || (pa == best_a && pk < best_k)) { best_a = pa; best_v = pv; best_k = pk; }
+        }
+        if (!valid) return;
+        const uint16_t d = f16_sat_bits(best_v / -16.0f);
+        const float delta = f16_value(d);
+        uint32_t word = 0, high = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            uint32_t q = 16;
+            if (delta != 0.0f) q = (uint32_t)((int)fminf(fmaxf(rintf(v[i] / delta), -16.0f), 15.0f) + 16);
+            word |= (q & 15u) << (4 * i);
+            high |= (q >> 4) << i;
+        }
+        *reinterpret_cast<uint32_t*>(codes + word_off4(n, k0, K)) = word;
+        const int64_t slot = scale_slot<kQ5_0>(n, k0 >> 5, K);
+        // this thread's 8 fifth bits are byte (k0 % 32) / 8 of the block's word
+        scales[L.hb_off + 4 * slot + ((k0 & 31) >> 3)] = (uint8_t)high;
+        if ((k0 & 31) == 0) reinterpret_cast<uint16_t*>(scales)[slot] = d;
     } else {  // kQ4_0
         // signed element of largest magnitude; first index (ascending k) on ties
         float best_a = -1.0f, best_v = 0.0f;
@@ -360,6 +396,15 @@ __global__ __launch_bounds__(256) void k_dequant_chunks(const uint8_t* __restric
             // q * delta is exact (4 + 11 significant bits): one rounding, in the add
 #pragma unroll
             for (int i = 0; i < 8; i++) o[i] = __fadd_rn(__fmul_rn((float)((word >> (4 * i)) & 15u), delta), mu);
+        } else if constexpr (FMT == kQ5_0) {
+            const int64_t slot = scale_slot<kQ5_0>(n, k0 >> 5, K);
+            const float delta = f16_value(reinterpret_cast<const uint16_t*>(scales)[slot]);
+            const uint32_t high = scales[L.hb_off + 4 * slot + ((k0 & 31) >> 3)];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int q = (int)(((word >> (4 * i)) & 15u) | (((high >> i) & 1u) << 4));
+                o[i] = __fmul_rn((float)(q - 16), delta);
+            }
         } else {  // kQ4_0
             const float delta = f16_value(reinterpret_cast<const uint16_t*>(scales)[scale_slot<kQ4_0>(n, k0 >> 5, K)]);
 #pragma unroll
@@ -404,6 +449,9 @@ hipError_t launch_quantize(int fmt, bool dq, int64_t n, int64_t k, const float* 
     case kQ4_1:
         hipLaunchKernelGGL((k_quant_chunks<kQ4_1, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
         break;
+    case kQ5_0:
+        hipLaunchKernelGGL((k_quant_chunks<kQ5_0, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
+        break;
     case kQ8_0:
         hipLaunchKernelGGL((k_quant_chunks<kQ8_0, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
         break;
@@ -430,6 +478,9 @@ hipError_t launch_dequantize(int fmt, bool dq, int64_t n, int64_t k, const uint8
         break;
     case kQ4_1:
         hipLaunchKernelGGL((k_dequant_chunks<kQ4_1, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);
+        break;
+    case kQ5_0:
+        hipLaunchKernelGGL((k_dequant_chunks<kQ5_0, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);
         break;
     case kQ8_0:
         hipLaunchKernelGGL((k_dequant_chunks<kQ8_0, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);

@@ -31,6 +31,7 @@ wq_status check_desc(const wq_desc* d, Desc* out) {
     case WQ_NVFP4: bk = 16; break;
     case WQ_Q4_0:
     case WQ_Q4_1:
+    case WQ_Q5_0:
     case WQ_Q8_0: bk = 32; break;
     default: return WQ_ERR_INVALID_ARG;
     }

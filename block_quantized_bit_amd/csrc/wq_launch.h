@@ -14,6 +14,7 @@ struct ScaleLayout {
     int64_t d_off;     // NF4+DQ: fp32 d[ng]
     int64_t mu_off;    // NF4+DQ: fp32 mean
     int64_t g_off;     // NVFP4: fp32 global scale
+    int64_t hb_off;    // Q5_0: 32-bit fifth-bit words, one per block, tile order
     int64_t bytes;     // total scales bytes
 };
 

@@ -10,7 +10,7 @@ from block_quantized_bit_amd import wq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "wq.h")
-NF4, NVFP4, Q4_0, Q8_0, Q4_1 = 1, 2, 3, 4, 5
+NF4, NVFP4, Q4_0, Q8_0, Q4_1, Q5_0 = 1, 2, 3, 4, 5, 6
 
 
 def _declared():
@@ -41,7 +41,7 @@ SHAPES = [(16, 128), (48, 384), (272, 640), (1536, 384), (3840, 1280), (1280, 51
 
 
 @pytest.mark.parametrize("fmt,dq", [(NF4, False), (NF4, True), (NVFP4, False), (Q4_0, False), (Q8_0, False),
-                                    (Q4_1, False)])
+                                    (Q4_1, False), (Q5_0, False)])
 def test_packed_size_matches_oracle(orc, fmt, dq):
     for n, k in SHAPES:
         assert wq.wq_packed_size(wq.desc(fmt, n, k, dq)) == orc.packed_size(fmt, dq, n, k)
@@ -69,7 +69,9 @@ def test_descriptor_validation():
         (wq.wq_desc(Q4_1, 0, 16, 64, 0, 0), 3),         # k % 128 for q4_1 too
         (wq.wq_desc(Q4_1, 16, 16, 128, 0, 0), 2),       # q4_1 blocks are 32
         (wq.wq_desc(Q4_1, 0, 16, 128, 256, 0), 2),      # double-quant only for NF4
-        (wq.wq_desc(6, 0, 16, 128, 0, 0), 1),           # past the last format
+        (wq.wq_desc(Q5_0, 0, 16, 64, 0, 0), 3),         # k % 128 for q5_0
+        (wq.wq_desc(Q5_0, 0, 16, 128, 256, 0), 2),      # double-quant only for NF4
+        (wq.wq_desc(7, 0, 16, 128, 0, 0), 1),           # past the last format
         (wq.wq_desc(Q8_0, 0, 16, 96, 0, 0), 3),         # k % 64 for q8_0
         (wq.wq_desc(Q8_0, 0, 0, 64, 0, 0), 3),          # n > 0
         (wq.wq_desc(NF4, 0, 16, 128, 0, 7), 1),         # reserved
@@ -141,6 +143,6 @@ def test_format_names():
     assert wq.format_from_name("nf4") == wq.format_from_name("4bit") == wq.format_from_name("INT4") == NF4
     assert wq.format_from_name("nvfp4") == NVFP4
     assert wq.format_from_name("q4_0") == Q4_0 and wq.format_from_name("q8_0") == Q8_0
-    assert wq.format_from_name("q4_1") == Q4_1
+    assert wq.format_from_name("q4_1") == Q4_1 and wq.format_from_name("q5_0") == Q5_0
     with pytest.raises(ValueError):
         wq.format_from_name("fp8")
