@@ -20,9 +20,9 @@
  *     short of VRAM", intro; "mbehr90/whisper-large-v3-turbo-nvfp4", section
  *     "What is quantized".
  *   - q8_0 / q4_0 block formats: "Run quantized Whisper on the fused Metal
- *     decode path", sections "Summary" and "Why the policy"; q4_1 and q5_0
- *     are named there too (section "Why the policy") as formats that decode
- *     correctly but lack fast kernels.
+ *     decode path", sections "Summary" and "Why the policy"; q4_1, q5_0 and
+ *     q4_k are named there too (section "Why the policy") as formats that
+ *     decode correctly but lack fast kernels.
  *   - Host reference path for quantized linears used to rule out kernel bugs:
  *     same page, section "Why the policy".
  * Everything the pages leave open (codebook values, rounding, tie-breaks,
@@ -44,6 +44,7 @@
 #define OR_Q8_0 4
 #define OR_Q4_1 5
 #define OR_Q5_0 6
+#define OR_Q4_K 7
 
 /* ------------------------------------------------------------------------ */
 /* Scalar codecs                                                              */
@@ -523,6 +524,88 @@ void or_q5_0_dequantize(int64_t n, int64_t k, const uint8_t* codes, const uint16
 }
 
 /* ------------------------------------------------------------------------ */
+/* q4_k: super-blocks of 256 along K, each 8 sub-blocks of 32; unsigned 4-bit   */
+/* codes, per sub-block a 6-bit scale and a 6-bit minimum, per super-block an    */
+/* fp16 d and an fp16 dmin.  The page only names the format; reading (one pass,  */
+/* no search over scales):                                                       */
+/*   per sub-block j: lo = min w, hi = max w; mn = lo if lo < 0 else 0;         */
+/*     r = fl(hi - mn), canonicalised to +0 unless r > 0; s_j = fl(r / 15);     */
+/*     o_j = fl(0 - mn)   (>= +0);                                               */
+/*   d = fp16(fl(max_j s_j / 63)), dmin = fp16(fl(max_j o_j / 63));              */
+/*   sc_j = 0 if float(d) == 0 else clamp(rint(fl(s_j / d)), 0, 63);             */
+/*   m_j  = 0 if float(dmin) == 0 else clamp(rint(fl(o_j / dmin)), 0, 63);       */
+/*   S_j = fl(d * sc_j), O_j = fl(dmin * m_j)  (both exact: 11 + 6 bits);         */
+/*   q = 0 if S_j == 0 else clamp(rint(fl(fl(w + O_j) / S_j)), 0, 15);           */
+/*   w^ = fl(S_j * q - O_j): S_j * q is exact (21 bits), so one rounding.         */
+/* sub: [n][k/32][2] bytes (sc, m); dd: [n][k/256][2] fp16 (d, dmin).            */
+/* ------------------------------------------------------------------------ */
+void or_q4_k_quantize(int64_t n, int64_t k, const float* w, uint8_t* codes, uint8_t* sub, uint16_t* dd) {
+    const int64_t nsb = k / 256;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t b = 0; b < nsb; b++) {
+            const float* src = w + r * k + b * 256;
+            float s[8], o[8], smax = 0.0f, omax = 0.0f;
+            for (int j = 0; j < 8; j++) {
+                float lo = src[32 * j], hi = src[32 * j];
+                for (int i = 1; i < 32; i++) {
+                    if (src[32 * j + i] < lo) lo = src[32 * j + i];
+                    if (src[32 * j + i] > hi) hi = src[32 * j + i];
+                }
+                const float mn = lo < 0.0f ? lo : 0.0f;
+                float range = hi - mn;
+                if (!(range > 0.0f)) range = 0.0f;
+                s[j] = range / 15.0f;
+                o[j] = 0.0f - mn;
+                if (s[j] > smax) smax = s[j];
+                if (o[j] > omax) omax = o[j];
+            }
+            const uint16_t db = or_fp16_encode(smax / 63.0f), mb = or_fp16_encode(omax / 63.0f);
+            dd[(r * nsb + b) * 2] = db;
+            dd[(r * nsb + b) * 2 + 1] = mb;
+            const float d = or_fp16_decode(db), dmin = or_fp16_decode(mb);
+            for (int j = 0; j < 8; j++) {
+                float sc = 0.0f, m = 0.0f;
+                if (d != 0.0f) {
+                    sc = rintf(s[j] / d);
+                    if (sc > 63.0f) sc = 63.0f;
+                    if (sc < 0.0f) sc = 0.0f;
+                }
+                if (dmin != 0.0f) {
+                    m = rintf(o[j] / dmin);
+                    if (m > 63.0f) m = 63.0f;
+                    if (m < 0.0f) m = 0.0f;
+                }
+                sub[((r * (k / 32)) + b * 8 + j) * 2] = (uint8_t)sc;
+                sub[((r * (k / 32)) + b * 8 + j) * 2 + 1] = (uint8_t)m;
+                const float S = d * sc, O = dmin * m;
+                for (int i = 0; i < 32; i++) {
+                    uint8_t q = 0;
+                    if (S != 0.0f) {
+                        const float t = src[32 * j + i] + O;
+                        float v = rintf(t / S);
+                        if (v > 15.0f) v = 15.0f;
+                        if (v < 0.0f) v = 0.0f;
+                        q = (uint8_t)v;
+                    }
+                    codes[r * k + b * 256 + 32 * j + i] = q;
+                }
+            }
+        }
+}
+
+void or_q4_k_dequantize(int64_t n, int64_t k, const uint8_t* codes, const uint8_t* sub, const uint16_t* dd, float* out) {
+    const int64_t nsb = k / 256;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t i = 0; i < k; i++) {
+            const int64_t b = i / 256, j = i / 32;
+            const float d = or_fp16_decode(dd[(r * nsb + b) * 2]), dmin = or_fp16_decode(dd[(r * nsb + b) * 2 + 1]);
+            const float S = d * (float)sub[(r * (k / 32) + j) * 2], O = dmin * (float)sub[(r * (k / 32) + j) * 2 + 1];
+            const float sq = S * (float)codes[r * k + i];      /* exact */
+            out[r * k + i] = sq - O;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Packed layout (the library's storage format; the pages give none).          */
 /*                                                                              */
 /* 4-bit codes (NF4, NVFP4, q4_0, q4_1): the matrix is cut into tiles of 16     */
@@ -541,6 +624,9 @@ void or_q5_0_dequantize(int64_t n, int64_t k, const uint8_t* codes, const uint16
 /*   NVFP4   E4M3 byte,   8 per row  (128 per tile), then at align16(nb): g    */
 /*   q4_0    fp16,        4 per row  (64 per tile)                              */
 /*   q4_1    fp16 pair (d, m), 4 per row  (64 pairs = 256 bytes per tile)       */
+/*   q4_k    per tile and row 8 bytes: the 4 sub-blocks' 6-bit scales, then    */
+/*           their 6-bit minimums (one byte each); then at align16(2 nb) the     */
+/*           fp16 pairs (d, dmin) of the super-blocks, row-major [n][k/256].     */
 /*   q5_0    fp16 d, 4 per row (like q4_0); then at align16(2 nb) a second     */
 /*           plane of one 32-bit word per block, same order (16 bytes per row   */
 /*           and tile): bit i holds bit 4 of the code of element i of the block; */
@@ -579,6 +665,11 @@ int or_packed_size(int fmt, int dq, int64_t n, int64_t k, int64_t* codes_bytes, 
         if (k % 128) return -1;
         *codes_bytes = n * k / 2;
         *scales_bytes = align16(2 * (n * k / 32)) + 4 * (n * k / 32);
+        return 0;
+    case OR_Q4_K:
+        if (k % 256) return -1;
+        *codes_bytes = n * k / 2;
+        *scales_bytes = align16(2 * (n * k / 32)) + 4 * (n * k / 256);
         return 0;
     case OR_Q8_0:
         if (k % 64) return -1;
@@ -736,6 +827,26 @@ int or_quantize_packed(int fmt, int dq, int64_t n, int64_t k, const float* w,
         or_pack_scales(n, k, 32, 128, 4, hb, scales_packed + align16(2 * nb));
         or_q5_0_dequantize(n, k, codes_logical, s, w_hat);
         free(s); free(hb); free(lo);
+        return 0;
+    }
+    if (fmt == OR_Q4_K) {
+        const int64_t nb = n * k / 32;
+        uint8_t* sub = (uint8_t*)malloc((size_t)(2 * nb));
+        uint16_t* dd = (uint16_t*)malloc((size_t)(4 * (n * k / 256)));
+        or_q4_k_quantize(n, k, w, codes_logical, sub, dd);
+        or_pack_codes4(n, k, codes_logical, codes_packed);
+        /* per tile and row: sc of its 4 sub-blocks, then m of them */
+        for (int64_t r = 0; r < n; r++)
+            for (int64_t b = 0; b < k / 32; b++) {
+                const int64_t kt = b / 4, bin = b % 4;
+                const int64_t tile = (r / 16) * (k / 128) + kt;
+                uint8_t* rec = scales_packed + tile * 128 + (r % 16) * 8;
+                rec[bin] = sub[(r * (k / 32) + b) * 2];
+                rec[4 + bin] = sub[(r * (k / 32) + b) * 2 + 1];
+            }
+        memcpy(scales_packed + align16(2 * nb), dd, (size_t)(4 * (n * k / 256)));
+        or_q4_k_dequantize(n, k, codes_logical, sub, dd, w_hat);
+        free(sub); free(dd);
         return 0;
     }
     if (fmt == OR_Q8_0) {

@@ -5,7 +5,7 @@ CPU-baseline leg of the bench, never by the library.  It shares no code with
 the HIP path; it only receives the same seeded inputs.
 
 Format numbers match the library's public enum values so a test can pass one
-number to both sides: NF4 = 1, NVFP4 = 2, Q4_0 = 3, Q8_0 = 4, Q4_1 = 5, Q5_0 = 6.
+number to both sides: NF4 = 1, NVFP4 = 2, Q4_0 = 3, Q8_0 = 4, Q4_1 = 5, Q5_0 = 6, Q4_K = 7.
 """
 from __future__ import annotations
 
@@ -15,7 +15,7 @@ import subprocess
 
 import numpy as np
 
-NF4, NVFP4, Q4_0, Q8_0, Q4_1, Q5_0 = 1, 2, 3, 4, 5, 6
+NF4, NVFP4, Q4_0, Q8_0, Q4_1, Q5_0, Q4_K = 1, 2, 3, 4, 5, 6, 7
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -73,6 +73,8 @@ def lib():
         L.or_q4_1_dequantize.argtypes = [i64, i64, P, P, P]
         L.or_q5_0_quantize.argtypes = [i64, i64, P, P, P]
         L.or_q5_0_dequantize.argtypes = [i64, i64, P, P, P]
+        L.or_q4_k_quantize.argtypes = [i64, i64, P, P, P, P]
+        L.or_q4_k_dequantize.argtypes = [i64, i64, P, P, P, P]
         L.or_packed_size.restype = ctypes.c_int
         L.or_packed_size.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64,
                                      ctypes.POINTER(i64), ctypes.POINTER(i64)]
@@ -252,6 +254,28 @@ def q5_0_dequantize(codes, scales):
     n, k = codes.shape
     out = np.zeros((n, k), np.float32)
     lib().or_q5_0_dequantize(n, k, _p(codes), _p(scales), _p(out))
+    return out
+
+
+def q4_k_quantize(w: np.ndarray):
+    """Logical codes [n,k], sub-block (sc, m) bytes [n*k/32, 2], super-block fp16
+    (d, dmin) [n*k/256, 2]."""
+    w = np.ascontiguousarray(w, np.float32)
+    n, k = w.shape
+    codes = np.zeros((n, k), np.uint8)
+    sub = np.zeros((n * k // 32, 2), np.uint8)
+    dd = np.zeros((n * k // 256, 2), np.uint16)
+    lib().or_q4_k_quantize(n, k, _p(w), _p(codes), _p(sub), _p(dd))
+    return codes, sub, dd
+
+
+def q4_k_dequantize(codes, sub, dd):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    sub = np.ascontiguousarray(sub, np.uint8)
+    dd = np.ascontiguousarray(dd, np.uint16)
+    n, k = codes.shape
+    out = np.zeros((n, k), np.float32)
+    lib().or_q4_k_dequantize(n, k, _p(codes), _p(sub), _p(dd), _p(out))
     return out
 
 

@@ -438,3 +438,85 @@ def test_q5_0_extreme_exact_zero_block_and_packing(orc):
             want = sum(1 << i for i in range(32) if codes[r, 32 * b + i] & 16)
             assert word == want
     assert np.array_equal(res["scales"][:128].view(np.uint16), sc.reshape(16, 4).reshape(-1))
+
+
+# ----------------------------------------------------------------- q4_k ----
+# q4_k is only named ("Run quantized Whisper on the fused Metal decode path",
+# "Why the policy"); the reading: per 32-value sub-block a scale (range / 15) and
+# an offset (-min when the minimum is negative), both as 6-bit multiples of the
+# 256-value super-block's fp16 d = max scale / 63 and dmin = max offset / 63;
+# codes = nearest of the 16 levels q*S - O.
+
+def _q4_k_scales(blk256):
+    """The scale derivation written out with numpy float32 operations."""
+    s, o = [], []
+    for j in range(8):
+        sb = blk256[32 * j:32 * j + 32]
+        lo, hi = sb.min(), sb.max()
+        mn = lo if lo < 0 else np.float32(0)
+        r = _f32(hi - mn)
+        r = r if r > 0 else np.float32(0)
+        s.append(_f32(r / _f32(15)))
+        o.append(_f32(np.float32(0) - mn))
+    d = _f16(_f32(max(s) / _f32(63)))
+    dm = _f16(_f32(max(o) / _f32(63)))
+    df, dmf = np.float32(d[0]), np.float32(dm[0])
+    sc = [0 if df == 0 else int(min(max(np.rint(_f32(sj / df)), 0), 63)) for sj in s]
+    m = [0 if dmf == 0 else int(min(max(np.rint(_f32(oj / dmf)), 0), 63)) for oj in o]
+    return d.view(np.uint16)[0], dm.view(np.uint16)[0], sc, m
+
+
+def test_q4_k_scales_and_brute_force(orc):
+    rng = np.random.default_rng(18)
+    w = (rng.standard_normal((16, 512)) * 0.02).astype(np.float32)
+    w[2, 256:288] = np.abs(w[2, 256:288])                 # a non-negative sub-block: offset 0
+    w[5, 300] = 0.2                                       # an outlier sets d for its super-block
+    codes, sub, dd = orc.q4_k_quantize(w)
+    assert codes.max() <= 15 and sub.max() <= 63
+    for r in range(16):
+        for b in range(2):
+            d, dm, sc, m = _q4_k_scales(w[r, 256 * b:256 * b + 256])
+            assert dd[r * 2 + b, 0] == d and dd[r * 2 + b, 1] == dm
+            df = Fraction(float(np.uint16(d).view(np.float16)))
+            dmf = Fraction(float(np.uint16(dm).view(np.float16)))
+            for j in range(8):
+                assert sub[(r * 16 + b * 8 + j), 0] == sc[j] and sub[(r * 16 + b * 8 + j), 1] == m[j]
+                S, O = df * sc[j], dmf * m[j]
+                if S == 0:
+                    assert np.all(codes[r, 256 * b + 32 * j:256 * b + 32 * j + 32] == 0)
+                    continue
+                for i in range(32):
+                    t = Fraction(float(w[r, 256 * b + 32 * j + i]))
+                    dist = [abs(t - (q * S - O)) for q in range(16)]
+                    qb = dist.index(min(dist))
+                    qi = int(codes[r, 256 * b + 32 * j + i])
+                    if qi != qb:                                # only a near-tie may differ
+                        assert abs(dist[qi] - dist[qb]) <= S / 2 ** 16
+    assert np.all(sub[(2 * 16 + 8), 1] == 0)                     # the non-negative sub-block has no offset
+
+
+def test_q4_k_zero_superblock_dequant_and_packing(orc):
+    rng = np.random.default_rng(19)
+    w = (rng.standard_normal((16, 256)) * 0.02).astype(np.float32)
+    w[3] = 0.0
+    w[4] = -0.0
+    codes, sub, dd = orc.q4_k_quantize(w)
+    w_hat = orc.q4_k_dequantize(codes, sub, dd)
+    for r in (3, 4):
+        assert dd[r, 0] == 0 and dd[r, 1] == 0 and np.all(codes[r] == 0) and np.all(w_hat[r] == 0)
+    # w^ = S q - O with S = d sc and O = dmin m, one rounding (S q is exact)
+    r, j = 0, 5
+    S = np.float32(np.uint16(dd[r, 0]).view(np.float16)) * np.float32(sub[r * 8 + j, 0])
+    O = np.float32(np.uint16(dd[r, 1]).view(np.float16)) * np.float32(sub[r * 8 + j, 1])
+    want = (S * codes[r, 32 * j:32 * j + 32].astype(np.float32)).astype(np.float32) - O
+    assert np.array_equal(w_hat[r, 32 * j:32 * j + 32], want.astype(np.float32))
+    # packed: per tile and row 8 bytes (the 4 sub-blocks' sc, then m), then the (d, dmin) plane
+    res = orc.quantize(7, w)
+    assert orc.packed_size(7, False, 16, 256) == (2048, 256 + 64)
+    sp = res["scales"]
+    for r, b in [(0, 0), (1, 5), (15, 7)]:
+        off = 128 * (b // 4) + 8 * r + (b % 4)
+        assert sp[off] == sub[r * 8 + b, 0] and sp[off + 4] == sub[r * 8 + b, 1]
+    ddp = sp[256:].view(np.uint16).reshape(16, 2)
+    assert np.array_equal(ddp, dd)
+    assert np.array_equal(res["w_hat"], w_hat)
