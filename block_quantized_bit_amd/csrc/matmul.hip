@@ -15,13 +15,14 @@
 // address is built with one v_perm_b32.  The GEMV table holds bf16 values (fed
 // straight to the MFMA), the GEMM table fp32 values (scaled exactly, then rounded
 // once to bf16).  NVFP4 codes and scales are decoded with the gfx950 fp4 / fp8
-// conversion instructions; q8_0 bytes, q4_1 and q5_0 codes (and q4_0 nibbles in
-// the GEMM) are converted to floats in registers.
+// conversion instructions; q8_0 bytes, q4_1, q5_0 and q4_k codes (and q4_0
+// nibbles in the GEMM) are converted to floats in registers.
 //
 // GEMV (m <= 16, decode): B = raw code values (NF4 level, q4_0 q-8, q8_0 q),
 //   the per-block scale is applied to the MFMA partial sum of each block; for
 //   NVFP4 (16-value blocks, two per 32-K slice) B = e2m1*scale (exact in bf16);
-//   for q4_1 (scale and minimum) and q5_0 (fifth bits) B = bf16(w^) as in the GEMM.
+//   for q4_1 (scale and minimum), q5_0 (fifth bits) and q4_k (two-level scales)
+//   B = bf16(w^) as in the GEMM.
 //   K is split over the waves of a workgroup and reduced in LDS.
 // GEMM (m >= 17, encoder): each wave dequantizes 64 columns x 128 K of W per
 //   step to bf16(w^) -- w^ computed exactly as the format defines it, then one
@@ -217,6 +218,30 @@ __device__ __forceinline__ u32x4 q5_0_operand(uint32_t word, uint32_t high8, uin
     return B;
 }
 
+// q4_k B operand for one 32-wide K slice (one sub-block): the slice's code word, the
+// sub-block's S = d * sc and O = dmin * m (both exact).  w^ = fl(c * S - O) with c * S exact
+// (4 + 17 significant bits), one fma; then one RNE to bf16.
+__device__ __forceinline__ u32x4 q4_k_operand(uint32_t word, float S, float O) {
+    uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+    // opaque to the optimizer, so that each byte converts with one v_cvt_f32_ubyteN
+    asm("" : "+v"(lo), "+v"(hi));
+    u32x4 B;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const float c0 = (float)((lo >> (8 * q)) & 255u);
+        const float c1 = (float)((hi >> (8 * q)) & 255u);
+        B[q] = pack_bf16_rne(__builtin_fmaf(c0, S, -O), __builtin_fmaf(c1, S, -O));
+    }
+    return B;
+}
+
+// S and O of sub-block j of a q4_k tile row: rec_sc / rec_m hold the 4 sub-blocks' 6-bit
+// scales / offsets (byte j), dm the super-block's fp16 d | dmin << 16.
+__device__ __forceinline__ void q4_k_sub(uint32_t rec_sc, uint32_t rec_m, uint32_t dm, int j, float& S, float& O) {
+    S = f16_value((uint16_t)(dm & 0xFFFFu)) * (float)((rec_sc >> (8 * j)) & 255u);
+    O = f16_value((uint16_t)(dm >> 16)) * (float)((rec_m >> (8 * j)) & 255u);
+}
+
 __device__ inline f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
@@ -340,7 +365,7 @@ constexpr int kGemvWaves = 8;   // waves per workgroup, all on one band, splitti
 // double quant with k <= 16384, plus two per band for the row's group scales -- a wait for at
 // most this many per tile outstanding can only wait longer than needed).
 template <int FMT, bool DQ>
-__device__ constexpr int gemv_w_loads() { return FMT == kQ5_0 ? 3 : 2; }
+__device__ constexpr int gemv_w_loads() { return (FMT == kQ5_0 || FMT == kQ4_K) ? 3 : 2; }
 
 // Double-quant group scales of one row, when the row holds <= 256 blocks (k <= 16384) and so
 // spans at most two 256-block groups: blocks j < jt of the row are in the first.
@@ -388,6 +413,13 @@ __device__ inline void gemv_load(GemvTile<FMT>& t, const KArgs& a, int64_t band,
         const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 64 + r * 4) * 2);
         t.sc[0] = v.x;
         t.sc[1] = v.y;
+    } else if constexpr (FMT == kQ4_K) {
+        // the row's sub-block record (4 scale bytes, 4 offset bytes) and its super-block's
+        // (d, dmin); a 128-K tile is half a 256-K super-block
+        const uint2 v = *reinterpret_cast<const uint2*>(a.scales + tile * 128 + r * 8);
+        t.sc[0] = v.x;
+        t.sc[1] = v.y;
+        t.sc[2] = *reinterpret_cast<const uint32_t*>(a.scales + a.L.kd_off + ((band * 16 + r) * (a.k >> 8) + (kt >> 1)) * 4);
     } else if constexpr (FMT == kQ5_0) {
         // the row's four fp16 scales (8 bytes), then its four fifth-bit words (16 bytes)
         const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 64 + r * 4) * 2);
@@ -489,6 +521,14 @@ __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const ui
         // B = bf16(w^), block j of the row for K slice j
 #pragma unroll
         for (int j = 0; j < 4; j++) acc = mfma(t.A[j], q4_1_operand(uw[j], t.sc[j]), acc);
+    } else if constexpr (FMT == kQ4_K) {
+        // B = bf16(w^), sub-block j of the row for K slice j
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            float S, O;
+            q4_k_sub(t.sc[0], t.sc[1], t.sc[2], j, S, O);
+            acc = mfma(t.A[j], q4_k_operand(uw[j], S, O), acc);
+        }
     } else if constexpr (FMT == kQ5_0) {
         // B = bf16(w^), block j of the row for K slice j; this lane's k are bits 8h .. 8h+7
         // of the block's fifth-bit word
@@ -905,15 +945,17 @@ struct GemmSrc {
     uint32_t wbytes, sbytes;    // one band's codes / scales
     const uint8_t* dt;          // double-quant group scales
     uint32_t dtbytes;
-    const uint8_t* hb[4];       // q5_0: fifth-bit words of the band's first tile
-    uint32_t hbbytes;
+    const uint8_t* hb[4];       // q5_0: fifth-bit words of the band's first tile; q4_k: the
+    uint32_t hbbytes;           //   (d, dmin) pairs of the band's rows, row-major
     const uint8_t* x;           // X row m0
     uint32_t xbytes;
 };
 
 // Vector memory instructions gemm_load_w issues per band (the pipeline waits count them).
 template <int FMT, bool DQ>
-__device__ constexpr int gemm_w_loads() { return FMT == kQ8_0 ? 4 : (FMT == kNF4 && DQ) ? 4 : FMT == kQ5_0 ? 3 : 2; }
+__device__ constexpr int gemm_w_loads() {
+    return FMT == kQ8_0 ? 4 : (FMT == kNF4 && DQ) ? 4 : (FMT == kQ5_0 || FMT == kQ4_K) ? 3 : 2;
+}
 
 // Codes and scales of K step st (one 16 x 128 tile, two 16 x 64 tiles for Q8_0) of band nf.
 // rowblk: index of the first 64-value block of the lane's row (double quant only).
@@ -934,6 +976,13 @@ __device__ __forceinline__ void gemm_load_w(GemmW<FMT>& w, const GemmSrc& S, int
             const int64_t b0 = rowblk + 2 * st;
             w.sc[1] = __builtin_amdgcn_raw_buffer_load_b32(buf_res_uni(S.dt, S.dtbytes), (uint32_t)(b0 >> 8) * 4u, 0, 0);
             w.sc[2] = __builtin_amdgcn_raw_buffer_load_b32(buf_res_uni(S.dt, S.dtbytes), (uint32_t)((b0 + 1) >> 8) * 4u, 0, 0);
+        } else if constexpr (FMT == kQ4_K) {   // record (4 sc, 4 m bytes), then the super-block's (d, dmin)
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(buf_res_uni(S.scale[nf], S.sbytes), r * 8, uni(st * 128), 0);
+            w.sc[0] = v[0];
+            w.sc[1] = v[1];
+            // row r's pairs are S.hbbytes / 16 apart; step st is in super-block st / 2
+            w.sc[2] = __builtin_amdgcn_raw_buffer_load_b32(buf_res_uni(S.hb[nf], S.hbbytes), r * (S.hbbytes >> 4),
+                                                           uni((st >> 1) * 4), 0);
         } else if constexpr (FMT == kQ5_0) {   // 4 x fp16 d (8 bytes), 4 fifth-bit words (16 bytes)
             const auto v = __builtin_amdgcn_raw_buffer_load_b64(buf_res_uni(S.scale[nf], S.sbytes), r * 8, uni(st * 128), 0);
             w.sc[0] = v[0];
@@ -996,6 +1045,11 @@ __device__ __forceinline__ u32x4 gemm_dequant(const GemmW<FMT>& w, int j, const 
     } else if constexpr (FMT == kQ4_1) {
         const uint32_t word = j == 0 ? w.code[0].x : j == 1 ? w.code[0].y : j == 2 ? w.code[0].z : w.code[0].w;
         B = q4_1_operand(word, w.sc[j]);
+    } else if constexpr (FMT == kQ4_K) {
+        const uint32_t word = j == 0 ? w.code[0].x : j == 1 ? w.code[0].y : j == 2 ? w.code[0].z : w.code[0].w;
+        float Sj, Oj;
+        q4_k_sub(w.sc[0], w.sc[1], w.sc[2], j, Sj, Oj);
+        B = q4_k_operand(word, Sj, Oj);
     } else if constexpr (FMT == kQ5_0) {
         // hs = 8 h for q5_0: this lane's k are bits 8h .. 8h+7 of block j's fifth-bit word
         const uint32_t word = j == 0 ? w.code[0].x : j == 1 ? w.code[0].y : j == 2 ? w.code[0].z : w.code[0].w;
@@ -1194,8 +1248,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
         S.scale[nf] = a.scales + band * KT * SB;
         rowblk[nf] = (band * 16 + r) * (K / 64);
         if constexpr (FMT == kQ5_0) S.hb[nf] = a.scales + a.L.hb_off + band * KT * 256;
+        if constexpr (FMT == kQ4_K) S.hb[nf] = a.scales + a.L.kd_off + band * 16 * (K / 256) * 4;
     }
-    S.hbbytes = (uint32_t)(KT * 256);
+    S.hbbytes = FMT == kQ4_K ? (uint32_t)(16 * (K / 256) * 4) : (uint32_t)(KT * 256);
     S.wbytes = (uint32_t)(KT * kTileBytes);
     S.sbytes = (uint32_t)(KT * SB);
     S.dt = a.scales + a.L.d_off;
@@ -1598,9 +1653,9 @@ static void gemv_launch_ni(const KArgs& a, hipStream_t st) {
     const int64_t nbands = a.n / 16;
     // Many more bands than resident waves, K <= 10 tiles, X fits in LDS: the
     // streaming kernel (two workgroups of 4 waves per CU, each wave >= 4 bands).
-    // (q4_1 and q5_0 have no streaming variant: their 16 more bytes of scales per row and
-    // tile take the general kernel)
-    if constexpr (FMT != kQ4_1 && FMT != kQ5_0) {
+    // (q4_1, q5_0 and q4_k have no streaming variant: their wider scale records take the
+    // general kernel)
+    if constexpr (FMT != kQ4_1 && FMT != kQ5_0 && FMT != kQ4_K) {
         if (nbands >= kStreamMinBands && (int64_t)a.m * a.k <= kStreamXMax && KT <= 10) {
             const unsigned grid = 2 * kNumCU;
             if (KT <= 4) hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 4>), dim3(grid), dim3(256), 0, st, a);
@@ -1635,6 +1690,7 @@ hipError_t launch_gemv(const MatmulProblem& p, hipStream_t st) {
     case kQ4_0: gemv_dispatch_ni<kQ4_0, false>(a, st); break;
     case kQ4_1: gemv_dispatch_ni<kQ4_1, false>(a, st); break;
     case kQ5_0: gemv_dispatch_ni<kQ5_0, false>(a, st); break;
+    case kQ4_K: gemv_dispatch_ni<kQ4_K, false>(a, st); break;
     case kQ8_0: gemv_dispatch_ni<kQ8_0, false>(a, st); break;
     default: return hipErrorInvalidValue;
     }
@@ -1667,6 +1723,7 @@ hipError_t launch_gemm(const MatmulProblem& p, hipStream_t st) {
     case kQ4_0: gemm_launch<kQ4_0, false>(s.nb, grid, a, st); break;
     case kQ4_1: gemm_launch<kQ4_1, false>(s.nb, grid, a, st); break;
     case kQ5_0: gemm_launch<kQ5_0, false>(s.nb, grid, a, st); break;
+    case kQ4_K: gemm_launch<kQ4_K, false>(s.nb, grid, a, st); break;
     case kQ8_0: gemm_launch<kQ8_0, false>(s.nb, grid, a, st); break;
     default: return hipErrorInvalidValue;
     }

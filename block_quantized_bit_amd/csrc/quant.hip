@@ -7,7 +7,7 @@
 // for the Whisper engine", "What's here"); NVFP4 ("asr: add a 4-bit nvfp4 option
 // for cards short of VRAM", intro; "mbehr90/whisper-large-v3-turbo-nvfp4", "What
 // is quantized"); q4_0 / q8_0 ("Run quantized Whisper on the fused Metal decode
-// path", "Summary"); q4_1 and q5_0 (same page, "Why the policy").  One matrix at a time, as the checkpoint streams in ("asr:
+// path", "Summary"); q4_1, q5_0 and q4_k (same page, "Why the policy").  One matrix at a time, as the checkpoint streams in ("asr:
 // add a 4-bit nf4 option for the Whisper engine", "Why NF4 and not the NVFP4
 // snapshot Parakeet ships"); the only temporary storage is the codes buffer.
 #include "wq_device.h"
@@ -39,6 +39,12 @@ ScaleLayout scale_layout(int fmt, bool dq, int64_t n, int64_t k) {
     case kQ5_0:
         L.hb_off = align16(2 * L.nb);    // fp16 d per block, then one 32-bit fifth-bit word per block
         L.bytes = L.hb_off + 4 * L.nb;
+        break;
+    case kQ4_K:
+        // (sc, m) bytes per 32-value sub-block (per tile and row: 4 sc, then 4 m), then the
+        // fp16 (d, dmin) pair of each 256-value super-block, row-major
+        L.kd_off = align16(2 * L.nb);
+        L.bytes = L.kd_off + 4 * (n * k / 256);
         break;
     default:
         L.bytes = 2 * L.nb;
@@ -207,6 +213,55 @@ __global__ __launch_bounds__(256) void k_quant_chunks(const float* __restrict__ 
         *reinterpret_cast<uint32_t*>(codes + word_off4(n, k0, K)) = word;
         if ((k0 & 31) == 0)
             reinterpret_cast<uint32_t*>(scales)[scale_slot<kQ4_1>(n, k0 >> 5, K)] = (uint32_t)d | ((uint32_t)m << 16);
+    } else if constexpr (FMT == kQ4_K) {
+        // sub-block (4 threads) minimum and maximum, then the super-block (32 threads)
+        // maxima of the sub-block scales and offsets; every lane takes part in the shuffles
+        float lo = v[0], hi = v[0];
+#pragma unroll
+        for (int i = 1; i < 8; i++) {
+            lo = fminf(lo, v[i]);
+            hi = fmaxf(hi, v[i]);
+        }
+#pragma unroll
+        for (int s = 1; s <= 2; s <<= 1) {
+            lo = fminf(lo, __shfl_xor(lo, s, 4));
+            hi = fmaxf(hi, __shfl_xor(hi, s, 4));
+        }
+        // the sign of a zero minimum or maximum cannot matter: mn is +0 unless negative and
+        // the range is canonicalised to +0
+        const float mn = lo < 0.0f ? lo : 0.0f;
+        float range = hi - mn;
+        if (!(range > 0.0f)) range = 0.0f;
+        const float s_sub = range / 15.0f;
+        const float o_sub = 0.0f - mn;
+        float smax = s_sub, omax = o_sub;        // all >= +0, so fmaxf is exact and order-free
+#pragma unroll
+        for (int s = 4; s <= 16; s <<= 1) {
+            smax = fmaxf(smax, __shfl_xor(smax, s, 32));
+            omax = fmaxf(omax, __shfl_xor(omax, s, 32));
+        }
+        if (!valid) return;
+        const uint16_t db = f16_sat_bits(smax / 63.0f), mb = f16_sat_bits(omax / 63.0f);
+        const float d = f16_value(db), dmin = f16_value(mb);
+        const float sc = d != 0.0f ? fminf(fmaxf(rintf(s_sub / d), 0.0f), 63.0f) : 0.0f;
+        const float m = dmin != 0.0f ? fminf(fmaxf(rintf(o_sub / dmin), 0.0f), 63.0f) : 0.0f;
+        const float S = __fmul_rn(d, sc), O = __fmul_rn(dmin, m);     // exact
+        uint32_t word = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            uint32_t q = 0;
+            if (S != 0.0f) q = (uint32_t)fminf(fmaxf(rintf((v[i] + O) / S), 0.0f), 15.0f);
+            word |= q << (4 * i);
+        }
+        *reinterpret_cast<uint32_t*>(codes + word_off4(n, k0, K)) = word;
+        if ((k0 & 31) == 0) {
+            uint8_t* rec = scales + ((n >> 4) * (K >> 7) + (k0 >> 7)) * 128 + (n & 15) * 8;
+            const int bin = (int)((k0 >> 5) & 3);
+            rec[bin] = (uint8_t)sc;
+            rec[4 + bin] = (uint8_t)m;
+        }
+        if ((k0 & 255) == 0)
+            *reinterpret_cast<uint32_t*>(scales + L.kd_off + (n * (K >> 8) + (k0 >> 8)) * 4) = (uint32_t)db | ((uint32_t)mb << 16);
     } else if constexpr (FMT == kQ5_0) {
         // signed element of largest magnitude; first index (ascending k) on ties
         float best_a = -1.0f, best_v = 0.0f;
@@ -396,6 +451,15 @@ __global__ __launch_bounds__(256) void k_dequant_chunks(const uint8_t* __restric
             // q * delta is exact (4 + 11 significant bits): one rounding, in the add
 #pragma unroll
             for (int i = 0; i < 8; i++) o[i] = __fadd_rn(__fmul_rn((float)((word >> (4 * i)) & 15u), delta), mu);
+        } else if constexpr (FMT == kQ4_K) {
+            const uint8_t* rec = scales + ((n >> 4) * (K >> 7) + (k0 >> 7)) * 128 + (n & 15) * 8;
+            const int bin = (int)((k0 >> 5) & 3);
+            const uint32_t dm = *reinterpret_cast<const uint32_t*>(scales + L.kd_off + (n * (K >> 8) + (k0 >> 8)) * 4);
+            const float S = __fmul_rn(f16_value((uint16_t)(dm & 0xFFFFu)), (float)rec[bin]);
+            const float O = __fmul_rn(f16_value((uint16_t)(dm >> 16)), (float)rec[4 + bin]);
+            // S * q is exact (21 significant bits): one rounding, in the subtraction
+#pragma unroll
+            for (int i = 0; i < 8; i++) o[i] = __fsub_rn(__fmul_rn(S, (float)((word >> (4 * i)) & 15u)), O);
         } else if constexpr (FMT == kQ5_0) {
             const int64_t slot = scale_slot<kQ5_0>(n, k0 >> 5, K);
             const float delta = f16_value(reinterpret_cast<const uint16_t*>(scales)[slot]);
@@ -452,6 +516,9 @@ hipError_t launch_quantize(int fmt, bool dq, int64_t n, int64_t k, const float* 
     case kQ5_0:
         hipLaunchKernelGGL((k_quant_chunks<kQ5_0, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
         break;
+    case kQ4_K:
+        hipLaunchKernelGGL((k_quant_chunks<kQ4_K, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
+        break;
     case kQ8_0:
         hipLaunchKernelGGL((k_quant_chunks<kQ8_0, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
         break;
@@ -481,6 +548,9 @@ hipError_t launch_dequantize(int fmt, bool dq, int64_t n, int64_t k, const uint8
         break;
     case kQ5_0:
         hipLaunchKernelGGL((k_dequant_chunks<kQ5_0, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);
+        break;
+    case kQ4_K:
+        hipLaunchKernelGGL((k_dequant_chunks<kQ4_K, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);
         break;
     case kQ8_0:
         hipLaunchKernelGGL((k_dequant_chunks<kQ8_0, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);

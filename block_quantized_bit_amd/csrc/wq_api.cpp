@@ -33,6 +33,7 @@ wq_status check_desc(const wq_desc* d, Desc* out) {
     case WQ_Q4_1:
     case WQ_Q5_0:
     case WQ_Q8_0: bk = 32; break;
+    case WQ_Q4_K: bk = 256; break;
     default: return WQ_ERR_INVALID_ARG;
     }
     if (d->block != 0 && d->block != bk) return WQ_ERR_UNSUPPORTED;
@@ -41,7 +42,7 @@ wq_status check_desc(const wq_desc* d, Desc* out) {
     } else if (d->dq_group != 0) {
         return WQ_ERR_UNSUPPORTED;
     }
-    const int64_t tk = d->format == WQ_Q8_0 ? 64 : 128;
+    const int64_t tk = d->format == WQ_Q8_0 ? 64 : d->format == WQ_Q4_K ? 256 : 128;
     if (d->n <= 0 || d->k <= 0 || d->n % 16 != 0 || d->k % tk != 0) return WQ_ERR_SHAPE;
     if (d->n > (int64_t(1) << 40) / d->k) return WQ_ERR_SHAPE;   // keep every byte offset far from overflow
     out->fmt = d->format;
