@@ -22,7 +22,8 @@
  *   - q8_0 / q4_0 block formats: "Run quantized Whisper on the fused Metal
  *     decode path", sections "Summary" and "Why the policy"; q4_1, q5_0 and
  *     q4_k are named there too (section "Why the policy") as formats that
- *     decode correctly but lack fast kernels.
+ *     decode correctly but lack fast kernels, and q6_k as one the encoder may
+ *     use (same section).
  *   - Host reference path for quantized linears used to rule out kernel bugs:
  *     same page, section "Why the policy".
  * Everything the pages leave open (codebook values, rounding, tie-breaks,
@@ -45,6 +46,7 @@
 #define OR_Q4_1 5
 #define OR_Q5_0 6
 #define OR_Q4_K 7
+#define OR_Q6_K 8
 
 /* ------------------------------------------------------------------------ */
 /* Scalar codecs                                                              */
@@ -606,6 +608,69 @@ void or_q4_k_dequantize(int64_t n, int64_t k, const uint8_t* codes, const uint8_
 }
 
 /* ------------------------------------------------------------------------ */
+/* q6_k: super-blocks of 256 along K, each 16 sub-blocks of 16; signed 6-bit     */
+/* codes, an int8 scale per sub-block, an fp16 d per super-block.  The page only */
+/* names the format; reading (one pass, as q4_0 per sub-block):                  */
+/*   per sub-block j: m = signed element of largest magnitude (first in          */
+/*     ascending k on a tie); s_j = fl(m / -32);                                  */
+/*   d = fp16(fl(max_j |s_j| / 127));                                            */
+/*   sc_j = 0 if float(d) == 0 else clamp(rint(fl(s_j / d)), -127, 127);         */
+/*   S_j = fl(d * sc_j)  (exact: 11 + 7 bits);                                    */
+/*   q = 32 if S_j == 0 else clamp(rint(fl(w / S_j)), -32, 31) + 32  (0..63);    */
+/*   w^ = fl(S_j * (q - 32)), exact (at most 24 significant bits).                */
+/* sc: [n][k/16] int8; d: [n][k/256] fp16.                                        */
+/* ------------------------------------------------------------------------ */
+void or_q6_k_quantize(int64_t n, int64_t k, const float* w, uint8_t* codes, int8_t* sc, uint16_t* dsb) {
+    const int64_t nsb = k / 256;
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t b = 0; b < nsb; b++) {
+            const float* src = w + r * k + b * 256;
+            float s[16], amax = 0.0f;
+            for (int j = 0; j < 16; j++) {
+                float a = 0.0f, m = src[16 * j];
+                for (int i = 0; i < 16; i++) {
+                    const float t = fabsf(src[16 * j + i]);
+                    if (t > a) { a = t; m = src[16 * j + i]; }
+                }
+                s[j] = m / -32.0f;
+                if (fabsf(s[j]) > amax) amax = fabsf(s[j]);
+            }
+            const uint16_t db = or_fp16_encode(amax / 127.0f);
+            dsb[r * nsb + b] = db;
+            const float d = or_fp16_decode(db);
+            for (int j = 0; j < 16; j++) {
+                float c = 0.0f;
+                if (d != 0.0f) {
+                    c = rintf(s[j] / d);
+                    if (c > 127.0f) c = 127.0f;
+                    if (c < -127.0f) c = -127.0f;
+                }
+                sc[r * (k / 16) + b * 16 + j] = (int8_t)c;
+                const float S = d * c;
+                for (int i = 0; i < 16; i++) {
+                    uint8_t q = 32;
+                    if (S != 0.0f) {
+                        float v = rintf(src[16 * j + i] / S);
+                        if (v > 31.0f) v = 31.0f;
+                        if (v < -32.0f) v = -32.0f;
+                        q = (uint8_t)((int)v + 32);
+                    }
+                    codes[r * k + b * 256 + 16 * j + i] = q;
+                }
+            }
+        }
+}
+
+void or_q6_k_dequantize(int64_t n, int64_t k, const uint8_t* codes, const int8_t* sc, const uint16_t* dsb, float* out) {
+    for (int64_t r = 0; r < n; r++)
+        for (int64_t i = 0; i < k; i++) {
+            const float d = or_fp16_decode(dsb[r * (k / 256) + i / 256]);
+            const float S = d * (float)sc[r * (k / 16) + i / 16];
+            out[r * k + i] = S * (float)((int)codes[r * k + i] - 32);
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Packed layout (the library's storage format; the pages give none).          */
 /*                                                                              */
 /* 4-bit codes (NF4, NVFP4, q4_0, q4_1): the matrix is cut into tiles of 16     */
@@ -627,6 +692,12 @@ void or_q4_k_dequantize(int64_t n, int64_t k, const uint8_t* codes, const uint8_
 /*   q4_k    per tile and row 8 bytes: the 4 sub-blocks' 6-bit scales, then    */
 /*           their 6-bit minimums (one byte each); then at align16(2 nb) the     */
 /*           fp16 pairs (d, dmin) of the super-blocks, row-major [n][k/256].     */
+/*   q6_k    codes: the low 4 bits in the 4-bit tiles, then (after n k / 2      */
+/*           bytes) a plane of 512 bytes per tile: slot s gets 8 bytes, two per   */
+/*           K slice j (2j: bit 4 of element i of the slot's 8 k at bit i; 2j+1:  */
+/*           bit 5).  scales: per tile and row 8 int8 sub-block scales (one per   */
+/*           16 k), then at align16(n k / 16) the fp16 d per super-block,        */
+/*           row-major [n][k/256].                                               */
 /*   q5_0    fp16 d, 4 per row (like q4_0); then at align16(2 nb) a second     */
 /*           plane of one 32-bit word per block, same order (16 bytes per row   */
 /*           and tile): bit i holds bit 4 of the code of element i of the block; */
@@ -670,6 +741,11 @@ int or_packed_size(int fmt, int dq, int64_t n, int64_t k, int64_t* codes_bytes, 
         if (k % 256) return -1;
         *codes_bytes = n * k / 2;
         *scales_bytes = align16(2 * (n * k / 32)) + 4 * (n * k / 256);
+        return 0;
+    case OR_Q6_K:
+        if (k % 256) return -1;
+        *codes_bytes = n * k / 2 + n * k / 4;
+        *scales_bytes = align16(n * k / 16) + 2 * (n * k / 256);
         return 0;
     case OR_Q8_0:
         if (k % 64) return -1;
@@ -847,6 +923,33 @@ int or_quantize_packed(int fmt, int dq, int64_t n, int64_t k, const float* w,
         memcpy(scales_packed + align16(2 * nb), dd, (size_t)(4 * (n * k / 256)));
         or_q4_k_dequantize(n, k, codes_logical, sub, dd, w_hat);
         free(sub); free(dd);
+        return 0;
+    }
+    if (fmt == OR_Q6_K) {
+        int8_t* sc = (int8_t*)malloc((size_t)(n * k / 16));
+        uint16_t* dsb = (uint16_t*)malloc((size_t)(2 * (n * k / 256)));
+        uint8_t* lo = (uint8_t*)malloc((size_t)(n * k));
+        or_q6_k_quantize(n, k, w, codes_logical, sc, dsb);
+        for (int64_t i = 0; i < n * k; i++) lo[i] = codes_logical[i] & 15;
+        or_pack_codes4(n, k, lo, codes_packed);
+        uint8_t* high = codes_packed + n * k / 2;
+        memset(high, 0, (size_t)(n * k / 4));
+        for (int64_t r = 0; r < n; r++)
+            for (int64_t kk = 0; kk < k; kk++) {
+                const int64_t kin = kk % 128, j = kin / 32, h = (kin % 32) / 8, i = kin % 8;
+                const int64_t tile = (r / 16) * (k / 128) + kk / 128, slot = h * 16 + r % 16;
+                const uint8_t q = codes_logical[r * k + kk];
+                high[tile * 512 + slot * 8 + 2 * j] |= (uint8_t)(((q >> 4) & 1) << i);
+                high[tile * 512 + slot * 8 + 2 * j + 1] |= (uint8_t)(((q >> 5) & 1) << i);
+            }
+        for (int64_t r = 0; r < n; r++)
+            for (int64_t t = 0; t < k / 16; t++) {
+                const int64_t tile = (r / 16) * (k / 128) + t / 8;
+                scales_packed[tile * 128 + (r % 16) * 8 + t % 8] = (uint8_t)sc[r * (k / 16) + t];
+            }
+        memcpy(scales_packed + align16(n * k / 16), dsb, (size_t)(2 * (n * k / 256)));
+        or_q6_k_dequantize(n, k, codes_logical, sc, dsb, w_hat);
+        free(sc); free(dsb); free(lo);
         return 0;
     }
     if (fmt == OR_Q8_0) {

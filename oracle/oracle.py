@@ -5,7 +5,8 @@ CPU-baseline leg of the bench, never by the library.  It shares no code with
 the HIP path; it only receives the same seeded inputs.
 
 Format numbers match the library's public enum values so a test can pass one
-number to both sides: NF4 = 1, NVFP4 = 2, Q4_0 = 3, Q8_0 = 4, Q4_1 = 5, Q5_0 = 6, Q4_K = 7.
+number to both sides: NF4 = 1, NVFP4 = 2, Q4_0 = 3, Q8_0 = 4, Q4_1 = 5, Q5_0 = 6, Q4_K = 7,
+Q6_K = 8.
 """
 from __future__ import annotations
 
@@ -15,7 +16,7 @@ import subprocess
 
 import numpy as np
 
-NF4, NVFP4, Q4_0, Q8_0, Q4_1, Q5_0, Q4_K = 1, 2, 3, 4, 5, 6, 7
+NF4, NVFP4, Q4_0, Q8_0, Q4_1, Q5_0, Q4_K, Q6_K = 1, 2, 3, 4, 5, 6, 7, 8
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
@@ -75,6 +76,8 @@ def lib():
         L.or_q5_0_dequantize.argtypes = [i64, i64, P, P, P]
         L.or_q4_k_quantize.argtypes = [i64, i64, P, P, P, P]
         L.or_q4_k_dequantize.argtypes = [i64, i64, P, P, P, P]
+        L.or_q6_k_quantize.argtypes = [i64, i64, P, P, P, P]
+        L.or_q6_k_dequantize.argtypes = [i64, i64, P, P, P, P]
         L.or_packed_size.restype = ctypes.c_int
         L.or_packed_size.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64,
                                      ctypes.POINTER(i64), ctypes.POINTER(i64)]
@@ -276,6 +279,27 @@ def q4_k_dequantize(codes, sub, dd):
     n, k = codes.shape
     out = np.zeros((n, k), np.float32)
     lib().or_q4_k_dequantize(n, k, _p(codes), _p(sub), _p(dd), _p(out))
+    return out
+
+
+def q6_k_quantize(w: np.ndarray):
+    """Logical 6-bit codes [n,k] (0..63), int8 sub-block scales [n*k/16], fp16 d [n*k/256]."""
+    w = np.ascontiguousarray(w, np.float32)
+    n, k = w.shape
+    codes = np.zeros((n, k), np.uint8)
+    sc = np.zeros(n * k // 16, np.int8)
+    d = np.zeros(n * k // 256, np.uint16)
+    lib().or_q6_k_quantize(n, k, _p(w), _p(codes), _p(sc), _p(d))
+    return codes, sc, d
+
+
+def q6_k_dequantize(codes, sc, d):
+    codes = np.ascontiguousarray(codes, np.uint8)
+    sc = np.ascontiguousarray(sc, np.int8)
+    d = np.ascontiguousarray(d, np.uint16)
+    n, k = codes.shape
+    out = np.zeros((n, k), np.float32)
+    lib().or_q6_k_dequantize(n, k, _p(codes), _p(sc), _p(d), _p(out))
     return out
 
 

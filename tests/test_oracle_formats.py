@@ -520,3 +520,71 @@ def test_q4_k_zero_superblock_dequant_and_packing(orc):
     ddp = sp[256:].view(np.uint16).reshape(16, 2)
     assert np.array_equal(ddp, dd)
     assert np.array_equal(res["w_hat"], w_hat)
+
+
+# ----------------------------------------------------------------- q6_k ----
+# q6_k is only named ("Run quantized Whisper on the fused Metal decode path",
+# "Why the policy"); the reading: per 16-value sub-block s = (signed extreme) / -32,
+# d = fp16(max |s| / 127), int8 sc = rint(s / d), S = d*sc, 6-bit codes
+# q = clamp(rint(w / S), -32, 31) + 32, w^ = S*(q - 32).
+
+def test_q6_k_scales_and_brute_force(orc):
+    rng = np.random.default_rng(20)
+    w = (rng.standard_normal((16, 512)) * 0.02).astype(np.float32)
+    w[4, 100] = -0.3                                      # an outlier sets d for its super-block
+    codes, sc, d = orc.q6_k_quantize(w)
+    assert codes.max() <= 63
+    for r in range(16):
+        for b in range(2):
+            blk = w[r, 256 * b:256 * b + 256]
+            s = []
+            for j in range(16):
+                sb = blk[16 * j:16 * j + 16]
+                jj = int(np.argmax(np.abs(sb)))            # first index on ties
+                s.append(_f32(sb[jj] / _f32(-32)))
+            want_d = _f16(_f32(max(abs(x) for x in s) / _f32(127))).view(np.uint16)[0]
+            assert d[r * 2 + b] == want_d
+            df = np.float32(np.uint16(want_d).view(np.float16))
+            for j in range(16):
+                want_sc = 0 if df == 0 else int(min(max(np.rint(_f32(s[j] / df)), -127), 127))
+                assert sc[r * 32 + b * 16 + j] == want_sc
+                S = Fraction(float(df)) * want_sc
+                seg = slice(256 * b + 16 * j, 256 * b + 16 * j + 16)
+                if S == 0:
+                    assert np.all(codes[r, seg] == 32)
+                    continue
+                for i in range(16):
+                    t = Fraction(float(w[r, 256 * b + 16 * j + i]))
+                    dist = [abs(t - (q - 32) * S) for q in range(64)]
+                    qb = dist.index(min(dist))
+                    qi = int(codes[r, 256 * b + 16 * j + i])
+                    if qi != qb:                                      # only a near-tie may differ
+                        assert abs(dist[qi] - dist[qb]) <= abs(S) / 2 ** 16
+
+
+def test_q6_k_zero_superblock_exact_levels_and_packing(orc):
+    w = np.zeros((16, 256), np.float32)
+    rng = np.random.default_rng(21)
+    w[1] = (rng.standard_normal(256) * 0.02).astype(np.float32)
+    codes, sc, d = orc.q6_k_quantize(w)
+    w_hat = orc.q6_k_dequantize(codes, sc, d)
+    assert d[0] == 0 and np.all(codes[0] == 32) and np.all(w_hat[0] == 0)       # all-zero super-block
+    S = np.float32(np.uint16(d[1]).view(np.float16)) * np.float32(sc[16 + 3])
+    want = (S * (codes[1, 48:64].astype(np.float32) - np.float32(32))).astype(np.float32)
+    assert np.array_equal(w_hat[1, 48:64], want)
+    res = orc.quantize(8, w)
+    assert orc.packed_size(8, False, 16, 256) == (2048 + 1024, 256 + 32)
+    cp = res["codes"]
+    assert np.array_equal(orc.unpack_codes4(cp[:2048], 16, 256), codes & 15)
+    high = cp[2048:]
+    for r, kk in [(1, 0), (1, 77), (1, 255), (5, 130)]:
+        kin, tile = kk % 128, kk // 128
+        j, h, i = kin // 32, (kin % 32) // 8, kin % 8
+        base = tile * 512 + (h * 16 + r) * 8 + 2 * j
+        assert (high[base] >> i) & 1 == (codes[r, kk] >> 4) & 1
+        assert (high[base + 1] >> i) & 1 == (codes[r, kk] >> 5) & 1
+    sp = res["scales"]
+    for r, t in [(1, 0), (1, 9), (15, 15)]:
+        assert sp[(t // 8) * 128 + r * 8 + t % 8].astype(np.int8) == sc[r * 16 + t]
+    assert np.array_equal(sp[256:].view(np.uint16), d)
+    assert np.array_equal(res["w_hat"], w_hat)
