@@ -285,7 +285,7 @@ def main():
         ys = [torch.empty((1, e["n"]), dtype=torch.int16, device=dev) for e in base]
         for name, fmt, dq in (("nf4", wq.WQ_NF4, False), ("nvfp4", wq.WQ_NVFP4, False),
                               ("q4_0", wq.WQ_Q4_0, False), ("q4_1", wq.WQ_Q4_1, False), ("q5_0", wq.WQ_Q5_0, False),
-                              ("q4_k", wq.WQ_Q4_K, False), ("q8_0", wq.WQ_Q8_0, False)):
+                              ("q4_k", wq.WQ_Q4_K, False), ("q6_k", wq.WQ_Q6_K, False), ("q8_0", wq.WQ_Q8_0, False)):
             mats = [quantize_dev(fmt, torch.from_numpy(e["w"]).to(dev), dq) for e in base]
             nbytes = sum(c.numel() + s_.numel() for _, c, s_ in mats)
             pn = max(1, -(-(1 << 30) // nbytes))
@@ -483,7 +483,7 @@ def main():
         layer_shapes = [(ENC_D, ENC_D)] * 4 + [(ENC_FFN, ENC_D), (ENC_D, ENC_FFN)]
         mb4 = 4 * ENC_M
         for fmt_name, fmt in (("q8_0", wq.WQ_Q8_0), ("q4_0", wq.WQ_Q4_0), ("q4_1", wq.WQ_Q4_1), ("q5_0", wq.WQ_Q5_0),
-                              ("q4_k", wq.WQ_Q4_K)):
+                              ("q4_k", wq.WQ_Q4_K), ("q6_k", wq.WQ_Q6_K)):
             lay = []
             for i, (n, k) in enumerate(layer_shapes):
                 w, b, x = linear_case(4000 + i, n, k, mb4)

@@ -15,14 +15,14 @@
 // address is built with one v_perm_b32.  The GEMV table holds bf16 values (fed
 // straight to the MFMA), the GEMM table fp32 values (scaled exactly, then rounded
 // once to bf16).  NVFP4 codes and scales are decoded with the gfx950 fp4 / fp8
-// conversion instructions; q8_0 bytes, q4_1, q5_0 and q4_k codes (and q4_0
-// nibbles in the GEMM) are converted to floats in registers.
+// conversion instructions; q8_0 bytes, q4_1, q5_0, q4_k and q6_k codes (and
+// q4_0 nibbles in the GEMM) are converted to floats in registers.
 //
 // GEMV (m <= 16, decode): B = raw code values (NF4 level, q4_0 q-8, q8_0 q),
 //   the per-block scale is applied to the MFMA partial sum of each block; for
 //   NVFP4 (16-value blocks, two per 32-K slice) B = e2m1*scale (exact in bf16);
-//   for q4_1 (scale and minimum), q5_0 (fifth bits) and q4_k (two-level scales)
-//   B = bf16(w^) as in the GEMM.
+//   for q4_1 (scale and minimum), q5_0 (fifth bits), q4_k and q6_k (two-level
+//   scales) B = bf16(w^) as in the GEMM.
 //   K is split over the waves of a workgroup and reduced in LDS.
 // GEMM (m >= 17, encoder): each wave dequantizes 64 columns x 128 K of W per
 //   step to bf16(w^) -- w^ computed exactly as the format defines it, then one
@@ -242,6 +242,38 @@ __device__ __forceinline__ void q4_k_sub(uint32_t rec_sc, uint32_t rec_m, uint32
     O = f16_value((uint16_t)(dm >> 16)) * (float)((rec_m >> (8 * j)) & 255u);
 }
 
+// q6_k B operand for one 32-wide K slice: the slice's code word (low 4 bits, nibble i =
+// k 8h + i), bits 4 (b4) and 5 (b5) of those 8 codes (bit i), and the lane's sub-block S
+// = d * sc (exact).  Each bit set moves to its byte as in q5_0_operand (bit 2p of a parity
+// -> bit 8p + 4, one 24-bit multiply), bit 5 one place higher.  c = q (0..63);
+// w^ = (c - 32) * S = fl(c * S - 32 S) exactly (at most 24 significant bits), one fma.
+__device__ __forceinline__ u32x4 q6_k_operand(uint32_t word, uint32_t b4, uint32_t b5, float S) {
+    uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+    lo |= __umul24(b4 & 0x55u, 0x410410u) & 0x10101010u;
+    lo |= (__umul24(b5 & 0x55u, 0x410410u) & 0x10101010u) << 1;
+    hi |= __umul24((b4 >> 1) & 0x55u, 0x410410u) & 0x10101010u;
+    hi |= (__umul24((b5 >> 1) & 0x55u, 0x410410u) & 0x10101010u) << 1;
+    // opaque to the optimizer, so that each byte converts with one v_cvt_f32_ubyteN
+    asm("" : "+v"(lo), "+v"(hi));
+    const float s32 = -32.0f * S;
+    u32x4 B;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const float c0 = (float)((lo >> (8 * q)) & 255u);
+        const float c1 = (float)((hi >> (8 * q)) & 255u);
+        B[q] = pack_bf16_rne(__builtin_fmaf(c0, S, s32), __builtin_fmaf(c1, S, s32));
+    }
+    return B;
+}
+
+// q6_k: S of sub-block t (0..7) of a tile row from its int8 scale record (r0: sub-blocks
+// 0..3, r1: 4..7) and the super-block's fp16 d; bits 4 / 5 of K slice j from the lane's
+// 8-byte high record (h0: slices 0, 1; h1: slices 2, 3).
+__device__ __forceinline__ float q6_k_scale(uint32_t r0, uint32_t r1, uint32_t dbits, int t) {
+    const uint32_t w = t < 4 ? r0 : r1;
+    return f16_value((uint16_t)(dbits & 0xFFFFu)) * (float)(int8_t)(uint8_t)(w >> (8 * (t & 3)));
+}
+
 __device__ inline f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
@@ -365,7 +397,7 @@ constexpr int kGemvWaves = 8;   // waves per workgroup, all on one band, splitti
 // double quant with k <= 16384, plus two per band for the row's group scales -- a wait for at
 // most this many per tile outstanding can only wait longer than needed).
 template <int FMT, bool DQ>
-__device__ constexpr int gemv_w_loads() { return (FMT == kQ5_0 || FMT == kQ4_K) ? 3 : 2; }
+__device__ constexpr int gemv_w_loads() { return FMT == kQ6_K ? 4 : (FMT == kQ5_0 || FMT == kQ4_K) ? 3 : 2; }
 
 // Double-quant group scales of one row, when the row holds <= 256 blocks (k <= 16384) and so
 // spans at most two 256-block groups: blocks j < jt of the row are in the first.
@@ -413,6 +445,16 @@ __device__ inline void gemv_load(GemvTile<FMT>& t, const KArgs& a, int64_t band,
         const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 64 + r * 4) * 2);
         t.sc[0] = v.x;
         t.sc[1] = v.y;
+    } else if constexpr (FMT == kQ6_K) {
+        // the row's 8 sub-block scales, this lane's 8 bytes of bits 4-5 (after the n k / 2
+        // code bytes) and the super-block's d
+        const uint2 v = *reinterpret_cast<const uint2*>(a.scales + tile * 128 + r * 8);
+        t.sc[0] = v.x;
+        t.sc[1] = v.y;
+        const uint2 hb = *reinterpret_cast<const uint2*>(a.codes + a.n * a.k / 2 + tile * 512 + lane * 8);
+        t.sc[2] = hb.x;
+        t.sc[3] = hb.y;
+        t.sc[4] = *reinterpret_cast<const uint16_t*>(a.scales + a.L.kd_off + ((band * 16 + r) * (a.k >> 8) + (kt >> 1)) * 2);
     } else if constexpr (FMT == kQ4_K) {
         // the row's sub-block record (4 scale bytes, 4 offset bytes) and its super-block's
         // (d, dmin); a 128-K tile is half a 256-K super-block
@@ -521,6 +563,14 @@ __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const ui
         // B = bf16(w^), block j of the row for K slice j
 #pragma unroll
         for (int j = 0; j < 4; j++) acc = mfma(t.A[j], q4_1_operand(uw[j], t.sc[j]), acc);
+    } else if constexpr (FMT == kQ6_K) {
+        // B = bf16(w^); K slice j spans sub-blocks 2j (h = 0, 1) and 2j + 1 (h = 2, 3)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float S = q6_k_scale(t.sc[0], t.sc[1], t.sc[4], 2 * j + (h >> 1));
+            const uint32_t hw = t.sc[2 + (j >> 1)] >> (16 * (j & 1));
+            acc = mfma(t.A[j], q6_k_operand(uw[j], hw & 255u, (hw >> 8) & 255u, S), acc);
+        }
     } else if constexpr (FMT == kQ4_K) {
         // B = bf16(w^), sub-block j of the row for K slice j
 #pragma unroll
@@ -946,7 +996,10 @@ struct GemmSrc {
     const uint8_t* dt;          // double-quant group scales
     uint32_t dtbytes;
     const uint8_t* hb[4];       // q5_0: fifth-bit words of the band's first tile; q4_k: the
-    uint32_t hbbytes;           //   (d, dmin) pairs of the band's rows, row-major
+    uint32_t hbbytes;           //   (d, dmin) pairs of the band's rows, row-major; q6_k: the
+                                //   band's bit 4-5 records
+    const uint8_t* kd[4];       // q6_k: the fp16 d of the band's rows, row-major
+    uint32_t kdbytes;
     const uint8_t* x;           // X row m0
     uint32_t xbytes;
 };
@@ -954,7 +1007,7 @@ struct GemmSrc {
 // Vector memory instructions gemm_load_w issues per band (the pipeline waits count them).
 template <int FMT, bool DQ>
 __device__ constexpr int gemm_w_loads() {
-    return FMT == kQ8_0 ? 4 : (FMT == kNF4 && DQ) ? 4 : (FMT == kQ5_0 || FMT == kQ4_K) ? 3 : 2;
+    return (FMT == kQ8_0 || FMT == kQ6_K) ? 4 : (FMT == kNF4 && DQ) ? 4 : (FMT == kQ5_0 || FMT == kQ4_K) ? 3 : 2;
 }
 
 // Codes and scales of K step st (one 16 x 128 tile, two 16 x 64 tiles for Q8_0) of band nf.
@@ -976,6 +1029,16 @@ __device__ __forceinline__ void gemm_load_w(GemmW<FMT>& w, const GemmSrc& S, int
             const int64_t b0 = rowblk + 2 * st;
             w.sc[1] = __builtin_amdgcn_raw_buffer_load_b32(buf_res_uni(S.dt, S.dtbytes), (uint32_t)(b0 >> 8) * 4u, 0, 0);
             w.sc[2] = __builtin_amdgcn_raw_buffer_load_b32(buf_res_uni(S.dt, S.dtbytes), (uint32_t)((b0 + 1) >> 8) * 4u, 0, 0);
+        } else if constexpr (FMT == kQ6_K) {   // 8 int8 scales, the lane's bit 4-5 record, then d
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(buf_res_uni(S.scale[nf], S.sbytes), r * 8, uni(st * 128), 0);
+            w.sc[0] = v[0];
+            w.sc[1] = v[1];
+            const auto hv = __builtin_amdgcn_raw_buffer_load_b64(buf_res_uni(S.hb[nf], S.hbbytes), lane * 8, uni(st * 512), 0);
+            w.sc[2] = hv[0];
+            w.sc[3] = hv[1];
+            // row r's d values are S.kdbytes / 16 apart; step st is in super-block st / 2
+            w.sc[4] = __builtin_amdgcn_raw_buffer_load_b16(buf_res_uni(S.kd[nf], S.kdbytes), r * (S.kdbytes >> 4),
+                                                           uni((st >> 1) * 2), 0);
         } else if constexpr (FMT == kQ4_K) {   // record (4 sc, 4 m bytes), then the super-block's (d, dmin)
             const auto v = __builtin_amdgcn_raw_buffer_load_b64(buf_res_uni(S.scale[nf], S.sbytes), r * 8, uni(st * 128), 0);
             w.sc[0] = v[0];
@@ -1045,6 +1108,12 @@ __device__ __forceinline__ u32x4 gemm_dequant(const GemmW<FMT>& w, int j, const 
     } else if constexpr (FMT == kQ4_1) {
         const uint32_t word = j == 0 ? w.code[0].x : j == 1 ? w.code[0].y : j == 2 ? w.code[0].z : w.code[0].w;
         B = q4_1_operand(word, w.sc[j]);
+    } else if constexpr (FMT == kQ6_K) {
+        // hs = 8 (h >> 1): K slice j spans sub-blocks 2j (h = 0, 1) and 2j + 1 (h = 2, 3)
+        const uint32_t word = j == 0 ? w.code[0].x : j == 1 ? w.code[0].y : j == 2 ? w.code[0].z : w.code[0].w;
+        const float Sj = q6_k_scale(w.sc[0], w.sc[1], w.sc[4], 2 * j + (int)(hs >> 3));
+        const uint32_t hw = w.sc[2 + (j >> 1)] >> (16 * (j & 1));
+        B = q6_k_operand(word, hw & 255u, (hw >> 8) & 255u, Sj);
     } else if constexpr (FMT == kQ4_K) {
         const uint32_t word = j == 0 ? w.code[0].x : j == 1 ? w.code[0].y : j == 2 ? w.code[0].z : w.code[0].w;
         float Sj, Oj;
@@ -1249,8 +1318,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
         rowblk[nf] = (band * 16 + r) * (K / 64);
         if constexpr (FMT == kQ5_0) S.hb[nf] = a.scales + a.L.hb_off + band * KT * 256;
         if constexpr (FMT == kQ4_K) S.hb[nf] = a.scales + a.L.kd_off + band * 16 * (K / 256) * 4;
+        if constexpr (FMT == kQ6_K) {
+            S.hb[nf] = a.codes + N * K / 2 + band * KT * 512;
+            S.kd[nf] = a.scales + a.L.kd_off + band * 16 * (K / 256) * 2;
+        }
     }
-    S.hbbytes = FMT == kQ4_K ? (uint32_t)(16 * (K / 256) * 4) : (uint32_t)(KT * 256);
+    S.hbbytes = FMT == kQ4_K ? (uint32_t)(16 * (K / 256) * 4) : FMT == kQ6_K ? (uint32_t)(KT * 512) : (uint32_t)(KT * 256);
+    S.kdbytes = (uint32_t)(16 * (K / 256) * 2);
     S.wbytes = (uint32_t)(KT * kTileBytes);
     S.sbytes = (uint32_t)(KT * SB);
     S.dt = a.scales + a.L.d_off;
@@ -1653,9 +1727,9 @@ static void gemv_launch_ni(const KArgs& a, hipStream_t st) {
     const int64_t nbands = a.n / 16;
     // Many more bands than resident waves, K <= 10 tiles, X fits in LDS: the
     // streaming kernel (two workgroups of 4 waves per CU, each wave >= 4 bands).
-    // (q4_1, q5_0 and q4_k have no streaming variant: their wider scale records take the
-    // general kernel)
-    if constexpr (FMT != kQ4_1 && FMT != kQ5_0 && FMT != kQ4_K) {
+    // (q4_1, q5_0, q4_k and q6_k have no streaming variant: their wider scale records take
+    // the general kernel)
+    if constexpr (FMT != kQ4_1 && FMT != kQ5_0 && FMT != kQ4_K && FMT != kQ6_K) {
         if (nbands >= kStreamMinBands && (int64_t)a.m * a.k <= kStreamXMax && KT <= 10) {
             const unsigned grid = 2 * kNumCU;
             if (KT <= 4) hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 4>), dim3(grid), dim3(256), 0, st, a);
@@ -1691,6 +1765,7 @@ hipError_t launch_gemv(const MatmulProblem& p, hipStream_t st) {
     case kQ4_1: gemv_dispatch_ni<kQ4_1, false>(a, st); break;
     case kQ5_0: gemv_dispatch_ni<kQ5_0, false>(a, st); break;
     case kQ4_K: gemv_dispatch_ni<kQ4_K, false>(a, st); break;
+    case kQ6_K: gemv_dispatch_ni<kQ6_K, false>(a, st); break;
     case kQ8_0: gemv_dispatch_ni<kQ8_0, false>(a, st); break;
     default: return hipErrorInvalidValue;
     }
@@ -1724,6 +1799,7 @@ hipError_t launch_gemm(const MatmulProblem& p, hipStream_t st) {
     case kQ4_1: gemm_launch<kQ4_1, false>(s.nb, grid, a, st); break;
     case kQ5_0: gemm_launch<kQ5_0, false>(s.nb, grid, a, st); break;
     case kQ4_K: gemm_launch<kQ4_K, false>(s.nb, grid, a, st); break;
+    case kQ6_K: gemm_launch<kQ6_K, false>(s.nb, grid, a, st); break;
     case kQ8_0: gemm_launch<kQ8_0, false>(s.nb, grid, a, st); break;
     default: return hipErrorInvalidValue;
     }

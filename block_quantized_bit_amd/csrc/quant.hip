@@ -7,7 +7,7 @@
 // for the Whisper engine", "What's here"); NVFP4 ("asr: add a 4-bit nvfp4 option
 // for cards short of VRAM", intro; "mbehr90/whisper-large-v3-turbo-nvfp4", "What
 // is quantized"); q4_0 / q8_0 ("Run quantized Whisper on the fused Metal decode
-// path", "Summary"); q4_1, q5_0 and q4_k (same page, "Why the policy").  One matrix at a time, as the checkpoint streams in ("asr:
+// path", "Summary"); q4_1, q5_0, q4_k and q6_k (same page, "Why the policy").  One matrix at a time, as the checkpoint streams in ("asr:
 // add a 4-bit nf4 option for the Whisper engine", "Why NF4 and not the NVFP4
 // snapshot Parakeet ships"); the only temporary storage is the codes buffer.
 #include "wq_device.h"
@@ -45,6 +45,12 @@ ScaleLayout scale_layout(int fmt, bool dq, int64_t n, int64_t k) {
         // fp16 (d, dmin) pair of each 256-value super-block, row-major
         L.kd_off = align16(2 * L.nb);
         L.bytes = L.kd_off + 4 * (n * k / 256);
+        break;
+    case kQ6_K:
+        // an int8 scale per 16-value sub-block (per tile and row: 8), then the fp16 d of each
+        // 256-value super-block, row-major
+        L.kd_off = align16(L.nb);
+        L.bytes = L.kd_off + 2 * (n * k / 256);
         break;
     default:
         L.bytes = 2 * L.nb;
@@ -262,6 +268,52 @@ __global__ __launch_bounds__(256) void k_quant_chunks(const float* __restrict__ 
         }
         if ((k0 & 255) == 0)
             *reinterpret_cast<uint32_t*>(scales + L.kd_off + (n * (K >> 8) + (k0 >> 8)) * 4) = (uint32_t)db | ((uint32_t)mb << 16);
+    } else if constexpr (FMT == kQ6_K) {
+        // sub-block (2 threads): signed element of largest magnitude, first index on ties
+        float best_a = -1.0f, best_v = 0.0f;
+        int best_k = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const float t = fabsf(v[i]);
+            if (t > best_a) { best_a = t; best_v = v[i]; best_k = (int)(k0 & 15) + i; }
+        }
+        {
+            const float pa = __shfl_xor(best_a, 1, 2);
+            const float pv = __shfl_xor(best_v, 1, 2);
+            const int pk = __shfl_xor(best_k, 1, 2);
+            if (pa > best_a || (pa == best_a && pk < best_k)) { best_a = pa; best_v = pv; best_k = pk; }
+        }
+        const float s_sub = best_v / -32.0f;
+        float amax = fabsf(s_sub);               // >= +0: fmaxf is exact and order-free
+#pragma unroll
+        for (int s = 2; s <= 16; s <<= 1) amax = fmaxf(amax, __shfl_xor(amax, s, 32));
+        if (!valid) return;
+        const uint16_t db = f16_sat_bits(amax / 127.0f);
+        const float d = f16_value(db);
+        const float sc = d != 0.0f ? fminf(fmaxf(rintf(s_sub / d), -127.0f), 127.0f) : 0.0f;
+        const float S = __fmul_rn(d, sc);        // exact
+        uint32_t word = 0, b4 = 0, b5 = 0;
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            uint32_t q = 32;
+            if (S != 0.0f) q = (uint32_t)((int)fminf(fmaxf(rintf(v[i] / S), -32.0f), 31.0f) + 32);
+            word |= (q & 15u) << (4 * i);
+            b4 |= ((q >> 4) & 1u) << i;
+            b5 |= ((q >> 5) & 1u) << i;
+        }
+        *reinterpret_cast<uint32_t*>(codes + word_off4(n, k0, K)) = word;
+        // bits 4 and 5: plane after the n*k/2 code bytes, 8 bytes per tile slot, two per K slice
+        {
+            const int64_t tile = (n >> 4) * (K >> 7) + (k0 >> 7);
+            const int kin = (int)(k0 & 127), j = kin >> 5, h = (kin & 31) >> 3;
+            uint8_t* hp = codes + N * K / 2 + tile * 512 + (h * 16 + (n & 15)) * 8 + 2 * j;
+            hp[0] = (uint8_t)b4;
+            hp[1] = (uint8_t)b5;
+        }
+        if ((k0 & 15) == 0)
+            scales[((n >> 4) * (K >> 7) + (k0 >> 7)) * 128 + (n & 15) * 8 + ((k0 & 127) >> 4)] = (uint8_t)(int8_t)sc;
+        if ((k0 & 255) == 0)
+            *reinterpret_cast<uint16_t*>(scales + L.kd_off + (n * (K >> 8) + (k0 >> 8)) * 2) = db;
     } else if constexpr (FMT == kQ5_0) {
         // signed element of largest magnitude; first index (ascending k) on ties
         float best_a = -1.0f, best_v = 0.0f;
@@ -451,6 +503,18 @@ __global__ __launch_bounds__(256) void k_dequant_chunks(const uint8_t* __restric
             // q * delta is exact (4 + 11 significant bits): one rounding, in the add
 #pragma unroll
             for (int i = 0; i < 8; i++) o[i] = __fadd_rn(__fmul_rn((float)((word >> (4 * i)) & 15u), delta), mu);
+        } else if constexpr (FMT == kQ6_K) {
+            const int64_t tile = (n >> 4) * (K >> 7) + (k0 >> 7);
+            const int kin = (int)(k0 & 127), j = kin >> 5, h = (kin & 31) >> 3;
+            const uint8_t* hp = codes + N * K / 2 + tile * 512 + (h * 16 + (n & 15)) * 8 + 2 * j;
+            const uint32_t b4 = hp[0], b5 = hp[1];
+            const float d = f16_value(*reinterpret_cast<const uint16_t*>(scales + L.kd_off + (n * (K >> 8) + (k0 >> 8)) * 2));
+            const float S = __fmul_rn(d, (float)(int8_t)scales[tile * 128 + (n & 15) * 8 + (kin >> 4)]);
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int q = (int)(((word >> (4 * i)) & 15u) | (((b4 >> i) & 1u) << 4) | (((b5 >> i) & 1u) << 5));
+                o[i] = __fmul_rn(S, (float)(q - 32));
+            }
         } else if constexpr (FMT == kQ4_K) {
             const uint8_t* rec = scales + ((n >> 4) * (K >> 7) + (k0 >> 7)) * 128 + (n & 15) * 8;
             const int bin = (int)((k0 >> 5) & 3);
@@ -519,6 +583,9 @@ hipError_t launch_quantize(int fmt, bool dq, int64_t n, int64_t k, const float* 
     case kQ4_K:
         hipLaunchKernelGGL((k_quant_chunks<kQ4_K, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
         break;
+    case kQ6_K:
+        hipLaunchKernelGGL((k_quant_chunks<kQ6_K, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
+        break;
     case kQ8_0:
         hipLaunchKernelGGL((k_quant_chunks<kQ8_0, 0>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
         break;
@@ -551,6 +618,9 @@ hipError_t launch_dequantize(int fmt, bool dq, int64_t n, int64_t k, const uint8
         break;
     case kQ4_K:
         hipLaunchKernelGGL((k_dequant_chunks<kQ4_K, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);
+        break;
+    case kQ6_K:
+        hipLaunchKernelGGL((k_dequant_chunks<kQ6_K, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);
         break;
     case kQ8_0:
         hipLaunchKernelGGL((k_dequant_chunks<kQ8_0, false>), dim3(grid), dim3(256), 0, s, codes, scales, n, k, out, L);

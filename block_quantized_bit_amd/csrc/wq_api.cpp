@@ -33,7 +33,8 @@ wq_status check_desc(const wq_desc* d, Desc* out) {
     case WQ_Q4_1:
     case WQ_Q5_0:
     case WQ_Q8_0: bk = 32; break;
-    case WQ_Q4_K: bk = 256; break;
+    case WQ_Q4_K:
+    case WQ_Q6_K: bk = 256; break;
     default: return WQ_ERR_INVALID_ARG;
     }
     if (d->block != 0 && d->block != bk) return WQ_ERR_UNSUPPORTED;
@@ -42,7 +43,7 @@ wq_status check_desc(const wq_desc* d, Desc* out) {
     } else if (d->dq_group != 0) {
         return WQ_ERR_UNSUPPORTED;
     }
-    const int64_t tk = d->format == WQ_Q8_0 ? 64 : d->format == WQ_Q4_K ? 256 : 128;
+    const int64_t tk = d->format == WQ_Q8_0 ? 64 : (d->format == WQ_Q4_K || d->format == WQ_Q6_K) ? 256 : 128;
     if (d->n <= 0 || d->k <= 0 || d->n % 16 != 0 || d->k % tk != 0) return WQ_ERR_SHAPE;
     if (d->n > (int64_t(1) << 40) / d->k) return WQ_ERR_SHAPE;   // keep every byte offset far from overflow
     out->fmt = d->format;
@@ -122,7 +123,7 @@ wq_status wq_packed_size(const wq_desc* d, size_t* codes_bytes, size_t* scales_b
     wq_status st = check_desc(d, &dd);
     if (st != WQ_OK) return st;
     if (!codes_bytes || !scales_bytes) return WQ_ERR_INVALID_ARG;
-    *codes_bytes = (size_t)(dd.fmt == WQ_Q8_0 ? dd.n * dd.k : dd.n * dd.k / 2);
+    *codes_bytes = (size_t)(dd.fmt == WQ_Q8_0 ? dd.n * dd.k : dd.fmt == WQ_Q6_K ? dd.n * dd.k / 4 * 3 : dd.n * dd.k / 2);
     *scales_bytes = (size_t)wq::scale_layout(dd.fmt, dd.dq, dd.n, dd.k).bytes;
     return WQ_OK;
 }

@@ -4,8 +4,8 @@
 // Formats: NF4 ("asr: add a 4-bit nf4 option for the Whisper engine", "What's
 // here"), NVFP4 ("asr: add a 4-bit nvfp4 option for cards short of VRAM", intro;
 // "mbehr90/whisper-large-v3-turbo-nvfp4", "What is quantized"), q4_0 / q8_0
-// ("Run quantized Whisper on the fused Metal decode path", "Summary"); q4_1, q5_0 and
-// q4_k (same page, "Why the policy").
+// ("Run quantized Whisper on the fused Metal decode path", "Summary"); q4_1, q5_0,
+// q4_k and q6_k (same page, "Why the policy").
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -15,7 +15,7 @@
 
 namespace wq {
 
-enum Fmt : int { kNF4 = 1, kNVFP4 = 2, kQ4_0 = 3, kQ8_0 = 4, kQ4_1 = 5, kQ5_0 = 6, kQ4_K = 7 };
+enum Fmt : int { kNF4 = 1, kNVFP4 = 2, kQ4_0 = 3, kQ8_0 = 4, kQ4_1 = 5, kQ5_0 = 6, kQ4_K = 7, kQ6_K = 8 };
 
 // ---------------------------------------------------------------------------
 // Packed layout.
@@ -31,7 +31,7 @@ constexpr int kTileBytes = 1024;
 
 __host__ __device__ constexpr int tile_k(int fmt) { return fmt == kQ8_0 ? 64 : 128; }
 __host__ __device__ constexpr int block_k(int fmt) {
-    return fmt == kNF4 ? 64 : fmt == kNVFP4 ? 16 : 32;
+    return fmt == kNF4 ? 64 : (fmt == kNVFP4 || fmt == kQ6_K) ? 16 : 32;
 }
 // scale entries per row per tile
 __host__ __device__ constexpr int blocks_per_tile_row(int fmt) { return tile_k(fmt) / block_k(fmt); }

@@ -15,7 +15,8 @@ struct ScaleLayout {
     int64_t mu_off;    // NF4+DQ: fp32 mean
     int64_t g_off;     // NVFP4: fp32 global scale
     int64_t hb_off;    // Q5_0: 32-bit fifth-bit words, one per block, tile order
-    int64_t kd_off;    // Q4_K: fp16 (d, dmin) per super-block, row-major [n][k/256]
+    int64_t kd_off;    // Q4_K: fp16 (d, dmin) per super-block; Q6_K: fp16 d per super-block;
+                       //   row-major [n][k/256]
     int64_t bytes;     // total scales bytes
 };
 

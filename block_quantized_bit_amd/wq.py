@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_HERE, "libwq.so")
 WQ_OK = 0
 STATUS_NAMES = {0: "WQ_OK", 1: "WQ_ERR_INVALID_ARG", 2: "WQ_ERR_UNSUPPORTED", 3: "WQ_ERR_SHAPE",
                 4: "WQ_ERR_ALIGNMENT", 5: "WQ_ERR_MIXED_FORMAT", 6: "WQ_ERR_WORKSPACE", 7: "WQ_ERR_HIP"}
-WQ_NF4, WQ_NVFP4, WQ_Q4_0, WQ_Q8_0, WQ_Q4_1, WQ_Q5_0, WQ_Q4_K = 1, 2, 3, 4, 5, 6, 7
+WQ_NF4, WQ_NVFP4, WQ_Q4_0, WQ_Q8_0, WQ_Q4_1, WQ_Q5_0, WQ_Q4_K, WQ_Q6_K = 1, 2, 3, 4, 5, 6, 7, 8
 WQ_BF16, WQ_F32 = 1, 2
 
 EXPORTS = ("wq_status_str", "wq_packed_size", "wq_quantize", "wq_dequantize",
@@ -26,7 +26,8 @@ EXPORTS = ("wq_status_str", "wq_packed_size", "wq_quantize", "wq_dequantize",
 # Format names accepted by the harness; aliases follow the NF4 option's names
 # ("asr: add a 4-bit nf4 option for the Whisper engine": nf4, aliases 4bit, int4).
 _FORMAT_NAMES = {"nf4": WQ_NF4, "4bit": WQ_NF4, "int4": WQ_NF4, "nvfp4": WQ_NVFP4,
-                 "q4_0": WQ_Q4_0, "q8_0": WQ_Q8_0, "q4_1": WQ_Q4_1, "q5_0": WQ_Q5_0, "q4_k": WQ_Q4_K}
+                 "q4_0": WQ_Q4_0, "q8_0": WQ_Q8_0, "q4_1": WQ_Q4_1, "q5_0": WQ_Q5_0, "q4_k": WQ_Q4_K,
+                 "q6_k": WQ_Q6_K}
 
 
 def format_from_name(name: str) -> int:

@@ -26,6 +26,9 @@
  *   Q4_K   256-value super-blocks of eight 32-value sub-blocks: unsigned 4-bit
  *          codes, per sub-block a 6-bit scale and a 6-bit offset, per super-block
  *          an fp16 d and an fp16 dmin (same passage).
+ *   Q6_K   256-value super-blocks of sixteen 16-value sub-blocks: signed 6-bit
+ *          codes, an int8 scale per sub-block, an fp16 d per super-block (same
+ *          passage, as a format the encoder may use).
  * The pages leave the exact rounding rules, the NF4 levels, the double-quant
  * scheme and the storage layout open; this library fixes them as follows.
  *   NF4     levels: QLoRA's NormalFloat quantiles (binary64 construction, rounded
@@ -47,6 +50,10 @@
  *           fp16(max s / 63), dmin = fp16(max o / 63); sc = rint(s/d), m = rint(o/dmin)
  *           in 0..63; S = d*sc, O = dmin*m; q = clamp(rint((w + O)/S), 0, 15);
  *           w^ = S*q - O.  One pass, no search over scales.
+ *   Q6_K    per sub-block s = m/-32 with m as for Q4_0; d = fp16(max |s| / 127),
+ *           sc = clamp(rint(s/d), -127, 127), S = d*sc; q = clamp(rint(w/S), -32,
+ *           31) + 32; w^ = S*(q - 32).  The low 4 bits of q are stored as a 4-bit
+ *           code, bits 4 and 5 after all the 4-bit codes (512 bytes per tile).
  *   Layout  codes in 1 KiB tiles of 16 rows x 128 K (64 K for Q8_0), ordered by
  *           16-row band then K; 16-byte slot s of a tile holds row s%16, and its
  *           32-bit word j holds k = 32j + 8(s/16) + 0..7 (Q8_0: 8-byte word j);
@@ -62,7 +69,7 @@
  *   - A HIP launch error maps to WQ_ERR_HIP.
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *   - Shapes: n > 0 and n % 16 == 0; k > 0 and k % 128 == 0 (NF4, NVFP4, Q4_0, Q4_1, Q5_0),
- *     k % 256 == 0 (Q4_K)
+ *     k % 256 == 0 (Q4_K, Q6_K)
  *     or k % 64 == 0 (Q8_0); m >= 0 (m == 0 is a no-op that returns WQ_OK).
  */
 #ifndef LIBWQ_WQ_H
@@ -86,14 +93,15 @@ typedef enum {
     WQ_ERR_HIP = 7            /* a HIP runtime call or kernel launch failed */
 } wq_status;
 
-typedef enum { WQ_NF4 = 1, WQ_NVFP4 = 2, WQ_Q4_0 = 3, WQ_Q8_0 = 4, WQ_Q4_1 = 5, WQ_Q5_0 = 6, WQ_Q4_K = 7 } wq_format;
+typedef enum { WQ_NF4 = 1, WQ_NVFP4 = 2, WQ_Q4_0 = 3, WQ_Q8_0 = 4, WQ_Q4_1 = 5, WQ_Q5_0 = 6, WQ_Q4_K = 7,
+               WQ_Q6_K = 8 } wq_format;
 
 typedef enum { WQ_BF16 = 1, WQ_F32 = 2 } wq_dtype;
 
 /* One quantized weight matrix W[n, k] (PyTorch Linear layout: [out, in]).
  *   format   : wq_format
  *   block    : 0 (= the format's block) or exactly 64 (NF4), 16 (NVFP4), 32 (Q4_0, Q8_0, Q4_1, Q5_0),
- *              256 (Q4_K, the super-block)
+ *              256 (Q4_K, Q6_K: the super-block)
  *   n, k     : matrix shape
  *   dq_group : NF4 only: 0 = plain fp32 absmax per block, 256 = double quantization
  *              (int8 absmax codes, one fp32 scale per 256 consecutive blocks in
@@ -118,13 +126,15 @@ typedef struct {
 const char* wq_status_str(wq_status s);
 
 /* Host-only.  Bytes of the two packed buffers for descriptor d:
- *   codes : n*k/2 (4-bit formats) or n*k (Q8_0)
+ *   codes : n*k/2 (4-bit formats), n*k (Q8_0) or 3*n*k/4 (Q6_K)
  *   scales: NF4 4*n*k/64; NF4+DQ align16(n*k/64) + 4*ceil(n*k/64/256) + 4;
  *           NVFP4 align16(n*k/16) + 4; Q4_0 and Q8_0 2*n*k/32; Q4_1 4*n*k/32
  *           (an fp16 pair d, m per block); Q5_0 align16(2*n*k/32) + 4*n*k/32
  *           (fp16 d per block, then one 32-bit word of fifth bits per block);
  *           Q4_K align16(2*n*k/32) + 4*n*k/256 (a 6-bit scale and offset byte per
- *           sub-block, then an fp16 pair d, dmin per super-block). */
+ *           sub-block, then an fp16 pair d, dmin per super-block); Q6_K
+ *           align16(n*k/16) + 2*n*k/256 (an int8 scale per 16-value sub-block, then
+ *           an fp16 d per super-block). */
 wq_status wq_packed_size(const wq_desc* d, size_t* codes_bytes, size_t* scales_bytes);
 
 /* Quantize fp32 W[n,k] (row-major, leading dimension k, 16-byte aligned) into the

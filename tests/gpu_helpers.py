@@ -11,7 +11,7 @@ from block_quantized_bit_amd import wq
 from block_quantized_bit_amd.inputs import bf16_bits_to_f32
 
 DEV = "cuda:0"
-NAMES = {1: "nf4", 2: "nvfp4", 3: "q4_0", 4: "q8_0", 5: "q4_1", 6: "q5_0", 7: "q4_k"}
+NAMES = {1: "nf4", 2: "nvfp4", 3: "q4_0", 4: "q8_0", 5: "q4_1", 6: "q5_0", 7: "q4_k", 8: "q6_k"}
 
 
 def require_gpu():

@@ -10,7 +10,7 @@ from block_quantized_bit_amd import wq
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "wq.h")
-NF4, NVFP4, Q4_0, Q8_0, Q4_1, Q5_0, Q4_K = 1, 2, 3, 4, 5, 6, 7
+NF4, NVFP4, Q4_0, Q8_0, Q4_1, Q5_0, Q4_K, Q6_K = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 def _declared():
@@ -41,11 +41,11 @@ SHAPES = [(16, 128), (48, 384), (272, 640), (1536, 384), (3840, 1280), (1280, 51
 
 
 @pytest.mark.parametrize("fmt,dq", [(NF4, False), (NF4, True), (NVFP4, False), (Q4_0, False), (Q8_0, False),
-                                    (Q4_1, False), (Q5_0, False), (Q4_K, False)])
+                                    (Q4_1, False), (Q5_0, False), (Q4_K, False), (Q6_K, False)])
 def test_packed_size_matches_oracle(orc, fmt, dq):
     for n, k in SHAPES:
-        if fmt == Q4_K and k % 256:
-            continue                                   # q4_k needs whole 256-value super-blocks
+        if fmt in (Q4_K, Q6_K) and k % 256:
+            continue                                   # q4_k and q6_k need whole 256-value super-blocks
         assert wq.wq_packed_size(wq.desc(fmt, n, k, dq)) == orc.packed_size(fmt, dq, n, k)
     # q8_0 also accepts K % 64 == 0
     if fmt == Q8_0:
@@ -75,7 +75,8 @@ def test_descriptor_validation():
         (wq.wq_desc(Q5_0, 0, 16, 128, 256, 0), 2),      # double-quant only for NF4
         (wq.wq_desc(Q4_K, 0, 16, 384, 0, 0), 3),        # k % 256 for q4_k (super-blocks)
         (wq.wq_desc(Q4_K, 32, 16, 256, 0, 0), 2),       # its block is the 256-value super-block
-        (wq.wq_desc(8, 0, 16, 128, 0, 0), 1),           # past the last format
+        (wq.wq_desc(Q6_K, 0, 16, 640, 0, 0), 3),        # k % 256 for q6_k
+        (wq.wq_desc(9, 0, 16, 128, 0, 0), 1),           # past the last format
         (wq.wq_desc(Q8_0, 0, 16, 96, 0, 0), 3),         # k % 64 for q8_0
         (wq.wq_desc(Q8_0, 0, 0, 64, 0, 0), 3),          # n > 0
         (wq.wq_desc(NF4, 0, 16, 128, 0, 7), 1),         # reserved
@@ -148,6 +149,6 @@ def test_format_names():
     assert wq.format_from_name("nvfp4") == NVFP4
     assert wq.format_from_name("q4_0") == Q4_0 and wq.format_from_name("q8_0") == Q8_0
     assert wq.format_from_name("q4_1") == Q4_1 and wq.format_from_name("q5_0") == Q5_0
-    assert wq.format_from_name("q4_k") == Q4_K
+    assert wq.format_from_name("q4_k") == Q4_K and wq.format_from_name("q6_k") == Q6_K
     with pytest.raises(ValueError):
         wq.format_from_name("fp8")

@@ -14,15 +14,15 @@ from gpu_helpers import (abs_dot, check_bound, dev_bf16, gpu_dequantize, gpu_mat
 
 pytestmark = pytest.mark.gpu
 
-NF4, NVFP4, Q4_0, Q8_0, Q4_1, Q5_0, Q4_K = 1, 2, 3, 4, 5, 6, 7
+NF4, NVFP4, Q4_0, Q8_0, Q4_1, Q5_0, Q4_K, Q6_K = 1, 2, 3, 4, 5, 6, 7, 8
 FORMATS = [(NF4, False), (NF4, True), (NVFP4, False), (Q4_0, False), (Q8_0, False), (Q4_1, False), (Q5_0, False),
-           (Q4_K, False)]
-FMT_IDS = ["nf4", "nf4dq", "nvfp4", "q4_0", "q8_0", "q4_1", "q5_0", "q4_k"]
+           (Q4_K, False), (Q6_K, False)]
+FMT_IDS = ["nf4", "nf4dq", "nvfp4", "q4_0", "q8_0", "q4_1", "q5_0", "q4_k", "q6_k"]
 
 
 def kfor(fmt, k):
-    """q4_k's 256-value super-blocks need k % 256 == 0: the next such k for it."""
-    return (k + 255) // 256 * 256 if fmt == Q4_K else k
+    """q4_k's and q6_k's 256-value super-blocks need k % 256 == 0: the next such k for them."""
+    return (k + 255) // 256 * 256 if fmt in (Q4_K, Q6_K) else k
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -108,8 +108,9 @@ def test_quantize_special_values(orc, fmt, dq):
     (Q4_1, False, [(1280, 1280), (5120, 1280), (1280, 5120)]),
     (Q5_0, False, [(1280, 1280), (5120, 1280), (1280, 5120)]),
     (Q4_K, False, [(1280, 1280), (5120, 1280), (1280, 5120)]),
+    (Q6_K, False, [(1280, 1280), (5120, 1280), (1280, 5120)]),
 ], ids=["decoder-nf4dq", "encoder-nvfp4", "encoder-q8_0", "encoder-q4_0", "encoder-q4_1", "encoder-q5_0",
-        "encoder-q4_k"])
+        "encoder-q4_k", "encoder-q6_k"])
 def test_quantize_full_whisper_shapes(orc, fmt, dq, shapes):
     for i, (n, k) in enumerate(shapes):
         kw = dict(outlier_frac=0.001) if fmt == NF4 else (dict(row_lognormal_sigma=0.3) if fmt == NVFP4 else {})
@@ -189,8 +190,9 @@ STREAM_N = 131072
     (Q4_1, False, 1280, 1, True, wq.WQ_BF16),    # q4_1 takes the general kernel, bands pipelined
     (Q5_0, False, 640, 3, True, wq.WQ_F32),      # so does q5_0
     (Q4_K, False, 768, 2, True, wq.WQ_BF16),     # and q4_k (three super-blocks per row)
+    (Q6_K, False, 512, 4, False, wq.WQ_F32),     # and q6_k
 ], ids=["nf4dq-k1280-m1", "nvfp4-k384-m3", "q8_0-k256-m2", "q4_0-k640-m5", "nf4-k512-m15", "nf4-k384-m16",
-        "q4_1-k1280-m1", "q5_0-k640-m3", "q4_k-k768-m2"])
+        "q4_1-k1280-m1", "q5_0-k640-m3", "q4_k-k768-m2", "q6_k-k512-m4"])
 def test_streaming_gemv_many_bands(orc, fmt, dq, k, m, use_bias, ydt):
     d, codes, scales, ref, b = quantized(orc, fmt, dq, 6000 + k, STREAM_N, k, outlier_frac=0.001)
     x = gen_x(np.random.default_rng(6100 + k), m, k)
@@ -248,8 +250,9 @@ def _sample_rows(m, seed):
     (Q4_1, 1500, [(1280, 1280), (5120, 1280), (1280, 5120)], {}),
     (Q5_0, 1500, [(1280, 1280), (5120, 1280), (1280, 5120)], {}),
     (Q4_K, 1500, [(1280, 1280), (5120, 1280), (1280, 5120)], {}),
+    (Q6_K, 1500, [(1280, 1280), (5120, 1280), (1280, 5120)], {}),
 ], ids=["encoder-nvfp4-1500", "layer-q8_0-6000", "layer-q4_0-6000", "sweep-q8_0-1500", "encoder-q4_1-1500",
-        "encoder-q5_0-1500", "encoder-q4_k-1500"])
+        "encoder-q5_0-1500", "encoder-q4_k-1500", "encoder-q6_k-1500"])
 @pytest.mark.parametrize("ydt", [wq.WQ_F32, wq.WQ_BF16], ids=["f32", "bf16"])
 def test_encoder_gemm_sampled_rows(orc, fmt, m, shapes, kw, ydt):
     """Full-size encoder GEMMs (bf16 output is the timed configuration); 64 sampled
