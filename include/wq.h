@@ -1,6 +1,6 @@
 /*
- * wq.h -- libwq: weight-only 4-bit (and 8-bit) matmul with dequantization fused
- * in, for AMD Instinct MI355X (gfx950).
+ * wq.h -- libwq: weight-only 4-bit (and 5-, 6- and 8-bit) matmul with
+ * dequantization fused in, for AMD Instinct MI355X (gfx950).
  *
  * Y[M,N] = X[M,K] * W^[N,K]^T + b, where X is bf16, W^ is the dequantized form
  * of a block-quantized weight matrix, accumulation is fp32.
@@ -57,7 +57,9 @@
  *   Layout  codes in 1 KiB tiles of 16 rows x 128 K (64 K for Q8_0), ordered by
  *           16-row band then K; 16-byte slot s of a tile holds row s%16, and its
  *           32-bit word j holds k = 32j + 8(s/16) + 0..7 (Q8_0: 8-byte word j);
- *           scales are grouped per tile in row-major (row, block) order.
+ *           scales are grouped per tile in row-major (row, block) order; the
+ *           per-super-block values of Q4_K and Q6_K follow in a row-major
+ *           [n][k/256] plane.
  *
  * Conventions for every call:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  libwq never
@@ -68,9 +70,9 @@
  *     fallback to a dense or unfused path and no silent format conversion.
  *   - A HIP launch error maps to WQ_ERR_HIP.
  *   - bf16 tensors are passed as uint16_t bit patterns.
- *   - Shapes: n > 0 and n % 16 == 0; k > 0 and k % 128 == 0 (NF4, NVFP4, Q4_0, Q4_1, Q5_0),
- *     k % 256 == 0 (Q4_K, Q6_K)
- *     or k % 64 == 0 (Q8_0); m >= 0 (m == 0 is a no-op that returns WQ_OK).
+ *   - Shapes: n > 0 and n % 16 == 0; k > 0 and k % 128 == 0 (NF4, NVFP4, Q4_0,
+ *     Q4_1, Q5_0), k % 256 == 0 (Q4_K, Q6_K) or k % 64 == 0 (Q8_0); m >= 0
+ *     (m == 0 is a no-op that returns WQ_OK).
  */
 #ifndef LIBWQ_WQ_H
 #define LIBWQ_WQ_H
