@@ -49,11 +49,14 @@ def gpu_dequantize(d, codes, scales):
     return out.cpu().numpy()
 
 
-def workspace(d, m):
+def workspace(d, m, seed=77):
+    """The workspace a call asks for, filled with seeded random bytes: the library
+    must not rely on its contents."""
     b = wq.wq_workspace_size(d, m)
     if b == 0:
         return None, 0
-    return torch.zeros(b, dtype=torch.uint8, device=DEV), b
+    junk = np.random.default_rng(seed).integers(0, 256, size=b, dtype=np.uint8)
+    return torch.from_numpy(junk).to(DEV), b
 
 
 def gpu_matmul(d, codes, scales, x_bits: np.ndarray, bias_bits, ydt=wq.WQ_F32, use_ws=True,

@@ -147,7 +147,7 @@ def test_gemm_split_k_full_tiles(orc, fmt, dq, ydt, ldy_pad, k):
     """Few output tiles (N = 512) with several full 128-row tiles (M = 300) and long K:
     the GEMM splits K (in 2 pieces at K = 5120, 4 at K = 6144, 8 at K = 12288), deposits full-tile
     partials with vector stores and reduces them in a second kernel (vector or
-    per-element stores, by output alignment)."""
+    per-element stores, by output alignment).  The workspace starts as random bytes."""
     n, m = 512, 300
     d, codes, scales, ref, b = quantized(orc, fmt, dq, 4200, n, k)
     x = linear_case(4200, n, k, m)[2]
@@ -313,6 +313,48 @@ def test_repeatable_and_workspace_reusable(orc, fmt, dq, m):
     rows = _sample_rows(m, 1)
     check_bound(outs[0].cpu().numpy()[rows], orc.matmul(x, ref["w_hat"], b, rows=rows),
                 abs_dot(x, ref["w_hat"], rows=rows), what="repeat")
+
+
+@pytest.mark.parametrize("fmt,dq", [(NVFP4, False), (NF4, True), (Q8_0, False)], ids=["nvfp4", "nf4dq", "q8_0"])
+@pytest.mark.parametrize("m", [1500, 200], ids=["2pieces", "4pieces"])
+def test_split_k_graph_replays(orc, fmt, dq, m):
+    """A K-split GEMM (fc2 shape, 1280 x 5120) captured in a HIP graph: every replay,
+    with eager calls on the same workspace in between, gives the eager result bit for
+    bit, and that result meets the bound."""
+    n, k = 1280, 5120
+    d, codes, scales, ref, b = quantized(orc, fmt, dq, 4300, n, k)
+    x = linear_case(4300, n, k, m)[2]
+    X = dev_bf16(x)
+    B = dev_bf16(b)
+    ws, wsb = workspace(d, m, seed=5)
+    assert ws is not None
+    say("graph replays", NAMES[fmt], m, n, k)
+    st = torch.cuda.Stream()
+    Y0 = torch.empty((m, n), dtype=torch.float32, device=DEV)
+    Y = torch.empty((m, n), dtype=torch.float32, device=DEV)
+    with torch.cuda.stream(st):
+        wq.wq_matmul(d, m, X, k, codes, scales, B, Y0, wq.WQ_F32, n, ws, wsb, stream=st)
+    st.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            wq.wq_matmul(d, m, X, k, codes, scales, B, Y, wq.WQ_F32, n, ws, wsb, stream=st)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        Y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Y0), f"replay {rep} differs from the eager result"
+        if rep % 2 == 1:
+            # an eager call with its own token on the same workspace between replays
+            Y2 = torch.empty((m, n), dtype=torch.float32, device=DEV)
+            wq.wq_matmul(d, m, X, k, codes, scales, B, Y2, wq.WQ_F32, n, ws, wsb)
+            torch.cuda.synchronize()
+            assert torch.equal(Y2, Y0), "eager call between replays differs"
+    rows = _sample_rows(m, 6)
+    check_bound(Y0.cpu().numpy()[rows], orc.matmul(x, ref["w_hat"], b, rows=rows),
+                abs_dot(x, ref["w_hat"], rows=rows), what=f"graph split-K {NAMES[fmt]} m={m}")
 
 
 # --------------------------------------------------------------- fused QKV / merged K/V
