@@ -310,6 +310,60 @@ def main():
         log(f"[bench] decode M=1 by format: {out}")
         return out
 
+    def quality_part():
+        """Per format, on the same fp32 weights: the relative L2 error of one Linear's output
+        against the unquantized fp32 product (a diagnostic of the format, not a gate), and
+        the time of wq_quantize.  Matrices: decoder fc1 (5120 x 1280, 0.1 % outliers x 8) at
+        M = 16 and encoder fc1 (5120 x 1280, per-row std from LogNormal(0, 0.3)) at M = 1500.
+        The fp32 and bf16-weight references are torch matmuls in fp32 (TF32 off)."""
+        torch.backends.cuda.matmul.allow_tf32 = False
+        fmts = (("nf4", wq.WQ_NF4, False), ("nf4dq", wq.WQ_NF4, True), ("nvfp4", wq.WQ_NVFP4, False),
+                ("q4_0", wq.WQ_Q4_0, False), ("q4_1", wq.WQ_Q4_1, False), ("q5_0", wq.WQ_Q5_0, False),
+                ("q4_k", wq.WQ_Q4_K, False), ("q6_k", wq.WQ_Q6_K, False), ("q8_0", wq.WQ_Q8_0, False))
+        cases = (("decoder_fc1_m16", linear_case(2002, ENC_FFN, ENC_D, 16, outlier_frac=0.001), 16),
+                 ("encoder_fc1_m1500", linear_case(3000, ENC_FFN, ENC_D, ENC_M, row_lognormal_sigma=0.3), ENC_M))
+        out = {"how": "rel_l2 = ||Y - Y_fp32|| / ||Y_fp32||, Y_fp32 = X W^T + b in fp32; "
+                      "bf16_weights = the same with W rounded to bf16; quantize_us = one wq_quantize "
+                      "(fp32 W in HBM), mean of 10 after a warm-up call"}
+        for cname, (w, b, x), m in cases:
+            n, k = w.shape
+            W = torch.from_numpy(w).to(dev)
+            X = bf16_dev(x)
+            Xf = X.view(torch.bfloat16).float()
+            Bf = bf16_dev(b).view(torch.bfloat16).float()
+            ref = Xf @ W.t() + Bf
+            nref = torch.linalg.vector_norm(ref).item()
+            row = {"bf16_weights": round(torch.linalg.vector_norm(
+                Xf @ W.to(torch.bfloat16).float().t() + Bf - ref).item() / nref, 6)}
+            for name, fmt, dq in fmts:
+                d, c, s_ = quantize_dev(fmt, W, dq)
+                Y = torch.empty((m, n), dtype=torch.float32, device=dev)
+                nb = wq.wq_workspace_size(d, m)
+                ws = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+                wq.wq_matmul(d, m, X, k, c, s_, bf16_dev(b), Y, wq.WQ_F32, n, ws if nb else None, nb)
+                rel = torch.linalg.vector_norm(Y - ref).item() / nref
+                ent = {"rel_l2": round(rel, 6)}
+                if cname == "decoder_fc1_m16":
+                    with torch.cuda.stream(stream):
+                        wq.wq_quantize(d, W, c, s_, stream=stream)
+                        e0 = torch.cuda.Event(enable_timing=True)
+                        e1 = torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        for _ in range(10):
+                            wq.wq_quantize(d, W, c, s_, stream=stream)
+                        e1.record(stream)
+                    torch.cuda.synchronize()
+                    tq = e0.elapsed_time(e1) * 1e3 / 10
+                    ent["quantize_us"] = round(tq, 1)
+                    ent["quantize_GBps_fp32_in"] = round(n * k * 4 / tq / 1e3, 1)
+                row[name] = ent
+                del c, s_
+            out[cname] = row
+            del W
+            torch.cuda.empty_cache()
+        log(f"[bench] quality and quantize time: {out}")
+        return out
+
     def sweep_part():
         """large-v3-turbo's Linears as a decoder and an encoder call them.
         Decoder step: 4 layers x {self-attn Q/K/V (one wq_matmul_qkv), self O, cross Q, cross O,
@@ -475,6 +529,9 @@ def main():
 
         # ---- the decode set (M = 1) in every format, same weights ----
         extras["decode_m1_by_format"] = decode_by_format()
+
+        # ---- output error of each format against fp32 weights, and wq_quantize time ----
+        extras["quality_and_quantize_time"] = quality_part()
 
         # ---- large-v3-turbo sweep: the whole per-token decoder step and the q8_0 encoder ----
         extras.update(sweep_part())

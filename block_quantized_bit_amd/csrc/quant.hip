@@ -11,6 +11,7 @@
 // add a 4-bit nf4 option for the Whisper engine", "Why NF4 and not the NVFP4
 // snapshot Parakeet ships"); the only temporary storage is the codes buffer.
 #include "wq_device.h"
+#include <climits>
 #include "wq_launch.h"
 
 namespace wq {
@@ -377,21 +378,123 @@ __global__ __launch_bounds__(256) void k_quant_chunks(const float* __restrict__ 
     }
 }
 
-// Double-quant mean: one thread sums the nb absmax values in binary64 in
-// ascending block order, divides in binary64 and rounds to binary32.
-__global__ void k_dq_mean(const float* __restrict__ a, int64_t nb, uint8_t* __restrict__ scales, int64_t mu_off) {
-    if (threadIdx.x != 0 || blockIdx.x != 0) return;
-    double s = 0.0;
-    const float4* a4 = reinterpret_cast<const float4*>(a);
-    for (int64_t i = 0; i < nb / 4; i++) {
-        const float4 t = a4[i];
-        s += (double)t.x;
-        s += (double)t.y;
-        s += (double)t.z;
-        s += (double)t.w;
+// Double-quant mean: the nb absmax values summed in binary64 in ascending block
+// order, divided in binary64 and rounded to binary32.
+//
+// Fast path, exact: write every nonzero value as odd * 2^e (odd < 2^24).  With
+// L = 2^min(e), every partial sum of the sequence is a multiple of L; if the whole
+// sum is below 2^53 L, each partial sum is representable in binary64, so every
+// ascending addition is exact and the sequential sum is the exact sum.  The
+// workgroup then adds the values as integers in units of L, in any order.
+// Otherwise (values spanning a very wide range), thread 0 runs the ascending chain
+// of additions, with the workgroup staging the values through two LDS buffers.
+constexpr int kMeanThreads = 1024;
+constexpr int kMeanChunk = 4096;   // floats per LDS buffer
+
+__device__ inline void odd_exp(float v, uint32_t& odd, int& e) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t be = u >> 23, mant = u & 0x7FFFFFu;
+    const uint32_t m = be == 0 ? mant : (mant | 0x800000u);
+    const int tz = __builtin_ctz(m);
+    odd = m >> tz;
+    e = (be == 0 ? -149 : (int)be - 150) + tz;
+}
+
+__global__ __launch_bounds__(kMeanThreads) void k_dq_mean(const float* __restrict__ a, int64_t nb,
+                                                          uint8_t* __restrict__ scales, int64_t mu_off) {
+    __shared__ __attribute__((aligned(16))) float buf[2][kMeanChunk];
+    __shared__ int emin_s[kMeanThreads / 64];
+    __shared__ unsigned long long sum_s[kMeanThreads / 64];
+    __shared__ int bad_s[kMeanThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    constexpr int kWaves = kMeanThreads / 64;
+
+    // smallest exponent of a lowest set bit
+    int emin = INT_MAX;
+    for (int64_t i = tid; i < nb; i += kMeanThreads) {
+        const float v = a[i];
+        if (v != 0.0f) {
+            uint32_t odd;
+            int e;
+            odd_exp(v, odd, e);
+            emin = min(emin, e);
+        }
     }
-    for (int64_t i = (nb / 4) * 4; i < nb; i++) s += (double)a[i];
-    *reinterpret_cast<float*>(scales + mu_off) = (float)(s / (double)nb);
+    for (int o = 32; o > 0; o >>= 1) emin = min(emin, __shfl_xor(emin, o));
+    if (lane == 0) emin_s[wave] = emin;
+    __syncthreads();
+    emin = emin_s[0];
+    for (int w = 1; w < kWaves; w++) emin = min(emin, emin_s[w]);
+
+    // integer sum in units of 2^emin; any term or partial sum reaching 2^53 ends the fast path
+    constexpr unsigned long long kLimit = 1ull << 53;
+    unsigned long long acc = 0;
+    int bad = 0;
+    if (emin != INT_MAX) {
+        for (int64_t i = tid; i < nb; i += kMeanThreads) {
+            const float v = a[i];
+            if (v == 0.0f) continue;
+            uint32_t odd;
+            int e;
+            odd_exp(v, odd, e);
+            const int sh = e - emin;
+            if (sh >= 40) { bad = 1; break; }                 // odd << sh would pass 2^63
+            acc += (unsigned long long)odd << sh;              // each term < 2^63, acc < 2^53 before
+            if (acc >= kLimit) { bad = 1; break; }
+        }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        acc += __shfl_xor(acc, o);   // < 64 * 2^53: no wrap
+        bad |= __shfl_xor(bad, o);
+    }
+    if (lane == 0) {
+        sum_s[wave] = acc;
+        bad_s[wave] = bad;
+    }
+    __syncthreads();
+    unsigned long long total = 0;
+    for (int w = 0; w < kWaves; w++) {
+        total += sum_s[w];
+        bad |= bad_s[w];
+    }
+    if (!bad && total < kLimit) {
+        if (tid == 0) {
+            const double s = emin == INT_MAX ? 0.0 : ldexp((double)total, emin);
+            *reinterpret_cast<float*>(scales + mu_off) = (float)(s / (double)nb);
+        }
+        return;
+    }
+
+    // ascending chain
+    const int64_t nchunks = (nb + kMeanChunk - 1) / kMeanChunk;
+    auto stage = [&](int64_t c) {
+        float* dst = buf[c & 1];
+        for (int i = tid; i < kMeanChunk; i += kMeanThreads) {
+            const int64_t idx = c * kMeanChunk + i;
+            dst[i] = idx < nb ? a[idx] : 0.0f;
+        }
+    };
+    double s = 0.0;
+    stage(0);
+    __syncthreads();
+    for (int64_t c = 0; c < nchunks; c++) {
+        if (c + 1 < nchunks) stage(c + 1);
+        if (tid == 0) {
+            const float* src = buf[c & 1];
+            const int cnt = (int)std::min<int64_t>(kMeanChunk, nb - c * kMeanChunk);
+            int i = 0;
+            for (; i + 4 <= cnt; i += 4) {
+                const float4 t = *reinterpret_cast<const float4*>(src + i);
+                s += (double)t.x;
+                s += (double)t.y;
+                s += (double)t.z;
+                s += (double)t.w;
+            }
+            for (; i < cnt; i++) s += (double)src[i];
+        }
+        __syncthreads();   // chunk c + 1 is staged; buffer c & 1 is free for chunk c + 2
+    }
+    if (tid == 0) *reinterpret_cast<float*>(scales + mu_off) = (float)(s / (double)nb);
 }
 
 // Double-quant groups: one wave per 256 consecutive blocks (logical order).
@@ -558,7 +661,7 @@ hipError_t launch_quantize(int fmt, bool dq, int64_t n, int64_t k, const float* 
         } else {
             float* scratch = reinterpret_cast<float*>(codes);   // nb floats <= n*k/2 bytes
             hipLaunchKernelGGL((k_quant_chunks<kNF4, 1>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, scratch, L);
-            hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(64), 0, s, scratch, L.nb, scales, L.mu_off);
+            hipLaunchKernelGGL(k_dq_mean, dim3(1), dim3(kMeanThreads), 0, s, scratch, L.nb, scales, L.mu_off);
             hipLaunchKernelGGL(k_dq_groups, dim3((unsigned)L.ng), dim3(64), 0, s, scratch, L.nb, k, scales, L);
             hipLaunchKernelGGL((k_quant_chunks<kNF4, 2>), dim3(grid), dim3(256), 0, s, w, n, k, codes, scales, nullptr, L);
         }

@@ -100,6 +100,25 @@ def test_quantize_special_values(orc, fmt, dq):
     assert np.array_equal(gpu_dequantize(d, codes, scales).view(np.uint32), ref["w_hat"].view(np.uint32))
 
 
+@pytest.mark.parametrize("wide", [False, True], ids=["integer-sum", "ascending-chain"])
+def test_double_quant_mean_both_paths(orc, wide):
+    """The double-quant mean (ascending binary64 sum of the absmax values) on its two
+    GPU paths, bit-exact against the oracle: absmax values of one magnitude make every
+    ascending addition exact, so the integer sum of the workgroup is taken; one row
+    scaled by 1e-12 spreads their lowest set bits over more than 2^40, which sends the
+    sum down the sequential chain (20 800 blocks: five 4096-value chunks and a ragged one)."""
+    rng = np.random.default_rng(17)
+    n, k = 1040, 1280
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+    if wide:
+        w[7] *= np.float32(1e-12)
+    say("dq mean", "wide" if wide else "narrow")
+    ref = orc.quantize(NF4, w, True)
+    d, codes, scales = gpu_quantize(NF4, w, True)
+    assert np.array_equal(scales.cpu().numpy(), ref["scales"]), "scales (mean, group scales, int8 absmax) differ"
+    assert np.array_equal(codes.cpu().numpy(), ref["codes"])
+
+
 @pytest.mark.parametrize("fmt,dq,shapes", [
     (NF4, True, [(3840, 1280), (1280, 1280), (5120, 1280), (1280, 5120)]),
     (NVFP4, False, [(5120, 1280), (1280, 5120)]),
