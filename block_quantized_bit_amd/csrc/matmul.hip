@@ -636,18 +636,30 @@ __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const ui
 template <int FMT, bool DQ, int C>
 __device__ constexpr bool gemv_dq_rows() { return FMT == kNF4 && DQ && C < 8; }
 
+// The row's double-quant group scales (and, when mu is non-null, the matrix mean) are
+// requested right after the first tile: the first tile's use needs them, and a wait for
+// everything older than the band's requests (the X copy) does not wait for them.
 template <int FMT, bool DQ, int C, bool XL>
 __device__ __forceinline__ void gemv_load_band(GemvTile<FMT> (&R)[C], DqRow& dq, const KArgs& a, int64_t band,
                                                int64_t c0, int wave, int lane, int r, const uint16_t* xrow,
-                                               int64_t KT) {
+                                               int64_t KT, float* mu = nullptr) {
     constexpr bool DR = gemv_dq_rows<FMT, DQ, C>();
-    if constexpr (DR) dq = dq_row(a, band * 16 + r);
 #pragma unroll
     for (int s = 0; s < C; s++) {
         const int64_t kt = std::min<int64_t>(wave + (c0 + s) * kGemvWaves, KT - 1);
         gemv_load<FMT, DQ, XL>(R[s], a, band, kt, lane, r, xrow, KT, DR ? &dq : nullptr);
+        if (s == 0) {
+            if constexpr (DR) dq = dq_row(a, band * 16 + r);
+            if constexpr (FMT == kNF4 && DQ) {
+                if (mu) *mu = load_f32_vmem(a.scales + a.L.mu_off);
+            }
+        }
     }
 }
+
+// Register loads a band request issues: C tiles, plus the row's two group scales.
+template <int FMT, bool DQ, int C>
+__device__ constexpr int gemv_band_loads() { return C * gemv_w_loads<FMT, DQ>() + (gemv_dq_rows<FMT, DQ, C>() ? 2 : 0); }
 
 // XL: the A operands come from the LDS copy of X (xl = this lane's row, chunk h), read here.
 template <int FMT, bool DQ, int NI, int C, bool XL>
@@ -720,9 +732,14 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
     const int64_t KT = a.k / tile_k(FMT);
     const int64_t nbands = a.n / 16;
 
+    // The double-quant mean sits with the scales, in memory as cold as the weights.  With X
+    // copied to LDS it is requested with the first band's tiles (after the copy), so that
+    // the wait for the copy does not wait for it; without the copy, up front.
     float g = 1.0f, mu = 0.0f;
     if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.scales + a.L.g_off);
-    if constexpr (FMT == kNF4 && DQ) mu = load_f32_vmem(a.scales + a.L.mu_off);
+    if constexpr (FMT == kNF4 && DQ && !XL) mu = load_f32_vmem(a.scales + a.L.mu_off);
+    constexpr int kMuLoads = (FMT == kNF4 && DQ && XL) ? 1 : 0;
+    float* const mu_first = kMuLoads ? &mu : nullptr;
     const uint16_t* xrow = a.x + (int64_t)(r < a.m ? r : 0) * a.ldx + h * 8;
     // the LDS copy of X is chunk-major: chunk c of row r at element 8 (c m + r); the
     // one-token instantiation (NI = 1 is only launched for m = 1) gets a constant stride,
@@ -744,10 +761,10 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
         for (int64_t c0 = 0; c0 < per_wave; c0 += C) {
             GemvTile<FMT> R[C];
             DqRow dq;
-            gemv_load_band<FMT, DQ, C, XL>(R, dq, a, band, c0, wave, lane, r, xrow, KT);
+            gemv_load_band<FMT, DQ, C, XL>(R, dq, a, band, c0, wave, lane, r, xrow, KT, c0 == 0 ? mu_first : nullptr);
             if (c0 == 0) {
                 if constexpr (XL) {
-                    lds_barrier_vm<C * gemv_w_loads<FMT, DQ>()>();
+                    lds_barrier_vm<gemv_band_loads<FMT, DQ, C>() + kMuLoads>();
                 } else {
                     if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
                     __syncthreads();
@@ -765,9 +782,9 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
             if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
             gemv_stage_x(xs_dyn, a, wave, lane);
         }
-        gemv_load_band<FMT, DQ, C, XL>(R0, dq0, a, band, 0, wave, lane, r, xrow, KT);
+        gemv_load_band<FMT, DQ, C, XL>(R0, dq0, a, band, 0, wave, lane, r, xrow, KT, mu_first);
         if constexpr (XL) {
-            lds_barrier_vm<C * gemv_w_loads<FMT, DQ>()>();
+            lds_barrier_vm<gemv_band_loads<FMT, DQ, C>() + kMuLoads>();
         } else {
             if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
             __syncthreads();
