@@ -90,10 +90,14 @@ def lib():
 
 
 def _ptr(t):
+    """Device address of a tensor argument.  A host tensor is refused here: the library
+    hands its pointers to GPU kernels, which cannot read host memory."""
     if t is None:
         return None
     if isinstance(t, int):
         return t
+    if not getattr(t, "is_cuda", False):
+        raise ValueError(f"libwq takes device buffers; got a tensor on {getattr(t, 'device', type(t))}")
     return t.data_ptr()
 
 

@@ -152,3 +152,13 @@ def test_format_names():
     assert wq.format_from_name("q4_k") == Q4_K and wq.format_from_name("q6_k") == Q6_K
     with pytest.raises(ValueError):
         wq.format_from_name("fp8")
+
+
+def test_binding_refuses_host_tensors():
+    """The binding passes tensors' device addresses; a host tensor is refused before any
+    call into the library, which would hand its address to a GPU kernel."""
+    import torch
+    d = wq.desc(NVFP4, 32, 256)
+    w = torch.zeros((32, 256), dtype=torch.float32)
+    with pytest.raises(ValueError, match="device buffers"):
+        wq.wq_quantize(d, w, FAKE, FAKE, stream=0)
