@@ -1594,11 +1594,12 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, int global_scale
     if (hb) reduce_store(a, qb, vb, g);
 }
 
-// The same for exactly KS pieces (2 or 4): each thread owns 8 / KS quads, spaced 256
-// apart, and issues all 8 of its partial loads before adding any (pieces in order).
+// The same for exactly KS pieces (2 or 4): each thread owns 2 quads, spaced 256 apart,
+// and issues all 2 KS of its partial loads before adding any (pieces in order).  (Four
+// quads per thread at KS = 2 measured 0.7-1 us slower on the M = 1500 fc2 shape.)
 template <int KS>
 __global__ __launch_bounds__(256) void k_splitk_reduce_n(KArgs a, int global_scale) {
-    constexpr int Q = 8 / KS;
+    constexpr int Q = 2;
     const float g = global_scale ? *reinterpret_cast<const float*>(a.scales + a.L.g_off) : 1.0f;
     const int64_t total = (int64_t)a.m * (a.n / 4);
     const int64_t q0 = (int64_t)blockIdx.x * (256 * Q) + threadIdx.x;
@@ -1824,7 +1825,7 @@ hipError_t launch_gemm(const MatmulProblem& p, hipStream_t st) {
         const int64_t nquads = p.m * (p.n / 4);
         const int gs = (int)(p.fmt == kNVFP4);
         if (s.ksplit == 2)
-            hipLaunchKernelGGL(k_splitk_reduce_n<2>, dim3((unsigned)((nquads + 1023) / 1024)), dim3(256), 0, st, a, gs);
+            hipLaunchKernelGGL(k_splitk_reduce_n<2>, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a, gs);
         else if (s.ksplit == 4)
             hipLaunchKernelGGL(k_splitk_reduce_n<4>, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a, gs);
         else
