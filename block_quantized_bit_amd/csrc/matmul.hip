@@ -518,7 +518,7 @@ __device__ __forceinline__ void gemv_stage_x(uint16_t* xs, const KArgs& a, int w
 // NF4 and Q4_0 codes become bf16 pairs through the LDS table; NVFP4 and Q8_0
 // convert in registers.
 template <int FMT>
-__device__ constexpr bool gemv_uses_lut() { return FMT == kNF4 || FMT == kQ4_0; }
+__host__ __device__ constexpr bool gemv_uses_lut() { return FMT == kNF4 || FMT == kQ4_0; }
 
 template <int FMT, bool DQ, int NI>
 __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const uint32_t* lut, uint32_t lane4,
@@ -1710,12 +1710,22 @@ static int gemv_chunk(int64_t KT) {
 
 constexpr int64_t kGemvXlMax = 32768;   // bf16 elements of X (m * k) copied to LDS by the decode GEMV
 
+// Two workgroups per CU for the small-C kernels (<= 128 VGPRs) when their LDS fits twice:
+// with a code table, an X copy of at most 8 KiB; without one, the reduction buffer and the
+// X copy twice in the CU's 160 KiB.
+template <int FMT, int C>
+static bool gemv_two_per_cu(size_t xbytes) {
+    constexpr size_t kLdsPerCu = 160 * 1024;
+    const size_t red = sizeof(f32x4) * kGemvWaves * 64;
+    if (C > 2) return false;
+    return gemv_uses_lut<FMT>() ? xbytes <= 8192 : 2 * (red + 16 + xbytes) <= kLdsPerCu;
+}
+
 template <int FMT, bool DQ, int NI, int C, bool XL>
 static void gemv_launch_cx(const KArgs& a, int64_t nbands, int64_t KT, hipStream_t st) {
     const dim3 block(64 * kGemvWaves);
     const size_t xbytes = XL ? (size_t)a.m * (size_t)a.k * 2 : 0;
-    // two workgroups per CU fit when the X copy leaves room for two code tables
-    const int64_t per_cu = (C <= 2 && xbytes <= 8192) ? 2 : 1;
+    const int64_t per_cu = gemv_two_per_cu<FMT, C>(xbytes) ? 2 : 1;
     // band pipelining only where its two register sets fit without spilling (C <= 2), and only
     // when the bands outnumber the workgroups that fit at once
     if constexpr (C <= 2) {
@@ -1734,7 +1744,9 @@ static void gemv_launch_cx(const KArgs& a, int64_t nbands, int64_t KT, hipStream
 template <int FMT, bool DQ, int NI, int C>
 static void gemv_launch_c(const KArgs& a, int64_t nbands, int64_t KT, hipStream_t st) {
     const int64_t mk = (int64_t)a.m * a.k;
-    const bool xl = mk <= kGemvXlMax && nbands <= 2 * kNumCU && (mk * 2 <= 8192 || nbands <= kNumCU);
+    // the X copy when all bands run in one round of resident workgroups
+    const bool xl = mk <= kGemvXlMax && nbands <= 2 * kNumCU &&
+                    (mk * 2 <= 8192 || nbands <= kNumCU || (!gemv_uses_lut<FMT>() && gemv_two_per_cu<FMT, C>((size_t)mk * 2)));
     if (xl) gemv_launch_cx<FMT, DQ, NI, C, true>(a, nbands, KT, st);
     else gemv_launch_cx<FMT, DQ, NI, C, false>(a, nbands, KT, st);
 }
