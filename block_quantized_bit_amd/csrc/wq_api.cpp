@@ -46,6 +46,7 @@ wq_status check_desc(const wq_desc* d, Desc* out) {
     const int64_t tk = d->format == WQ_Q8_0 ? 64 : (d->format == WQ_Q4_K || d->format == WQ_Q6_K) ? 256 : 128;
     if (d->n <= 0 || d->k <= 0 || d->n % 16 != 0 || d->k % tk != 0) return WQ_ERR_SHAPE;
     if (d->n > (int64_t(1) << 40) / d->k) return WQ_ERR_SHAPE;   // keep every byte offset far from overflow
+    if (d->k > (int64_t(1) << 24)) return WQ_ERR_SHAPE;           // a band's codes within one 32-bit buffer range
     out->fmt = d->format;
     out->dq = d->format == WQ_NF4 && d->dq_group == 256;
     out->n = d->n;
@@ -70,7 +71,7 @@ wq_status check_matmul(const wq_desc* d, int64_t m, const uint16_t* x, int64_t l
     if ((st = check_packed(w)) != WQ_OK) return st;
     if (m < 0 || m > 0x7FFFFFFF) return WQ_ERR_SHAPE;
     if (!x) return WQ_ERR_INVALID_ARG;
-    if (ldx < dd.k || ldx % 8 != 0) return WQ_ERR_INVALID_ARG;
+    if (ldx < dd.k || ldx % 8 != 0 || ldx > (int64_t(1) << 24)) return WQ_ERR_INVALID_ARG;   // 128 rows of X < 4 GiB
     if (!aligned(x, 16)) return WQ_ERR_ALIGNMENT;
     if (bias && !aligned(bias, 2)) return WQ_ERR_ALIGNMENT;
     if (ydt != WQ_BF16 && ydt != WQ_F32) return WQ_ERR_INVALID_ARG;

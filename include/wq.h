@@ -72,7 +72,9 @@
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *   - Shapes: n > 0 and n % 16 == 0; k > 0 and k % 128 == 0 (NF4, NVFP4, Q4_0,
  *     Q4_1, Q5_0), k % 256 == 0 (Q4_K, Q6_K) or k % 64 == 0 (Q8_0); m >= 0
- *     (m == 0 is a no-op that returns WQ_OK).
+ *     (m == 0 is a no-op that returns WQ_OK).  k <= 2^24 and n * k <= 2^40, so that
+ *     a 16-row band of codes and a 128-row tile of X (ldx <= 2^24) each stay under
+ *     the 4 GiB that one buffer descriptor of the kernels addresses.
  */
 #ifndef LIBWQ_WQ_H
 #define LIBWQ_WQ_H

@@ -80,6 +80,8 @@ def test_descriptor_validation():
         (wq.wq_desc(Q8_0, 0, 16, 96, 0, 0), 3),         # k % 64 for q8_0
         (wq.wq_desc(Q8_0, 0, 0, 64, 0, 0), 3),          # n > 0
         (wq.wq_desc(NF4, 0, 16, 128, 0, 7), 1),         # reserved
+        (wq.wq_desc(NF4, 0, 16, (1 << 24) + 128, 0, 0), 3),   # k beyond one band's 32-bit buffer range
+        (wq.wq_desc(NF4, 0, 1 << 20, 1 << 21, 0, 0), 3),      # n * k beyond 2^40
     ]
     for d, want in bad:
         assert _status(wq.wq_packed_size, d) == want
@@ -100,6 +102,7 @@ def test_matmul_argument_validation_returns_before_launch():
     assert mm(x=FAKE + 8) == 4
     assert mm(ldx=200) == 1
     assert mm(ldx=260) == 1             # ldx % 8
+    assert mm(ldx=(1 << 24) + 8) == 1   # 128 rows of X must stay within one 32-bit buffer range
     assert mm(codes=None) == 1
     assert mm(scales=FAKE + 4) == 4
     assert mm(bias=FAKE + 1) == 4
