@@ -1744,9 +1744,13 @@ static void gemv_launch_cx(const KArgs& a, int64_t nbands, int64_t KT, hipStream
 template <int FMT, bool DQ, int NI, int C>
 static void gemv_launch_c(const KArgs& a, int64_t nbands, int64_t KT, hipStream_t st) {
     const int64_t mk = (int64_t)a.m * a.k;
-    // the X copy when all bands run in one round of resident workgroups
+    // The X copy when all bands run in one round of resident workgroups.  The table formats
+    // fit one workgroup per CU with a larger copy; from 12 tokens on, the copy with two bands
+    // pipelined per workgroup beats reading 12-16 rows of X from L2 per tile (measured at the
+    // fc1 shape, 320 bands: 8 tokens 5.3 vs 5.4 us, 12 tokens 6.1 vs 5.7, 16 tokens 6.7 vs 6.1).
     const bool xl = mk <= kGemvXlMax && nbands <= 2 * kNumCU &&
-                    (mk * 2 <= 8192 || nbands <= kNumCU || (!gemv_uses_lut<FMT>() && gemv_two_per_cu<FMT, C>((size_t)mk * 2)));
+                    (mk * 2 <= 8192 || nbands <= kNumCU || (!gemv_uses_lut<FMT>() && gemv_two_per_cu<FMT, C>((size_t)mk * 2)) ||
+                     (gemv_uses_lut<FMT>() && C <= 2 && a.m >= 12));
     if (xl) gemv_launch_cx<FMT, DQ, NI, C, true>(a, nbands, KT, st);
     else gemv_launch_cx<FMT, DQ, NI, C, false>(a, nbands, KT, st);
 }
