@@ -196,12 +196,12 @@ def test_decoder_gemv_set_full(orc, m, ydt):
 @pytest.mark.parametrize("fmt,dq", [(NVFP4, False), (Q4_1, False), (Q5_0, False), (Q4_K, False), (Q6_K, False),
                                     (NF4, True), (Q4_0, False), (Q8_0, False)],
                          ids=["nvfp4", "q4_1", "q5_0", "q4_k", "q6_k", "nf4dq", "q4_0", "q8_0"])
-@pytest.mark.parametrize("m", [1, 5, 16])
+@pytest.mark.parametrize("m", [1, 5, 11, 12, 16])
 def test_decode_fc1_shape_many_tokens(orc, fmt, dq, m):
     """fc1 geometry (5120 x 1280, 320 bands) at one and several tokens: at several tokens the
     formats without a code table copy X to LDS with two workgroups per CU (one round for all
-    bands), the table formats read X from L2; q8_0 takes 4-tile rounds.  Every output is
-    checked."""
+    bands), the table formats read X from L2 below 12 tokens and copy it, two bands pipelined
+    per workgroup, from 12 on; q8_0 takes 4-tile rounds.  Every output is checked."""
     n, k = 5120, kfor(fmt, 1280)
     d, codes, scales, ref, b = quantized(orc, fmt, dq, 2002, n, k, outlier_frac=0.001)
     x = linear_case(2002, n, k, 16, outlier_frac=0.001)[2][:m]
