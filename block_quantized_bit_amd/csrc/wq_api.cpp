@@ -7,6 +7,7 @@
 // no dense or unfused fallback.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "wq.h"
@@ -93,6 +94,34 @@ wq_status check_matmul(const wq_desc* d, int64_t m, const uint16_t* x, int64_t l
     p->ws_bytes = ws_bytes;
     p->out.f32 = ydt == WQ_F32;
     return WQ_OK;
+}
+
+int64_t floor_div(int64_t a, int64_t b) {   // b > 0
+    const int64_t q = a / b;
+    return (a % b != 0 && a < 0) ? q - 1 : q;
+}
+
+// Do two strided output windows share a byte?  Window i covers rows r = 0..m-1, each the
+// byte range [base_i + r*ld_i*es, base_i + r*ld_i*es + w_i*es).  Row r1 of A meets row r2
+// of B iff b + r2*lb < a_hi and b + r2*lb + wb > a_lo, an interval of r2 that is solved
+// in closed form; with equal strides r2 - r1 is the only unknown, so one interval covers
+// every row.
+bool windows_overlap(const void* pa, int64_t lda, int64_t wa, const void* pb, int64_t ldb, int64_t wb,
+                     int64_t m, int64_t es) {
+    const int64_t a = (int64_t)reinterpret_cast<uintptr_t>(pa), b = (int64_t)reinterpret_cast<uintptr_t>(pb);
+    const int64_t la = lda * es, lb = ldb * es, na = wa * es, nb = wb * es;
+    if (la == lb) {
+        // rows r1, r2 = r1 + t meet iff -nb < (b - a) + t*la < na, for some |t| <= m - 1
+        const int64_t d = b - a;
+        const int64_t tmin = floor_div(-nb - d, la) + 1, tmax = -floor_div(-(na - d), la) - 1;
+        return std::max<int64_t>(tmin, -(m - 1)) <= std::min<int64_t>(tmax, m - 1);
+    }
+    for (int64_t r1 = 0; r1 < m; r1++) {
+        const int64_t lo = a + r1 * la, hi = lo + na;
+        const int64_t r2min = floor_div(lo - nb - b, lb) + 1, r2max = -floor_div(-(hi - b), lb) - 1;
+        if (std::max<int64_t>(r2min, 0) <= std::min<int64_t>(r2max, m - 1)) return true;
+    }
+    return false;
 }
 
 wq_status run_matmul(const wq::MatmulProblem& p, void* stream) {
@@ -196,6 +225,12 @@ wq_status wq_matmul_qkv(const wq_desc* d, int64_t m, const uint16_t* x, int64_t 
         if (!aligned(y[i], ydt == WQ_F32 ? 4 : 2)) return WQ_ERR_ALIGNMENT;
         if (ldy[i] < split_n[i]) return WQ_ERR_INVALID_ARG;
     }
+    // the splits' destination windows must be disjoint (every output element is written once)
+    const int64_t es = ydt == WQ_F32 ? 4 : 2;
+    for (int i = 0; i < nsplit; i++)
+        for (int j = i + 1; j < nsplit; j++)
+            if (m > 0 && windows_overlap(y[i], ldy[i], split_n[i], y[j], ldy[j], split_n[j], m, es))
+                return WQ_ERR_INVALID_ARG;
     p.out.nsplit = nsplit;
     int64_t e = 0;
     for (int i = 0; i < 3; i++) {

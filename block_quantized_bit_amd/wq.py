@@ -153,6 +153,8 @@ def wq_matmul(d: wq_desc, m: int, x, ldx: int, codes, scales, bias, y, ydt: int,
 def wq_matmul_qkv(d: wq_desc, m: int, x, ldx: int, codes, scales, bias, split_n, ys, ldys, ydt: int,
                   ws=None, ws_bytes: int = 0, stream=None, check=True) -> int:
     ns = len(split_n)
+    if len(ys) != ns or len(ldys) != ns:
+        raise ValueError(f"wq_matmul_qkv: {ns} splits but {len(ys)} outputs and {len(ldys)} leading dimensions")
     sn = (ctypes.c_int64 * ns)(*[int(v) for v in split_n])
     yp = (ctypes.c_void_p * len(ys))(*[_ptr(v) for v in ys])
     lp = (ctypes.c_int64 * len(ldys))(*[int(v) for v in ldys])

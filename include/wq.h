@@ -186,7 +186,8 @@ wq_status wq_matmul(const wq_desc* d, int64_t m, const uint16_t* x, int64_t ldx,
  * columns [0, n0) go to y[0], [n0, n0+n1) to y[1], [n0+n1, n) to y[2],
  * each with its own leading dimension ldy[i] >= split_n[i], so the destinations
  * may be rows of a K/V cache slab; nothing outside each m x split_n[i] window is
- * touched.  bias is bf16 [n] or NULL (use zeros where a split has none, e.g. the
+ * touched.  The windows must not share a byte (WQ_ERR_INVALID_ARG otherwise; the
+ * check is closed-form for equal leading dimensions and O(m) for different ones).  bias is bf16 [n] or NULL (use zeros where a split has none, e.g. the
  * key projection).  nsplit is 2 (merged cross-attention K/V) or 3 (Q/K/V);
  * split_n[i] > 0 and sum(split_n) == d->n.  Passages: "Run quantized Whisper on
  * the fused Metal decode path", "Summary" (fused Q/K/V writing into slab rows

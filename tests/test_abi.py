@@ -136,6 +136,16 @@ def test_qkv_argument_validation():
     assert q([32, 32, 32], ys=[FAKE, None, FAKE]) == 1
     assert q([32, 32, 32], ys=[FAKE, FAKE + 1, FAKE]) == 4
     assert q([32, 32, 32], ldys=[32, 16, 32]) == 1
+    # destination windows that share a byte are refused before anything is enqueued
+    assert q([32, 32, 32], ys=[FAKE, FAKE, FAKE + 1024]) == 1            # same base
+    assert q([32, 32, 32], ys=[FAKE, FAKE + 62, FAKE + 1024]) == 1       # 1 bf16 column of row 0 shared
+    # slab rows: three windows interleaved in rows of 96 (row r of split i at 96r + 32i); a
+    # one-element shift makes row 0 of split 1 end inside row 0 of split 2
+    assert q([32, 32, 32], ys=[FAKE, FAKE + 66, FAKE + 128], ldys=[96, 96, 96]) == 1
+    # different strides: row 1 of the first window (stride 64) meets row 0 of the second
+    assert q([32, 32, 32], ys=[FAKE, FAKE + 2 * 64 + 8, FAKE + 4096], ldys=[64, 32, 32]) == 1
+    with pytest.raises(ValueError):
+        wq.wq_matmul_qkv(d, 2, FAKE, 256, FAKE, FAKE, None, [32, 32, 32], [FAKE, FAKE], [32, 32, 32], wq.WQ_BF16)
 
 
 def test_quantize_argument_validation():
