@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 
 #include "wq.h"
 #include "wq_launch.h"
@@ -130,6 +131,33 @@ wq_status run_matmul(const wq::MatmulProblem& p, void* stream) {
     return from_hip(p.m <= 16 ? wq::launch_gemv(p, s) : wq::launch_gemm(p, s));
 }
 
+// Device scratch of the allocation-free entry point: the fp32 partial sums of a K-split GEMM.
+// The split schedule never asks for more than 16 MiB (fewer than 128 output tiles of at
+// most 128 x 128, times at most 256 / tiles pieces, times 4 bytes).  Each GPU the library
+// runs on holds its own copy of this array from module load until the process ends.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The device address of the current device's copy of `scratch`, looked up once per device
+// with that device current.  In host code the array's name is only a host-side stand-in.
+wq_status scratch_for_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return WQ_ERR_HIP;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    if (g_scratch_err[dev] != hipSuccess || !g_scratch_ptr[dev]) return WQ_ERR_HIP;
+    *out = g_scratch_ptr[dev];
+    return WQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -199,6 +227,28 @@ wq_status wq_matmul(const wq_desc* d, int64_t m, const uint16_t* x, int64_t ldx,
     if (!y) return WQ_ERR_INVALID_ARG;
     if (!aligned(y, ydt == WQ_F32 ? 4 : 2)) return WQ_ERR_ALIGNMENT;
     if (ldy < p.n) return WQ_ERR_INVALID_ARG;
+    p.out.nsplit = 1;
+    p.out.y[0] = y;
+    p.out.ldy[0] = ldy;
+    p.out.end[0] = p.out.end[1] = p.out.end[2] = p.n;
+    return run_matmul(p, stream);
+}
+
+wq_status wq_matmul_noalloc(const wq_desc* d, int64_t m, const uint16_t* x, int64_t ldx, wq_packed w,
+                            const uint16_t* bias, void* y, int32_t ydt, int64_t ldy, void* stream) {
+    wq::MatmulProblem p{};
+    wq_status st = check_matmul(d, m, x, ldx, w, bias, ydt, nullptr, 0, &p);
+    if (st != WQ_OK) return st;
+    if (!y) return WQ_ERR_INVALID_ARG;
+    if (!aligned(y, ydt == WQ_F32 ? 4 : 2)) return WQ_ERR_ALIGNMENT;
+    if (ldy < p.n) return WQ_ERR_INVALID_ARG;
+    if (m == 0) return WQ_OK;
+    const size_t need = wq::matmul_workspace_bytes(p.fmt, p.m, p.n, p.k);
+    if (need > kScratchBytes) return WQ_ERR_WORKSPACE;
+    if (need > 0) {
+        if ((st = scratch_for_current_device(&p.ws)) != WQ_OK) return st;
+        p.ws_bytes = kScratchBytes;
+    }
     p.out.nsplit = 1;
     p.out.y[0] = y;
     p.out.ldy[0] = ldy;

@@ -21,7 +21,7 @@ WQ_NF4, WQ_NVFP4, WQ_Q4_0, WQ_Q8_0, WQ_Q4_1, WQ_Q5_0, WQ_Q4_K, WQ_Q6_K = 1, 2, 3
 WQ_BF16, WQ_F32 = 1, 2
 
 EXPORTS = ("wq_status_str", "wq_packed_size", "wq_quantize", "wq_dequantize",
-           "wq_workspace_size", "wq_matmul", "wq_matmul_qkv")
+           "wq_workspace_size", "wq_matmul", "wq_matmul_noalloc", "wq_matmul_qkv")
 
 # Format names accepted by the harness; aliases follow the NF4 option's names
 # ("asr: add a 4-bit nf4 option for the Whisper engine": nf4, aliases 4bit, int4).
@@ -82,6 +82,8 @@ def lib():
         L.wq_workspace_size.argtypes = [pd, i64, ctypes.POINTER(ctypes.c_size_t)]
         L.wq_matmul.restype = ctypes.c_int
         L.wq_matmul.argtypes = [pd, i64, P, i64, wq_packed, P, P, ctypes.c_int32, i64, P, ctypes.c_size_t, P]
+        L.wq_matmul_noalloc.restype = ctypes.c_int
+        L.wq_matmul_noalloc.argtypes = [pd, i64, P, i64, wq_packed, P, P, ctypes.c_int32, i64, P]
         L.wq_matmul_qkv.restype = ctypes.c_int
         L.wq_matmul_qkv.argtypes = [pd, i64, P, i64, wq_packed, P, ctypes.c_int32, ctypes.POINTER(i64),
                                     ctypes.POINTER(P), ctypes.POINTER(i64), ctypes.c_int32, P, ctypes.c_size_t, P]
@@ -148,6 +150,13 @@ def wq_matmul(d: wq_desc, m: int, x, ldx: int, codes, scales, bias, y, ydt: int,
     st = lib().wq_matmul(ctypes.byref(d), int(m), _ptr(x), int(ldx), wq_packed(_ptr(codes), _ptr(scales)),
                          _ptr(bias), _ptr(y), int(ydt), int(ldy), _ptr(ws), int(ws_bytes), _stream(stream))
     return _check(st, "wq_matmul", check)
+
+
+def wq_matmul_noalloc(d: wq_desc, m: int, x, ldx: int, codes, scales, bias, y, ydt: int, ldy: int,
+                      stream=None, check=True) -> int:
+    st = lib().wq_matmul_noalloc(ctypes.byref(d), int(m), _ptr(x), int(ldx), wq_packed(_ptr(codes), _ptr(scales)),
+                                 _ptr(bias), _ptr(y), int(ydt), int(ldy), _stream(stream))
+    return _check(st, "wq_matmul_noalloc", check)
 
 
 def wq_matmul_qkv(d: wq_desc, m: int, x, ldx: int, codes, scales, bias, split_n, ys, ldys, ydt: int,

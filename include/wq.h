@@ -181,6 +181,19 @@ wq_status wq_matmul(const wq_desc* d, int64_t m, const uint16_t* x, int64_t ldx,
                     const uint16_t* bias, void* y, int32_t ydt, int64_t ldy,
                     void* ws, size_t ws_bytes, void* stream);
 
+/* wq_matmul without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, layouts, bound and errors as wq_matmul.  The K-split
+ * partial sums go to a static device array of 16 MiB that the library holds on each
+ * GPU it runs on until the process ends; no call allocates or frees anything.  A
+ * shape whose split would need more than 16 MiB returns WQ_ERR_WORKSPACE (the current
+ * schedules never do).  Every call on one GPU shares that GPU's array: calls that may
+ * overlap on one GPU (different streams, or graphs replayed concurrently) race and
+ * must be ordered by the caller.  The first call on a device looks up that device's
+ * copy of the array (a HIP symbol query, no allocation); a failure returns WQ_ERR_HIP. */
+wq_status wq_matmul_noalloc(const wq_desc* d, int64_t m, const uint16_t* x, int64_t ldx, wq_packed w,
+                            const uint16_t* bias, void* y, int32_t ydt, int64_t ldy, void* stream);
+
 /* Fused projection over a row-concatenated weight W[n0 + n1 (+ n2), k] in one
  * pass over W (one kernel; a K-split GEMM adds one small reduction kernel):
  * columns [0, n0) go to y[0], [n0, n0+n1) to y[1], [n0+n1, n) to y[2],
