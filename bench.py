@@ -568,16 +568,25 @@ def main():
     print(json.dumps(result), flush=True)
 
 
+def source_digest(paths):
+    """sha256 over the named kernel sources (relative to the repository root), in order."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in paths:
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    return h.hexdigest()
+
+
 def measured_traffic(key, field="traffic_bytes_per_launch"):
     """HBM bytes (per launch, or per step for the encoder) from the committed rocprofv3
-    counter runs, or None when the kernel source changed since those counters were taken."""
-    import hashlib
+    counter runs, or None when the kernel sources changed since those counters were taken
+    (each record names its sources and their sha256)."""
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "traffic.json")))[key]
-        src = open(os.path.join(ROOT, "block_quantized_bit_amd", "csrc", "matmul.hip"), "rb").read()
-    except (OSError, KeyError, ValueError):
+        digest = source_digest(rec["sources"])
+    except (OSError, KeyError, ValueError, TypeError):
         return None
-    if hashlib.sha256(src).hexdigest() != rec.get("matmul_hip_sha256"):
+    if digest != rec.get("sources_sha256"):
         return None
     return rec[field]
 

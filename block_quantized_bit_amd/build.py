@@ -28,7 +28,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 SOURCES = [
     ("quant.hip", ["-ffp-contract=off"]),
-    ("matmul.hip", []),
+    ("gemv.hip", []),
+    ("gemm.hip", []),
     ("wq_api.cpp", ["-x", "hip"]),
 ]
 

@@ -1,0 +1,688 @@
+// gemv.hip -- the decode GEMV (m <= 16): the general kernel and the streaming kernel
+// for matrices far taller than the chip, with their launchers.
+#include "mm_common.h"
+
+namespace wq {
+
+// ===========================================================================
+template <int FMT>
+struct GemvTile {
+    uint4 code;             // this lane's 16 bytes of the tile
+    uint32_t sc[6];         // raw scale words (format dependent)
+    u32x4 A[tile_k(FMT) / 32];
+};
+
+constexpr int kGemvWaves = 8;   // waves per workgroup, all on one band, splitting its K range
+
+// Vector memory instructions gemv_load issues for a tile's codes and scales (X excluded; for
+// double quant with k <= 16384, plus two per band for the row's group scales -- a wait for at
+// most this many per tile outstanding can only wait longer than needed).
+template <int FMT, bool DQ>
+__device__ constexpr int gemv_w_loads() { return FMT == kQ6_K ? 4 : (FMT == kQ5_0 || FMT == kQ4_K) ? 3 : 2; }
+
+// Double-quant group scales of one row, when the row holds <= 256 blocks (k <= 16384) and so
+// spans at most two 256-block groups: blocks j < jt of the row are in the first.
+struct DqRow {
+    float dA, dB;
+    int32_t jt;
+};
+
+__device__ inline DqRow dq_row(const KArgs& a, int64_t row) {
+    const int64_t nbr = a.k / 64, b0 = row * nbr;
+    const int64_t gA = b0 >> 8, gB = (b0 + nbr - 1) >> 8;
+    const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
+    return DqRow{dt[gA], dt[gB], (int32_t)((gA + 1) * 256 - b0)};
+}
+
+// dq: non-null when the double-quant group scales come from the row's pair (DqRow) instead of
+// being gathered per tile.
+template <int FMT, bool DQ, bool XL = false>
+__device__ inline void gemv_load(GemvTile<FMT>& t, const KArgs& a, int64_t band, int64_t kt, int lane, int r,
+                                 const uint16_t* xrow, int64_t KT, const DqRow* dq = nullptr) {
+    constexpr int TK = tile_k(FMT);
+    const int64_t tile = band * KT + kt;
+    {
+        // weights are read exactly once: non-temporal
+        const u32x4 c = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.codes + tile * kTileBytes + lane * 16));
+        t.code = make_uint4(c[0], c[1], c[2], c[3]);
+    }
+    if constexpr (FMT == kNF4) {
+        if constexpr (DQ) {
+            t.sc[0] = *reinterpret_cast<const uint16_t*>(a.scales + tile * 32 + r * 2);
+            if (dq) {
+                // group scales: taken from the row's pair at use time (gemv_dq_scales)
+            } else {
+                const int64_t b0 = (band * 16 + r) * (a.k / 64) + kt * 2;
+                const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
+                t.sc[1] = __float_as_uint(dt[b0 >> 8]);
+                t.sc[2] = __float_as_uint(dt[(b0 + 1) >> 8]);
+            }
+        } else {
+            const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 32 + r * 2) * 4);
+            t.sc[0] = v.x;
+            t.sc[1] = v.y;
+        }
+    } else if constexpr (FMT == kQ4_0) {
+        const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 64 + r * 4) * 2);
+        t.sc[0] = v.x;
+        t.sc[1] = v.y;
+    } else if constexpr (FMT == kQ6_K) {
+        // the row's 8 sub-block scales, this lane's 8 bytes of bits 4-5 (after the n k / 2
+        // code bytes) and the super-block's d
+        const uint2 v = *reinterpret_cast<const uint2*>(a.scales + tile * 128 + r * 8);
+        t.sc[0] = v.x;
+        t.sc[1] = v.y;
+        const uint2 hb = *reinterpret_cast<const uint2*>(a.codes + a.n * a.k / 2 + tile * 512 + lane * 8);
+        t.sc[2] = hb.x;
+        t.sc[3] = hb.y;
+        t.sc[4] = *reinterpret_cast<const uint16_t*>(a.scales + a.L.kd_off + ((band * 16 + r) * (a.k >> 8) + (kt >> 1)) * 2);
+    } else if constexpr (FMT == kQ4_K) {
+        // the row's sub-block record (4 scale bytes, 4 offset bytes) and its super-block's
+        // (d, dmin); a 128-K tile is half a 256-K super-block
+        const uint2 v = *reinterpret_cast<const uint2*>(a.scales + tile * 128 + r * 8);
+        t.sc[0] = v.x;
+        t.sc[1] = v.y;
+        t.sc[2] = *reinterpret_cast<const uint32_t*>(a.scales + a.L.kd_off + ((band * 16 + r) * (a.k >> 8) + (kt >> 1)) * 4);
+    } else if constexpr (FMT == kQ5_0) {
+        // the row's four fp16 scales (8 bytes), then its four fifth-bit words (16 bytes)
+        const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 64 + r * 4) * 2);
+        t.sc[0] = v.x;
+        t.sc[1] = v.y;
+        const uint4 hb = *reinterpret_cast<const uint4*>(a.scales + a.L.hb_off + tile * 256 + r * 16);
+        t.sc[2] = hb.x;
+        t.sc[3] = hb.y;
+        t.sc[4] = hb.z;
+        t.sc[5] = hb.w;
+    } else if constexpr (FMT == kQ4_1) {
+        // the row's four (d, m) pairs of the tile: 16 bytes
+        const uint4 v = *reinterpret_cast<const uint4*>(a.scales + tile * 256 + r * 16);
+        t.sc[0] = v.x;
+        t.sc[1] = v.y;
+        t.sc[2] = v.z;
+        t.sc[3] = v.w;
+    } else if constexpr (FMT == kNVFP4) {
+        const uint2 v = *reinterpret_cast<const uint2*>(a.scales + tile * 128 + r * 8);
+        t.sc[0] = v.x;
+        t.sc[1] = v.y;
+    } else {
+        t.sc[0] = *reinterpret_cast<const uint32_t*>(a.scales + (tile * 32 + r * 2) * 2);
+    }
+    // rows r >= m read row 0 (always valid); their products only reach output rows that are never stored
+    if constexpr (!XL) {
+#pragma unroll
+        for (int j = 0; j < TK / 32; j++) {
+            const uint4 v = *reinterpret_cast<const uint4*>(xrow + kt * TK + 32 * j);
+            t.A[j] = u32x4{v.x, v.y, v.z, v.w};
+        }
+    }
+}
+
+// X (m rows of k bf16) copied once into LDS by LDS-direct loads of 16 bytes per lane,
+// chunk-major: chunk c (elements 8c .. 8c+7) of row r lands at byte 16 (c m + r).  The
+// 16 lanes that read one K chunk for 16 different rows (an A-operand read at m = 16)
+// then touch 256 contiguous bytes; row-major rows k * 2 bytes apart would all fall on
+// the same banks.  An LDS-direct load writes its lanes' chunks contiguously, and here
+// lane i of the copy fetches destination chunk i, so only the source addresses move.
+__device__ __forceinline__ void gemv_stage_x(uint16_t* xs, const KArgs& a, int wave, int lane) {
+    // the copy is used for m * k <= 32768 elements, so chunk indices fit 32 bits
+    const uint32_t m = (uint32_t)a.m;
+    const uint32_t nchunks = m * (uint32_t)(a.k / 8);
+    for (uint32_t c0 = (uint32_t)wave * 64; c0 < nchunks; c0 += 64 * kGemvWaves) {
+        const uint32_t i = c0 + (uint32_t)lane;
+        if (i < nchunks) {
+            const uint32_t c = m == 1 ? i : i / m, row = i - c * m;
+            __builtin_amdgcn_global_load_lds(a.x + (int64_t)row * a.ldx + (int64_t)c * 8, xs + c0 * 8, 16, 0, 0);
+        }
+    }
+}
+
+// NF4 and Q4_0 codes become bf16 pairs through the LDS table; NVFP4 and Q8_0
+// convert in registers.
+template <int FMT>
+__host__ __device__ constexpr bool gemv_uses_lut() { return FMT == kNF4 || FMT == kQ4_0; }
+
+template <int FMT, bool DQ, int NI>
+__device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const uint32_t* lut, uint32_t lane4,
+                                    int h, float mu) {
+    const uint32_t uw[4] = {t.code.x, t.code.y, t.code.z, t.code.w};
+    if constexpr (FMT == kNF4) {
+        float s0, s1;
+        if constexpr (DQ) {
+            s0 = __fadd_rn(__fmul_rn((float)(int8_t)(t.sc[0] & 255u), __uint_as_float(t.sc[1])), mu);
+            s1 = __fadd_rn(__fmul_rn((float)(int8_t)((t.sc[0] >> 8) & 255u), __uint_as_float(t.sc[2])), mu);
+        } else {
+            s0 = __uint_as_float(t.sc[0]);
+            s1 = __uint_as_float(t.sc[1]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; kb++) {
+            f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < 2; jj++) {
+                const int j = kb * 2 + jj;
+                u32x4 B;
+#pragma unroll
+                for (int q = 0; q < 4; q++) B[q] = lut_pair(lut, lane4, uw[j], q);
+                p = mfma(t.A[j], B, p);
+            }
+            const float s = kb ? s1 : s0;
+#pragma unroll
+            for (int i = 0; i < NI; i++) acc[i] += p[i] * s;
+        }
+    } else if constexpr (FMT == kQ4_0) {
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            u32x4 B;
+#pragma unroll
+            for (int q = 0; q < 4; q++) B[q] = lut_pair(lut, lane4, uw[j], q);
+            const f32x4 p = mfma(t.A[j], B, f32x4{0.f, 0.f, 0.f, 0.f});
+            const float s = f16_value((uint16_t)(t.sc[j >> 1] >> (16 * (j & 1))));
+#pragma unroll
+            for (int i = 0; i < NI; i++) acc[i] += p[i] * s;
+        }
+    } else if constexpr (FMT == kQ4_1) {
+        // B = bf16(w^), block j of the row for K slice j
+#pragma unroll
+        for (int j = 0; j < 4; j++) acc = mfma(t.A[j], q4_1_operand(uw[j], t.sc[j]), acc);
+    } else if constexpr (FMT == kQ6_K) {
+        // B = bf16(w^); K slice j spans sub-blocks 2j (h = 0, 1) and 2j + 1 (h = 2, 3)
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float S = q6_k_scale(t.sc[0], t.sc[1], t.sc[4], 2 * j + (h >> 1));
+            const uint32_t hw = t.sc[2 + (j >> 1)] >> (16 * (j & 1));
+            acc = mfma(t.A[j], q6_k_operand(uw[j], hw & 255u, (hw >> 8) & 255u, S), acc);
+        }
+    } else if constexpr (FMT == kQ4_K) {
+        // B = bf16(w^), sub-block j of the row for K slice j
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            float S, O;
+            q4_k_sub(t.sc[0], t.sc[1], t.sc[2], j, S, O);
+            acc = mfma(t.A[j], q4_k_operand(uw[j], S, O), acc);
+        }
+    } else if constexpr (FMT == kQ5_0) {
+        // B = bf16(w^), block j of the row for K slice j; this lane's k are bits 8h .. 8h+7
+        // of the block's fifth-bit word
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint16_t db = (uint16_t)(t.sc[j >> 1] >> (16 * (j & 1)));
+            acc = mfma(t.A[j], q5_0_operand(uw[j], (t.sc[2 + j] >> (8 * h)) & 255u, db), acc);
+        }
+    } else if constexpr (FMT == kNVFP4) {
+        // block 2j + (h >> 1) of the row: byte 2 (j & 1) + (h >> 1) of scale word j >> 1
+        const uint32_t hs = 8u * (uint32_t)(h >> 1);
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const uint32_t sw = t.sc[j >> 1] >> hs;
+            const float s = (j & 1) ? __builtin_amdgcn_cvt_f32_fp8((int)sw, 2) : __builtin_amdgcn_cvt_f32_fp8((int)sw, 0);
+            u32x4 B;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                // e2m1 pair of byte q (low nibble first) times the E4M3 scale: exact, so keeping
+                // the upper halves of the fp32 products is the exact bf16 value
+                f32x2 v;
+                if (q == 0) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(uw[j], 1.0f, 0);
+                else if (q == 1) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(uw[j], 1.0f, 1);
+                else if (q == 2) v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(uw[j], 1.0f, 2);
+                else v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(uw[j], 1.0f, 3);
+                B[q] = __builtin_amdgcn_perm(__float_as_uint(v[1] * s), __float_as_uint(v[0] * s), 0x07060302u);
+            }
+            acc = mfma(t.A[j], B, acc);
+        }
+    } else {  // kQ8_0: 16 x 64 tile, K slices j = 0, 1
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            u32x4 B;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const uint32_t wv = uw[2 * j + (q >> 1)];
+                const int sh = 16 * (q & 1);
+                const float f0 = (float)(int)(int8_t)(wv >> sh);
+                const float f1 = (float)(int)(int8_t)(wv >> (sh + 8));
+                B[q] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+            }
+            const f32x4 p = mfma(t.A[j], B, f32x4{0.f, 0.f, 0.f, 0.f});
+            const float s = f16_value((uint16_t)(t.sc[0] >> (16 * j)));
+#pragma unroll
+            for (int i = 0; i < NI; i++) acc[i] += p[i] * s;
+        }
+    }
+}
+
+// Wave w of a workgroup owns tiles w, w + 8, w + 16, ... of its band's K range:
+// C of them, all requested before any is used.  A band is finished by summing
+// the 8 waves' 16x16 partial tiles in LDS in wave order.
+// Double quant with fewer than 8 tiles per wave (k <= 5120 here) takes the row's two group
+// scales once per band (DqRow) instead of two gathers per tile.
+template <int FMT, bool DQ, int C>
+__device__ constexpr bool gemv_dq_rows() { return FMT == kNF4 && DQ && C < 8; }
+
+// The row's double-quant group scales (and, when mu is non-null, the matrix mean) are
+// requested right after the first tile: the first tile's use needs them, and a wait for
+// everything older than the band's requests (the X copy) does not wait for them.
+template <int FMT, bool DQ, int C, bool XL>
+__device__ __forceinline__ void gemv_load_band(GemvTile<FMT> (&R)[C], DqRow& dq, const KArgs& a, int64_t band,
+                                               int64_t c0, int wave, int lane, int r, const uint16_t* xrow,
+                                               int64_t KT, float* mu = nullptr) {
+    constexpr bool DR = gemv_dq_rows<FMT, DQ, C>();
+#pragma unroll
+    for (int s = 0; s < C; s++) {
+        const int64_t kt = std::min<int64_t>(wave + (c0 + s) * kGemvWaves, KT - 1);
+        gemv_load<FMT, DQ, XL>(R[s], a, band, kt, lane, r, xrow, KT, DR ? &dq : nullptr);
+        if (s == 0) {
+            if constexpr (DR) dq = dq_row(a, band * 16 + r);
+            if constexpr (FMT == kNF4 && DQ) {
+                if (mu) *mu = load_f32_vmem(a.scales + a.L.mu_off);
+            }
+        }
+    }
+}
+
+// Register loads a band request issues: C tiles, plus the row's two group scales.
+template <int FMT, bool DQ, int C>
+__device__ constexpr int gemv_band_loads() { return C * gemv_w_loads<FMT, DQ>() + (gemv_dq_rows<FMT, DQ, C>() ? 2 : 0); }
+
+// XL: the A operands come from the LDS copy of X (xl = this lane's row, chunk h), read here.
+template <int FMT, bool DQ, int NI, int C, bool XL>
+__device__ __forceinline__ void gemv_consume_band(GemvTile<FMT> (&R)[C], const DqRow& dq, f32x4& acc, int64_t c0,
+                                                  int wave, int64_t KT, const uint32_t* lut, uint32_t lane4, int h,
+                                                  float mu, const uint16_t* xl, int64_t xm8) {
+    constexpr int TK = tile_k(FMT);
+#pragma unroll
+    for (int s = 0; s < C; s++) {
+        const int64_t kt = wave + (c0 + s) * kGemvWaves;
+        if (kt < KT) {
+            if constexpr (gemv_dq_rows<FMT, DQ, C>()) {
+                R[s].sc[1] = __float_as_uint(2 * kt < dq.jt ? dq.dA : dq.dB);
+                R[s].sc[2] = __float_as_uint(2 * kt + 1 < dq.jt ? dq.dA : dq.dB);
+            }
+            if constexpr (XL) {
+#pragma unroll
+                for (int j = 0; j < TK / 32; j++) {
+                    // chunk kt TK / 8 + 4 j + h of this lane's row, chunk-major (gemv_stage_x)
+                    const uint4 v = *reinterpret_cast<const uint4*>(xl + (kt * (TK / 8) + 4 * j) * xm8);
+                    R[s].A[j] = u32x4{v.x, v.y, v.z, v.w};
+                }
+            }
+            gemv_consume<FMT, DQ, NI>(R[s], acc, lut, lane4, h, mu);
+        }
+    }
+}
+
+__device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kGemvWaves][64], const f32x4& acc,
+                                                 int64_t band, int wave, int lane, float g) {
+    const int r = lane & 15, h = lane >> 4;
+    red[wave][lane] = acc;
+    __syncthreads();
+    if (wave == 0) {
+        f32x4 v = red[0][lane];
+#pragma unroll
+        for (int w = 1; w < kGemvWaves; w++) v += red[w][lane];
+        const ColOut c = col_out(a, band * 16 + r);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int mm = 4 * h + i;
+            if (mm < a.m) put_out(a, c, mm, v[i], g);
+        }
+    }
+    __syncthreads();
+}
+
+// PIPE = false: every workgroup owns one band (grid == number of bands), its
+//   tiles come in rounds of C per wave (one round when K <= 8 * C tiles).
+// PIPE = true : workgroups loop over bands; each wave holds all its tiles of a
+//   band in one round (K <= 8 * C tiles) and requests the next band's tiles
+//   before using the current ones.  The prefetch index is clamped to the last
+//   band, so the requests are unconditional.
+// XL: X is copied once into (dynamic) LDS at the start -- a few LDS-direct loads
+//   per workgroup instead of four 64-lane loads per tile and wave -- and the A
+//   operands are read from there; used when m * k is small (decode).  The copy
+//   is requested before the weights, so waiting for it (vmcnt = the weight loads
+//   issued after it) never waits for a weight load.
+template <int FMT, bool DQ, int NI, int C, bool PIPE, bool XL>
+__global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArgs a) {
+    __shared__ uint32_t lut[gemv_uses_lut<FMT>() ? kLutWords : 1];
+    __shared__ f32x4 red[kGemvWaves][64];
+    extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15;
+    const int h = lane >> 4;
+    const uint32_t lane4 = (uint32_t)lane << 2;
+    const int64_t KT = a.k / tile_k(FMT);
+    const int64_t nbands = a.n / 16;
+
+    // The double-quant mean sits with the scales, in memory as cold as the weights.  With X
+    // copied to LDS it is requested with the first band's tiles (after the copy), so that
+    // the wait for the copy does not wait for it; without the copy, up front.
+    float g = 1.0f, mu = 0.0f;
+    if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.scales + a.L.g_off);
+    if constexpr (FMT == kNF4 && DQ && !XL) mu = load_f32_vmem(a.scales + a.L.mu_off);
+    constexpr int kMuLoads = (FMT == kNF4 && DQ && XL) ? 1 : 0;
+    float* const mu_first = kMuLoads ? &mu : nullptr;
+    const uint16_t* xrow = a.x + (int64_t)(r < a.m ? r : 0) * a.ldx + h * 8;
+    // the LDS copy of X is chunk-major: chunk c of row r at element 8 (c m + r); the
+    // one-token instantiation (NI = 1 is only launched for m = 1) gets a constant stride,
+    // so its reads keep immediate offsets
+    const int64_t xm8 = NI == 1 ? 8 : (int64_t)a.m * 8;
+    const uint16_t* xl = xs_dyn + (int64_t)h * xm8 + (int64_t)(r < a.m ? r : 0) * 8;
+    const int64_t per_wave = (KT + kGemvWaves - 1) / kGemvWaves;
+
+    if constexpr (!PIPE) {
+        const int64_t band = blockIdx.x;
+        // With XL the code table is filled first: LDS writes issued while the LDS-direct X copy
+        // is in flight would have to wait for every load.  Otherwise it is filled while the first
+        // tiles are in flight.
+        if constexpr (XL) {
+            if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
+            gemv_stage_x(xs_dyn, a, wave, lane);
+        }
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int64_t c0 = 0; c0 < per_wave; c0 += C) {
+            GemvTile<FMT> R[C];
+            DqRow dq;
+            gemv_load_band<FMT, DQ, C, XL>(R, dq, a, band, c0, wave, lane, r, xrow, KT, c0 == 0 ? mu_first : nullptr);
+            if (c0 == 0) {
+                if constexpr (XL) {
+                    lds_barrier_vm<gemv_band_loads<FMT, DQ, C>() + kMuLoads>();
+                } else {
+                    if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
+                    __syncthreads();
+                }
+            }
+            gemv_consume_band<FMT, DQ, NI, C, XL>(R, dq, acc, c0, wave, KT, lut, lane4, h, mu, xl, xm8);
+        }
+        gemv_finish_band(a, red, acc, band, wave, lane, g);
+    } else {
+        const int64_t stride = gridDim.x;
+        GemvTile<FMT> R0[C], R1[C];
+        DqRow dq0, dq1;
+        int64_t band = blockIdx.x;
+        if constexpr (XL) {
+            if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
+            gemv_stage_x(xs_dyn, a, wave, lane);
+        }
+        gemv_load_band<FMT, DQ, C, XL>(R0, dq0, a, band, 0, wave, lane, r, xrow, KT, mu_first);
+        if constexpr (XL) {
+            lds_barrier_vm<gemv_band_loads<FMT, DQ, C>() + kMuLoads>();
+        } else {
+            if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
+            __syncthreads();
+        }
+        for (; band < nbands; band += 2 * stride) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            gemv_load_band<FMT, DQ, C, XL>(R1, dq1, a, std::min<int64_t>(band + stride, nbands - 1), 0, wave, lane,
+                                          r, xrow, KT);
+            gemv_consume_band<FMT, DQ, NI, C, XL>(R0, dq0, acc, 0, wave, KT, lut, lane4, h, mu, xl, xm8);
+            gemv_finish_band(a, red, acc, band, wave, lane, g);
+            if (band + stride >= nbands) break;
+            acc = f32x4{0.f, 0.f, 0.f, 0.f};
+            gemv_load_band<FMT, DQ, C, XL>(R0, dq0, a, std::min<int64_t>(band + 2 * stride, nbands - 1), 0, wave,
+                                          lane, r, xrow, KT);
+            gemv_consume_band<FMT, DQ, NI, C, XL>(R1, dq1, acc, 0, wave, KT, lut, lane4, h, mu, xl, xm8);
+            gemv_finish_band(a, red, acc, band + stride, wave, lane, g);
+        }
+    }
+}
+
+// ===========================================================================
+// Streaming GEMV (many more bands than workgroups, short K, small X): each wave
+// owns whole bands, so there is no cross-wave reduction and no barrier in the
+// loop.  A band's T tiles are requested one band ahead into the other of two
+// register sets.  Loads are buffer loads whose base is the band's first tile
+// (wave-uniform, scalar arithmetic) with a per-lane offset fixed for the whole
+// kernel, so addressing costs no vector instructions; the descriptor covers
+// exactly the band's K tiles, so slots s >= K/tile_k read zeros (the buffer
+// range check) and take their A operand from a zero row.  X is staged once per
+// workgroup in LDS and read there as the MFMA A operand; the double-quant
+// group scales of a lane's row are fetched once per band (a row of <= 10 tiles
+// spans at most two 256-block groups).
+// ===========================================================================
+constexpr int kStreamXMax = 8192 - 128;   // bf16 elements of X staged in LDS (m * k), then 128 zeros
+
+// Scale bytes per tile and per lane (one row of the tile) in the packed layout.
+template <int FMT, bool DQ>
+__device__ constexpr int tile_scale_bytes() {
+    return FMT == kQ8_0 ? 64 : (FMT == kNF4 && DQ) ? 32 : 128;
+}
+
+struct StreamTile {
+    u32x4 code;
+    uint32_t sc[2];
+};
+
+struct StreamBand {
+    uint32_t braw;     // bias (bf16 bits) of this lane's column
+    float dA, dB;      // double quant: group scales of the first / last block of the lane's row
+    int32_t jt;        // double quant: blocks of the row that belong to group A
+};
+
+template <int FMT, bool DQ, int T>
+__device__ __forceinline__ void stream_load_band(StreamTile (&R)[T], StreamBand& B, const KArgs& a, int64_t band,
+                                                 int lane, int r, int64_t KT) {
+    constexpr int SB = tile_scale_bytes<FMT, DQ>();
+    const BufRes rc = buf_res(a.codes + band * KT * kTileBytes, (uint32_t)(KT * kTileBytes));
+    const BufRes rs = buf_res(a.scales + band * KT * SB, (uint32_t)(KT * SB));
+#pragma unroll
+    for (int s = 0; s < T; s++) {
+        R[s].code = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16 + s * kTileBytes, 0, kNT));
+        if constexpr (FMT == kNF4 && DQ) {
+            R[s].sc[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, r * 2 + s * SB, 0, kNT);
+        } else if constexpr (FMT == kQ8_0) {
+            R[s].sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, r * 4 + s * SB, 0, kNT);
+        } else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, r * 8 + s * SB, 0, kNT);
+            R[s].sc[0] = v[0];
+            R[s].sc[1] = v[1];
+        }
+    }
+    const int64_t col = band * 16 + r;
+    B.braw = a.bias ? (uint32_t)a.bias[col] : 0u;
+    if constexpr (FMT == kNF4 && DQ) {
+        const int64_t nbr = a.k / 64;                 // blocks per row
+        const int64_t b0 = col * nbr;                 // first block of the row
+        const int64_t gA = b0 >> 8, gB = (b0 + nbr - 1) >> 8;
+        const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
+        B.dA = dt[gA];
+        B.dB = dt[gB];
+        B.jt = (int32_t)((gA + 1) * 256 - b0);
+    }
+}
+
+template <int FMT, bool DQ, int NI, int T>
+__device__ __forceinline__ void stream_band(const StreamTile (&R)[T], const StreamBand& B, const KArgs& a,
+                                            int64_t band, const uint16_t* xrow, const uint16_t* xzero, int h,
+                                            uint32_t lane4, const uint32_t* lut, float mu, float g, int64_t KT) {
+    constexpr int TK = tile_k(FMT);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < T; s++) {
+        {
+            GemvTile<FMT> t;
+            t.code = make_uint4(R[s].code[0], R[s].code[1], R[s].code[2], R[s].code[3]);
+            t.sc[0] = R[s].sc[0];
+            t.sc[1] = R[s].sc[1];
+            if constexpr (FMT == kNF4 && DQ) {
+                t.sc[1] = __float_as_uint(2 * s < B.jt ? B.dA : B.dB);
+                t.sc[2] = __float_as_uint(2 * s + 1 < B.jt ? B.dA : B.dB);
+            }
+            // rows r >= m read row 0: their products only reach output rows that are never stored
+            const uint16_t* xp = s < KT ? xrow + s * TK : xzero;
+#pragma unroll
+            for (int j = 0; j < TK / 32; j++) {
+                const uint4 v = *reinterpret_cast<const uint4*>(xp + 32 * j);
+                t.A[j] = u32x4{v.x, v.y, v.z, v.w};
+            }
+            gemv_consume<FMT, DQ, NI>(t, acc, lut, lane4, h, mu);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep tiles in order: bounded register use
+    }
+    // lane (h, r) holds rows 4h .. 4h+3 of column band * 16 + r
+    ColOut c = col_out_nobias(a, band * 16 + (__lane_id() & 15));
+    c.bias = bf16_value((uint16_t)B.braw);
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        const int mm = 4 * h + i;
+        if (mm < a.m) put_out(a, c, mm, acc[i], g);
+    }
+}
+
+template <int FMT, bool DQ, int NI, int T>
+__global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
+    __shared__ uint32_t lut[gemv_uses_lut<FMT>() ? kLutWords : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kStreamXMax + 128];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15;
+    const int h = lane >> 4;
+    const uint32_t lane4 = (uint32_t)lane << 2;
+    const int64_t KT = a.k / tile_k(FMT);
+    const int64_t nbands = a.n / 16;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+
+    float g = 1.0f, mu = 0.0f;
+    if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.scales + a.L.g_off);
+    if constexpr (FMT == kNF4 && DQ) mu = load_f32_vmem(a.scales + a.L.mu_off);
+
+    int64_t band = (int64_t)blockIdx.x * 4 + wave;
+    StreamTile R0[T], R1[T];
+    StreamBand B0, B1;
+    stream_load_band<FMT, DQ, T>(R0, B0, a, std::min<int64_t>(band, nbands - 1), lane, r, KT);
+    // stage X (m rows of k bf16, rows contiguous in LDS) and the zero row
+    if (tid < 16) *reinterpret_cast<uint4*>(xs + kStreamXMax + tid * 8) = make_uint4(0u, 0u, 0u, 0u);
+    const int64_t nx = (int64_t)a.m * a.k;
+    for (int64_t i = (int64_t)tid * 8; i < nx; i += 256 * 8) {
+        const int64_t row = i / a.k, col = i - row * a.k;
+        *reinterpret_cast<uint4*>(xs + i) = *reinterpret_cast<const uint4*>(a.x + row * a.ldx + col);
+    }
+    if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 256>(lut);
+    __syncthreads();
+    const uint16_t* xrow = xs + (r < a.m ? r : 0) * a.k + h * 8;
+    const uint16_t* xzero = xs + kStreamXMax + h * 8;
+
+    for (; band < nbands; band += 2 * stride) {
+        stream_load_band<FMT, DQ, T>(R1, B1, a, std::min<int64_t>(band + stride, nbands - 1), lane, r, KT);
+        stream_band<FMT, DQ, NI, T>(R0, B0, a, band, xrow, xzero, h, lane4, lut, mu, g, KT);
+        if (band + stride >= nbands) break;
+        stream_load_band<FMT, DQ, T>(R0, B0, a, std::min<int64_t>(band + 2 * stride, nbands - 1), lane, r, KT);
+        stream_band<FMT, DQ, NI, T>(R1, B1, a, band + stride, xrow, xzero, h, lane4, lut, mu, g, KT);
+    }
+}
+
+constexpr int64_t kStreamMinBands = 4 * 2 * 4 * kNumCU;   // bands per wave x waves
+
+size_t gemv_workspace_bytes(int, int64_t, int64_t, int64_t) { return 0; }
+
+size_t matmul_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k) {
+    return m <= 16 ? gemv_workspace_bytes(fmt, m, n, k) : gemm_workspace_bytes(fmt, m, n, k);
+}
+
+// Tiles per wave per round: the smallest offered count covering the band's K
+// range in one round (K <= 64 tiles), else rounds of 8.
+static int gemv_chunk(int64_t KT) {
+    const int64_t pw = (KT + kGemvWaves - 1) / kGemvWaves;
+    return pw <= 1 ? 1 : pw <= 2 ? 2 : pw <= 4 ? 4 : pw <= 5 ? 5 : 8;
+}
+
+constexpr int64_t kGemvXlMax = 32768;   // bf16 elements of X (m * k) copied to LDS by the decode GEMV
+
+// Two workgroups per CU for the small-C kernels (<= 128 VGPRs) when their LDS fits twice:
+// with a code table, an X copy of at most 8 KiB; without one, the reduction buffer and the
+// X copy twice in the CU's 160 KiB.
+template <int FMT, int C>
+static bool gemv_two_per_cu(size_t xbytes) {
+    constexpr size_t kLdsPerCu = 160 * 1024;
+    const size_t red = sizeof(f32x4) * kGemvWaves * 64;
+    if (C > 2) return false;
+    return gemv_uses_lut<FMT>() ? xbytes <= 8192 : 2 * (red + 16 + xbytes) <= kLdsPerCu;
+}
+
+template <int FMT, bool DQ, int NI, int C, bool XL>
+static void gemv_launch_cx(const KArgs& a, int64_t nbands, int64_t KT, hipStream_t st) {
+    const dim3 block(64 * kGemvWaves);
+    const size_t xbytes = XL ? (size_t)a.m * (size_t)a.k * 2 : 0;
+    const int64_t per_cu = gemv_two_per_cu<FMT, C>(xbytes) ? 2 : 1;
+    // band pipelining only where its two register sets fit without spilling (C <= 2), and only
+    // when the bands outnumber the workgroups that fit at once
+    if constexpr (C <= 2) {
+        const int64_t resident = per_cu * (int64_t)kNumCU;
+        if (nbands > resident && (KT + kGemvWaves - 1) / kGemvWaves <= C) {
+            hipLaunchKernelGGL((k_gemv<FMT, DQ, NI, C, true, XL>), dim3((unsigned)resident), block, xbytes, st, a);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((k_gemv<FMT, DQ, NI, C, false, XL>), dim3((unsigned)nbands), block, xbytes, st, a);
+}
+
+// The LDS copy of X is used when it is small enough, when every band gets its own workgroup
+// (no band pipelining: its per-band barriers would wait for the prefetched band's loads), and
+// when it either keeps two workgroups per CU (<= 8 KiB) or the bands fit one per CU anyway.
+template <int FMT, bool DQ, int NI, int C>
+static void gemv_launch_c(const KArgs& a, int64_t nbands, int64_t KT, hipStream_t st) {
+    const int64_t mk = (int64_t)a.m * a.k;
+    // The X copy when all bands run in one round of resident workgroups.  The table formats
+    // fit one workgroup per CU with a larger copy; from 12 tokens on, the copy with two bands
+    // pipelined per workgroup beats reading 12-16 rows of X from L2 per tile (measured at the
+    // fc1 shape, 320 bands: 8 tokens 5.3 vs 5.4 us, 12 tokens 6.1 vs 5.7, 16 tokens 6.7 vs 6.1).
+    const bool xl = mk <= kGemvXlMax && nbands <= 2 * kNumCU &&
+                    (mk * 2 <= 8192 || nbands <= kNumCU || (!gemv_uses_lut<FMT>() && gemv_two_per_cu<FMT, C>((size_t)mk * 2)) ||
+                     (gemv_uses_lut<FMT>() && C <= 2 && a.m >= 12));
+    if (xl) gemv_launch_cx<FMT, DQ, NI, C, true>(a, nbands, KT, st);
+    else gemv_launch_cx<FMT, DQ, NI, C, false>(a, nbands, KT, st);
+}
+
+template <int FMT, bool DQ, int NI>
+static void gemv_launch_ni(const KArgs& a, hipStream_t st) {
+    const int64_t KT = a.k / tile_k(FMT);
+    const int64_t nbands = a.n / 16;
+    // Many more bands than resident waves, K <= 10 tiles, X fits in LDS: the
+    // streaming kernel (two workgroups of 4 waves per CU, each wave >= 4 bands).
+    // (q4_1, q5_0, q4_k and q6_k have no streaming variant: their wider scale records take
+    // the general kernel)
+    if constexpr (FMT != kQ4_1 && FMT != kQ5_0 && FMT != kQ4_K && FMT != kQ6_K) {
+        if (nbands >= kStreamMinBands && (int64_t)a.m * a.k <= kStreamXMax && KT <= 10) {
+            const unsigned grid = 2 * kNumCU;
+            if (KT <= 4) hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 4>), dim3(grid), dim3(256), 0, st, a);
+            else hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 10>), dim3(grid), dim3(256), 0, st, a);
+            return;
+        }
+    }
+    switch (gemv_chunk(KT)) {
+    case 1: gemv_launch_c<FMT, DQ, NI, 1>(a, nbands, KT, st); break;
+    case 2: gemv_launch_c<FMT, DQ, NI, 2>(a, nbands, KT, st); break;
+    case 4: gemv_launch_c<FMT, DQ, NI, 4>(a, nbands, KT, st); break;
+    case 5: gemv_launch_c<FMT, DQ, NI, 5>(a, nbands, KT, st); break;
+    default: gemv_launch_c<FMT, DQ, NI, 8>(a, nbands, KT, st); break;
+    }
+}
+
+template <int FMT, bool DQ>
+static void gemv_dispatch_ni(const KArgs& a, hipStream_t st) {
+    // one token updates one accumulator row per lane; more tokens update all four
+    if (a.m == 1) gemv_launch_ni<FMT, DQ, 1>(a, st);
+    else gemv_launch_ni<FMT, DQ, 4>(a, st);
+}
+
+hipError_t launch_gemv(const MatmulProblem& p, hipStream_t st) {
+    const KArgs a = make_args(p);
+    switch (p.fmt) {
+    case kNF4:
+        if (p.dq) gemv_dispatch_ni<kNF4, true>(a, st);
+        else gemv_dispatch_ni<kNF4, false>(a, st);
+        break;
+    case kNVFP4: gemv_dispatch_ni<kNVFP4, false>(a, st); break;
+    case kQ4_0: gemv_dispatch_ni<kQ4_0, false>(a, st); break;
+    case kQ4_1: gemv_dispatch_ni<kQ4_1, false>(a, st); break;
+    case kQ5_0: gemv_dispatch_ni<kQ5_0, false>(a, st); break;
+    case kQ4_K: gemv_dispatch_ni<kQ4_K, false>(a, st); break;
+    case kQ6_K: gemv_dispatch_ni<kQ6_K, false>(a, st); break;
+    case kQ8_0: gemv_dispatch_ni<kQ8_0, false>(a, st); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace wq

@@ -1,0 +1,439 @@
+// mm_common.h -- shared by the matmul kernels (gemv.hip, gemm.hip): Y = X * W^T + b with W kept packed and dequantized inside the
+// kernel (the fused dequant-matmul: "asr: add a 4-bit nf4 option for the Whisper
+// engine", "Why NF4 and not the NVFP4 snapshot Parakeet ships"; W4A16 GEMM:
+// "mbehr90/whisper-large-v3-turbo-nvfp4", "What is quantized").
+//
+// Both kernels use the gfx950 16x16x32 bf16 MFMA.  The packed layout puts, in
+// each 16-byte slot of a 16x128 weight tile, exactly the 8 consecutive-k values a
+// lane supplies as its B operand for each of the tile's four 32-wide K slices,
+// so a wave turns one 1 KiB tile load (64 lanes x 16 B, fully coalesced) into
+// four MFMA B operands without any data exchange.
+//
+// NF4 codes (and q4_0 codes in the GEMV) are decoded through byte-indexed tables
+// in LDS (one entry per code byte, i.e. two values per lookup), replicated per
+// lane so that concurrent lookups of different bytes hit different banks; the LDS
+// address is built with one v_perm_b32.  The GEMV table holds bf16 values (fed
+// straight to the MFMA), the GEMM table fp32 values (scaled exactly, then rounded
+// once to bf16).  NVFP4 codes and scales are decoded with the gfx950 fp4 / fp8
+// conversion instructions; q8_0 bytes, q4_1, q5_0, q4_k and q6_k codes (and
+// q4_0 nibbles in the GEMM) are converted to floats in registers.
+//
+// GEMV (m <= 16, decode): B = raw code values (NF4 level, q4_0 q-8, q8_0 q),
+//   the per-block scale is applied to the MFMA partial sum of each block; for
+//   NVFP4 (16-value blocks, two per 32-K slice) B = e2m1*scale (exact in bf16);
+//   for q4_1 (scale and minimum), q5_0 (fifth bits), q4_k and q6_k (two-level
+//   scales) B = bf16(w^) as in the GEMM.
+//   K is split over the waves of a workgroup and reduced in LDS.
+// GEMM (m >= 17, encoder): each wave dequantizes 64 columns x 128 K of W per
+//   step to bf16(w^) -- w^ computed exactly as the format defines it, then one
+//   round-to-nearest-even -- straight into MFMA B registers; the X tile
+//   (128 x 128 bf16) is shared through LDS.  Few output tiles split K across
+//   workgroups into an fp32 workspace, summed in order by a second kernel.
+#pragma once
+
+#include "wq_device.h"
+#include "wq_launch.h"
+
+#include <algorithm>
+
+namespace wq {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kLutWords = 256 * 64;   // 256 byte values x 64 lane slots
+
+struct KArgs {
+    const uint16_t* x;
+    int64_t ldx;
+    int m;
+    int64_t n, k;
+    const uint8_t* codes;
+    const uint8_t* scales;
+    const uint16_t* bias;
+    OutSplit out;
+    ScaleLayout L;
+    int ksplit;          // K pieces per output tile
+    int64_t kt_per;      // K tiles (of tile_k) per piece
+    float* partial;      // [ksplit][m][n] when ksplit > 1
+    int64_t tiles_m, tiles_n;
+    int out_vec;         // every output split allows 4-column vector stores (alignment, split ends % 4)
+    int out_v16;         // bf16 output whose splits allow 8-column (16-byte) stores
+};
+
+// One fp32 value at a uniform address (the NVFP4 global scale, the double-quant mean),
+// read with a vector buffer load.  A plain read of a uniform address becomes a scalar
+// load, and scalar loads share one wait counter with the kernel-argument loads: the
+// kernel's first wait for an argument would then also wait for this value's trip to
+// memory, before any weight load is issued.
+__device__ inline float load_f32_vmem(const uint8_t* p) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p), (short)0, 4, 0x00020000);
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, 0, 0, 0));
+}
+
+// NF4 level of code c as a 16-way select over literals.  Table fills use these
+// rather than indexing the level arrays: a per-lane index would turn into a
+// vector memory load, and waiting for it would also wait for every weight load
+// already in flight.
+__device__ inline uint32_t nf4_level_bf16_sel(uint32_t c) {
+    uint32_t v = kNf4LevelBf16[0];
+#pragma unroll
+    for (uint32_t i = 1; i < 16; i++) v = ((c & 15u) == i) ? (uint32_t)kNf4LevelBf16[i] : v;
+    return v;
+}
+
+__device__ inline float nf4_level_sel(uint32_t c) {
+    uint32_t v = kNf4LevelBits[0];
+#pragma unroll
+    for (uint32_t i = 1; i < 16; i++) v = ((c & 15u) == i) ? kNf4LevelBits[i] : v;
+    return __uint_as_float(v);
+}
+
+// bf16 image of a 4-bit code's value (before any block scale).
+template <int FMT>
+__device__ inline uint32_t code_bf16(uint32_t c) {
+    if constexpr (FMT == kNF4) {
+        return nf4_level_bf16_sel(c);
+    } else if constexpr (FMT == kQ4_0) {
+        return __float_as_uint((float)((int)(c & 15u) - 8)) >> 16;          // exact
+    } else {  // NVFP4
+        float v = e2m1_mag_value(c & 7u);
+        if (c & 8u) v = -v;
+        return __float_as_uint(v) >> 16;                                       // exact
+    }
+}
+
+// Fill the replicated byte table: word (e * 64 + slot) = bf16(lo nibble) | bf16(hi nibble) << 16,
+// e = 16 * hi + lo.  Thread t (of NT = 256 or 512) owns 4 slots of entries with
+// lo = (t >> 4) & 15 and hi = t >> 8 (mod NT / 256): the lo value is looked up
+// once, the hi value is the same for a whole wave.
+template <int FMT, int NT>
+__device__ inline void build_lut(uint32_t* lut) {
+    static_assert(NT == 256 || NT == 512, "table fill for blocks of 256 or 512 threads");
+    const int t = threadIdx.x;
+    const int slot4 = (t & 15) * 4;
+    const uint32_t lo = (t >> 4) & 15;
+    const uint32_t vlo = code_bf16<FMT>(lo);
+    const uint32_t hsub = __builtin_amdgcn_readfirstlane(t >> 8);
+#pragma unroll
+    for (uint32_t h0 = 0; h0 < 16; h0 += NT / 256) {
+        const uint32_t hi = h0 + hsub;
+        uint32_t vhi = code_bf16<FMT>(h0);
+        if constexpr (NT == 512) vhi = hsub ? code_bf16<FMT>(h0 + 1) : vhi;
+        const uint32_t v = vlo | (vhi << 16);
+        *reinterpret_cast<uint4*>(lut + (hi * 16 + lo) * 64 + slot4) = make_uint4(v, v, v, v);
+    }
+}
+
+// Two bf16 code values for byte p of `word`, from lane `lane4/4`'s copy of the table.
+__device__ inline uint32_t lut_pair(const uint32_t* lut, uint32_t lane4, uint32_t word, int p) {
+    // address = (byte_p << 8) | (lane << 2): byte 0 from lane4, byte 1 from word's byte p
+    const uint32_t addr = __builtin_amdgcn_perm(lane4, word, 0x0C0C0004u | ((uint32_t)p << 8));
+    return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(lut) + addr);
+}
+
+// fp32 value of a 4-bit code (before any block scale); exact for every format.
+template <int FMT>
+__device__ inline float code_f32(uint32_t c) {
+    if constexpr (FMT == kNF4) {
+        return nf4_level_sel(c);
+    } else if constexpr (FMT == kQ4_0) {
+        return (float)((int)(c & 15u) - 8);
+    } else {  // NVFP4
+        const float v = e2m1_mag_value(c & 7u);
+        return (c & 8u) ? -v : v;
+    }
+}
+
+// Replicated byte -> (fp32 lo-nibble value, fp32 hi-nibble value) table with 32
+// lane copies: pair (e, slot) at byte offset e * 256 + slot * 8.
+template <int FMT>
+__device__ inline void build_lut_f32(uint32_t* lut) {
+    const int t = threadIdx.x;             // 256 threads: entry 16 * hi + lo with lo = t >> 4
+    const int slot = (t & 15) * 2;
+    const uint32_t lo = __float_as_uint(code_f32<FMT>((uint32_t)t >> 4));
+#pragma unroll
+    for (uint32_t e0 = 0; e0 < 256; e0 += 16) {
+        const uint32_t hi = __float_as_uint(code_f32<FMT>(e0 >> 4));
+        *reinterpret_cast<uint4*>(lut + (e0 + (t >> 4)) * 64 + slot * 2) = make_uint4(lo, hi, lo, hi);
+    }
+}
+
+// The two fp32 code values for byte p of `word`, from copy (lane & 31) of the table.
+__device__ inline float2 lut_pair_f32(const uint32_t* lut, uint32_t lane8, uint32_t word, int p) {
+    const uint32_t addr = __builtin_amdgcn_perm(lane8, word, 0x0C0C0004u | ((uint32_t)p << 8));
+    return *reinterpret_cast<const float2*>(reinterpret_cast<const char*>(lut) + addr);
+}
+
+__device__ inline float lo_f(uint32_t pr) { return __uint_as_float(pr << 16); }
+__device__ inline float hi_f(uint32_t pr) { return __uint_as_float(pr & 0xFFFF0000u); }
+
+__device__ inline uint32_t pack_bf16_rne(float a, float b) {
+    f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// q4_1 B operand for one 32-wide K slice: the slice's code word (nibble i = k 8h + i)
+// and its block's fp16 pair dm = d | m << 16.  w^ = fl(c * d + m) with c * d exact (4 + 11
+// significant bits), so one fma is the format's w^; then one RNE to bf16.
+__device__ __forceinline__ u32x4 q4_1_operand(uint32_t word, uint32_t dm) {
+    const float d = f16_value((uint16_t)(dm & 0xFFFFu)), m = f16_value((uint16_t)(dm >> 16));
+    uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+    // opaque to the optimizer, so that each byte converts with one v_cvt_f32_ubyteN
+    asm("" : "+v"(lo), "+v"(hi));
+    u32x4 B;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const float c0 = (float)((lo >> (8 * q)) & 255u);
+        const float c1 = (float)((hi >> (8 * q)) & 255u);
+        B[q] = pack_bf16_rne(__builtin_fmaf(c0, d, m), __builtin_fmaf(c1, d, m));
+    }
+    return B;
+}
+
+// q5_0 B operand for one 32-wide K slice: the slice's code word (low 4 bits, nibble i =
+// k 8h + i), the 8 fifth bits of those k (bit i) and the block's fp16 scale.  The fifth
+// bits move to bit 4 of the byte their nibble lands in with one 24-bit multiply per
+// parity: in e = bits & 0x55 (bits 2p), e * 0x410410 puts bit 2p at 8p + 4 (the shifts
+// 4, 10, 16, 22 add 6p + 4 for term p; every other term lands on a different even bit and
+// any carry stops at the odd bit above it), then & 0x10101010 keeps bits 8p + 4.
+// c = q + 16 (0..31) as a float; w^ = (c - 16) * d = fl(c * d - 16 d) exactly (both products
+// fit 16 significant bits), one fma; then one RNE to bf16.
+__device__ __forceinline__ u32x4 q5_0_operand(uint32_t word, uint32_t high8, uint16_t dbits) {
+    const float d = f16_value(dbits);
+    const float d16 = -16.0f * d;
+    uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+    lo |= __umul24(high8 & 0x55u, 0x410410u) & 0x10101010u;
+    hi |= __umul24((high8 >> 1) & 0x55u, 0x410410u) & 0x10101010u;
+    // opaque to the optimizer, so that each byte converts with one v_cvt_f32_ubyteN
+    asm("" : "+v"(lo), "+v"(hi));
+    u32x4 B;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const float c0 = (float)((lo >> (8 * q)) & 255u);
+        const float c1 = (float)((hi >> (8 * q)) & 255u);
+        B[q] = pack_bf16_rne(__builtin_fmaf(c0, d, d16), __builtin_fmaf(c1, d, d16));
+    }
+    return B;
+}
+
+// q4_k B operand for one 32-wide K slice (one sub-block): the slice's code word, the
+// sub-block's S = d * sc and O = dmin * m (both exact).  w^ = fl(c * S - O) with c * S exact
+// (4 + 17 significant bits), one fma; then one RNE to bf16.
+__device__ __forceinline__ u32x4 q4_k_operand(uint32_t word, float S, float O) {
+    uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+    // opaque to the optimizer, so that each byte converts with one v_cvt_f32_ubyteN
+    asm("" : "+v"(lo), "+v"(hi));
+    u32x4 B;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const float c0 = (float)((lo >> (8 * q)) & 255u);
+        const float c1 = (float)((hi >> (8 * q)) & 255u);
+        B[q] = pack_bf16_rne(__builtin_fmaf(c0, S, -O), __builtin_fmaf(c1, S, -O));
+    }
+    return B;
+}
+
+// S and O of sub-block j of a q4_k tile row: rec_sc / rec_m hold the 4 sub-blocks' 6-bit
+// scales / offsets (byte j), dm the super-block's fp16 d | dmin << 16.
+__device__ __forceinline__ void q4_k_sub(uint32_t rec_sc, uint32_t rec_m, uint32_t dm, int j, float& S, float& O) {
+    S = f16_value((uint16_t)(dm & 0xFFFFu)) * (float)((rec_sc >> (8 * j)) & 255u);
+    O = f16_value((uint16_t)(dm >> 16)) * (float)((rec_m >> (8 * j)) & 255u);
+}
+
+// q6_k B operand for one 32-wide K slice: the slice's code word (low 4 bits, nibble i =
+// k 8h + i), bits 4 (b4) and 5 (b5) of those 8 codes (bit i), and the lane's sub-block S
+// = d * sc (exact).  Each bit set moves to its byte as in q5_0_operand (bit 2p of a parity
+// -> bit 8p + 4, one 24-bit multiply), bit 5 one place higher.  c = q (0..63);
+// w^ = (c - 32) * S = fl(c * S - 32 S) exactly (at most 24 significant bits), one fma.
+__device__ __forceinline__ u32x4 q6_k_operand(uint32_t word, uint32_t b4, uint32_t b5, float S) {
+    uint32_t lo = word & 0x0F0F0F0Fu, hi = (word >> 4) & 0x0F0F0F0Fu;
+    lo |= __umul24(b4 & 0x55u, 0x410410u) & 0x10101010u;
+    lo |= (__umul24(b5 & 0x55u, 0x410410u) & 0x10101010u) << 1;
+    hi |= __umul24((b4 >> 1) & 0x55u, 0x410410u) & 0x10101010u;
+    hi |= (__umul24((b5 >> 1) & 0x55u, 0x410410u) & 0x10101010u) << 1;
+    // opaque to the optimizer, so that each byte converts with one v_cvt_f32_ubyteN
+    asm("" : "+v"(lo), "+v"(hi));
+    const float s32 = -32.0f * S;
+    u32x4 B;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        const float c0 = (float)((lo >> (8 * q)) & 255u);
+        const float c1 = (float)((hi >> (8 * q)) & 255u);
+        B[q] = pack_bf16_rne(__builtin_fmaf(c0, S, s32), __builtin_fmaf(c1, S, s32));
+    }
+    return B;
+}
+
+// q6_k: S of sub-block t (0..7) of a tile row from its int8 scale record (r0: sub-blocks
+// 0..3, r1: 4..7) and the super-block's fp16 d; bits 4 / 5 of K slice j from the lane's
+// 8-byte high record (h0: slices 0, 1; h1: slices 2, 3).
+__device__ __forceinline__ float q6_k_scale(uint32_t r0, uint32_t r1, uint32_t dbits, int t) {
+    const uint32_t w = t < 4 ? r0 : r1;
+    return f16_value((uint16_t)(dbits & 0xFFFFu)) * (float)(int8_t)(uint8_t)(w >> (8 * (t & 3)));
+}
+
+__device__ inline f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// Output.  A lane's output column is fixed for a whole tile, so the split it
+// falls in, its base pointer and leading dimension are selected once per
+// column (constant-index kernel-argument reads, then selects) and the bias is
+// read once per column.
+// ---------------------------------------------------------------------------
+struct ColOut {
+    char* p;       // address of element (row 0, this column)
+    int64_t ld;    // row stride in bytes
+    float bias;
+};
+
+__device__ inline ColOut col_out(const KArgs& a, int64_t col) {
+    const OutSplit& o = a.out;
+    const bool s1 = col >= o.end[0], s2 = col >= o.end[1];
+    char* const y0 = reinterpret_cast<char*>(o.y[0]);
+    char* const y1 = reinterpret_cast<char*>(o.y[1]);
+    char* const y2 = reinterpret_cast<char*>(o.y[2]);
+    char* const base = s2 ? y2 : (s1 ? y1 : y0);
+    const int64_t ld = s2 ? o.ldy[2] : (s1 ? o.ldy[1] : o.ldy[0]);
+    const int64_t c0 = s2 ? o.end[1] : (s1 ? o.end[0] : 0);
+    const int64_t es = o.f32 ? 4 : 2;
+    ColOut c;
+    c.p = base + (col - c0) * es;
+    c.ld = ld * es;
+    c.bias = a.bias ? bf16_value(a.bias[col]) : 0.0f;
+    return c;
+}
+
+__device__ inline ColOut col_out_nobias(const KArgs& a, int64_t col) {
+    const OutSplit& o = a.out;
+    const bool s1 = col >= o.end[0], s2 = col >= o.end[1];
+    char* const y0 = reinterpret_cast<char*>(o.y[0]);
+    char* const y1 = reinterpret_cast<char*>(o.y[1]);
+    char* const y2 = reinterpret_cast<char*>(o.y[2]);
+    char* const base = s2 ? y2 : (s1 ? y1 : y0);
+    const int64_t ld = s2 ? o.ldy[2] : (s1 ? o.ldy[1] : o.ldy[0]);
+    const int64_t c0 = s2 ? o.end[1] : (s1 ? o.end[0] : 0);
+    const int64_t es = o.f32 ? 4 : 2;
+    ColOut c;
+    c.p = base + (col - c0) * es;
+    c.ld = ld * es;
+    c.bias = 0.0f;
+    return c;
+}
+
+// y = acc * g + bias, converted and stored at row m.
+__device__ inline void put_out(const KArgs& a, const ColOut& c, int64_t m, float v, float g) {
+    const float r = v * g + c.bias;
+    char* const p = c.p + m * c.ld;
+    if (a.out.f32) *reinterpret_cast<float*>(p) = r;
+    else *reinterpret_cast<uint16_t*>(p) = bf16_rne(r);
+}
+
+// 4 x 4 transpose inside each quad of lanes (t = lane & 3): on entry v[i] is
+// element (row i, column t) of the quad's block, on exit v[j] is (row t, column j).
+// Two exchange stages, with lane t ^ 1 and then lane t ^ 2.
+__device__ __forceinline__ float dpp_xor1(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+}
+__device__ __forceinline__ void quad_transpose(float (&v)[4], int t) {
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; i++) p[i] = dpp_xor1(v[i ^ 1]);
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = ((i ^ t) & 1) ? p[i] : v[i];
+#pragma unroll
+    for (int i = 0; i < 4; i++) p[i] = dpp_xor2(v[i ^ 2]);
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = ((i ^ t) & 2) ? p[i] : v[i];
+}
+
+// Workgroup barrier for data written to LDS by this workgroup's LDS-direct loads
+// and LDS stores, when the N most recent vector-memory requests (register
+// loads) may stay in flight: s_waitcnt vmcnt(N) lgkmcnt(0), then s_barrier.
+// __syncthreads() would wait for every outstanding load here, because its fence
+// cannot tell the LDS-direct loads from the later register loads.  The compiler
+// is kept from moving memory accesses across the barrier.
+template <int N>
+__device__ __forceinline__ void lds_barrier_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0070);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// s_waitcnt vmcnt(N) with lgkmcnt and expcnt left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// ===========================================================================
+// GEMV, m <= 16.  Work item = (16-row band, K piece).  Each wave owns whole
+// items (no cross-wave reduction); an item's tiles are fetched C at a time --
+// codes, scales and X operands of all C tiles are requested before any is
+// used -- so every wave keeps up to C KiB of weights in flight.  Lane l owns row
+// (l & 15) of the band as B operand and row (l & 15) of X as A operand; the
+// 16x16 result tile has D[4*(l>>4)+i][l&15] in lane l.
+constexpr int kBufWord3 = 0x00020000;   // buffer descriptor word 3: raw, untyped access
+
+typedef __amdgpu_buffer_rsrc_t BufRes;
+
+__device__ inline BufRes buf_res(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufWord3);
+}
+
+// The same for a base and size that are equal in every lane but that the
+// compiler cannot prove so (results of 64-bit division, values held in
+// arrays): read them from the first active lane.
+__device__ inline uint32_t uni(uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane((int)v); }
+__device__ inline int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline BufRes buf_res_uni(const void* base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t u = (uint64_t)uni((uint32_t)b) | ((uint64_t)uni((uint32_t)(b >> 32)) << 32);
+    return buf_res(reinterpret_cast<const void*>(u), uni(bytes));
+}
+
+// Buffer-load cache policy for data read exactly once (GEMV weights): non-temporal.
+// On this chip a read-only stream with this hint runs about 12% faster than with
+// the default policy.
+constexpr int kNT = 2;
+
+
+constexpr int kNumCU = 256;
+
+inline KArgs make_args(const MatmulProblem& p) {
+    KArgs a{};
+    a.x = p.x;
+    a.ldx = p.ldx;
+    a.m = (int)p.m;
+    a.n = p.n;
+    a.k = p.k;
+    a.codes = p.codes;
+    a.scales = p.scales;
+    a.bias = p.bias;
+    a.out = p.out;
+    a.L = scale_layout(p.fmt, p.dq, p.n, p.k);
+    a.ksplit = 1;
+    const uintptr_t align = p.out.f32 ? 16 : 8;
+    a.out_vec = 1;
+    a.out_v16 = p.out.f32 ? 0 : 1;
+    for (int i = 0; i < p.out.nsplit; i++) {
+        const uintptr_t y = reinterpret_cast<uintptr_t>(p.out.y[i]);
+        if (y % align != 0 || p.out.ldy[i] % 4 != 0 || p.out.end[i] % 4 != 0) a.out_vec = 0;
+        if (y % 16 != 0 || p.out.ldy[i] % 8 != 0 || p.out.end[i] % 8 != 0) a.out_v16 = 0;
+    }
+    return a;
+}
+
+}  // namespace wq
