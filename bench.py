@@ -83,46 +83,75 @@ def main():
     cal2.copy_(cal)
     torch.cuda.synchronize()
 
+    # a device copy of 512 MiB each way (1 GiB of traffic) evicts the 256 MB Infinity Cache
+    flush_src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush_dst = torch.empty_like(flush_src)
+    timing_info = {}
+
+    def capture(enqueue, n_slots, count, start):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(stream):
+            enqueue(start % n_slots, stream)            # untimed eager pass before capture
+            stream.synchronize()
+            with torch.cuda.graph(g, stream=stream):
+                for s in range(count):
+                    enqueue((start + s) % n_slots, stream)
+        return g
+
     def run_graph_steps(enqueue, n_slots, steps, warmup, per_graph=None):
-        """Capture one graph over `per_graph` consecutive steps (default: one per slot;
-        step s uses slot s % n_slots), replay it; returns seconds for `steps` steps."""
+        """Time `steps` steps replayed from captured HIP graphs; step s of the run uses slot
+        s % n_slots of a weight pool.  Warmup runs steps 0 .. warmup-1, the timed steps are
+        warmup .. warmup+steps-1 (graphs of one full cycle of the pool, or of `per_graph`
+        steps, then the remainder).  Every timed graph is replayed once before the warmup (its
+        first launch uploads it), and for a pool of several slots a 1 GiB device copy runs
+        between the warmup and the timed steps, so the timed steps start with none of their
+        weights in the Infinity Cache whatever `steps` and `warmup` are; within the timed steps
+        a slot is read again only after the whole pool.  Returns seconds for the timed steps."""
         per = per_graph or n_slots
-        graphs = {}
-
-        def graph_for(count):
-            if count not in graphs:
-                g = torch.cuda.CUDAGraph()
-                with torch.cuda.stream(stream):
-                    enqueue(0, stream)                      # untimed eager pass before capture
-                    stream.synchronize()
-                    with torch.cuda.graph(g, stream=stream):
-                        for s in range(count):
-                            enqueue(s % n_slots, stream)
-                graphs[count] = g
-            return graphs[count]
-
-        def replay(total):
-            full, rest = divmod(total, per)
-            for _ in range(full):
-                graph_for(per).replay()
-            if rest:
-                graph_for(rest).replay()
-
+        start = warmup % n_slots
+        full, rest = divmod(steps, per)
+        timed = []
+        if full:
+            timed.append((capture(enqueue, n_slots, per, start), full))
+        if rest:
+            timed.append((capture(enqueue, n_slots, rest, start + full * per), 1))
+        for g, _ in timed:
+            g.replay()
         if warmup:
-            replay(warmup)
+            wg = capture(enqueue, n_slots, min(warmup, per), 0)
+            for _ in range(-(-warmup // per)):
+                wg.replay()
         torch.cuda.synchronize()
+        cold = n_slots > 1
+        if cold:
+            flush_dst.copy_(flush_src)
+            torch.cuda.synchronize()
         ev0 = torch.cuda.Event(enable_timing=True)
         ev1 = torch.cuda.Event(enable_timing=True)
-        graph_for(per)
-        if steps % per:
-            graph_for(steps % per)
-        torch.cuda.synchronize()
         with torch.cuda.stream(stream):
             ev0.record(stream)
-            replay(steps)
+            for g, reps in timed:
+                for _ in range(reps):
+                    g.replay()
             ev1.record(stream)
         torch.cuda.synchronize()
+        timing_info.clear()
+        timing_info.update({"slots": n_slots, "timed_first_slot": start,
+                            "cold": ("1 GiB device copy between warmup and the timed steps; a slot is re-read only "
+                                     "after the whole pool") if cold else "one weight set, reused (not cold)"})
         return ev0.elapsed_time(ev1) / 1e3
+
+    def sclk_mhz():
+        """Current shader clock from the driver's table (the entry marked '*'), or None."""
+        import glob
+        for f in glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"):
+            try:
+                for line in open(f):
+                    if line.strip().endswith("*"):
+                        return float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
 
     def enc_step(s_, st, layers, m):
         for e in layers:
@@ -132,8 +161,10 @@ def main():
     def encoder_part():
         # ---- encoder GEMM, NVFP4, M = 1500: fc1 + fc2 ----
         enc = []
+        enc_cases = []
         for i, (n, k) in enumerate([(ENC_FFN, ENC_D), (ENC_D, ENC_FFN)]):
             w, b, x = linear_case(3000 + i, n, k, ENC_M, row_lognormal_sigma=0.3)
+            enc_cases.append((w, b, x))
             d, c, s = quantize_dev(wq.WQ_NVFP4, torch.from_numpy(w).to(dev), False)
             nb = wq.wq_workspace_size(d, ENC_M)
             enc.append(dict(d=d, c=c, s=s, b=bf16_dev(b), x=bf16_dev(x), n=n, k=k,
@@ -143,6 +174,7 @@ def main():
         reps = 50
         # ten steps per captured graph, so that graph launches do not count against the kernels
         te = run_graph_steps(lambda s_, st: enc_step(s_, st, enc, ENC_M), 1, reps, 10, per_graph=10)
+        mhz = sclk_mhz()
         flops = sum(2.0 * ENC_M * e["n"] * e["k"] for e in enc)
         tflops = flops * reps / te / 1e12
         encoder = {
@@ -157,8 +189,15 @@ def main():
                          "traffic": measured_traffic("encoder_nvfp4_m1500", "traffic_bytes_per_step"),
                          "traffic_per": "step (fc1 + fc2 + K-split reduce)",
                          "algorithmic_bytes_per_step": sum(e["c"].numel() + e["s"].numel() + 2 * ENC_M * (e["k"] + e["n"])
-                                                           + 2 * e["n"] for e in enc)},
+                                                           + 2 * e["n"] for e in enc),
+                         # the same against the dense peak at the shader clock the driver reported right
+                         # after the timed steps (256 CUs x 4096 bf16 flop per clock); null if unreadable
+                         "sclk_mhz": mhz,
+                         "peak_at_sclk": round(256 * 4096 * mhz * 1e6 / 1e12, 1) if mhz else None,
+                         "frac_at_sclk": round(tflops / (256 * 4096 * mhz * 1e6 / 1e12), 4) if mhz else None},
         }
+        if not args.no_cpu:
+            encoder["cpu_baseline"] = cpu_baseline_encoder(enc_cases)
         log(f"[bench] encoder NVFP4 M=1500: {encoder['us_per_step']} us, {tflops:.1f} TFLOP/s")
         encoder_part.layers = enc
         return encoder
@@ -365,86 +404,116 @@ def main():
         return out
 
     def sweep_part():
-        """large-v3-turbo's Linears as a decoder and an encoder call them.
-        Decoder step: 4 layers x {self-attn Q/K/V (one wq_matmul_qkv), self O, cross Q, cross O,
-        fc1, fc2} = 24 launches, NF4 + double-quant, at M = 1 and 16, cycled over a >= 1 GiB pool
-        (cross-attention K/V is computed once per utterance and is not part of a token's step).
-        Encoder: 32 layers x {Q, K, V, O, fc1, fc2} = 192 launches, q8_0, M = 1500.  Weights are
-        drawn on the device from a seeded generator (only their shapes matter for timing)."""
+        """large-v3-turbo's 232 Linears as the export policy assigns them and its call plan
+        groups them (block_quantized_bit_amd.policy, "nf4dq" requested: encoder q8_0, decoder
+        NF4 + double-quant).  Per decoded token: 24 decoder calls (self-attention Q/K/V as one
+        wq_matmul_qkv, self O, cross Q, cross O, fc1, fc2 per layer) at M = 1 and 16, cycled over a
+        >= 1 GiB pool.  Once per utterance: the 4 merged cross-attention K/V calls (wq_matmul_qkv,
+        2 splits, 2560 x 1280) at M = 1500 encoder frames.  Encoder: 32 x {Q/K/V as one
+        wq_matmul_qkv (3840 x 1280), O, fc1, fc2} = 128 calls at M = 1500 (668 MB of q8_0 weights,
+        read from HBM on every pass).  Weights are drawn on the device from a seeded generator
+        (only their shapes matter for timing); key projections have no bias."""
+        from block_quantized_bit_amd import policy as P
         out = {}
         gen = torch.Generator(device=dev).manual_seed(5000)
-        dec_shapes = [("qkv", 3840, 1280), ("self_o", 1280, 1280), ("cross_q", 1280, 1280),
-                      ("cross_o", 1280, 1280), ("fc1", 5120, 1280), ("fc2", 1280, 5120)]
-        layers = []
-        for _ in range(4):
-            for name, n, k in dec_shapes:
-                w = torch.randn((n, k), device=dev, generator=gen, dtype=torch.float32) * 0.02
-                d, c, s_ = quantize_dev(wq.WQ_NF4, w, True)
-                layers.append(dict(name=name, n=n, k=k, d=d, c=c, s=s_,
-                                   bias=(torch.randn(n, device=dev, generator=gen) * 0.01).to(torch.bfloat16)))
-        step_bytes = sum(e["c"].numel() + e["s"].numel() for e in layers)
+        calls = P.plan(P.make_policy("nf4dq"))
+
+        def make(c):
+            w = torch.randn((c.n, c.k), device=dev, generator=gen, dtype=torch.float32) * 0.02
+            d = P.fmt_desc(c.fmt, c.n, c.k)
+            cb, sb = wq.wq_packed_size(d)
+            cc = torch.empty(cb, dtype=torch.uint8, device=dev)
+            ss = torch.empty(sb, dtype=torch.uint8, device=dev)
+            wq.wq_quantize(d, w, cc, ss)
+            bias = (torch.randn(c.n, device=dev, generator=gen) * 0.01).to(torch.bfloat16)
+            col = 0
+            for name, width in zip(c.names, c.split_n):
+                if name.endswith(".k"):
+                    bias[col:col + width] = 0
+                col += width
+            return dict(call=c, d=d, c=cc, s=ss, bias=bias)
+
+        def enqueue(e, m, x, y, c_, s_, ws, nb, st):
+            c = e["call"]
+            if c.fused:
+                p0 = y.data_ptr()
+                offs = np.cumsum((0,) + c.split_n[:-1])
+                wq.wq_matmul_qkv(e["d"], m, x, c.k, c_, s_, e["bias"], list(c.split_n),
+                                 [p0 + 2 * int(o) for o in offs], [c.n] * len(c.split_n), wq.WQ_BF16,
+                                 ws if nb else None, nb, stream=st)
+            else:
+                wq.wq_matmul(e["d"], m, x, c.k, c_, s_, e["bias"], y, wq.WQ_BF16, c.n, ws if nb else None, nb,
+                             stream=st)
+
+        # ---- per-token decoder calls, pooled ----
+        dec = [make(c) for c in calls if c.rows == "tokens"]
+        step_bytes = sum(e["c"].numel() + e["s"].numel() for e in dec)
         spool_n = max(1, -(-(1 << 30) // step_bytes))
-        spool = [[(e["c"].clone(), e["s"].clone()) for e in layers] for _ in range(spool_n)]
+        spool = [[(e["c"].clone(), e["s"].clone()) for e in dec] for _ in range(spool_n)]
         xk = {k: torch.randn((16, k), device=dev, generator=gen).to(torch.bfloat16) for k in (1280, 5120)}
         torch.cuda.synchronize()
         for m in (1, 16):
             ys = {n: torch.empty((m, n), dtype=torch.bfloat16, device=dev) for n in (1280, 3840, 5120)}
 
             def dec_step(slot, st, m=m, ys=ys):
-                for j, e in enumerate(layers):
-                    c, s_ = spool[slot][j]
-                    y = ys[e["n"]]
-                    if e["name"] == "qkv":
-                        p0 = y.data_ptr()
-                        wq.wq_matmul_qkv(e["d"], m, xk[e["k"]], e["k"], c, s_, e["bias"], [1280, 1280, 1280],
-                                         [p0, p0 + 2 * 1280, p0 + 2 * 2560], [3840] * 3, wq.WQ_BF16, stream=st)
-                    else:
-                        wq.wq_matmul(e["d"], m, xk[e["k"]], e["k"], c, s_, e["bias"], y, wq.WQ_BF16, e["n"],
-                                     stream=st)
+                for j, e in enumerate(dec):
+                    c_, s_ = spool[slot][j]
+                    enqueue(e, m, xk[e["call"].k], ys[e["call"].n], c_, s_, None, 0, st)
 
             t = run_graph_steps(dec_step, spool_n, spool_n * 2, spool_n) / (spool_n * 2)
-            alg = step_bytes + sum(2 * m * (e["k"] + e["n"]) + 2 * e["n"] for e in layers)
-            out[f"decoder_step_m{m}"] = {"launches": len(layers), "us_per_step": round(t * 1e6, 2),
-                                         "weight_bytes": step_bytes, "weight_GBps": round(step_bytes / t / 1e9, 1),
+            alg = step_bytes + sum(2 * m * (e["call"].k + e["call"].n) + 2 * e["call"].n for e in dec)
+            out[f"decoder_step_m{m}"] = {"launches": len(dec), "linears": sum(len(e["call"].names) for e in dec),
+                                         "us_per_step": round(t * 1e6, 2), "weight_bytes": step_bytes,
+                                         "weight_GBps": round(step_bytes / t / 1e9, 1),
                                          "algorithmic_GBps": round(alg / t / 1e9, 1),
-                                         "us_per_launch": round(t * 1e6 / len(layers), 3)}
+                                         "us_per_launch": round(t * 1e6 / len(dec), 3), "timing": dict(timing_info)}
             log(f"[bench] decoder step M={m}: {out[f'decoder_step_m{m}']}")
-        del spool, layers
+        del spool, dec
         torch.cuda.empty_cache()
-        # encoder sweep, q8_0, M = 1500
-        enc_shapes = [(1280, 1280)] * 4 + [(5120, 1280), (1280, 5120)]
+        # the launch floor in the same setting: 24 one-element kernels per graph replay
+        tiny = torch.zeros(1, device=dev)
+        te_ = run_graph_steps(lambda s_, st: [tiny.add_(1.0) for _ in range(24)], 1, 20, 5, per_graph=5) / 20
+        out["empty_launch_floor"] = {"launches": 24, "us_per_launch": round(te_ * 1e6 / 24, 3),
+                                     "how": "24 one-element torch kernels per HIP graph step"}
+
+        # ---- encoder-frame calls: cross-attention K/V (once per utterance) and the encoder ----
         xs = {k: torch.randn((ENC_M, k), device=dev, generator=gen).to(torch.bfloat16) for k in (1280, 5120)}
-        ys = {n: torch.empty((ENC_M, n), dtype=torch.bfloat16, device=dev) for n in (1280, 5120)}
-        lin = []
-        for _ in range(32):
-            for n, k in enc_shapes:
-                w = torch.randn((n, k), device=dev, generator=gen, dtype=torch.float32) * 0.02
-                d, c, s_ = quantize_dev(wq.WQ_Q8_0, w, False)
-                nb = wq.wq_workspace_size(d, ENC_M)
-                lin.append(dict(d=d, c=c, s=s_, n=n, k=k, nb=nb, bias=torch.zeros(n, dtype=torch.bfloat16, device=dev)))
-        wsz = max(e["nb"] for e in lin)
-        wsb = torch.zeros(max(wsz, 16), dtype=torch.uint8, device=dev)
-        torch.cuda.synchronize()
-
-        def enc_sweep(s_, st):
+        ys = {n: torch.empty((ENC_M, n), dtype=torch.bfloat16, device=dev) for n in (1280, 2560, 3840, 5120)}
+        for key, sel, reps in (("cross_kv_nf4dq_m1500", lambda c: c.rows == "frames_once", 20),
+                               ("encoder_sweep_q8_0_m1500", lambda c: c.names[0].startswith("encoder"), 3)):
+            lin = [make(c) for c in calls if sel(c)]
             for e in lin:
-                wq.wq_matmul(e["d"], ENC_M, xs[e["k"]], e["k"], e["c"], e["s"], e["bias"], ys[e["n"]], wq.WQ_BF16,
-                             e["n"], wsb if e["nb"] else None, e["nb"], stream=st)
+                e["nb"] = wq.wq_workspace_size(e["d"], ENC_M)
+            wsz = max(e["nb"] for e in lin)
+            wsb = torch.zeros(max(wsz, 16), dtype=torch.uint8, device=dev)
+            torch.cuda.synchronize()
 
-        reps = 3
-        t = run_graph_steps(enc_sweep, 1, reps, 1, per_graph=1) / reps
-        fl = sum(2.0 * ENC_M * e["n"] * e["k"] for e in lin)
-        out["encoder_sweep_q8_0_m1500"] = {"launches": len(lin), "us": round(t * 1e6, 1),
-                                           "weight_bytes": sum(e["c"].numel() + e["s"].numel() for e in lin),
-                                           "TFLOPs": round(fl / t / 1e12, 2),
-                                           "frac_mfma": round(fl / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
-        log(f"[bench] encoder sweep q8_0: {out['encoder_sweep_q8_0_m1500']}")
-        del lin
-        torch.cuda.empty_cache()
+            def run_all(s_, st, lin=lin, wsb=wsb):
+                for e in lin:
+                    enqueue(e, ENC_M, xs[e["call"].k], ys[e["call"].n], e["c"], e["s"], wsb, e["nb"], st)
+
+            t = run_graph_steps(run_all, 1, reps, 1, per_graph=1) / reps
+            fl = sum(2.0 * ENC_M * e["call"].n * e["call"].k for e in lin)
+            out[key] = {"launches": len(lin), "linears": sum(len(e["call"].names) for e in lin),
+                        "us": round(t * 1e6, 1), "weight_bytes": sum(e["c"].numel() + e["s"].numel() for e in lin),
+                        "TFLOPs": round(fl / t / 1e12, 2), "frac_mfma": round(fl / t / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            log(f"[bench] {key}: {out[key]}")
+            del lin
+            torch.cuda.empty_cache()
+        out["linears_232"] = {
+            "what": "every Linear once: the encoder's 128 calls and the 4 cross-attention K/V calls at 1500 "
+                    "frames, plus one decoded step of the 24 per-token calls at M = 16",
+            "launches": out["encoder_sweep_q8_0_m1500"]["launches"] + out["cross_kv_nf4dq_m1500"]["launches"]
+                        + out["decoder_step_m16"]["launches"],
+            "linears": out["encoder_sweep_q8_0_m1500"]["linears"] + out["cross_kv_nf4dq_m1500"]["linears"]
+                       + out["decoder_step_m16"]["linears"],
+            "us": round(out["encoder_sweep_q8_0_m1500"]["us"] + out["cross_kv_nf4dq_m1500"]["us"]
+                        + out["decoder_step_m16"]["us_per_step"], 1)}
         return out
 
     outs1, wss1 = decode_buffers(1)
     t = run_graph_steps(lambda s, st: enqueue_decode_step(1, s, outs1, wss1, st), pool_n, args.steps, args.warmup)
+    main_timing = dict(timing_info)
     ms_per_step = t * 1e3 / args.steps
     value = set_bytes * args.steps / t / 1e9
     per_launch_bytes = decode_bytes(1) / len(base)
@@ -470,8 +539,11 @@ def main():
             "workload": "whisper-large-v3-turbo decoder GEMV set, NF4 + double-quant (64-blocks, int8 absmax "
                         "in 256-block groups), M=1: fused QKV 1280->3840 (wq_matmul_qkv), out 1280->1280, "
                         "fc1 1280->5120, fc2 5120->1280; bf16 activations and outputs",
-            "weights": f"{set_bytes} B per step, cycled over {pool_n} copies ({pool_n * set_bytes / 2**30:.2f} GiB) "
-                       "so each step reads from HBM",
+            "weights": f"{set_bytes} B per step, cycled over {pool_n} copies ({pool_n * set_bytes / 2**30:.2f} GiB)",
+            "cold": main_timing["cold"],
+            "timed_slots": f"{main_timing['timed_first_slot']} .. {(main_timing['timed_first_slot'] + args.steps - 1) % pool_n}"
+                           f" (mod {pool_n})",
+            "bytes_read_timed": set_bytes * args.steps,
             "launches_per_step": len(base),
             "timing": "HIP graph replay, HIP events on the launch stream",
         },
@@ -536,23 +608,40 @@ def main():
         # ---- large-v3-turbo sweep: the whole per-token decoder step and the q8_0 encoder ----
         extras.update(sweep_part())
 
-        # ---- one encoder layer at batch 4 (M = 6000), q8_0 and q4_0 on identical weights ----
-        layer_shapes = [(ENC_D, ENC_D)] * 4 + [(ENC_FFN, ENC_D), (ENC_D, ENC_FFN)]
+        # ---- one encoder layer at batch 4 (M = 6000), q8_0 and q4_0 on identical weights: Q/K/V as
+        # one wq_matmul_qkv over the concatenated weights (3840 x 1280), then O, fc1, fc2 ----
         mb4 = 4 * ENC_M
         for fmt_name, fmt in (("q8_0", wq.WQ_Q8_0), ("q4_0", wq.WQ_Q4_0), ("q4_1", wq.WQ_Q4_1), ("q5_0", wq.WQ_Q5_0),
                               ("q4_k", wq.WQ_Q4_K), ("q6_k", wq.WQ_Q6_K)):
+            parts = [linear_case(4000 + i, ENC_D, ENC_D, mb4) for i in range(4)] + \
+                    [linear_case(4004, ENC_FFN, ENC_D, mb4), linear_case(4005, ENC_D, ENC_FFN, mb4)]
+            spec = [(np.concatenate([p[0] for p in parts[:3]]), np.concatenate([parts[0][1], np.zeros_like(parts[1][1]),
+                                                                               parts[2][1]]), parts[0][2], 3)]
+            spec += [(p[0], p[1], p[2], 1) for p in parts[3:]]
             lay = []
-            for i, (n, k) in enumerate(layer_shapes):
-                w, b, x = linear_case(4000 + i, n, k, mb4)
+            for w, b, x, nsplit in spec:
+                n, k = w.shape
                 d, c, s = quantize_dev(fmt, torch.from_numpy(w).to(dev), False)
                 nb = wq.wq_workspace_size(d, mb4)
-                lay.append(dict(d=d, c=c, s=s, b=bf16_dev(b), x=bf16_dev(x), n=n, k=k,
+                lay.append(dict(d=d, c=c, s=s, b=bf16_dev(b), x=bf16_dev(x), n=n, k=k, nsplit=nsplit,
                                 y=torch.empty((mb4, n), dtype=torch.int16, device=dev),
                                 ws=torch.zeros(max(nb, 16), dtype=torch.uint8, device=dev), nb=nb))
+
+            def layer_step(s_, st, lay=lay):
+                for e in lay:
+                    if e["nsplit"] == 3:
+                        p0 = e["y"].data_ptr()
+                        wq.wq_matmul_qkv(e["d"], mb4, e["x"], e["k"], e["c"], e["s"], e["b"], [ENC_D] * 3,
+                                         [p0, p0 + 2 * ENC_D, p0 + 4 * ENC_D], [e["n"]] * 3, wq.WQ_BF16,
+                                         e["ws"] if e["nb"] else None, e["nb"], stream=st)
+                    else:
+                        wq.wq_matmul(e["d"], mb4, e["x"], e["k"], e["c"], e["s"], e["b"], e["y"], wq.WQ_BF16, e["n"],
+                                     e["ws"] if e["nb"] else None, e["nb"], stream=st)
+
             reps = 10
-            tl = run_graph_steps(lambda s_, st: enc_step(s_, st, lay, mb4), 1, reps, 5, per_graph=5)
-            fl = sum(2.0 * mb4 * n * k for n, k in layer_shapes)
-            extras[f"encoder_layer_b4_{fmt_name}"] = {"us_per_layer": round(tl * 1e6 / reps, 1),
+            tl = run_graph_steps(layer_step, 1, reps, 5, per_graph=5)
+            fl = sum(2.0 * mb4 * e["n"] * e["k"] for e in lay)
+            extras[f"encoder_layer_b4_{fmt_name}"] = {"launches": len(lay), "us_per_layer": round(tl * 1e6 / reps, 1),
                                                       "TFLOPs": round(fl * reps / tl / 1e12, 2),
                                                       "frac_mfma": round(fl * reps / tl / 1e12 / BF16_PEAK_TFLOPS, 4)}
             log(f"[bench] layer b4 {fmt_name}: {extras[f'encoder_layer_b4_{fmt_name}']}")
@@ -618,6 +707,35 @@ def cpu_baseline(base, set_bytes):
     return {"value": round(set_bytes * steps / el / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{steps} whole decode steps (4 matrices, M=1: dequantize to fp32 + fp32 matmul) "
                       f"in {el:.1f} s; dequantize single-threaded, matmul OpenMP over rows"}
+
+
+def cpu_baseline_encoder(cases):
+    """The plain C oracle, as it stands, on the encoder step (NVFP4 fc1 + fc2, M = 1500): each
+    matrix is quantized and dequantized to fp32 once (not timed), then the fp32 matmul runs over
+    row blocks of X (OpenMP over rows) until 10 s have passed; TFLOP/s counts the rows done."""
+    cores = len(os.sched_getaffinity(0))
+    os.environ["OMP_NUM_THREADS"] = str(cores)
+    from oracle import oracle as O
+    prepared = []
+    for w, b, x in cases:
+        q = O.quantize(2, w, False)        # NVFP4
+        prepared.append((x, q["w_hat"], b, w.shape[0], w.shape[1]))
+    rows = np.arange(64)
+    flop = 0.0
+    t0 = time.perf_counter()
+    blocks = 0
+    while True:
+        for x, w_hat, b, n, k in prepared:
+            r = (rows + 64 * blocks) % x.shape[0]
+            O.matmul(x, w_hat, b, rows=r)
+            flop += 2.0 * len(r) * n * k
+        blocks += 1
+        el = time.perf_counter() - t0
+        if el > 10.0:
+            break
+    return {"value": round(flop / el / 1e12, 6), "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{blocks} blocks of 64 rows of X through fc1 and fc2 (fp32 matmul on the oracle's "
+                      f"dequantized NVFP4 weights) in {el:.1f} s; quantize/dequantize not timed"}
 
 
 if __name__ == "__main__":
