@@ -24,6 +24,8 @@
  *     q4_k are named there too (section "Why the policy") as formats that
  *     decode correctly but lack fast kernels, and q6_k as one the encoder may
  *     use (same section).
+ *   - NVFP4 activations quantized per 16-value group at run time (W4A4):
+ *     "mbehr90/whisper-large-v3-turbo-nvfp4", section "What is quantized".
  *   - Host reference path for quantized linears used to rule out kernel bugs:
  *     same page, section "Why the policy".
  * Everything the pages leave open (codebook values, rounding, tie-breaks,
@@ -962,6 +964,61 @@ int or_quantize_packed(int fmt, int dq, int64_t n, int64_t k, const float* w,
         return 0;
     }
     return -1;
+}
+
+/* ------------------------------------------------------------------------ */
+/* NVFP4 activations (W4A4): "mbehr90/whisper-large-v3-turbo-nvfp4", section    */
+/* "What is quantized": activations are quantized per 16-value group at run    */
+/* time, the weights keep their NVFP4 form, and the product is W4A4.            */
+/* Reading: X[m][k] (bf16, widened exactly) is quantized exactly as an NVFP4     */
+/* weight matrix is (or_nvfp4_quantize: one FP32 global scale from the absmax   */
+/* of the whole X of the call, an E4M3 scale per 16 values along k, E2M1 codes).*/
+/* The calibrated static activation scale of a checkpoint is not available, so  */
+/* the global scale is the call's own.  Packed layout (row-major, no tiles):    */
+/*   codes : byte r*k/2 + i/2 holds element i of row r, even i in the low       */
+/*           nibble;                                                             */
+/*   scales: byte r*(k/16) + b holds block b of row r (E4M3); the FP32 global    */
+/*           scale follows at byte offset align16(m*k/16).                       */
+/* x_hat[r][i] = fl(fl(e2m1 * e4m3) * g) as for weights.                         */
+/* ------------------------------------------------------------------------ */
+int64_t or_act_scales_bytes(int64_t m, int64_t k) { return align16(m * (k / 16)) + 4; }
+
+void or_quantize_act_nvfp4(int64_t m, int64_t k, const uint16_t* x, uint8_t* codes_packed, uint8_t* scales_packed,
+                           uint8_t* codes_logical, float* x_hat) {
+    float* xf = (float*)malloc(sizeof(float) * (size_t)(m * k));
+    for (int64_t i = 0; i < m * k; i++) xf[i] = or_bf16_to_f32(x[i]);
+    float g;
+    or_nvfp4_quantize(m, k, xf, codes_logical, scales_packed, &g);      /* scales: [m][k/16] bytes */
+    memcpy(scales_packed + align16(m * (k / 16)), &g, 4);
+    memset(scales_packed + m * (k / 16), 0, (size_t)(align16(m * (k / 16)) - m * (k / 16)));
+    for (int64_t i = 0; i < m * k; i += 2)
+        codes_packed[i / 2] = (uint8_t)((codes_logical[i] & 15) | ((codes_logical[i + 1] & 15) << 4));
+    or_nvfp4_dequantize(m, k, codes_logical, scales_packed, g, x_hat);
+    free(xf);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Matmul reference with fp32 activations (the W4A4 product of dequantized     */
+/* activations and weights): y[r][n] = fl(s + b[n]), s accumulating            */
+/* fl(s + fl(x[r][k] * w^[n][k])) over k ascending, as or_matmul_rows.          */
+/* ------------------------------------------------------------------------ */
+void or_matmul_rows_f32x(int64_t nrows, const int64_t* rows, int64_t n, int64_t k,
+                         const float* x, const float* w_hat, const uint16_t* bias, float* y) {
+    #pragma omp parallel for schedule(static)
+    for (int64_t rr = 0; rr < nrows; rr++) {
+        int64_t m = rows ? rows[rr] : rr;
+        const float* xr = x + m * k;
+        for (int64_t c = 0; c < n; c++) {
+            const float* wr = w_hat + c * k;
+            float s = 0.0f;
+            for (int64_t kk = 0; kk < k; kk++) {
+                float p = xr[kk] * wr[kk];
+                s = s + p;
+            }
+            float b = bias ? or_bf16_to_f32(bias[c]) : 0.0f;
+            y[rr * n + c] = s + b;
+        }
+    }
 }
 
 /* ------------------------------------------------------------------------ */

@@ -88,6 +88,10 @@ def lib():
         L.or_quantize_packed.restype = ctypes.c_int
         L.or_quantize_packed.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, P, P, P, P, P]
         L.or_matmul_rows.argtypes = [i64, P, i64, i64, P, P, P, P]
+        L.or_act_scales_bytes.restype = i64
+        L.or_act_scales_bytes.argtypes = [i64, i64]
+        L.or_quantize_act_nvfp4.argtypes = [i64, i64, P, P, P, P, P]
+        L.or_matmul_rows_f32x.argtypes = [i64, P, i64, i64, P, P, P, P]
         _lib = L
     return _lib
 
@@ -372,6 +376,43 @@ def matmul(x_bf16: np.ndarray, w_hat: np.ndarray, bias_bf16=None, rows=None):
     y = np.zeros((nr, n), np.float32)
     b = None if bias_bf16 is None else np.ascontiguousarray(bias_bf16, np.uint16)
     lib().or_matmul_rows(nr, rp, n, k, _p(x), _p(w_hat), None if b is None else _p(b), _p(y))
+    return y
+
+
+def quantize_act_nvfp4(x_bf16: np.ndarray):
+    """NVFP4 activations (W4A4): X[m,k] bf16 bits -> dict(codes=[m*k/2] packed row-major,
+    scales=E4M3 [m][k/16] then the fp32 global scale at align16(m*k/16), logical=[m,k] codes,
+    x_hat=[m,k] fp32, g=global scale)."""
+    x = np.ascontiguousarray(x_bf16, np.uint16)
+    m, k = x.shape
+    if k % 16:
+        raise ValueError("k must be a multiple of 16")
+    codes = np.zeros(m * k // 2, np.uint8)
+    scales = np.zeros(int(lib().or_act_scales_bytes(m, k)), np.uint8)
+    logical = np.zeros((m, k), np.uint8)
+    x_hat = np.zeros((m, k), np.float32)
+    lib().or_quantize_act_nvfp4(m, k, _p(x), _p(codes), _p(scales), _p(logical), _p(x_hat))
+    g = np.frombuffer(scales[-4:].tobytes(), np.float32)[0]
+    return dict(codes=codes, scales=scales, logical=logical, x_hat=x_hat, g=np.float32(g))
+
+
+def matmul_f32x(x: np.ndarray, w_hat: np.ndarray, bias_bf16=None, rows=None):
+    """y = X * W^T + b with fp32 X (the dequantized activations of a W4A4 product), fp32 sums
+    in k-ascending order as matmul()."""
+    x = np.ascontiguousarray(x, np.float32)
+    w_hat = np.ascontiguousarray(w_hat, np.float32)
+    m, k = x.shape
+    n = w_hat.shape[0]
+    assert w_hat.shape[1] == k
+    rp = None
+    nr = m
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, np.int64)
+        nr = rows.size
+        rp = _p(rows)
+    y = np.zeros((nr, n), np.float32)
+    b = None if bias_bf16 is None else np.ascontiguousarray(bias_bf16, np.uint16)
+    lib().or_matmul_rows_f32x(nr, rp, n, k, _p(x), _p(w_hat), None if b is None else _p(b), _p(y))
     return y
 
 
