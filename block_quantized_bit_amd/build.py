@@ -2,7 +2,7 @@
 
     python -m block_quantized_bit_amd.build
 
-quant.hip (bit-exact quantize/dequantize) is compiled with -ffp-contract=off so
+quant.hip and act.hip (bit-exact quantizers) are compiled with -ffp-contract=off so
 no multiply-add is fused; every HIP file is compiled with packed-fp32 ops
 disabled.
 """
@@ -28,6 +28,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 
 SOURCES = [
     ("quant.hip", ["-ffp-contract=off"]),
+    ("act.hip", ["-ffp-contract=off"]),
     ("gemv.hip", []),
     ("gemm.hip", []),
     ("wq_api.cpp", ["-x", "hip"]),

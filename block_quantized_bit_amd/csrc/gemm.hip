@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     const int64_t nbands = N / 16;
 
     float g = 1.0f, mu = 0.0f;
-    if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.scales + a.L.g_off);
+    if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.gs);
     if constexpr (FMT == kNF4 && DQ) mu = load_f32_vmem(a.scales + a.L.mu_off);
 
     // descriptors: band tiles of this wave (bands past n re-read the last band), X rows m0 ..
@@ -593,7 +593,7 @@ __device__ inline void reduce_store(const KArgs& a, int64_t q, const f32x4& v, f
 // row each) 256 quads apart, so eight 16-byte loads are in flight per thread.
 // Runs after k_gemm on the same stream, so every partial is complete and visible.
 __global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, int global_scale) {
-    const float g = global_scale ? *reinterpret_cast<const float*>(a.scales + a.L.g_off) : 1.0f;
+    const float g = global_scale ? *reinterpret_cast<const float*>(a.gs) : 1.0f;
     const int64_t total = (int64_t)a.m * (a.n / 4);
     const int64_t qa = (int64_t)blockIdx.x * 512 + threadIdx.x, qb = qa + 256;
     if (qa >= total) return;
@@ -630,7 +630,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, int global_scale
 template <int KS>
 __global__ __launch_bounds__(256) void k_splitk_reduce_n(KArgs a, int global_scale) {
     constexpr int Q = 2;
-    const float g = global_scale ? *reinterpret_cast<const float*>(a.scales + a.L.g_off) : 1.0f;
+    const float g = global_scale ? *reinterpret_cast<const float*>(a.gs) : 1.0f;
     const int64_t total = (int64_t)a.m * (a.n / 4);
     const int64_t q0 = (int64_t)blockIdx.x * (256 * Q) + threadIdx.x;
     if (q0 >= total) return;

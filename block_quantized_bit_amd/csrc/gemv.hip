@@ -357,7 +357,7 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
     // copied to LDS it is requested with the first band's tiles (after the copy), so that
     // the wait for the copy does not wait for it; without the copy, up front.
     float g = 1.0f, mu = 0.0f;
-    if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.scales + a.L.g_off);
+    if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.gs);
     if constexpr (FMT == kNF4 && DQ && !XL) mu = load_f32_vmem(a.scales + a.L.mu_off);
     constexpr int kMuLoads = (FMT == kNF4 && DQ && XL) ? 1 : 0;
     float* const mu_first = kMuLoads ? &mu : nullptr;
@@ -544,7 +544,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
     const int64_t stride = (int64_t)gridDim.x * 4;
 
     float g = 1.0f, mu = 0.0f;
-    if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.scales + a.L.g_off);
+    if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.gs);
     if constexpr (FMT == kNF4 && DQ) mu = load_f32_vmem(a.scales + a.L.mu_off);
 
     int64_t band = (int64_t)blockIdx.x * 4 + wave;

@@ -53,6 +53,7 @@ struct KArgs {
     int64_t n, k;
     const uint8_t* codes;
     const uint8_t* scales;
+    const uint8_t* gs;   // NVFP4: address of the fp32 factor applied in the epilogue (the global scale)
     const uint16_t* bias;
     OutSplit out;
     ScaleLayout L;
@@ -424,6 +425,7 @@ inline KArgs make_args(const MatmulProblem& p) {
     a.bias = p.bias;
     a.out = p.out;
     a.L = scale_layout(p.fmt, p.dq, p.n, p.k);
+    a.gs = p.gscale ? reinterpret_cast<const uint8_t*>(p.gscale) : p.scales + a.L.g_off;
     a.ksplit = 1;
     const uintptr_t align = p.out.f32 ? 16 : 8;
     a.out_vec = 1;

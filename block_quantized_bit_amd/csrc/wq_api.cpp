@@ -125,6 +125,18 @@ bool windows_overlap(const void* pa, int64_t lda, int64_t wa, const void* pb, in
     return false;
 }
 
+// NVFP4 activations: k a multiple of 16 and m*k <= 2^34 (chunk indices of 8 values fit 32 bits).
+bool act_shape_ok(int64_t m, int64_t k) {
+    if (m < 0 || k <= 0 || k % 16 != 0 || k > (int64_t(1) << 24)) return false;
+    return m <= (int64_t(1) << 34) / k;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+size_t w4a4_workspace(int64_t m, int64_t n, int64_t k) {
+    return 256 + align256((size_t)m * (size_t)k * 2) + wq::matmul_workspace_bytes(WQ_NVFP4, m, n, k);
+}
+
 wq_status run_matmul(const wq::MatmulProblem& p, void* stream) {
     if (p.m == 0) return WQ_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -294,6 +306,80 @@ wq_status wq_matmul_qkv(const wq_desc* d, int64_t m, const uint16_t* x, int64_t 
         }
         p.out.end[i] = e;
     }
+    return run_matmul(p, stream);
+}
+
+wq_status wq_act_packed_size(int64_t m, int64_t k, size_t* codes_bytes, size_t* scales_bytes) {
+    if (!codes_bytes || !scales_bytes) return WQ_ERR_INVALID_ARG;
+    if (!act_shape_ok(m, k)) return WQ_ERR_SHAPE;
+    *codes_bytes = (size_t)(m * k / 2);
+    *scales_bytes = (size_t)wq::act_scales_bytes(m, k);
+    return WQ_OK;
+}
+
+wq_status wq_quantize_act(int64_t m, int64_t k, const uint16_t* x, int64_t ldx, void* codes, void* scales,
+                          void* stream) {
+    if (!act_shape_ok(m, k)) return WQ_ERR_SHAPE;
+    if (!x || !codes || !scales) return WQ_ERR_INVALID_ARG;
+    if (ldx < k || ldx % 8 != 0 || ldx > (int64_t(1) << 24)) return WQ_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(codes, 16) || !aligned(scales, 16)) return WQ_ERR_ALIGNMENT;
+    if (m == 0) return WQ_OK;
+    return from_hip(wq::launch_quantize_act(m, k, x, ldx, static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales),
+                                            static_cast<hipStream_t>(stream)));
+}
+
+wq_status wq_w4a4_workspace_size(const wq_desc* d, int64_t m, size_t* bytes) {
+    Desc dd;
+    wq_status st = check_desc(d, &dd);
+    if (st != WQ_OK) return st;
+    if (dd.fmt != WQ_NVFP4) return WQ_ERR_UNSUPPORTED;
+    if (!bytes) return WQ_ERR_INVALID_ARG;
+    if (m < 0 || m > 0x7FFFFFFF || !act_shape_ok(m, dd.k)) return WQ_ERR_SHAPE;
+    *bytes = m == 0 ? 0 : w4a4_workspace(m, dd.n, dd.k);
+    return WQ_OK;
+}
+
+wq_status wq_matmul_w4a4(const wq_desc* d, int64_t m, const void* xcodes, const void* xscales, wq_packed w,
+                         const uint16_t* bias, void* y, int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                         void* stream) {
+    Desc dd;
+    wq_status st = check_desc(d, &dd);
+    if (st != WQ_OK) return st;
+    if (dd.fmt != WQ_NVFP4) return WQ_ERR_UNSUPPORTED;
+    if (m < 0 || m > 0x7FFFFFFF || !act_shape_ok(m, dd.k)) return WQ_ERR_SHAPE;
+    if (!xcodes || !xscales) return WQ_ERR_INVALID_ARG;
+    if (!aligned(xcodes, 16) || !aligned(xscales, 16)) return WQ_ERR_ALIGNMENT;
+    if (m > 0) {
+        if (!ws || ws_bytes < w4a4_workspace(m, dd.n, dd.k)) return WQ_ERR_WORKSPACE;
+        if (!aligned(ws, 16)) return WQ_ERR_ALIGNMENT;
+    }
+    // workspace: [0, 256) the epilogue factor g_w * g_x; then the expanded activations
+    // X'[m][k] (bf16); then the matmul's own workspace
+    uint8_t* const base = static_cast<uint8_t*>(ws);
+    const size_t xe_bytes = align256((size_t)m * (size_t)dd.k * 2);
+    // (m == 0: X' is never read; the codes pointer stands in for it in the checks)
+    const uint16_t* const xe = m > 0 ? reinterpret_cast<const uint16_t*>(base + 256) : static_cast<const uint16_t*>(xcodes);
+    void* const mws = m > 0 ? base + 256 + xe_bytes : nullptr;
+    const size_t mws_bytes = m > 0 ? ws_bytes - 256 - xe_bytes : 0;
+    wq::MatmulProblem p{};
+    st = check_matmul(d, m, xe, dd.k, w, bias, ydt, mws, mws_bytes, &p);
+    if (st != WQ_OK) return st;
+    if (!y) return WQ_ERR_INVALID_ARG;
+    if (!aligned(y, ydt == WQ_F32 ? 4 : 2)) return WQ_ERR_ALIGNMENT;
+    if (ldy < p.n) return WQ_ERR_INVALID_ARG;
+    if (m == 0) return WQ_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const wq::ScaleLayout L = wq::scale_layout(dd.fmt, false, dd.n, dd.k);
+    float* const gprod = reinterpret_cast<float*>(base);
+    hipError_t e = wq::launch_expand_act(m, dd.k, static_cast<const uint8_t*>(xcodes),
+                                         static_cast<const uint8_t*>(xscales), p.scales + L.g_off,
+                                         reinterpret_cast<uint16_t*>(base + 256), gprod, s);
+    if (e != hipSuccess) return WQ_ERR_HIP;
+    p.gscale = gprod;
+    p.out.nsplit = 1;
+    p.out.y[0] = y;
+    p.out.ldy[0] = ldy;
+    p.out.end[0] = p.out.end[1] = p.out.end[2] = p.n;
     return run_matmul(p, stream);
 }
 

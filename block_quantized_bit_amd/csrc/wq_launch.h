@@ -49,6 +49,7 @@ struct MatmulProblem {
     OutSplit out;
     void* ws;
     size_t ws_bytes;
+    const float* gscale;   // NVFP4: epilogue factor in device memory; null = the weights' global scale
 };
 
 // Workspace bytes the schedule for (fmt, m, n, k) would like (0 = none).
@@ -59,5 +60,14 @@ hipError_t launch_gemm(const MatmulProblem& p, hipStream_t s);   // m >= 17
 
 size_t gemv_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k);
 size_t gemm_workspace_bytes(int fmt, int64_t m, int64_t n, int64_t k);
+
+// NVFP4 activations (act.hip): packed row-major codes [m][k/2] and scales [m][k/16]
+// followed by the fp32 global scale at align16(m*k/16).
+int64_t act_scales_bytes(int64_t m, int64_t k);
+hipError_t launch_quantize_act(int64_t m, int64_t k, const uint16_t* x, int64_t ldx, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s);
+// xe[m][k] = bf16(+-e2m1 * s) (exact) and *gprod = g_w * g_x, with g_w read at gw.
+hipError_t launch_expand_act(int64_t m, int64_t k, const uint8_t* codes, const uint8_t* scales,
+                             const uint8_t* gw, uint16_t* xe, float* gprod, hipStream_t s);
 
 }  // namespace wq

@@ -21,7 +21,8 @@ WQ_NF4, WQ_NVFP4, WQ_Q4_0, WQ_Q8_0, WQ_Q4_1, WQ_Q5_0, WQ_Q4_K, WQ_Q6_K = 1, 2, 3
 WQ_BF16, WQ_F32 = 1, 2
 
 EXPORTS = ("wq_status_str", "wq_packed_size", "wq_quantize", "wq_dequantize",
-           "wq_workspace_size", "wq_matmul", "wq_matmul_noalloc", "wq_matmul_qkv")
+           "wq_workspace_size", "wq_matmul", "wq_matmul_noalloc", "wq_matmul_qkv",
+           "wq_act_packed_size", "wq_quantize_act", "wq_w4a4_workspace_size", "wq_matmul_w4a4")
 
 # Format names accepted by the harness; aliases follow the NF4 option's names
 # ("asr: add a 4-bit nf4 option for the Whisper engine": nf4, aliases 4bit, int4).
@@ -87,6 +88,14 @@ def lib():
         L.wq_matmul_qkv.restype = ctypes.c_int
         L.wq_matmul_qkv.argtypes = [pd, i64, P, i64, wq_packed, P, ctypes.c_int32, ctypes.POINTER(i64),
                                     ctypes.POINTER(P), ctypes.POINTER(i64), ctypes.c_int32, P, ctypes.c_size_t, P]
+        L.wq_act_packed_size.restype = ctypes.c_int
+        L.wq_act_packed_size.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_size_t)]
+        L.wq_quantize_act.restype = ctypes.c_int
+        L.wq_quantize_act.argtypes = [i64, i64, P, i64, P, P, P]
+        L.wq_w4a4_workspace_size.restype = ctypes.c_int
+        L.wq_w4a4_workspace_size.argtypes = [pd, i64, ctypes.POINTER(ctypes.c_size_t)]
+        L.wq_matmul_w4a4.restype = ctypes.c_int
+        L.wq_matmul_w4a4.argtypes = [pd, i64, P, P, wq_packed, P, P, ctypes.c_int32, i64, P, ctypes.c_size_t, P]
         _lib = L
     return _lib
 
@@ -170,3 +179,29 @@ def wq_matmul_qkv(d: wq_desc, m: int, x, ldx: int, codes, scales, bias, split_n,
     st = lib().wq_matmul_qkv(ctypes.byref(d), int(m), _ptr(x), int(ldx), wq_packed(_ptr(codes), _ptr(scales)),
                              _ptr(bias), ns, sn, yp, lp, int(ydt), _ptr(ws), int(ws_bytes), _stream(stream))
     return _check(st, "wq_matmul_qkv", check)
+
+
+def wq_act_packed_size(m: int, k: int):
+    cb = ctypes.c_size_t()
+    sb = ctypes.c_size_t()
+    _check(lib().wq_act_packed_size(int(m), int(k), ctypes.byref(cb), ctypes.byref(sb)), "wq_act_packed_size", True)
+    return cb.value, sb.value
+
+
+def wq_quantize_act(m: int, k: int, x, ldx: int, codes, scales, stream=None, check=True) -> int:
+    st = lib().wq_quantize_act(int(m), int(k), _ptr(x), int(ldx), _ptr(codes), _ptr(scales), _stream(stream))
+    return _check(st, "wq_quantize_act", check)
+
+
+def wq_w4a4_workspace_size(d: wq_desc, m: int) -> int:
+    b = ctypes.c_size_t()
+    _check(lib().wq_w4a4_workspace_size(ctypes.byref(d), int(m), ctypes.byref(b)), "wq_w4a4_workspace_size", True)
+    return b.value
+
+
+def wq_matmul_w4a4(d: wq_desc, m: int, xcodes, xscales, codes, scales, bias, y, ydt: int, ldy: int,
+                   ws=None, ws_bytes: int = 0, stream=None, check=True) -> int:
+    st = lib().wq_matmul_w4a4(ctypes.byref(d), int(m), _ptr(xcodes), _ptr(xscales),
+                              wq_packed(_ptr(codes), _ptr(scales)), _ptr(bias), _ptr(y), int(ydt), int(ldy),
+                              _ptr(ws), int(ws_bytes), _stream(stream))
+    return _check(st, "wq_matmul_w4a4", check)

@@ -214,6 +214,48 @@ wq_status wq_matmul_qkv(const wq_desc* d, int64_t m, const uint16_t* x, int64_t 
                         void* const* y, const int64_t* ldy, int32_t ydt,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* ---- NVFP4 activations and the W4A4 product ---------------------------------
+ * "mbehr90/whisper-large-v3-turbo-nvfp4", section "What is quantized": activations
+ * are quantized per 16-value group at run time and multiplied with NVFP4 weights
+ * (W4A4; section "Honest summary: on H100 this is not a win" names it the Blackwell
+ * mode).  The activation rule is the NVFP4 weight rule applied to X: g_x =
+ * absmax(X)/2688 over the whole [m, k] input of the call (fp32), per 16 consecutive
+ * k an E4M3 scale E4M3(block absmax / (6 g_x)), nearest-even saturating at 448,
+ * codes E2M1(x / (scale * g_x)) nearest, ties to even, sign kept (also of zeros);
+ * x^ = e2m1 * scale * g_x.  Inputs must be finite.
+ * Packed activations are plain row-major (no tiles):
+ *   codes : m*k/2 bytes; byte r*k/2 + j holds elements 2j (low nibble) and 2j+1 of row r
+ *   scales: E4M3 byte r*(k/16) + b for block b of row r, zero pad bytes, then the fp32
+ *           g_x at byte align16(m*k/16); align16(m*k/16) + 4 bytes in all.
+ * Shapes: k % 16 == 0, k <= 2^24, m >= 0, m*k <= 2^34 (else WQ_ERR_SHAPE). */
+
+/* Host-only.  Bytes of the packed activation buffers for an [m, k] input. */
+wq_status wq_act_packed_size(int64_t m, int64_t k, size_t* codes_bytes, size_t* scales_bytes);
+
+/* Quantize X[m, k] (bf16, leading dimension ldx >= k, ldx % 8 == 0, ldx <= 2^24;
+ * 16-byte aligned) to packed NVFP4 activations.  codes and scales (device, 16-byte
+ * aligned, sizes from wq_act_packed_size) are written whole; the codes buffer also
+ * holds the per-workgroup maxima between the call's kernels.  Codes, scales and g_x
+ * are bit-exact with the rule above.  m == 0 is a no-op. */
+wq_status wq_quantize_act(int64_t m, int64_t k, const uint16_t* x, int64_t ldx, void* codes, void* scales,
+                          void* stream);
+
+/* Workspace bytes wq_matmul_w4a4 needs for descriptor d (NVFP4 only, else
+ * WQ_ERR_UNSUPPORTED) at m rows: 256 + align256(2*m*k) + the matmul's own share. */
+wq_status wq_w4a4_workspace_size(const wq_desc* d, int64_t m, size_t* bytes);
+
+/* Y = X^ * W^T + bias with X^ the packed NVFP4 activations [m, k] (xcodes, xscales as
+ * written by wq_quantize_act, 16-byte aligned) and W packed NVFP4 (d->format ==
+ * WQ_NVFP4, else WQ_ERR_UNSUPPORTED).  bias, y, ydt, ldy as for wq_matmul.  ws is
+ * required (WQ_ERR_WORKSPACE when NULL or smaller than wq_w4a4_workspace_size): the
+ * call expands the activations there to the exact bf16 values e2m1 * scale and runs
+ * the NVFP4 matmul on them with the one epilogue factor g_w * g_x.  Per element
+ * |y - y_ref| <= 4e-3 * sum_k |x^_k * w^_k| + 1e-6 against the fp32 reference
+ * y_ref = sum_k x^_k w^_k + b (plus the final bf16 rounding for WQ_BF16). */
+wq_status wq_matmul_w4a4(const wq_desc* d, int64_t m, const void* xcodes, const void* xscales, wq_packed w,
+                         const uint16_t* bias, void* y, int32_t ydt, int64_t ldy, void* ws, size_t ws_bytes,
+                         void* stream);
+
 #ifdef __cplusplus
 }
 #endif

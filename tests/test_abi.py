@@ -16,7 +16,7 @@ NF4, NVFP4, Q4_0, Q8_0, Q4_1, Q5_0, Q4_K, Q6_K = 1, 2, 3, 4, 5, 6, 7, 8
 def _declared():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(wq_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(wq_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_header_declares_the_boundary():
@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     for name in _declared():
         assert hasattr(L, name), name
     out = os.popen(f"nm -D --defined-only {wq.LIB_PATH}").read()
-    exported = set(re.findall(r" T (wq_[a-z_]+)", out))
+    exported = set(re.findall(r" T (wq_[a-z0-9_]+)", out))
     assert set(_declared()) <= exported
 
 
@@ -155,6 +155,42 @@ def test_quantize_argument_validation():
     assert _status(wq.wq_quantize, d, FAKE, None, FAKE, 0) == 1
     assert _status(wq.wq_dequantize, d, FAKE, FAKE, FAKE + 8, 0) == 4
     assert _status(wq.wq_dequantize, wq.desc(NVFP4, 32, 200), FAKE, FAKE, FAKE, 0) == 3
+
+
+def test_w4a4_argument_validation():
+    """NVFP4 activations and the W4A4 product: every check returns before anything is enqueued."""
+    assert wq.wq_act_packed_size(1500, 1280) == (1500 * 640, 1500 * 80 + 4)
+    assert wq.wq_act_packed_size(3, 48) == (72, 16 + 4)            # 9 scale bytes, padded to 16, then g
+    with pytest.raises(wq.WqError):
+        wq.wq_act_packed_size(4, 24)                               # k % 16
+    qa = lambda **kw: _status(wq.wq_quantize_act, kw.get("m", 4), kw.get("k", 256), kw.get("x", FAKE),
+                              kw.get("ldx", 256), kw.get("codes", FAKE), kw.get("scales", FAKE), 0)
+    assert qa(k=200) == 3
+    assert qa(m=-1) == 3
+    assert qa(m=1 << 27, k=1 << 10) == 3                           # m*k above 2^34
+    assert qa(x=None) == 1 and qa(codes=None) == 1 and qa(scales=None) == 1
+    assert qa(ldx=128) == 1 and qa(ldx=260) == 1
+    assert qa(x=FAKE + 2) == 4 and qa(codes=FAKE + 4) == 4 and qa(scales=FAKE + 8) == 4
+    assert qa(m=0) == 0
+    d = wq.desc(NVFP4, 256, 512)
+    need = wq.wq_w4a4_workspace_size(d, 20)
+    assert need >= 256 + 20 * 512 * 2
+    assert wq.wq_w4a4_workspace_size(d, 0) == 0
+    with pytest.raises(wq.WqError):
+        wq.wq_w4a4_workspace_size(wq.desc(NF4, 256, 512), 20)   # NVFP4 weights only
+    mm = lambda **kw: _status(wq.wq_matmul_w4a4, kw.get("d", d), kw.get("m", 20), kw.get("xc", FAKE),
+                              kw.get("xs", FAKE), kw.get("codes", FAKE), kw.get("scales", FAKE), kw.get("bias", None),
+                              kw.get("y", FAKE), kw.get("ydt", wq.WQ_F32), kw.get("ldy", 256), kw.get("ws", FAKE),
+                              kw.get("ws_bytes", need), 0)
+    assert mm(d=wq.desc(Q4_0, 256, 512)) == 2
+    assert mm(xc=None) == 1 and mm(xs=None) == 1
+    assert mm(xc=FAKE + 8) == 4 and mm(xs=FAKE + 4) == 4
+    assert mm(ws=None) == 6 and mm(ws_bytes=need - 1) == 6
+    assert mm(ws=FAKE + 8) == 4
+    assert mm(codes=None) == 1 and mm(y=None) == 1 and mm(ldy=128) == 1 and mm(ydt=5) == 1
+    assert mm(bias=FAKE + 1) == 4
+    assert mm(m=-1) == 3
+    assert mm(m=0, ws=None, ws_bytes=0) == 0
 
 
 def test_format_names():
