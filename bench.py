@@ -12,7 +12,8 @@ slots are captured once in a HIP graph and replayed.  `value` is weight bytes
 (codes + scales) per second over exactly K timed steps.
 
 Also reported (same JSON line): the encoder GEMM at M=1500 in NVFP4 (fc1 + fc2,
-TFLOP/s), one encoder layer at batch 4 (M=6000) in q8_0 and q4_0, the decode
+TFLOP/s), the same GEMMs as NVFP4 W4A4 (runtime-quantized activations), one
+encoder layer at batch 4 (M=6000) in q8_0 and q4_0, the decode
 set at M=4 and M=16, a 433 MB streaming GEMV (NF4+DQ, M=1), the dominant
 kernels' roofline fractions, an unfused ablation (dequantize, cast, library
 GEMM) and a dense bf16 GEMM at the encoder and decode shapes, and the CPU
@@ -33,6 +34,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+FP4_PEAK_TFLOPS = 10100.0      # MI355X dense fp4 MFMA
 DECODER = [("qkv", 3840, 1280), ("out", 1280, 1280), ("fc1", 5120, 1280), ("fc2", 1280, 5120)]
 ENC_D, ENC_FFN, ENC_M = 1280, 5120, 1500
 
@@ -50,6 +52,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the decode set (for profiling)")
     ap.add_argument("--encoder-only", action="store_true",
                     help="only the encoder GEMMs (NVFP4, M=1500), for MFMA counter runs")
+    ap.add_argument("--w4a4-only", action="store_true",
+                    help="only the NVFP4 W4A4 encoder GEMMs (M=1500), for profiling")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -202,8 +206,69 @@ def main():
         encoder_part.layers = enc
         return encoder
 
+    def w4a4_part(w4a16_us=None):
+        """NVFP4 W4A4 at the encoder shape: fc1 (1280 -> 5120) and fc2 (5120 -> 1280) on
+        X[1500, *] with activations quantized at run time.  Timed twice: the two
+        wq_matmul_w4a4 calls on activations already packed (their producer quantizes them),
+        and the whole W4A4 step with wq_quantize_act of each input in front."""
+        lay = []
+        for i, (n, k) in enumerate([(ENC_FFN, ENC_D), (ENC_D, ENC_FFN)]):
+            w, b, x = linear_case(3000 + i, n, k, ENC_M, row_lognormal_sigma=0.3)
+            d, c, s = quantize_dev(wq.WQ_NVFP4, torch.from_numpy(w).to(dev), False)
+            cb, sb = wq.wq_act_packed_size(ENC_M, k)
+            nb = wq.wq_w4a4_workspace_size(d, ENC_M)
+            e = dict(d=d, c=c, s=s, b=bf16_dev(b), x=bf16_dev(x), n=n, k=k,
+                     xc=torch.empty(cb, dtype=torch.uint8, device=dev), xs=torch.empty(sb, dtype=torch.uint8, device=dev),
+                     y=torch.empty((ENC_M, n), dtype=torch.int16, device=dev),
+                     ws=torch.zeros(nb, dtype=torch.uint8, device=dev), nb=nb)
+            wq.wq_quantize_act(ENC_M, k, e["x"], k, e["xc"], e["xs"])
+            lay.append(e)
+        torch.cuda.synchronize()
+
+        def mm_step(s_, st):
+            for e in lay:
+                wq.wq_matmul_w4a4(e["d"], ENC_M, e["xc"], e["xs"], e["c"], e["s"], e["b"], e["y"], wq.WQ_BF16, e["n"],
+                                  e["ws"], e["nb"], stream=st)
+
+        def full_step(s_, st):
+            for e in lay:
+                wq.wq_quantize_act(ENC_M, e["k"], e["x"], e["k"], e["xc"], e["xs"], stream=st)
+                wq.wq_matmul_w4a4(e["d"], ENC_M, e["xc"], e["xs"], e["c"], e["s"], e["b"], e["y"], wq.WQ_BF16, e["n"],
+                                  e["ws"], e["nb"], stream=st)
+
+        def act_step(s_, st):
+            for e in lay:
+                wq.wq_quantize_act(ENC_M, e["k"], e["x"], e["k"], e["xc"], e["xs"], stream=st)
+
+        reps = 50
+        flops = sum(2.0 * ENC_M * e["n"] * e["k"] for e in lay)
+        tm = run_graph_steps(mm_step, 1, reps, 10, per_graph=10)
+        tf = run_graph_steps(full_step, 1, reps, 10, per_graph=10)
+        ta = run_graph_steps(act_step, 1, reps, 10, per_graph=10)
+        tfl_m = flops * reps / tm / 1e12
+        out = {
+            "config": {"workload": "encoder fc1 1280->5120 and fc2 5120->1280, NVFP4 W4A4, X[1500,*] quantized "
+                                   "per 16 values at run time"},
+            "matmul_us_per_step": round(tm * 1e6 / reps, 2),
+            "TFLOPs": round(tfl_m, 2),
+            "frac_bf16_peak": round(tfl_m / BF16_PEAK_TFLOPS, 4),
+            "frac_fp4_peak": round(tfl_m / FP4_PEAK_TFLOPS, 4),
+            "contraction_unit": "bf16 MFMA on exact e2m1*E4M3 expansions (E4M3 per 16 has no exact form on the "
+                                "E8M0-per-32 fp4 MFMA)",
+            "with_act_quant_us_per_step": round(tf * 1e6 / reps, 2),
+            "TFLOPs_with_act_quant": round(flops * reps / tf / 1e12, 2),
+            "act_quant_us_per_step": round(ta * 1e6 / reps, 2),
+        }
+        if w4a16_us:
+            out["over_w4a16"] = round(tm * 1e6 / reps / w4a16_us, 3)
+        log(f"[bench] w4a4: {out}")
+        return out
+
     if args.encoder_only:
         print(json.dumps({"encoder": encoder_part()}), flush=True)
+        return
+    if args.w4a4_only:
+        print(json.dumps({"w4a4": w4a4_part()}), flush=True)
         return
 
     # ---------------- decode set: NF4 + double-quant, pool of weight copies ----------------
@@ -598,6 +663,7 @@ def main():
         encoder = encoder_part()
         extras["unfused_ablation"] = ablation_part(encoder_part.layers, encoder["us_per_step"], ms_per_step * 1e3)
         encoder_part.layers = None
+        extras["encoder_w4a4_nvfp4"] = w4a4_part(encoder["us_per_step"])
 
         # ---- the decode set (M = 1) in every format, same weights ----
         extras["decode_m1_by_format"] = decode_by_format()

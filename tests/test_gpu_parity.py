@@ -442,6 +442,37 @@ def test_matmul_qkv_into_slab_rows(orc, fmt, dq, m, splits):
                 what="qkv")
 
 
+@pytest.mark.parametrize("m", [1500, 6000])
+def test_encoder_qkv_q8_0_as_timed(orc, m):
+    """The encoder's fused Q/K/V in q8_0 exactly as the encoder sweep and the batch-4 layer
+    run it: one wq_matmul_qkv over the concatenated 3840 x 1280 weights, bf16 output, the
+    three 1280-column windows side by side in one [m, 3840] buffer (row stride 3840, key
+    bias zero).  Equal to the single-output call bit for bit, within the bound of the
+    oracle on sampled rows."""
+    n, k = 3 * 1280, 1280
+    d, codes, scales, ref, b = quantized(orc, Q8_0, False, 5100, n, k)
+    b = b.copy()
+    b[1280:2560] = 0
+    x = linear_case(5100, n, k, m)[2]
+    X, B = dev_bf16(x), dev_bf16(b)
+    say("encoder qkv q8_0", m)
+    Yq = torch.full((m, n), 0x7BAD, dtype=torch.int16, device=DEV)
+    p0 = Yq.data_ptr()
+    ws, wsb = workspace(d, m)
+    wq.wq_matmul_qkv(d, m, X, k, codes, scales, B, [1280] * 3, [p0, p0 + 2 * 1280, p0 + 4 * 1280], [n] * 3,
+                     wq.WQ_BF16, ws, wsb)
+    Y = torch.full((m, n), 0x7BAD, dtype=torch.int16, device=DEV)
+    ws2, wsb2 = workspace(d, m)
+    wq.wq_matmul(d, m, X, k, codes, scales, B, Y, wq.WQ_BF16, n, ws2, wsb2)
+    torch.cuda.synchronize()
+    yq = Yq.cpu().numpy()
+    assert np.array_equal(yq, Y.cpu().numpy())
+    rows = _sample_rows(m, 8)
+    y = bf16_bits_to_f32(yq.view(np.uint16))
+    check_bound(y[rows], orc.matmul(x, ref["w_hat"], b, rows=rows), abs_dot(x, ref["w_hat"], rows=rows),
+                bf16_out=True, what=f"encoder qkv q8_0 m={m}")
+
+
 def test_zero_rows_and_errors_touch_nothing(orc):
     d, codes, scales, ref, b = quantized(orc, NF4, False, 11, 272, 640, outlier_frac=0.01)
     Y = torch.full((4, 272), 3.0, dtype=torch.float32, device=DEV)
