@@ -257,13 +257,16 @@ __device__ __forceinline__ void gemm_dequant4(u32x4 (&B)[NB], const GemmW<FMT> (
 // dequantizes its slice-0 B fragments (when `more`), so the next step starts
 // with its operands in registers.  The next step's requests overwrite xcur's
 // buffer only after this synchronization.
+// half (q8_0 only; wave-uniform): the step holds only 64 K values (k an odd multiple of 64),
+// and the MFMAs of K slices 2 and 3 are skipped.  Their loads past k read zeros (W, through the
+// buffer range) or values of other columns (X), and never reach an MFMA.
 template <int FMT, bool DQ, int NB, int NWAIT, bool MORE>
 __device__ __forceinline__ void gemm_kstep(f32x4 (&acc)[8][NB], u32x4 (&A)[8], u32x4 (&B)[NB],
                                            const GemmW<FMT> (&wc)[NB], GemmW<FMT> (&wn)[NB], const GemmW<FMT> (&wf)[NB],
                                            const GemmSrc& S, const int64_t (&rowblk)[NB], const uint32_t (&xoff)[kXLoads],
                                            const uint8_t* xcur, uint8_t* xnext, const uint8_t* xfol, const uint32_t* lut,
                                            int nx, int wave, int lane, int r, int h, uint32_t lane8,
-                                           uint32_t hs, float mu) {
+                                           uint32_t hs, float mu, bool half = false) {
     gemm_load_w4<FMT, DQ, NB>(wn, S, rowblk, nx, lane, r);
     gemm_load_x_lds(xnext, S, xoff, wave, nx);
     const uint32_t arow = (uint32_t)r * 256u;
@@ -279,7 +282,8 @@ __device__ __forceinline__ void gemm_kstep(f32x4 (&acc)[8][NB], u32x4 (&A)[8], u
 #pragma unroll
         for (int mf = 0; mf < 8; mf++) {
 #pragma unroll
-            for (int nf = 0; nf < NB; nf++) acc[mf][nf] = mfma(A[mf], B[nf], acc[mf][nf]);
+            for (int nf = 0; nf < NB; nf++)
+                if (FMT != kQ8_0 || j < 2 || !half) acc[mf][nf] = mfma(A[mf], B[nf], acc[mf][nf]);
             if (refill) A[mf] = gemm_load_a(asrc, arow, mf, aslice, h, r);
         }
         // 8 NB MFMAs, each followed by a share of the next slice's dequant; the A
@@ -323,7 +327,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     const int64_t M = a.m, N = a.n, K = a.k;
     constexpr int TK = tile_k(FMT);
     const int64_t KT = K / TK;
-    const int64_t nsteps_total = K / BK;
+    // q8_0 k may be an odd multiple of 64: its last step is then half a step
+    const int64_t nsteps_total = FMT == kQ8_0 ? (K + BK - 1) / BK : K / BK;
 
     // XCD-aware item order.  Workgroups are dealt to the 8 XCDs in turn, so XCD x
     // gets the consecutive items [x * per_xcd, (x + 1) * per_xcd).  Items run K piece
@@ -398,6 +403,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
 
     // every K piece is non-empty (the schedule guarantees s0 < s1)
     const int first = (int)s0, last = (int)s1 - 1, end = (int)s1;
+    const bool half_last = FMT == kQ8_0 && (K % BK) != 0 && end == nsteps_total;
     GemmW<FMT> w0[NB], w1[NB];
     gemm_load_w4<FMT, DQ, NB>(w0, S, rowblk, first, lane, r);
     gemm_load_x_lds(xs0, S, xoff, wave, first);
@@ -438,10 +444,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
         gemm_kstep<FMT, DQ, NB, 0, true>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, last,
                                      wave, lane, r, h, lane8, hs, mu);
         gemm_kstep<FMT, DQ, NB, 0, false>(acc, A, B, w1, w0, w0, S, rowblk, xoff, xs1, xs0, xs0, lut, last,
-                                      wave, lane, r, h, lane8, hs, mu);
+                                      wave, lane, r, h, lane8, hs, mu, half_last);
     } else {
         gemm_kstep<FMT, DQ, NB, 0, false>(acc, A, B, w0, w1, w1, S, rowblk, xoff, xs0, xs1, xs1, lut, last,
-                                      wave, lane, r, h, lane8, hs, mu);
+                                      wave, lane, r, h, lane8, hs, mu, half_last);
     }
     wait_vm<0>();   // the last requests (re-reads of the last step) land before the workgroup ends
 
@@ -679,7 +685,7 @@ static Sched gemm_sched(int64_t m, int64_t n, int64_t k, bool allow_split) {
     s.nb = s.tiles_m * ((n + 255) / 256) < kNumCU / 2 ? 2 : 4;
     const int64_t bn = 64 * s.nb;
     s.tiles_n = (n + bn - 1) / bn;
-    const int64_t steps = k / BK;
+    const int64_t steps = (k + BK - 1) / BK;
     const int64_t tiles = s.tiles_m * s.tiles_n;
     int ks = 1;
     if (allow_split && tiles < kNumCU / 2) {

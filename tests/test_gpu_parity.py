@@ -158,6 +158,26 @@ def test_matmul_ragged(orc, fmt, dq, m):
     check_bound(y, y_ref, ad, bf16_out=True, what="bf16 out, odd ldy")
 
 
+@pytest.mark.parametrize("fmt,dq", [(NVFP4, False), (Q8_0, False), (Q4_0, False), (NF4, True), (Q6_K, False)],
+                         ids=["nvfp4", "q8_0", "q4_0", "nf4dq", "q6_k"])
+@pytest.mark.parametrize("k", [64, 128, 192, 256, 320, 384, 512, 640, 768, 896, 1664])
+def test_gemm_k_steps_and_pipeline_tails(orc, fmt, dq, k):
+    """GEMM (M = 100 and 300, 128 x 128 tiles) over every count of 128-wide K steps up to 7
+    and 13: the pipeline's prologue, its three-step loop and each of its tails; q8_0 also at
+    k = 64 mod 128 (its tiles are 64 wide)."""
+    if fmt != Q8_0 and k % 128:
+        pytest.skip("k must be a multiple of 128 for this format")
+    if fmt == Q6_K and k % 256:
+        pytest.skip("q6_k needs k % 256 == 0")
+    n = 272
+    d, codes, scales, ref, b = quantized(orc, fmt, dq, 4300, n, k)
+    for m in (100, 300):
+        x = linear_case(4300 + m, n, k, m)[2]
+        say("gemm k steps", NAMES[fmt], m, n, k)
+        y = gpu_matmul(d, codes, scales, x, b)
+        check_bound(y, orc.matmul(x, ref["w_hat"], b), abs_dot(x, ref["w_hat"]), what=f"{NAMES[fmt]} m={m} k={k}")
+
+
 @pytest.mark.parametrize("fmt,dq", FORMATS, ids=FMT_IDS)
 @pytest.mark.parametrize("ydt,ldy_pad", [(wq.WQ_F32, 0), (wq.WQ_BF16, 0), (wq.WQ_BF16, 1), (wq.WQ_F32, 3)],
                          ids=["f32", "bf16", "bf16-odd-ldy", "f32-odd-ldy"])
