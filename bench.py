@@ -52,6 +52,8 @@ def main():
     ap.add_argument("--no-extras", action="store_true", help="only the decode set (for profiling)")
     ap.add_argument("--encoder-only", action="store_true",
                     help="only the encoder GEMMs (NVFP4, M=1500), for MFMA counter runs")
+    ap.add_argument("--stream-only", action="store_true",
+                    help="only the 433 MB streaming GEMV (for profiling)")
     ap.add_argument("--w4a4-only", action="store_true",
                     help="only the NVFP4 W4A4 encoder GEMMs (M=1500), for profiling")
     args = ap.parse_args()
@@ -281,11 +283,42 @@ def main():
         log(f"[bench] w4a4: {out}")
         return out
 
+    def streaming_part():
+        """One launch streams 433 MB: the fc1 geometry (K = 1280) widened to N = 655360 rows,
+        NF4 + double-quant, M = 1; 20 timed launches on one weight set (larger than the
+        Infinity Cache, read in order, so every launch reads it from HBM)."""
+        gen = torch.Generator(device=dev).manual_seed(7)
+        ns, ks = 655360, 1280
+        wbig = torch.randn((ns, ks), device=dev, generator=gen, dtype=torch.float32) * 0.02
+        d_s, c_s, s_s = quantize_dev(wq.WQ_NF4, wbig, True)
+        del wbig
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        xs = bf16_dev(linear_case(9, 16, ks, 1)[2])
+        ys = torch.empty((1, ns), dtype=torch.int16, device=dev)
+        nbs = wq.wq_workspace_size(d_s, 1)
+        wss_ = torch.zeros(max(nbs, 16), dtype=torch.uint8, device=dev)
+        sbytes = c_s.numel() + s_s.numel()
+        reps = 20
+        ts = run_graph_steps(lambda s, st: wq.wq_matmul(d_s, 1, xs, ks, c_s, s_s, None, ys, wq.WQ_BF16, ns,
+                                                        wss_ if nbs else None, nbs, stream=st), 1, reps, 5, per_graph=5)
+        out = {"shape": f"M=1 N={ns} K={ks} NF4+DQ", "bytes": sbytes,
+               "us": round(ts * 1e6 / reps, 2),
+               "GBps": round(sbytes * reps / ts / 1e9, 1),
+               "frac_hbm": round(sbytes * reps / ts / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] streaming: {out}")
+        del c_s, s_s
+        torch.cuda.empty_cache()
+        return out
+
     if args.encoder_only:
         print(json.dumps({"encoder": encoder_part()}), flush=True)
         return
     if args.w4a4_only:
         print(json.dumps({"w4a4": w4a4_part()}), flush=True)
+        return
+    if args.stream_only:
+        print(json.dumps({"streaming_gemv": streaming_part()}), flush=True)
         return
 
     # ---------------- decode set: NF4 + double-quant, pool of weight copies ----------------
@@ -654,29 +687,7 @@ def main():
                                       "algorithmic_GBps": round(decode_bytes(m) * pool_n * 2 / tm / 1e9, 2)}
             log(f"[bench] decode M={m}: {extras[f'decode_m{m}']}")
 
-        # ---- streaming GEMV: one launch reads 433 MB (fc1 geometry, N = 655360) ----
-        gen = torch.Generator(device=dev).manual_seed(7)
-        ns, ks = 655360, 1280
-        wbig = torch.randn((ns, ks), device=dev, generator=gen, dtype=torch.float32) * 0.02
-        d_s, c_s, s_s = quantize_dev(wq.WQ_NF4, wbig, True)
-        del wbig
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
-        xs = bf16_dev(linear_case(9, 16, ks, 1)[2])
-        ys = torch.empty((1, ns), dtype=torch.int16, device=dev)
-        nbs = wq.wq_workspace_size(d_s, 1)
-        wss_ = torch.zeros(max(nbs, 16), dtype=torch.uint8, device=dev)
-        sbytes = c_s.numel() + s_s.numel()
-        reps = 20
-        ts = run_graph_steps(lambda s, st: wq.wq_matmul(d_s, 1, xs, ks, c_s, s_s, None, ys, wq.WQ_BF16, ns,
-                                                        wss_ if nbs else None, nbs, stream=st), 1, reps, 5, per_graph=5)
-        extras["streaming_gemv"] = {"shape": f"M=1 N={ns} K={ks} NF4+DQ", "bytes": sbytes,
-                                    "us": round(ts * 1e6 / reps, 2),
-                                    "GBps": round(sbytes * reps / ts / 1e9, 1),
-                                    "frac_hbm": round(sbytes * reps / ts / 1e9 / HBM_PEAK_GBS, 4)}
-        log(f"[bench] streaming: {extras['streaming_gemv']}")
-        del c_s, s_s
-        torch.cuda.empty_cache()
+        extras["streaming_gemv"] = streaming_part()
 
         encoder = encoder_part()
         extras["unfused_ablation"] = ablation_part(encoder_part.layers, encoder["us_per_step"], ms_per_step * 1e3)

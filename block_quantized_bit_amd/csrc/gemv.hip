@@ -458,25 +458,32 @@ struct StreamBand {
     int32_t jt;        // double quant: blocks of the row that belong to group A
 };
 
-template <int FMT, bool DQ, int T>
-__device__ __forceinline__ void stream_load_band(StreamTile (&R)[T], StreamBand& B, const KArgs& a, int64_t band,
-                                                 int lane, int r, int64_t KT) {
+// Request tile s of a band (codes and this lane's scale record) into R.
+template <int FMT, bool DQ>
+__device__ __forceinline__ void stream_load_tile(StreamTile& R, BufRes rc, BufRes rs, int s, int lane, int r) {
     constexpr int SB = tile_scale_bytes<FMT, DQ>();
-    const BufRes rc = buf_res(a.codes + band * KT * kTileBytes, (uint32_t)(KT * kTileBytes));
-    const BufRes rs = buf_res(a.scales + band * KT * SB, (uint32_t)(KT * SB));
-#pragma unroll
-    for (int s = 0; s < T; s++) {
-        R[s].code = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16 + s * kTileBytes, 0, kNT));
-        if constexpr (FMT == kNF4 && DQ) {
-            R[s].sc[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, r * 2 + s * SB, 0, kNT);
-        } else if constexpr (FMT == kQ8_0) {
-            R[s].sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, r * 4 + s * SB, 0, kNT);
-        } else {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, r * 8 + s * SB, 0, kNT);
-            R[s].sc[0] = v[0];
-            R[s].sc[1] = v[1];
-        }
+    R.code = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16 + s * kTileBytes, 0, kNT));
+    if constexpr (FMT == kNF4 && DQ) {
+        R.sc[0] = __builtin_amdgcn_raw_buffer_load_b16(rs, r * 2 + s * SB, 0, kNT);
+    } else if constexpr (FMT == kQ8_0) {
+        R.sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, r * 4 + s * SB, 0, kNT);
+    } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, r * 8 + s * SB, 0, kNT);
+        R.sc[0] = v[0];
+        R.sc[1] = v[1];
     }
+}
+
+template <int FMT, bool DQ>
+__device__ __forceinline__ void stream_band_res(const KArgs& a, int64_t band, int64_t KT, BufRes& rc, BufRes& rs) {
+    constexpr int SB = tile_scale_bytes<FMT, DQ>();
+    rc = buf_res(a.codes + band * KT * kTileBytes, (uint32_t)(KT * kTileBytes));
+    rs = buf_res(a.scales + band * KT * SB, (uint32_t)(KT * SB));
+}
+
+// The per-band values of this lane's column: bias and the double-quant group scales.
+template <int FMT, bool DQ>
+__device__ __forceinline__ void stream_load_band_consts(StreamBand& B, const KArgs& a, int64_t band, int r) {
     const int64_t col = band * 16 + r;
     B.braw = a.bias ? (uint32_t)a.bias[col] : 0u;
     if constexpr (FMT == kNF4 && DQ) {
@@ -490,11 +497,27 @@ __device__ __forceinline__ void stream_load_band(StreamTile (&R)[T], StreamBand&
     }
 }
 
-template <int FMT, bool DQ, int NI, int T>
-__device__ __forceinline__ void stream_band(const StreamTile (&R)[T], const StreamBand& B, const KArgs& a,
-                                            int64_t band, const uint16_t* xrow, const uint16_t* xzero, int h,
-                                            uint32_t lane4, const uint32_t* lut, float mu, float g, int64_t KT) {
+template <int FMT, bool DQ, int T>
+__device__ __forceinline__ void stream_load_band(StreamTile (&R)[T], StreamBand& B, const KArgs& a, int64_t band,
+                                                 int lane, int r, int64_t KT) {
+    BufRes rc, rs;
+    stream_band_res<FMT, DQ>(a, band, KT, rc, rs);
+#pragma unroll
+    for (int s = 0; s < T; s++) stream_load_tile<FMT, DQ>(R[s], rc, rs, s, lane, r);
+    stream_load_band_consts<FMT, DQ>(B, a, band, r);
+}
+
+// Consume band `band` from R and B.  REFILL: as soon as tile s has been used, its
+// registers request tile s of band `next`, and B is reloaded for `next` after the
+// outputs (otherwise the caller requests whole bands).
+template <int FMT, bool DQ, int NI, int T, bool REFILL>
+__device__ __forceinline__ void stream_band(StreamTile (&R)[T], StreamBand& B, const KArgs& a, int64_t band,
+                                            int64_t next, const uint16_t* xrow, const uint16_t* xzero, int h,
+                                            int lane, int r, uint32_t lane4, const uint32_t* lut, float mu, float g,
+                                            int64_t KT) {
     constexpr int TK = tile_k(FMT);
+    BufRes rc, rs;
+    if constexpr (REFILL) stream_band_res<FMT, DQ>(a, next, KT, rc, rs);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < T; s++) {
@@ -516,6 +539,7 @@ __device__ __forceinline__ void stream_band(const StreamTile (&R)[T], const Stre
             }
             gemv_consume<FMT, DQ, NI>(t, acc, lut, lane4, h, mu);
         }
+        if constexpr (REFILL) stream_load_tile<FMT, DQ>(R[s], rc, rs, s, lane, r);
         __builtin_amdgcn_sched_barrier(0);   // keep tiles in order: bounded register use
     }
     // lane (h, r) holds rows 4h .. 4h+3 of column band * 16 + r
@@ -526,8 +550,20 @@ __device__ __forceinline__ void stream_band(const StreamTile (&R)[T], const Stre
         const int mm = 4 * h + i;
         if (mm < a.m) put_out(a, c, mm, acc[i], g);
     }
+    if constexpr (REFILL) stream_load_band_consts<FMT, DQ>(B, a, next, r);
 }
 
+// Tile-by-tile refill for the one-token NF4 double-quant kernel, where it keeps more
+// requests in flight within the same registers; the other variants request whole
+// bands (the refill order costs them registers: spills for q4_0 and four-row tiles).
+template <int FMT, bool DQ, int NI>
+constexpr bool stream_refill() { return FMT == kNF4 && DQ && NI == 1; }
+
+// Each wave keeps two bands in two register sets.  With the refill order a set is
+// refilled tile by tile while it is consumed (between one and two bands of requests in
+// flight per wave); otherwise the next band's set is requested before the current one
+// is consumed.  Prefetch indices past the end are clamped to the last band (in-bounds
+// re-reads).
 template <int FMT, bool DQ, int NI, int T>
 __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
     __shared__ uint32_t lut[gemv_uses_lut<FMT>() ? kLutWords : 1];
@@ -542,15 +578,17 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
     const int64_t KT = a.k / tile_k(FMT);
     const int64_t nbands = a.n / 16;
     const int64_t stride = (int64_t)gridDim.x * 4;
+    const int64_t last = nbands - 1;
 
     float g = 1.0f, mu = 0.0f;
     if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.gs);
     if constexpr (FMT == kNF4 && DQ) mu = load_f32_vmem(a.scales + a.L.mu_off);
 
     int64_t band = (int64_t)blockIdx.x * 4 + wave;
+    constexpr bool RF = stream_refill<FMT, DQ, NI>();
     StreamTile R0[T], R1[T];
     StreamBand B0, B1;
-    stream_load_band<FMT, DQ, T>(R0, B0, a, std::min<int64_t>(band, nbands - 1), lane, r, KT);
+    stream_load_band<FMT, DQ, T>(R0, B0, a, std::min<int64_t>(band, last), lane, r, KT);
     // stage X (m rows of k bf16, rows contiguous in LDS) and the zero row
     if (tid < 16) *reinterpret_cast<uint4*>(xs + kStreamXMax + tid * 8) = make_uint4(0u, 0u, 0u, 0u);
     const int64_t nx = (int64_t)a.m * a.k;
@@ -558,17 +596,20 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
         const int64_t row = i / a.k, col = i - row * a.k;
         *reinterpret_cast<uint4*>(xs + i) = *reinterpret_cast<const uint4*>(a.x + row * a.ldx + col);
     }
+    if constexpr (RF) stream_load_band<FMT, DQ, T>(R1, B1, a, std::min<int64_t>(band + stride, last), lane, r, KT);
     if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 256>(lut);
     __syncthreads();
     const uint16_t* xrow = xs + (r < a.m ? r : 0) * a.k + h * 8;
     const uint16_t* xzero = xs + kStreamXMax + h * 8;
 
     for (; band < nbands; band += 2 * stride) {
-        stream_load_band<FMT, DQ, T>(R1, B1, a, std::min<int64_t>(band + stride, nbands - 1), lane, r, KT);
-        stream_band<FMT, DQ, NI, T>(R0, B0, a, band, xrow, xzero, h, lane4, lut, mu, g, KT);
+        const int64_t b1 = std::min<int64_t>(band + stride, last), b2 = std::min<int64_t>(band + 2 * stride, last);
+        if constexpr (!RF) stream_load_band<FMT, DQ, T>(R1, B1, a, b1, lane, r, KT);
+        stream_band<FMT, DQ, NI, T, RF>(R0, B0, a, band, b2, xrow, xzero, h, lane, r, lane4, lut, mu, g, KT);
         if (band + stride >= nbands) break;
-        stream_load_band<FMT, DQ, T>(R0, B0, a, std::min<int64_t>(band + 2 * stride, nbands - 1), lane, r, KT);
-        stream_band<FMT, DQ, NI, T>(R1, B1, a, band + stride, xrow, xzero, h, lane4, lut, mu, g, KT);
+        if constexpr (!RF) stream_load_band<FMT, DQ, T>(R0, B0, a, b2, lane, r, KT);
+        stream_band<FMT, DQ, NI, T, RF>(R1, B1, a, band + stride, std::min<int64_t>(band + 3 * stride, last), xrow,
+                                        xzero, h, lane, r, lane4, lut, mu, g, KT);
     }
 }
 

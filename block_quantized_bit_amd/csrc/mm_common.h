@@ -293,15 +293,32 @@ struct ColOut {
     float bias;
 };
 
+// Split i's output base, read through readfirstlane.  The three bases are the same in
+// every lane; selecting between plain reads of them lets the compiler fold the
+// per-lane choice into one per-lane load from the kernel-argument block, a vector
+// memory request whose wait (in-order counting) also waits for every weight request
+// the wave has in flight.
+// (The row strides and split ends likewise.)
+__device__ inline uint64_t out_uni64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+    return (uint64_t)lo | ((uint64_t)hi << 32);
+}
+__device__ inline char* out_base(const OutSplit& o, int i) {
+    return reinterpret_cast<char*>(out_uni64(reinterpret_cast<uint64_t>(o.y[i])));
+}
+__device__ inline int64_t out_ld(const OutSplit& o, int i) { return (int64_t)out_uni64((uint64_t)o.ldy[i]); }
+__device__ inline int64_t out_end(const OutSplit& o, int i) { return (int64_t)out_uni64((uint64_t)o.end[i]); }
+
 __device__ inline ColOut col_out(const KArgs& a, int64_t col) {
     const OutSplit& o = a.out;
     const bool s1 = col >= o.end[0], s2 = col >= o.end[1];
-    char* const y0 = reinterpret_cast<char*>(o.y[0]);
-    char* const y1 = reinterpret_cast<char*>(o.y[1]);
-    char* const y2 = reinterpret_cast<char*>(o.y[2]);
+    char* const y0 = out_base(o, 0);
+    char* const y1 = out_base(o, 1);
+    char* const y2 = out_base(o, 2);
     char* const base = s2 ? y2 : (s1 ? y1 : y0);
-    const int64_t ld = s2 ? o.ldy[2] : (s1 ? o.ldy[1] : o.ldy[0]);
-    const int64_t c0 = s2 ? o.end[1] : (s1 ? o.end[0] : 0);
+    const int64_t ld = s2 ? out_ld(o, 2) : (s1 ? out_ld(o, 1) : out_ld(o, 0));
+    const int64_t c0 = s2 ? out_end(o, 1) : (s1 ? out_end(o, 0) : 0);
     const int64_t es = o.f32 ? 4 : 2;
     ColOut c;
     c.p = base + (col - c0) * es;
@@ -313,12 +330,12 @@ __device__ inline ColOut col_out(const KArgs& a, int64_t col) {
 __device__ inline ColOut col_out_nobias(const KArgs& a, int64_t col) {
     const OutSplit& o = a.out;
     const bool s1 = col >= o.end[0], s2 = col >= o.end[1];
-    char* const y0 = reinterpret_cast<char*>(o.y[0]);
-    char* const y1 = reinterpret_cast<char*>(o.y[1]);
-    char* const y2 = reinterpret_cast<char*>(o.y[2]);
+    char* const y0 = out_base(o, 0);
+    char* const y1 = out_base(o, 1);
+    char* const y2 = out_base(o, 2);
     char* const base = s2 ? y2 : (s1 ? y1 : y0);
-    const int64_t ld = s2 ? o.ldy[2] : (s1 ? o.ldy[1] : o.ldy[0]);
-    const int64_t c0 = s2 ? o.end[1] : (s1 ? o.end[0] : 0);
+    const int64_t ld = s2 ? out_ld(o, 2) : (s1 ? out_ld(o, 1) : out_ld(o, 0));
+    const int64_t c0 = s2 ? out_end(o, 1) : (s1 ? out_end(o, 0) : 0);
     const int64_t es = o.f32 ? 4 : 2;
     ColOut c;
     c.p = base + (col - c0) * es;
@@ -327,12 +344,17 @@ __device__ inline ColOut col_out_nobias(const KArgs& a, int64_t col) {
     return c;
 }
 
-// y = acc * g + bias, converted and stored at row m.
+// y = acc * g + bias, converted and stored at row m.  The store names the global
+// address space: a generic (flat) store would make the compiler's wait insertion treat
+// the vector-memory counter as out of order for as long as the store is in flight,
+// and turn every later wait of a band loop into a wait for all requests.
+typedef __attribute__((address_space(1))) float gfloat_t;
+typedef __attribute__((address_space(1))) uint16_t gu16_t;
 __device__ inline void put_out(const KArgs& a, const ColOut& c, int64_t m, float v, float g) {
     const float r = v * g + c.bias;
     char* const p = c.p + m * c.ld;
-    if (a.out.f32) *reinterpret_cast<float*>(p) = r;
-    else *reinterpret_cast<uint16_t*>(p) = bf16_rne(r);
+    if (a.out.f32) *(gfloat_t*)p = r;
+    else *(gu16_t*)p = bf16_rne(r);
 }
 
 // 4 x 4 transpose inside each quad of lanes (t = lane & 3): on entry v[i] is
