@@ -318,7 +318,7 @@ __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kG
         f32x4 v = red[0][lane];
 #pragma unroll
         for (int w = 1; w < kGemvWaves; w++) v += red[w][lane];
-        const ColOut c = col_out(a, band * 16 + r);
+        const ColOut c = col_out<true>(a, band * 16 + r);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int mm = 4 * h + i;
@@ -543,7 +543,7 @@ __device__ __forceinline__ void stream_band(StreamTile (&R)[T], StreamBand& B, c
         __builtin_amdgcn_sched_barrier(0);   // keep tiles in order: bounded register use
     }
     // lane (h, r) holds rows 4h .. 4h+3 of column band * 16 + r
-    ColOut c = col_out_nobias(a, band * 16 + (__lane_id() & 15));
+    ColOut c = col_out_nobias<true>(a, band * 16 + (__lane_id() & 15));
     c.bias = bf16_value((uint16_t)B.braw);
 #pragma unroll
     for (int i = 0; i < 4; i++) {

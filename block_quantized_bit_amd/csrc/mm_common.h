@@ -293,32 +293,38 @@ struct ColOut {
     float bias;
 };
 
-// Split i's output base, read through readfirstlane.  The three bases are the same in
-// every lane; selecting between plain reads of them lets the compiler fold the
-// per-lane choice into one per-lane load from the kernel-argument block, a vector
+// Split i's output base, read through readfirstlane (UNI = true).  The three bases are
+// the same in every lane; selecting between plain reads of them lets the compiler fold
+// the per-lane choice into one per-lane load from the kernel-argument block, a vector
 // memory request whose wait (in-order counting) also waits for every weight request
-// the wave has in flight.
-// (The row strides and split ends likewise.)
+// the wave has in flight: the GEMV band loops read them this way.  (The row strides
+// and split ends likewise.)  The GEMM reads them plainly: it stores once, after its
+// last request, and the uniform copies held in scalar registers cost its main loop
+// spills.
 __device__ inline uint64_t out_uni64(uint64_t v) {
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
     return (uint64_t)lo | ((uint64_t)hi << 32);
 }
+template <bool UNI>
 __device__ inline char* out_base(const OutSplit& o, int i) {
-    return reinterpret_cast<char*>(out_uni64(reinterpret_cast<uint64_t>(o.y[i])));
+    return UNI ? reinterpret_cast<char*>(out_uni64(reinterpret_cast<uint64_t>(o.y[i]))) : reinterpret_cast<char*>(o.y[i]);
 }
-__device__ inline int64_t out_ld(const OutSplit& o, int i) { return (int64_t)out_uni64((uint64_t)o.ldy[i]); }
-__device__ inline int64_t out_end(const OutSplit& o, int i) { return (int64_t)out_uni64((uint64_t)o.end[i]); }
+template <bool UNI>
+__device__ inline int64_t out_ld(const OutSplit& o, int i) { return UNI ? (int64_t)out_uni64((uint64_t)o.ldy[i]) : o.ldy[i]; }
+template <bool UNI>
+__device__ inline int64_t out_end(const OutSplit& o, int i) { return UNI ? (int64_t)out_uni64((uint64_t)o.end[i]) : o.end[i]; }
 
+template <bool UNI = false>
 __device__ inline ColOut col_out(const KArgs& a, int64_t col) {
     const OutSplit& o = a.out;
     const bool s1 = col >= o.end[0], s2 = col >= o.end[1];
-    char* const y0 = out_base(o, 0);
-    char* const y1 = out_base(o, 1);
-    char* const y2 = out_base(o, 2);
+    char* const y0 = out_base<UNI>(o, 0);
+    char* const y1 = out_base<UNI>(o, 1);
+    char* const y2 = out_base<UNI>(o, 2);
     char* const base = s2 ? y2 : (s1 ? y1 : y0);
-    const int64_t ld = s2 ? out_ld(o, 2) : (s1 ? out_ld(o, 1) : out_ld(o, 0));
-    const int64_t c0 = s2 ? out_end(o, 1) : (s1 ? out_end(o, 0) : 0);
+    const int64_t ld = s2 ? out_ld<UNI>(o, 2) : (s1 ? out_ld<UNI>(o, 1) : out_ld<UNI>(o, 0));
+    const int64_t c0 = s2 ? out_end<UNI>(o, 1) : (s1 ? out_end<UNI>(o, 0) : 0);
     const int64_t es = o.f32 ? 4 : 2;
     ColOut c;
     c.p = base + (col - c0) * es;
@@ -327,15 +333,16 @@ __device__ inline ColOut col_out(const KArgs& a, int64_t col) {
     return c;
 }
 
+template <bool UNI = false>
 __device__ inline ColOut col_out_nobias(const KArgs& a, int64_t col) {
     const OutSplit& o = a.out;
     const bool s1 = col >= o.end[0], s2 = col >= o.end[1];
-    char* const y0 = out_base(o, 0);
-    char* const y1 = out_base(o, 1);
-    char* const y2 = out_base(o, 2);
+    char* const y0 = out_base<UNI>(o, 0);
+    char* const y1 = out_base<UNI>(o, 1);
+    char* const y2 = out_base<UNI>(o, 2);
     char* const base = s2 ? y2 : (s1 ? y1 : y0);
-    const int64_t ld = s2 ? out_ld(o, 2) : (s1 ? out_ld(o, 1) : out_ld(o, 0));
-    const int64_t c0 = s2 ? out_end(o, 1) : (s1 ? out_end(o, 0) : 0);
+    const int64_t ld = s2 ? out_ld<UNI>(o, 2) : (s1 ? out_ld<UNI>(o, 1) : out_ld<UNI>(o, 0));
+    const int64_t c0 = s2 ? out_end<UNI>(o, 1) : (s1 ? out_end<UNI>(o, 0) : 0);
     const int64_t es = o.f32 ? 4 : 2;
     ColOut c;
     c.p = base + (col - c0) * es;
