@@ -356,7 +356,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
 
     float g = 1.0f, mu = 0.0f;
     if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.gs);
-    if constexpr (FMT == kNF4 && DQ) mu = load_f32_vmem(a.scales + a.L.mu_off);
+    if constexpr (FMT == kNF4 && DQ) mu = load_f32_vmem(a.scales + a.mu_off);
 
     // descriptors: band tiles of this wave (bands past n re-read the last band), X rows m0 ..
     GemmSrc S;
@@ -368,19 +368,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
         S.code[nf] = a.codes + band * KT * kTileBytes;
         S.scale[nf] = a.scales + band * KT * SB;
         rowblk[nf] = (band * 16 + r) * (K / 64);
-        if constexpr (FMT == kQ5_0) S.hb[nf] = a.scales + a.L.hb_off + band * KT * 256;
-        if constexpr (FMT == kQ4_K) S.hb[nf] = a.scales + a.L.kd_off + band * 16 * (K / 256) * 4;
+        if constexpr (FMT == kQ5_0) S.hb[nf] = a.scales + a.hb_off + band * KT * 256;
+        if constexpr (FMT == kQ4_K) S.hb[nf] = a.scales + a.kd_off + band * 16 * (K / 256) * 4;
         if constexpr (FMT == kQ6_K) {
             S.hb[nf] = a.codes + N * K / 2 + band * KT * 512;
-            S.kd[nf] = a.scales + a.L.kd_off + band * 16 * (K / 256) * 2;
+            S.kd[nf] = a.scales + a.kd_off + band * 16 * (K / 256) * 2;
         }
     }
     S.hbbytes = FMT == kQ4_K ? (uint32_t)(16 * (K / 256) * 4) : FMT == kQ6_K ? (uint32_t)(KT * 512) : (uint32_t)(KT * 256);
     S.kdbytes = (uint32_t)(16 * (K / 256) * 2);
     S.wbytes = (uint32_t)(KT * kTileBytes);
     S.sbytes = (uint32_t)(KT * SB);
-    S.dt = a.scales + a.L.d_off;
-    S.dtbytes = (uint32_t)(a.L.ng * 4);
+    if constexpr (FMT == kNF4 && DQ) S.dt = a.scales + a.d_off;
+    S.dtbytes = (uint32_t)(a.ng * 4);
     {
         const int64_t xbytes = (M - m0) * a.ldx * 2;
         S.x = reinterpret_cast<const uint8_t*>(a.x + m0 * a.ldx);
@@ -508,7 +508,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
                     float v[4];
 #pragma unroll
                     for (int i = 0; i < 4; i++) v[i] = acc[mf][nf][i] * g + c.bias;
-                    if (a.out.f32) {
+                    if (a.f32) {
 #pragma unroll
                         for (int i = 0; i < 4; i++) *reinterpret_cast<float*>(p + i * c.ld) = v[i];
                     } else {
@@ -585,7 +585,7 @@ __device__ inline void reduce_store(const KArgs& a, int64_t q, const f32x4& v, f
 #pragma unroll
         for (int u = 0; u < 4; u++) o[u] = v[u] * g + (a.bias ? bf16_value(a.bias[col0 + u]) : 0.0f);
         char* p = c.p + mm * c.ld;
-        if (a.out.f32) *reinterpret_cast<f32x4*>(p) = f32x4{o[0], o[1], o[2], o[3]};
+        if (a.f32) *reinterpret_cast<f32x4*>(p) = f32x4{o[0], o[1], o[2], o[3]};
         else *reinterpret_cast<uint2*>(p) = make_uint2((uint32_t)bf16_rne(o[0]) | ((uint32_t)bf16_rne(o[1]) << 16),
                                                       (uint32_t)bf16_rne(o[2]) | ((uint32_t)bf16_rne(o[3]) << 16));
         return;

@@ -30,7 +30,7 @@ struct DqRow {
 __device__ inline DqRow dq_row(const KArgs& a, int64_t row) {
     const int64_t nbr = a.k / 64, b0 = row * nbr;
     const int64_t gA = b0 >> 8, gB = (b0 + nbr - 1) >> 8;
-    const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
+    const float* dt = reinterpret_cast<const float*>(a.scales + a.d_off);
     return DqRow{dt[gA], dt[gB], (int32_t)((gA + 1) * 256 - b0)};
 }
 
@@ -53,7 +53,7 @@ __device__ inline void gemv_load(GemvTile<FMT>& t, const KArgs& a, int64_t band,
                 // group scales: taken from the row's pair at use time (gemv_dq_scales)
             } else {
                 const int64_t b0 = (band * 16 + r) * (a.k / 64) + kt * 2;
-                const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
+                const float* dt = reinterpret_cast<const float*>(a.scales + a.d_off);
                 t.sc[1] = __float_as_uint(dt[b0 >> 8]);
                 t.sc[2] = __float_as_uint(dt[(b0 + 1) >> 8]);
             }
@@ -75,20 +75,20 @@ __device__ inline void gemv_load(GemvTile<FMT>& t, const KArgs& a, int64_t band,
         const uint2 hb = *reinterpret_cast<const uint2*>(a.codes + a.n * a.k / 2 + tile * 512 + lane * 8);
         t.sc[2] = hb.x;
         t.sc[3] = hb.y;
-        t.sc[4] = *reinterpret_cast<const uint16_t*>(a.scales + a.L.kd_off + ((band * 16 + r) * (a.k >> 8) + (kt >> 1)) * 2);
+        t.sc[4] = *reinterpret_cast<const uint16_t*>(a.scales + a.kd_off + ((band * 16 + r) * (a.k >> 8) + (kt >> 1)) * 2);
     } else if constexpr (FMT == kQ4_K) {
         // the row's sub-block record (4 scale bytes, 4 offset bytes) and its super-block's
         // (d, dmin); a 128-K tile is half a 256-K super-block
         const uint2 v = *reinterpret_cast<const uint2*>(a.scales + tile * 128 + r * 8);
         t.sc[0] = v.x;
         t.sc[1] = v.y;
-        t.sc[2] = *reinterpret_cast<const uint32_t*>(a.scales + a.L.kd_off + ((band * 16 + r) * (a.k >> 8) + (kt >> 1)) * 4);
+        t.sc[2] = *reinterpret_cast<const uint32_t*>(a.scales + a.kd_off + ((band * 16 + r) * (a.k >> 8) + (kt >> 1)) * 4);
     } else if constexpr (FMT == kQ5_0) {
         // the row's four fp16 scales (8 bytes), then its four fifth-bit words (16 bytes)
         const uint2 v = *reinterpret_cast<const uint2*>(a.scales + (tile * 64 + r * 4) * 2);
         t.sc[0] = v.x;
         t.sc[1] = v.y;
-        const uint4 hb = *reinterpret_cast<const uint4*>(a.scales + a.L.hb_off + tile * 256 + r * 16);
+        const uint4 hb = *reinterpret_cast<const uint4*>(a.scales + a.hb_off + tile * 256 + r * 16);
         t.sc[2] = hb.x;
         t.sc[3] = hb.y;
         t.sc[4] = hb.z;
@@ -272,7 +272,7 @@ __device__ __forceinline__ void gemv_load_band(GemvTile<FMT> (&R)[C], DqRow& dq,
         if (s == 0) {
             if constexpr (DR) dq = dq_row(a, band * 16 + r);
             if constexpr (FMT == kNF4 && DQ) {
-                if (mu) *mu = load_f32_vmem(a.scales + a.L.mu_off);
+                if (mu) *mu = load_f32_vmem(a.scales + a.mu_off);
             }
         }
     }
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
     // the wait for the copy does not wait for it; without the copy, up front.
     float g = 1.0f, mu = 0.0f;
     if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.gs);
-    if constexpr (FMT == kNF4 && DQ && !XL) mu = load_f32_vmem(a.scales + a.L.mu_off);
+    if constexpr (FMT == kNF4 && DQ && !XL) mu = load_f32_vmem(a.scales + a.mu_off);
     constexpr int kMuLoads = (FMT == kNF4 && DQ && XL) ? 1 : 0;
     float* const mu_first = kMuLoads ? &mu : nullptr;
     const uint16_t* xrow = a.x + (int64_t)(r < a.m ? r : 0) * a.ldx + h * 8;
@@ -395,7 +395,7 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
         }
         gemv_finish_band(a, red, acc, band, wave, lane, g);
     } else {
-        const int64_t stride = gridDim.x;
+        const int64_t stride = (int64_t)a.wg_per_cu * kNumCU;   // the grid (gemv_launch_cx)
         GemvTile<FMT> R0[C], R1[C];
         DqRow dq0, dq1;
         int64_t band = blockIdx.x;
@@ -440,6 +440,7 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
 // spans at most two 256-block groups).
 // ===========================================================================
 constexpr int kStreamXMax = 8192 - 128;   // bf16 elements of X staged in LDS (m * k), then 128 zeros
+constexpr int kStreamGrid = 2 * kNumCU;     // two workgroups of 4 waves per CU
 
 // Scale bytes per tile and per lane (one row of the tile) in the packed layout.
 template <int FMT, bool DQ>
@@ -490,7 +491,7 @@ __device__ __forceinline__ void stream_load_band_consts(StreamBand& B, const KAr
         const int64_t nbr = a.k / 64;                 // blocks per row
         const int64_t b0 = col * nbr;                 // first block of the row
         const int64_t gA = b0 >> 8, gB = (b0 + nbr - 1) >> 8;
-        const float* dt = reinterpret_cast<const float*>(a.scales + a.L.d_off);
+        const float* dt = reinterpret_cast<const float*>(a.scales + a.d_off);
         B.dA = dt[gA];
         B.dB = dt[gB];
         B.jt = (int32_t)((gA + 1) * 256 - b0);
@@ -577,12 +578,12 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
     const uint32_t lane4 = (uint32_t)lane << 2;
     const int64_t KT = a.k / tile_k(FMT);
     const int64_t nbands = a.n / 16;
-    const int64_t stride = (int64_t)gridDim.x * 4;
+    const int64_t stride = (int64_t)kStreamGrid * 4;   // waves of the grid (gemv_launch_ni)
     const int64_t last = nbands - 1;
 
     float g = 1.0f, mu = 0.0f;
     if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.gs);
-    if constexpr (FMT == kNF4 && DQ) mu = load_f32_vmem(a.scales + a.L.mu_off);
+    if constexpr (FMT == kNF4 && DQ) mu = load_f32_vmem(a.scales + a.mu_off);
 
     int64_t band = (int64_t)blockIdx.x * 4 + wave;
     constexpr bool RF = stream_refill<FMT, DQ, NI>();
@@ -651,7 +652,9 @@ static void gemv_launch_cx(const KArgs& a, int64_t nbands, int64_t KT, hipStream
     if constexpr (C <= 2) {
         const int64_t resident = per_cu * (int64_t)kNumCU;
         if (nbands > resident && (KT + kGemvWaves - 1) / kGemvWaves <= C) {
-            hipLaunchKernelGGL((k_gemv<FMT, DQ, NI, C, true, XL>), dim3((unsigned)resident), block, xbytes, st, a);
+            KArgs b = a;
+            b.wg_per_cu = (uint8_t)per_cu;
+            hipLaunchKernelGGL((k_gemv<FMT, DQ, NI, C, true, XL>), dim3((unsigned)resident), block, xbytes, st, b);
             return;
         }
     }
@@ -685,7 +688,7 @@ static void gemv_launch_ni(const KArgs& a, hipStream_t st) {
     // the general kernel)
     if constexpr (FMT != kQ4_1 && FMT != kQ5_0 && FMT != kQ4_K && FMT != kQ6_K) {
         if (nbands >= kStreamMinBands && (int64_t)a.m * a.k <= kStreamXMax && KT <= 10) {
-            const unsigned grid = 2 * kNumCU;
+            const unsigned grid = kStreamGrid;
             if (KT <= 4) hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 4>), dim3(grid), dim3(256), 0, st, a);
             else hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 10>), dim3(grid), dim3(256), 0, st, a);
             return;

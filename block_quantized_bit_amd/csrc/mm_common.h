@@ -46,24 +46,43 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kLutWords = 256 * 64;   // 256 byte values x 64 lane slots
 
+// Kernel arguments.  A launch reads its argument block from memory, cold, one 128-byte
+// line per round trip, and a second line on a kernel's path costs a GEMV launch up to
+// three quarters of a microsecond: every field a GEMV launch reads sits in the first
+// line (the 32-bit fields rest on the boundary's limits: n, ldy < 2^31).  The GEMM's
+// own fields follow, and after the struct the hidden arguments (grid size): GEMV kernels
+// take their grid from a field or a constant instead of gridDim.
 struct KArgs {
-    const uint16_t* x;
-    int64_t ldx;
-    int m;
-    int64_t n, k;
-    const uint8_t* codes;
-    const uint8_t* scales;
-    const uint8_t* gs;   // NVFP4: address of the fp32 factor applied in the epilogue (the global scale)
-    const uint16_t* bias;
-    OutSplit out;
-    ScaleLayout L;
-    int ksplit;          // K pieces per output tile
-    int64_t kt_per;      // K tiles (of tile_k) per piece
-    float* partial;      // [ksplit][m][n] when ksplit > 1
+    const uint16_t* x;       // 0x00
+    const uint8_t* codes;    // 0x08
+    const uint8_t* scales;   // 0x10
+    union {                  // 0x18 one per format:
+        const uint8_t* gs;   //   NVFP4: address of the fp32 factor applied in the epilogue (the global scale)
+        int64_t d_off;       //   NF4+DQ: fp32 group scales    } offsets into scales,
+        int64_t hb_off;      //   q5_0: fifth-bit words        } as in ScaleLayout
+        int64_t kd_off;      //   q4_k / q6_k: super-block scales
+    };
+    const uint16_t* bias;    // 0x20
+    char* y0;                // 0x28 output splits: columns [0, end0) -> y0, [end0, end1) -> y1,
+    char* y1;                // 0x30   [end1, n) -> y2 (one split: end0 = end1 = n)
+    char* y2;                // 0x38
+    int64_t n, k;            // 0x40, 0x48
+    int64_t ldx;             // 0x50
+    int64_t mu_off;          // 0x58 NF4+DQ: fp32 mean (offset into scales)
+    int m;                   // 0x60
+    int ldy0, ldy1, ldy2;    // 0x64 row strides of the splits (elements)
+    int end0, end1;          // 0x70
+    uint8_t f32;             // 0x78 1: fp32 output, 0: bf16
+    uint8_t out_vec;         // 0x79 every output split allows 4-column vector stores (alignment, split ends % 4)
+    uint8_t out_v16;         // 0x7A bf16 output whose splits allow 8-column (16-byte) stores
+    uint8_t wg_per_cu;       // 0x7B band-pipelined GEMV: workgroups per CU (its grid is that many per CU)
+    int ksplit;              // 0x7C K pieces per output tile
+    int64_t ng;              // 0x80 NF4+DQ: number of 256-block groups
+    int64_t kt_per;          // K tiles (of tile_k) per piece
+    float* partial;          // [ksplit][m][n] when ksplit > 1
     int64_t tiles_m, tiles_n;
-    int out_vec;         // every output split allows 4-column vector stores (alignment, split ends % 4)
-    int out_v16;         // bf16 output whose splits allow 8-column (16-byte) stores
 };
+static_assert(__builtin_offsetof(KArgs, ng) == 128, "the GEMV's arguments fill the first 128 bytes");
 
 // One fp32 value at a uniform address (the NVFP4 global scale, the double-quant mean),
 // read with a vector buffer load.  A plain read of a uniform address becomes a scalar
@@ -293,61 +312,47 @@ struct ColOut {
     float bias;
 };
 
-// Split i's output base, read through readfirstlane (UNI = true).  The three bases are
-// the same in every lane; selecting between plain reads of them lets the compiler fold
-// the per-lane choice into one per-lane load from the kernel-argument block, a vector
-// memory request whose wait (in-order counting) also waits for every weight request
-// the wave has in flight: the GEMV band loops read them this way.  (The row strides
-// and split ends likewise.)  The GEMM reads them plainly: it stores once, after its
-// last request, and the uniform copies held in scalar registers cost its main loop
-// spills.
-__device__ inline uint64_t out_uni64(uint64_t v) {
+// Output fields read through readfirstlane (UNI = true).  They are the same in every
+// lane; selecting between plain reads of them lets the compiler fold the per-lane
+// choice of split into one per-lane load from the argument block, a vector memory
+// request whose wait (in-order counting) also waits for every weight request the wave
+// has in flight: the GEMV band loops read them this way.  The GEMM reads them plainly:
+// it stores once, after its last request, and uniform copies held in scalar registers
+// cost its main loop spills.
+template <bool UNI>
+__device__ inline uint64_t out_u64(uint64_t v) {
+    if constexpr (!UNI) return v;
     const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
     const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
     return (uint64_t)lo | ((uint64_t)hi << 32);
 }
 template <bool UNI>
-__device__ inline char* out_base(const OutSplit& o, int i) {
-    return UNI ? reinterpret_cast<char*>(out_uni64(reinterpret_cast<uint64_t>(o.y[i]))) : reinterpret_cast<char*>(o.y[i]);
-}
+__device__ inline char* out_p(char* p) { return reinterpret_cast<char*>(out_u64<UNI>(reinterpret_cast<uint64_t>(p))); }
 template <bool UNI>
-__device__ inline int64_t out_ld(const OutSplit& o, int i) { return UNI ? (int64_t)out_uni64((uint64_t)o.ldy[i]) : o.ldy[i]; }
-template <bool UNI>
-__device__ inline int64_t out_end(const OutSplit& o, int i) { return UNI ? (int64_t)out_uni64((uint64_t)o.end[i]) : o.end[i]; }
-
-template <bool UNI = false>
-__device__ inline ColOut col_out(const KArgs& a, int64_t col) {
-    const OutSplit& o = a.out;
-    const bool s1 = col >= o.end[0], s2 = col >= o.end[1];
-    char* const y0 = out_base<UNI>(o, 0);
-    char* const y1 = out_base<UNI>(o, 1);
-    char* const y2 = out_base<UNI>(o, 2);
-    char* const base = s2 ? y2 : (s1 ? y1 : y0);
-    const int64_t ld = s2 ? out_ld<UNI>(o, 2) : (s1 ? out_ld<UNI>(o, 1) : out_ld<UNI>(o, 0));
-    const int64_t c0 = s2 ? out_end<UNI>(o, 1) : (s1 ? out_end<UNI>(o, 0) : 0);
-    const int64_t es = o.f32 ? 4 : 2;
-    ColOut c;
-    c.p = base + (col - c0) * es;
-    c.ld = ld * es;
-    c.bias = a.bias ? bf16_value(a.bias[col]) : 0.0f;
-    return c;
-}
+__device__ inline int64_t out_i(int64_t v) { return (int64_t)out_u64<UNI>((uint64_t)v); }
 
 template <bool UNI = false>
 __device__ inline ColOut col_out_nobias(const KArgs& a, int64_t col) {
-    const OutSplit& o = a.out;
-    const bool s1 = col >= o.end[0], s2 = col >= o.end[1];
-    char* const y0 = out_base<UNI>(o, 0);
-    char* const y1 = out_base<UNI>(o, 1);
-    char* const y2 = out_base<UNI>(o, 2);
+    const int64_t e0 = out_i<UNI>(a.end0), e1 = out_i<UNI>(a.end1);
+    const bool s1 = col >= e0, s2 = col >= e1;
+    char* const y0 = out_p<UNI>(a.y0);
+    char* const y1 = out_p<UNI>(a.y1);
+    char* const y2 = out_p<UNI>(a.y2);
     char* const base = s2 ? y2 : (s1 ? y1 : y0);
-    const int64_t ld = s2 ? out_ld<UNI>(o, 2) : (s1 ? out_ld<UNI>(o, 1) : out_ld<UNI>(o, 0));
-    const int64_t c0 = s2 ? out_end<UNI>(o, 1) : (s1 ? out_end<UNI>(o, 0) : 0);
-    const int64_t es = o.f32 ? 4 : 2;
+    const int64_t ld = s2 ? out_i<UNI>(a.ldy2) : (s1 ? out_i<UNI>(a.ldy1) : out_i<UNI>(a.ldy0));
+    const int64_t c0 = s2 ? e1 : (s1 ? e0 : 0);
+    const int64_t es = a.f32 ? 4 : 2;
     ColOut c;
     c.p = base + (col - c0) * es;
     c.ld = ld * es;
     c.bias = 0.0f;
+    return c;
+}
+
+template <bool UNI = false>
+__device__ inline ColOut col_out(const KArgs& a, int64_t col) {
+    ColOut c = col_out_nobias<UNI>(a, col);
+    c.bias = a.bias ? bf16_value(a.bias[col]) : 0.0f;
     return c;
 }
 
@@ -360,7 +365,7 @@ typedef __attribute__((address_space(1))) uint16_t gu16_t;
 __device__ inline void put_out(const KArgs& a, const ColOut& c, int64_t m, float v, float g) {
     const float r = v * g + c.bias;
     char* const p = c.p + m * c.ld;
-    if (a.out.f32) *(gfloat_t*)p = r;
+    if (a.f32) *(gfloat_t*)p = r;
     else *(gu16_t*)p = bf16_rne(r);
 }
 
@@ -452,9 +457,24 @@ inline KArgs make_args(const MatmulProblem& p) {
     a.codes = p.codes;
     a.scales = p.scales;
     a.bias = p.bias;
-    a.out = p.out;
-    a.L = scale_layout(p.fmt, p.dq, p.n, p.k);
-    a.gs = p.gscale ? reinterpret_cast<const uint8_t*>(p.gscale) : p.scales + a.L.g_off;
+    const ScaleLayout L = scale_layout(p.fmt, p.dq, p.n, p.k);
+    a.mu_off = L.mu_off;
+    a.ng = L.ng;
+    if (p.fmt == kNVFP4) a.gs = p.gscale ? reinterpret_cast<const uint8_t*>(p.gscale) : p.scales + L.g_off;
+    else if (p.fmt == kQ5_0) a.hb_off = L.hb_off;
+    else if (p.fmt == kQ4_K || p.fmt == kQ6_K) a.kd_off = L.kd_off;
+    else a.d_off = L.d_off;
+    a.f32 = (uint8_t)p.out.f32;
+    // unused splits repeat the last one (their column ranges are empty)
+    const int ns = p.out.nsplit;
+    a.y0 = reinterpret_cast<char*>(p.out.y[0]);
+    a.y1 = reinterpret_cast<char*>(p.out.y[ns > 1 ? 1 : 0]);
+    a.y2 = reinterpret_cast<char*>(p.out.y[ns > 2 ? 2 : ns - 1]);
+    a.ldy0 = (int)p.out.ldy[0];
+    a.ldy1 = (int)p.out.ldy[ns > 1 ? 1 : 0];
+    a.ldy2 = (int)p.out.ldy[ns > 2 ? 2 : ns - 1];
+    a.end0 = (int)(ns > 1 ? p.out.end[0] : p.n);
+    a.end1 = (int)(ns > 2 ? p.out.end[1] : p.n);
     a.ksplit = 1;
     const uintptr_t align = p.out.f32 ? 16 : 8;
     a.out_vec = 1;

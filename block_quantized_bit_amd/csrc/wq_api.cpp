@@ -64,6 +64,9 @@ wq_status check_packed(const wq_packed& w) {
 
 wq_status from_hip(hipError_t e) { return e == hipSuccess ? WQ_OK : WQ_ERR_HIP; }
 
+// Output columns and row strides of a matmul call travel as 32-bit kernel arguments.
+constexpr int64_t kMaxOut = 0x7FFFFFFF;
+
 // Common checks of a matmul call; fills everything of the problem except the outputs.
 wq_status check_matmul(const wq_desc* d, int64_t m, const uint16_t* x, int64_t ldx, wq_packed w,
                        const uint16_t* bias, int32_t ydt, void* ws, size_t ws_bytes, wq::MatmulProblem* p) {
@@ -72,6 +75,7 @@ wq_status check_matmul(const wq_desc* d, int64_t m, const uint16_t* x, int64_t l
     if (st != WQ_OK) return st;
     if ((st = check_packed(w)) != WQ_OK) return st;
     if (m < 0 || m > 0x7FFFFFFF) return WQ_ERR_SHAPE;
+    if (dd.n > kMaxOut) return WQ_ERR_SHAPE;   // output columns (and split ends) as 32-bit kernel arguments
     if (!x) return WQ_ERR_INVALID_ARG;
     if (ldx < dd.k || ldx % 8 != 0 || ldx > (int64_t(1) << 24)) return WQ_ERR_INVALID_ARG;   // 128 rows of X < 4 GiB
     if (!aligned(x, 16)) return WQ_ERR_ALIGNMENT;
@@ -238,7 +242,7 @@ wq_status wq_matmul(const wq_desc* d, int64_t m, const uint16_t* x, int64_t ldx,
     if (st != WQ_OK) return st;
     if (!y) return WQ_ERR_INVALID_ARG;
     if (!aligned(y, ydt == WQ_F32 ? 4 : 2)) return WQ_ERR_ALIGNMENT;
-    if (ldy < p.n) return WQ_ERR_INVALID_ARG;
+    if (ldy < p.n || ldy > kMaxOut) return WQ_ERR_INVALID_ARG;
     p.out.nsplit = 1;
     p.out.y[0] = y;
     p.out.ldy[0] = ldy;
@@ -253,7 +257,7 @@ wq_status wq_matmul_noalloc(const wq_desc* d, int64_t m, const uint16_t* x, int6
     if (st != WQ_OK) return st;
     if (!y) return WQ_ERR_INVALID_ARG;
     if (!aligned(y, ydt == WQ_F32 ? 4 : 2)) return WQ_ERR_ALIGNMENT;
-    if (ldy < p.n) return WQ_ERR_INVALID_ARG;
+    if (ldy < p.n || ldy > kMaxOut) return WQ_ERR_INVALID_ARG;
     if (m == 0) return WQ_OK;
     const size_t need = wq::matmul_workspace_bytes(p.fmt, p.m, p.n, p.k);
     if (need > kScratchBytes) return WQ_ERR_WORKSPACE;
@@ -285,7 +289,7 @@ wq_status wq_matmul_qkv(const wq_desc* d, int64_t m, const uint16_t* x, int64_t 
     for (int i = 0; i < nsplit; i++) {
         if (!y[i]) return WQ_ERR_INVALID_ARG;
         if (!aligned(y[i], ydt == WQ_F32 ? 4 : 2)) return WQ_ERR_ALIGNMENT;
-        if (ldy[i] < split_n[i]) return WQ_ERR_INVALID_ARG;
+        if (ldy[i] < split_n[i] || ldy[i] > kMaxOut) return WQ_ERR_INVALID_ARG;
     }
     // the splits' destination windows must be disjoint (every output element is written once)
     const int64_t es = ydt == WQ_F32 ? 4 : 2;
@@ -366,7 +370,7 @@ wq_status wq_matmul_w4a4(const wq_desc* d, int64_t m, const void* xcodes, const 
     if (st != WQ_OK) return st;
     if (!y) return WQ_ERR_INVALID_ARG;
     if (!aligned(y, ydt == WQ_F32 ? 4 : 2)) return WQ_ERR_ALIGNMENT;
-    if (ldy < p.n) return WQ_ERR_INVALID_ARG;
+    if (ldy < p.n || ldy > kMaxOut) return WQ_ERR_INVALID_ARG;
     if (m == 0) return WQ_OK;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const wq::ScaleLayout L = wq::scale_layout(dd.fmt, false, dd.n, dd.k);

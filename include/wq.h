@@ -168,7 +168,9 @@ wq_status wq_workspace_size(const wq_desc* d, int64_t m, size_t* bytes);
  *   w    : packed matrix for d
  *   bias : bf16 [n] or NULL (2-byte aligned)
  *   y    : [m, n] of type ydt (WQ_BF16 or WQ_F32), leading dimension ldy >= n,
- *          aligned to its element size.  Only the m x n window is written.
+ *          ldy <= 2^31 - 1, aligned to its element size.  Only the m x n window is
+ *          written.  (A matmul needs n <= 2^31 - 1, else WQ_ERR_SHAPE: output
+ *          columns and row strides travel as 32-bit kernel arguments.)
  *   ws   : workspace (see wq_workspace_size) or NULL; ws_bytes its size
  * Accumulation is fp32 over bf16 activations times bf16-rounded (or exact)
  * dequantized weights; per element |y - y_ref| <= 4e-3 * sum_k |x_k * w^_k| + 1e-6
@@ -197,7 +199,7 @@ wq_status wq_matmul_noalloc(const wq_desc* d, int64_t m, const uint16_t* x, int6
 /* Fused projection over a row-concatenated weight W[n0 + n1 (+ n2), k] in one
  * pass over W (one kernel; a K-split GEMM adds one small reduction kernel):
  * columns [0, n0) go to y[0], [n0, n0+n1) to y[1], [n0+n1, n) to y[2],
- * each with its own leading dimension ldy[i] >= split_n[i], so the destinations
+ * each with its own leading dimension split_n[i] <= ldy[i] <= 2^31 - 1, so the destinations
  * may be rows of a K/V cache slab; nothing outside each m x split_n[i] window is
  * touched.  The windows must not share a byte (WQ_ERR_INVALID_ARG otherwise; the
  * check is closed-form for equal leading dimensions and O(m) for different ones).  bias is bf16 [n] or NULL (use zeros where a split has none, e.g. the

@@ -110,6 +110,10 @@ def test_matmul_argument_validation_returns_before_launch():
     assert mm(y=FAKE + 2) == 4          # fp32 output needs 4-byte alignment
     assert mm(ydt=3) == 1
     assert mm(ldy=32) == 1
+    assert mm(ldy=1 << 31) == 1         # output strides and columns travel as 32-bit kernel arguments
+    big = wq.desc(NF4, (1 << 31) + 16, 128)
+    assert _status(wq.wq_packed_size, big) == 0                   # a valid weight ...
+    assert mm(d=big, ldx=128, ldy=(1 << 31) + 16) == 3             # ... too wide for a matmul
     assert mm(ws=FAKE + 8) == 4
     assert mm(d=wq.desc(NF4, 24, 256)) == 3
     # a workspace smaller than asked for is an error (only checked when a split is wanted)
@@ -136,6 +140,7 @@ def test_qkv_argument_validation():
     assert q([32, 32, 32], ys=[FAKE, None, FAKE]) == 1
     assert q([32, 32, 32], ys=[FAKE, FAKE + 1, FAKE]) == 4
     assert q([32, 32, 32], ldys=[32, 16, 32]) == 1
+    assert q([32, 32, 32], ldys=[32, 1 << 31, 32]) == 1
     # destination windows that share a byte are refused before anything is enqueued
     assert q([32, 32, 32], ys=[FAKE, FAKE, FAKE + 1024]) == 1            # same base
     assert q([32, 32, 32], ys=[FAKE, FAKE + 62, FAKE + 1024]) == 1       # 1 bf16 column of row 0 shared
@@ -188,6 +193,7 @@ def test_w4a4_argument_validation():
     assert mm(ws=None) == 6 and mm(ws_bytes=need - 1) == 6
     assert mm(ws=FAKE + 8) == 4
     assert mm(codes=None) == 1 and mm(y=None) == 1 and mm(ldy=128) == 1 and mm(ydt=5) == 1
+    assert mm(ldy=1 << 31) == 1
     assert mm(bias=FAKE + 1) == 4
     assert mm(m=-1) == 3
     assert mm(m=0, ws=None, ws_bytes=0) == 0
