@@ -335,21 +335,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     // by K piece, and within a piece in groups of kGroupM row tiles by all column
     // tiles, column-major inside the group: the items an XCD runs at one time cover
     // a compact block of row and column tiles, whose X rows and W bands its L2 holds.
+    // (the schedule of gemm_sched, derived here from the shape and the K-piece count)
     constexpr int64_t kGroupM = 6;
-    const int64_t tiles = a.tiles_m * a.tiles_n;
+    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int64_t tiles = tiles_m * tiles_n;
     const int64_t items = tiles * a.ksplit;
-    const int64_t per_xcd = (int64_t)gridDim.x / 8;
+    const int lks = __builtin_ctz((unsigned)a.ksplit);   // ksplit is a power of two (gemm_sched)
+    const int64_t kt_per = ((K + BK - 1) / BK + a.ksplit - 1) >> lks;
+    const int64_t per_xcd = (items + 7) / 8;     // the grid is per_xcd workgroups per XCD
     const int64_t item = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
     if (item >= items) return;
     const int ks = (int)(item / tiles);
     const int64_t ti = item - (int64_t)ks * tiles;
-    const int64_t grp = ti / (kGroupM * a.tiles_n);
-    const int64_t gm = std::min<int64_t>(kGroupM, a.tiles_m - grp * kGroupM);
-    const int64_t within = ti - grp * kGroupM * a.tiles_n;
+    const int64_t grp = ti / (kGroupM * tiles_n);
+    const int64_t gm = std::min<int64_t>(kGroupM, tiles_m - grp * kGroupM);
+    const int64_t within = ti - grp * kGroupM * tiles_n;
     const int64_t tm = grp * kGroupM + within % gm;
     const int64_t tn = within / gm;
     const int64_t m0 = tm * BM, n0 = tn * BN;
-    const int64_t s0 = ks * a.kt_per, s1 = std::min<int64_t>(nsteps_total, s0 + a.kt_per);  // in BK steps
+    const int64_t s0 = ks * kt_per, s1 = std::min<int64_t>(nsteps_total, s0 + kt_per);  // in BK steps
 
     const int64_t band0 = n0 / 16 + wave * NB;
     const int64_t nbands = N / 16;
@@ -380,7 +384,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     S.wbytes = (uint32_t)(KT * kTileBytes);
     S.sbytes = (uint32_t)(KT * SB);
     if constexpr (FMT == kNF4 && DQ) S.dt = a.scales + a.d_off;
-    S.dtbytes = (uint32_t)(a.ng * 4);
+    S.dtbytes = (uint32_t)(((N * (K / 64) + 255) / 256) * 4);   // double quant: one fp32 d per 256 blocks
     {
         const int64_t xbytes = (M - m0) * a.ldx * 2;
         S.x = reinterpret_cast<const uint8_t*>(a.x + m0 * a.ldx);
@@ -598,7 +602,7 @@ __device__ inline void reduce_store(const KArgs& a, int64_t q, const f32x4& v, f
 // convert and store.  A thread owns two quads (4 consecutive columns of one
 // row each) 256 quads apart, so eight 16-byte loads are in flight per thread.
 // Runs after k_gemm on the same stream, so every partial is complete and visible.
-__global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, int global_scale) {
+__global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, const float* __restrict__ partial, int global_scale) {
     const float g = global_scale ? *reinterpret_cast<const float*>(a.gs) : 1.0f;
     const int64_t total = (int64_t)a.m * (a.n / 4);
     const int64_t qa = (int64_t)blockIdx.x * 512 + threadIdx.x, qb = qa + 256;
@@ -606,8 +610,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, int global_scale
     const bool hb = qb < total;
     const int64_t pstride = (int64_t)a.m * a.n;
     // the partials are [ksplit][m][n] row-major with n % 4 == 0: quad q starts at element 4q
-    const float* pa = a.partial + qa * 4;
-    const float* pb = a.partial + (hb ? qb : qa) * 4;
+    const float* pa = partial + qa * 4;
+    const float* pb = partial + (hb ? qb : qa) * 4;
     // pieces are summed in order 0, 1, ...; their loads are issued four at a time (indices
     // past the last piece re-read it and are dropped)
     f32x4 va = {0.f, 0.f, 0.f, 0.f}, vb = {0.f, 0.f, 0.f, 0.f};
@@ -634,7 +638,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, int global_scale
 // and issues all 2 KS of its partial loads before adding any (pieces in order).  (Four
 // quads per thread at KS = 2 measured 0.7-1 us slower on the M = 1500 fc2 shape.)
 template <int KS>
-__global__ __launch_bounds__(256) void k_splitk_reduce_n(KArgs a, int global_scale) {
+__global__ __launch_bounds__(256) void k_splitk_reduce_n(KArgs a, const float* __restrict__ partial, int global_scale) {
     constexpr int Q = 2;
     const float g = global_scale ? *reinterpret_cast<const float*>(a.gs) : 1.0f;
     const int64_t total = (int64_t)a.m * (a.n / 4);
@@ -648,7 +652,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce_n(KArgs a, int global_sca
         const int64_t q = q0 + 256 * i < total ? q0 + 256 * i : q0;
 #pragma unroll
         for (int s = 0; s < KS; s++)
-            t[s][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(a.partial + s * pstride + q * 4));
+            t[s][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(partial + s * pstride + q * 4));
     }
 #pragma unroll
     for (int i = 0; i < Q; i++) {
@@ -691,7 +695,7 @@ static Sched gemm_sched(int64_t m, int64_t n, int64_t k, bool allow_split) {
     if (allow_split && tiles < kNumCU / 2) {
         while (tiles * ks * 2 <= kNumCU && steps / (ks * 2) >= kMinPieceSteps) ks *= 2;
     }
-    s.ksplit = ks;
+    s.ksplit = ks;                        // a power of two: k_gemm derives its pieces with a shift
     s.kt_per = (steps + ks - 1) / ks;     // every piece non-empty: (ks - 1) * kt_per < steps
     const int64_t items = tiles * ks;
     s.grid = (unsigned)(((items + 7) / 8) * 8);
@@ -716,34 +720,34 @@ hipError_t launch_gemm(const MatmulProblem& p, hipStream_t st) {
     const Sched s = gemm_sched(p.m, p.n, p.k, split);
     KArgs a = make_args(p);
     a.ksplit = s.ksplit;
-    a.kt_per = s.kt_per;
-    a.tiles_m = s.tiles_m;
-    a.tiles_n = s.tiles_n;
-    if (s.ksplit > 1) a.partial = reinterpret_cast<float*>(p.ws);
+    // the GEMM launch of a K split writes partials, not outputs: its y0 slot carries them
+    KArgs ag = a;
+    float* const partial = reinterpret_cast<float*>(p.ws);
+    if (s.ksplit > 1) ag.partial = partial;
     const dim3 grid(s.grid), block(256);
     switch (p.fmt) {
     case kNF4:
-        if (p.dq) gemm_launch<kNF4, true>(s.nb, grid, a, st);
-        else gemm_launch<kNF4, false>(s.nb, grid, a, st);
+        if (p.dq) gemm_launch<kNF4, true>(s.nb, grid, ag, st);
+        else gemm_launch<kNF4, false>(s.nb, grid, ag, st);
         break;
-    case kNVFP4: gemm_launch<kNVFP4, false>(s.nb, grid, a, st); break;
-    case kQ4_0: gemm_launch<kQ4_0, false>(s.nb, grid, a, st); break;
-    case kQ4_1: gemm_launch<kQ4_1, false>(s.nb, grid, a, st); break;
-    case kQ5_0: gemm_launch<kQ5_0, false>(s.nb, grid, a, st); break;
-    case kQ4_K: gemm_launch<kQ4_K, false>(s.nb, grid, a, st); break;
-    case kQ6_K: gemm_launch<kQ6_K, false>(s.nb, grid, a, st); break;
-    case kQ8_0: gemm_launch<kQ8_0, false>(s.nb, grid, a, st); break;
+    case kNVFP4: gemm_launch<kNVFP4, false>(s.nb, grid, ag, st); break;
+    case kQ4_0: gemm_launch<kQ4_0, false>(s.nb, grid, ag, st); break;
+    case kQ4_1: gemm_launch<kQ4_1, false>(s.nb, grid, ag, st); break;
+    case kQ5_0: gemm_launch<kQ5_0, false>(s.nb, grid, ag, st); break;
+    case kQ4_K: gemm_launch<kQ4_K, false>(s.nb, grid, ag, st); break;
+    case kQ6_K: gemm_launch<kQ6_K, false>(s.nb, grid, ag, st); break;
+    case kQ8_0: gemm_launch<kQ8_0, false>(s.nb, grid, ag, st); break;
     default: return hipErrorInvalidValue;
     }
     if (s.ksplit > 1) {
         const int64_t nquads = p.m * (p.n / 4);
         const int gs = (int)(p.fmt == kNVFP4);
         if (s.ksplit == 2)
-            hipLaunchKernelGGL(k_splitk_reduce_n<2>, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a, gs);
+            hipLaunchKernelGGL(k_splitk_reduce_n<2>, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a, partial, gs);
         else if (s.ksplit == 4)
-            hipLaunchKernelGGL(k_splitk_reduce_n<4>, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a, gs);
+            hipLaunchKernelGGL(k_splitk_reduce_n<4>, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a, partial, gs);
         else
-            hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a, gs);
+            hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a, partial, gs);
     }
     return hipGetLastError();
 }

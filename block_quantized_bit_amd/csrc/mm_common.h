@@ -49,9 +49,9 @@ constexpr int kLutWords = 256 * 64;   // 256 byte values x 64 lane slots
 // Kernel arguments.  A launch reads its argument block from memory, cold, one 128-byte
 // line per round trip, and a second line on a kernel's path costs a GEMV launch up to
 // three quarters of a microsecond: every field a GEMV launch reads sits in the first
-// line (the 32-bit fields rest on the boundary's limits: n, ldy < 2^31).  The GEMM's
-// own fields follow, and after the struct the hidden arguments (grid size): GEMV kernels
-// take their grid from a field or a constant instead of gridDim.
+// line (the 32-bit fields rest on the boundary's limits: n, ldy < 2^31), and the whole
+// block is that line: the kernels derive their schedules (tile counts, K pieces, grid)
+// from it rather than read the hidden arguments that follow it.
 struct KArgs {
     const uint16_t* x;       // 0x00
     const uint8_t* codes;    // 0x08
@@ -63,8 +63,11 @@ struct KArgs {
         int64_t kd_off;      //   q4_k / q6_k: super-block scales
     };
     const uint16_t* bias;    // 0x20
-    char* y0;                // 0x28 output splits: columns [0, end0) -> y0, [end0, end1) -> y1,
-    char* y1;                // 0x30   [end1, n) -> y2 (one split: end0 = end1 = n)
+    union {                  // 0x28 output splits: columns [0, end0) -> y0, [end0, end1) -> y1,
+        char* y0;            //   [end1, n) -> y2 (one split: end0 = end1 = n).  A K-split GEMM
+        float* partial;      //   launch (the reduce kernel writes the outputs) carries here its
+    };                       //   fp32 partials [ksplit][m][n]
+    char* y1;                // 0x30
     char* y2;                // 0x38
     int64_t n, k;            // 0x40, 0x48
     int64_t ldx;             // 0x50
@@ -76,13 +79,9 @@ struct KArgs {
     uint8_t out_vec;         // 0x79 every output split allows 4-column vector stores (alignment, split ends % 4)
     uint8_t out_v16;         // 0x7A bf16 output whose splits allow 8-column (16-byte) stores
     uint8_t wg_per_cu;       // 0x7B band-pipelined GEMV: workgroups per CU (its grid is that many per CU)
-    int ksplit;              // 0x7C K pieces per output tile
-    int64_t ng;              // 0x80 NF4+DQ: number of 256-block groups
-    int64_t kt_per;          // K tiles (of tile_k) per piece
-    float* partial;          // [ksplit][m][n] when ksplit > 1
-    int64_t tiles_m, tiles_n;
+    int ksplit;              // 0x7C GEMM: K pieces per output tile
 };
-static_assert(__builtin_offsetof(KArgs, ng) == 128, "the GEMV's arguments fill the first 128 bytes");
+static_assert(sizeof(KArgs) == 128, "the kernel arguments are one 128-byte line");
 
 // One fp32 value at a uniform address (the NVFP4 global scale, the double-quant mean),
 // read with a vector buffer load.  A plain read of a uniform address becomes a scalar
@@ -459,7 +458,6 @@ inline KArgs make_args(const MatmulProblem& p) {
     a.bias = p.bias;
     const ScaleLayout L = scale_layout(p.fmt, p.dq, p.n, p.k);
     a.mu_off = L.mu_off;
-    a.ng = L.ng;
     if (p.fmt == kNVFP4) a.gs = p.gscale ? reinterpret_cast<const uint8_t*>(p.gscale) : p.scales + L.g_off;
     else if (p.fmt == kQ5_0) a.hb_off = L.hb_off;
     else if (p.fmt == kQ4_K || p.fmt == kQ6_K) a.kd_off = L.kd_off;
