@@ -283,31 +283,40 @@ def main():
         log(f"[bench] w4a4: {out}")
         return out
 
-    def streaming_part():
+    def streaming_part(by_format=False):
         """One launch streams 433 MB: the fc1 geometry (K = 1280) widened to N = 655360 rows,
         NF4 + double-quant, M = 1; 20 timed launches on one weight set (larger than the
-        Infinity Cache, read in order, so every launch reads it from HBM)."""
+        Infinity Cache, read in order, so every launch reads it from HBM).  by_format: the
+        same matrix in every format as well (by_format key of the result)."""
         gen = torch.Generator(device=dev).manual_seed(7)
         ns, ks = 655360, 1280
         wbig = torch.randn((ns, ks), device=dev, generator=gen, dtype=torch.float32) * 0.02
-        d_s, c_s, s_s = quantize_dev(wq.WQ_NF4, wbig, True)
-        del wbig
-        torch.cuda.synchronize()
-        torch.cuda.empty_cache()
         xs = bf16_dev(linear_case(9, 16, ks, 1)[2])
         ys = torch.empty((1, ns), dtype=torch.int16, device=dev)
-        nbs = wq.wq_workspace_size(d_s, 1)
-        wss_ = torch.zeros(max(nbs, 16), dtype=torch.uint8, device=dev)
-        sbytes = c_s.numel() + s_s.numel()
-        reps = 20
-        ts = run_graph_steps(lambda s, st: wq.wq_matmul(d_s, 1, xs, ks, c_s, s_s, None, ys, wq.WQ_BF16, ns,
-                                                        wss_ if nbs else None, nbs, stream=st), 1, reps, 5, per_graph=5)
-        out = {"shape": f"M=1 N={ns} K={ks} NF4+DQ", "bytes": sbytes,
-               "us": round(ts * 1e6 / reps, 2),
-               "GBps": round(sbytes * reps / ts / 1e9, 1),
-               "frac_hbm": round(sbytes * reps / ts / 1e9 / HBM_PEAK_GBS, 4)}
+
+        def one(fmt, dq):
+            d_s, c_s, s_s = quantize_dev(fmt, wbig, dq)
+            torch.cuda.synchronize()
+            nbs = wq.wq_workspace_size(d_s, 1)
+            wss_ = torch.zeros(max(nbs, 16), dtype=torch.uint8, device=dev)
+            sbytes = c_s.numel() + s_s.numel()
+            reps = 20
+            ts = run_graph_steps(lambda s, st: wq.wq_matmul(d_s, 1, xs, ks, c_s, s_s, None, ys, wq.WQ_BF16, ns,
+                                                            wss_ if nbs else None, nbs, stream=st), 1, reps, 5, per_graph=5)
+            del c_s, s_s
+            return {"bytes": sbytes, "us": round(ts * 1e6 / reps, 2), "GBps": round(sbytes * reps / ts / 1e9, 1),
+                    "frac_hbm": round(sbytes * reps / ts / 1e9 / HBM_PEAK_GBS, 4)}
+
+        out = {"shape": f"M=1 N={ns} K={ks} NF4+DQ", **one(wq.WQ_NF4, True)}
         log(f"[bench] streaming: {out}")
-        del c_s, s_s
+        if by_format:
+            out["by_format"] = {}
+            for name, fmt in (("nf4", wq.WQ_NF4), ("nvfp4", wq.WQ_NVFP4), ("q4_0", wq.WQ_Q4_0), ("q4_1", wq.WQ_Q4_1),
+                              ("q5_0", wq.WQ_Q5_0), ("q4_k", wq.WQ_Q4_K), ("q6_k", wq.WQ_Q6_K), ("q8_0", wq.WQ_Q8_0)):
+                out["by_format"][name] = one(fmt, False)
+                torch.cuda.empty_cache()
+            log(f"[bench] streaming by format: {out['by_format']}")
+        del wbig
         torch.cuda.empty_cache()
         return out
 
@@ -687,7 +696,7 @@ def main():
                                       "algorithmic_GBps": round(decode_bytes(m) * pool_n * 2 / tm / 1e9, 2)}
             log(f"[bench] decode M={m}: {extras[f'decode_m{m}']}")
 
-        extras["streaming_gemv"] = streaming_part()
+        extras["streaming_gemv"] = streaming_part(by_format=True)
 
         encoder = encoder_part()
         extras["unfused_ablation"] = ablation_part(encoder_part.layers, encoder["us_per_step"], ms_per_step * 1e3)

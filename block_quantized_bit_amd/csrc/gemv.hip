@@ -448,7 +448,7 @@ constexpr int kStreamGrid = 2 * kNumCU;     // two workgroups of 4 waves per CU
 // Scale bytes per tile and per lane (one row of the tile) in the packed layout.
 template <int FMT, bool DQ>
 __device__ constexpr int tile_scale_bytes() {
-    return FMT == kQ8_0 ? 64 : (FMT == kNF4 && DQ) ? 32 : 128;
+    return FMT == kQ8_0 ? 64 : (FMT == kNF4 && DQ) ? 32 : FMT == kQ4_1 ? 256 : 128;
 }
 
 struct StreamTile {
@@ -617,6 +617,176 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Chunked streaming GEMV: the same scheme for every format whose band does not fit one
+// register set (q8_0's 64-wide tiles, K beyond 10 tiles) or whose scale records are wider
+// (q4_1, q5_0, q4_k, q6_k).  A wave walks items (band, chunk): a chunk is T consecutive
+// K tiles of a band, the accumulator runs across a band's chunks and the band's outputs
+// are stored after its last one.  The next item's tiles are requested into the other
+// register set before the current item is consumed.  Each chunk's requests go through
+// buffer descriptors that cover exactly its tiles (slots past the band's K read zeros
+// and take the zero row of X).
+// ---------------------------------------------------------------------------
+struct StreamChunkTile {
+    u32x4 code;
+    uint32_t sc[6];
+};
+
+struct StreamChunk {
+    uint32_t braw;     // bias (bf16 bits) of this lane's column
+};
+
+template <int FMT, bool DQ, int T>
+__device__ __forceinline__ void stream_load_chunk(StreamChunkTile (&R)[T], StreamChunk& B, const KArgs& a,
+                                                  int64_t band, int64_t t0, int64_t KT, int lane, int r) {
+    constexpr int SB = tile_scale_bytes<FMT, DQ>();
+    const int64_t tile0 = band * KT + t0;
+    const uint32_t nt = (uint32_t)std::min<int64_t>(T, KT - t0);
+    const BufRes rc = buf_res(a.codes + tile0 * kTileBytes, nt * (uint32_t)kTileBytes);
+    const BufRes rs = buf_res(a.scales + tile0 * SB, nt * (uint32_t)SB);
+    BufRes rh = rs, rk = rs;                      // (replaced below for the formats that use them)
+    if constexpr (FMT == kQ5_0) rh = buf_res(a.scales + a.hb_off + tile0 * 256, nt * 256u);
+    if constexpr (FMT == kQ6_K) rh = buf_res(a.codes + a.n * a.k / 2 + tile0 * 512, nt * 512u);
+    // the band's rows of super-block scales: (d, dmin) fp16 pairs (q4_k) or fp16 d (q6_k)
+    constexpr int KS = FMT == kQ4_K ? 4 : 2;
+    const int64_t spr = a.k >> 8;                 // super-blocks per row
+    if constexpr (FMT == kQ4_K || FMT == kQ6_K) rk = buf_res(a.scales + a.kd_off + band * 16 * spr * KS, (uint32_t)(16 * spr * KS));
+#pragma unroll
+    for (int s = 0; s < T; s++) {
+        R[s].code = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rc, lane * 16 + s * kTileBytes, 0, kNT));
+        if constexpr (FMT == kQ8_0) {
+            R[s].sc[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, r * 4 + s * SB, 0, kNT);
+        } else if constexpr (FMT == kQ4_1) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, r * 16 + s * SB, 0, kNT);
+#pragma unroll
+            for (int i = 0; i < 4; i++) R[s].sc[i] = v[i];
+        } else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, r * 8 + s * SB, 0, kNT);
+            R[s].sc[0] = v[0];
+            R[s].sc[1] = v[1];
+        }
+        if constexpr (FMT == kQ5_0) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rh, r * 16 + s * 256, 0, kNT);
+#pragma unroll
+            for (int i = 0; i < 4; i++) R[s].sc[2 + i] = v[i];
+        }
+        if constexpr (FMT == kQ6_K) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(rh, lane * 8 + s * 512, 0, kNT);
+            R[s].sc[2] = v[0];
+            R[s].sc[3] = v[1];
+            // the tile's super-block (slots past the band's K read a valid neighbour: their A is zero)
+            const uint32_t sb = (uint32_t)std::min<int64_t>((t0 + s) >> 1, spr - 1);
+            R[s].sc[4] = __builtin_amdgcn_raw_buffer_load_b16(rk, (uint32_t)((r * spr + sb) * 2), 0, 0);
+        }
+        if constexpr (FMT == kQ4_K) {
+            const uint32_t sb = (uint32_t)std::min<int64_t>((t0 + s) >> 1, spr - 1);
+            R[s].sc[2] = __builtin_amdgcn_raw_buffer_load_b32(rk, (uint32_t)((r * spr + sb) * 4), 0, 0);
+        }
+    }
+    B.braw = a.bias ? (uint32_t)a.bias[band * 16 + r] : 0u;
+}
+
+template <int FMT, bool DQ, int NI, int T>
+__device__ __forceinline__ void stream_consume_chunk(const StreamChunkTile (&R)[T], f32x4& acc, int64_t t0,
+                                                     int64_t KT, const uint16_t* xrow, const uint16_t* xzero,
+                                                     int h, uint32_t lane4, const uint32_t* lut, float mu) {
+    constexpr int TK = tile_k(FMT);
+#pragma unroll
+    for (int s = 0; s < T; s++) {
+        {
+            GemvTile<FMT> t;
+            t.code = make_uint4(R[s].code[0], R[s].code[1], R[s].code[2], R[s].code[3]);
+#pragma unroll
+            for (int i = 0; i < 6; i++) t.sc[i] = R[s].sc[i];
+            // rows r >= m read row 0: their products only reach output rows that are never stored
+            const uint16_t* xp = t0 + s < KT ? xrow + (t0 + s) * TK : xzero;
+#pragma unroll
+            for (int j = 0; j < TK / 32; j++) {
+                const uint4 v = *reinterpret_cast<const uint4*>(xp + 32 * j);
+                t.A[j] = u32x4{v.x, v.y, v.z, v.w};
+            }
+            gemv_consume<FMT, DQ, NI>(t, acc, lut, lane4, h, mu);
+        }
+        __builtin_amdgcn_sched_barrier(0);   // keep tiles in order: bounded register use
+    }
+}
+
+template <int FMT, bool DQ, int NI, int T>
+__global__ __launch_bounds__(256, 2) void k_gemv_stream_chunked(KArgs a) {
+    static_assert(!(FMT == kNF4 && DQ), "double quant streams through k_gemv_stream");
+    __shared__ uint32_t lut[gemv_uses_lut<FMT>() ? kLutWords : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[kStreamXMax + 128];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15;
+    const int h = lane >> 4;
+    const uint32_t lane4 = (uint32_t)lane << 2;
+    const int64_t KT = a.k / tile_k(FMT);
+    const int64_t nch = (KT + T - 1) / T;          // chunks per band
+    const int64_t nbands = a.n / 16;
+    const int64_t stride = (int64_t)kStreamGrid * 4;   // waves of the grid (gemv_launch_ni)
+    const int64_t band0 = (int64_t)blockIdx.x * 4 + wave;
+    // this wave's items: bands band0, band0 + stride, ..., each of nch chunks; requests for
+    // items past the last one re-read the wave's last item (in bounds, never consumed)
+    const int64_t nitems = band0 < nbands ? ((nbands - 1 - band0) / stride + 1) * nch : 0;
+    const int64_t ilast = nitems > 0 ? nitems - 1 : 0;
+    auto item_band = [&](int64_t i) { return std::min<int64_t>(band0 + (std::min(i, ilast) / nch) * stride, nbands - 1); };
+    auto item_t0 = [&](int64_t i) { return (std::min(i, ilast) % nch) * T; };
+
+    float g = 1.0f, mu = 0.0f;
+    if constexpr (FMT == kNVFP4) g = load_f32_vmem(a.gs);
+
+    StreamChunkTile R0[T], R1[T];
+    StreamChunk B0, B1;
+    stream_load_chunk<FMT, DQ, T>(R0, B0, a, item_band(0), item_t0(0), KT, lane, r);
+    // stage X (m rows of k bf16, rows contiguous in LDS) and the zero row
+    if (tid < 16) *reinterpret_cast<uint4*>(xs + kStreamXMax + tid * 8) = make_uint4(0u, 0u, 0u, 0u);
+    const int64_t nx = (int64_t)a.m * a.k;
+    for (int64_t i = (int64_t)tid * 8; i < nx; i += 256 * 8) {
+        const int64_t row = i / a.k, col = i - row * a.k;
+        *reinterpret_cast<uint4*>(xs + i) = *reinterpret_cast<const uint4*>(a.x + row * a.ldx + col);
+    }
+    if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 256>(lut);
+    __syncthreads();
+    const uint16_t* xrow = xs + (r < a.m ? r : 0) * a.k + h * 8;
+    const uint16_t* xzero = xs + kStreamXMax + h * 8;
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // the band's outputs, after its last chunk: lane (h, r) holds rows 4h .. 4h+3 of column band * 16 + r
+    auto finish = [&](int64_t i, uint32_t braw) {
+        if (i % nch != nch - 1) return;
+        ColOut c = col_out_nobias<true>(a, item_band(i) * 16 + r);
+        c.bias = bf16_value((uint16_t)braw);
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int mm = 4 * h + q;
+            if (mm < a.m) put_out(a, c, mm, acc[q], g);
+        }
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    for (int64_t i = 0; i < nitems; i += 2) {
+        stream_load_chunk<FMT, DQ, T>(R1, B1, a, item_band(i + 1), item_t0(i + 1), KT, lane, r);
+        stream_consume_chunk<FMT, DQ, NI, T>(R0, acc, item_t0(i), KT, xrow, xzero, h, lane4, lut, mu);
+        finish(i, B0.braw);
+        if (i + 1 >= nitems) break;
+        stream_load_chunk<FMT, DQ, T>(R0, B0, a, item_band(i + 2), item_t0(i + 2), KT, lane, r);
+        stream_consume_chunk<FMT, DQ, NI, T>(R1, acc, item_t0(i + 1), KT, xrow, xzero, h, lane4, lut, mu);
+        finish(i + 1, B1.braw);
+    }
+}
+
+// Tiles per chunk of the chunked streaming kernel.  Measured on the 433 MB streaming
+// shape (K = 1280): 10-tile chunks for q8_0 and q4_1 (q4_1 4.2 -> 4.7 TB/s against 5);
+// q5_0, q4_k and q6_k, whose per-value decode is longest, gain nothing from 10 and keep 5
+// (8 leaves a 2-tile second chunk and loses a quarter).  q4_0 with four-row accumulators
+// would spill at 10.
+template <int FMT, int NI>
+constexpr int stream_chunk_tiles() {
+    return (FMT == kQ5_0 || FMT == kQ4_K || FMT == kQ6_K || (FMT == kQ4_0 && NI == 4)) ? 5 : 10;
+}
+
 constexpr int64_t kStreamMinBands = 4 * 2 * 4 * kNumCU;   // bands per wave x waves
 
 size_t gemv_workspace_bytes(int, int64_t, int64_t, int64_t) { return 0; }
@@ -685,15 +855,26 @@ template <int FMT, bool DQ, int NI>
 static void gemv_launch_ni(const KArgs& a, hipStream_t st) {
     const int64_t KT = a.k / tile_k(FMT);
     const int64_t nbands = a.n / 16;
-    // Many more bands than resident waves, K <= 10 tiles, X fits in LDS: the
-    // streaming kernel (two workgroups of 4 waves per CU, each wave >= 4 bands).
-    // (q4_1, q5_0, q4_k and q6_k have no streaming variant: their wider scale records take
-    // the general kernel)
-    if constexpr (FMT != kQ4_1 && FMT != kQ5_0 && FMT != kQ4_K && FMT != kQ6_K) {
-        if (nbands >= kStreamMinBands && (int64_t)a.m * a.k <= kStreamXMax && KT <= 10) {
-            const unsigned grid = kStreamGrid;
-            if (KT <= 4) hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 4>), dim3(grid), dim3(256), 0, st, a);
-            else hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 10>), dim3(grid), dim3(256), 0, st, a);
+    // Many more bands than resident waves and X fits in LDS: the streaming kernels (two
+    // workgroups of 4 waves per CU, each wave >= 4 bands); the chunked one for wider scale
+    // records and for K beyond 10 tiles (double quant with K beyond 10 tiles takes the
+    // general kernel).
+    if (nbands >= kStreamMinBands && (int64_t)a.m * a.k <= kStreamXMax) {
+        const unsigned grid = kStreamGrid;
+        constexpr bool wide = FMT == kQ4_1 || FMT == kQ5_0 || FMT == kQ4_K || FMT == kQ6_K;
+        if constexpr (!wide) {
+            if (KT <= 4) {
+                hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 4>), dim3(grid), dim3(256), 0, st, a);
+                return;
+            }
+            if (KT <= 10) {
+                hipLaunchKernelGGL((k_gemv_stream<FMT, DQ, NI, 10>), dim3(grid), dim3(256), 0, st, a);
+                return;
+            }
+        }
+        // wider scale records, or K beyond one register set: chunks of T tiles
+        if constexpr (!(FMT == kNF4 && DQ)) {
+            hipLaunchKernelGGL((k_gemv_stream_chunked<FMT, DQ, NI, stream_chunk_tiles<FMT, NI>()>), dim3(grid), dim3(256), 0, st, a);
             return;
         }
     }

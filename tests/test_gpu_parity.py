@@ -244,12 +244,22 @@ STREAM_N = 131072
     (Q4_0, False, 640, 5, True, wq.WQ_F32),      # K = 5 tiles (the 10-tile variant)
     (NF4, False, 512, 15, True, wq.WQ_F32),      # m * k = 7680, near the most X the kernel stages
     (NF4, False, 384, 16, True, wq.WQ_BF16),     # all 16 rows, K = 3 tiles
-    (Q4_1, False, 1280, 1, True, wq.WQ_BF16),    # q4_1 takes the general kernel, bands pipelined
-    (Q5_0, False, 640, 3, True, wq.WQ_F32),      # so does q5_0
-    (Q4_K, False, 768, 2, True, wq.WQ_BF16),     # and q4_k (three super-blocks per row)
-    (Q6_K, False, 512, 4, False, wq.WQ_F32),     # and q6_k
+    # the chunked streaming kernel: chunks of 5 tiles for the wide-record formats, of 10 for K
+    # beyond 10 tiles; ragged last chunks, super-blocks split across chunks, four-row calls
+    (Q4_1, False, 1280, 1, True, wq.WQ_BF16),    # 2 chunks of 5
+    (Q5_0, False, 640, 3, True, wq.WQ_F32),      # 1 chunk
+    (Q4_K, False, 768, 2, True, wq.WQ_BF16),     # 5 + 1 tiles (three super-blocks per row)
+    (Q6_K, False, 512, 4, False, wq.WQ_F32),     # 1 chunk of 4
+    (Q6_K, False, 1280, 1, True, wq.WQ_BF16),    # super-block 2 spans chunks 0 and 1
+    (Q5_0, False, 1280, 6, True, wq.WQ_BF16),    # m * k = 7680
+    (Q4_K, False, 1536, 1, False, wq.WQ_F32),    # 5 + 1 + ... tiles, K = 12 tiles
+    (Q8_0, False, 1280, 1, True, wq.WQ_BF16),    # 20 tiles of 64: 2 chunks of 10
+    (NF4, False, 1536, 1, True, wq.WQ_F32),      # 10 + 2 tiles, code table
+    (NVFP4, False, 2048, 3, True, wq.WQ_BF16),   # 10 + 6 tiles, four-row accumulators
+    (Q4_0, False, 1536, 4, True, wq.WQ_F32),     # four-row q4_0: chunks of 5 (5 + 5 + 2 tiles)
 ], ids=["nf4dq-k1280-m1", "nvfp4-k384-m3", "q8_0-k256-m2", "q4_0-k640-m5", "nf4-k512-m15", "nf4-k384-m16",
-        "q4_1-k1280-m1", "q5_0-k640-m3", "q4_k-k768-m2", "q6_k-k512-m4"])
+        "q4_1-k1280-m1", "q5_0-k640-m3", "q4_k-k768-m2", "q6_k-k512-m4", "q6_k-k1280-m1", "q5_0-k1280-m6",
+        "q4_k-k1536-m1", "q8_0-k1280-m1", "nf4-k1536-m1", "nvfp4-k2048-m3", "q4_0-k1536-m4"])
 def test_streaming_gemv_many_bands(orc, fmt, dq, k, m, use_bias, ydt):
     d, codes, scales, ref, b = quantized(orc, fmt, dq, 6000 + k, STREAM_N, k, outlier_frac=0.001)
     x = gen_x(np.random.default_rng(6100 + k), m, k)
