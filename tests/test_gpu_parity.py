@@ -337,6 +337,22 @@ def test_encoder_gemm_sampled_rows(orc, fmt, m, shapes, kw, ydt):
 
 
 @pytest.mark.parametrize("fmt,dq", FORMATS, ids=FMT_IDS)
+@pytest.mark.parametrize("n,ydt", [(3840, wq.WQ_BF16), (3600, wq.WQ_F32)], ids=["n3840-bf16", "n3600-f32"])
+def test_gemm_qkv_width_and_ragged_columns(orc, fmt, dq, n, ydt):
+    """M = 1500 with N = 3840 (the fused Q/K/V projection) or 3600 (a last column tile of
+    which only 1 of the 4 waves' band groups exists).  64 sampled rows."""
+    m, k = 1500, 512
+    d, codes, scales, ref, b = quantized(orc, fmt, dq, 4400, n, k)
+    x = linear_case(4400, n, k, m)[2]
+    say("gemm qkv width", NAMES[fmt], m, n, k)
+    y = gpu_matmul(d, codes, scales, x, b, ydt=ydt)
+    rows = _sample_rows(m, 3)
+    check_bound(y[rows], orc.matmul(x, ref["w_hat"], b, rows=rows), abs_dot(x, ref["w_hat"], rows=rows),
+                bf16_out=ydt == wq.WQ_BF16, what=f"{NAMES[fmt]} qkv width n={n}")
+    assert np.all(np.isfinite(y))
+
+
+@pytest.mark.parametrize("fmt,dq", FORMATS, ids=FMT_IDS)
 @pytest.mark.parametrize("m", [1, 16, 100])
 def test_special_cases(orc, fmt, dq, m):
     n, k = 64, 256
