@@ -131,23 +131,32 @@ def make_policy(requested: str, overrides: dict[str, str] | None = None) -> Poli
 
 @dataclass(frozen=True)
 class Call:
-    """One libwq call: a single Linear (wq_matmul) or a fused group (wq_matmul_qkv)."""
+    """One libwq call: a single Linear (wq_matmul), a fused group (wq_matmul_qkv, each part to
+    its own destination), or a merged run of groups (`merged`: one wq_matmul over their
+    concatenated rows, whose output columns are the parts side by side)."""
     names: tuple[str, ...]
     fmt: str
-    n: int              # total output width (sum of the parts for a fused call)
+    n: int              # total output width (sum of the parts for a fused or merged call)
     k: int
     split_n: tuple[int, ...]   # part widths (one entry for a single Linear)
     rows: str
+    merged: bool = False
 
     @property
     def fused(self) -> bool:
-        return len(self.names) > 1
+        return len(self.names) > 1 and not self.merged
 
 
-def plan(pol: Policy) -> list[Call]:
+def plan(pol: Policy, merge_cross_kv: bool = False) -> list[Call]:
     """The calls that run every Linear once, in inventory order.  A group whose parts share
     one format becomes one fused call; otherwise each part is its own call (the mixed-format
-    fallback)."""
+    fallback).
+
+    merge_cross_kv: the decoder layers' cross-attention K/V all read the encoder output once per
+    utterance, so consecutive fused K/V calls of one format become one merged call over their
+    concatenated weights (N = 2560 per layer): one launch that fills the chip where each
+    layer's alone fills it about once.  Layers in another format, or split by the fallback,
+    keep their own calls."""
     lins = inventory()
     calls: list[Call] = []
     i = 0
@@ -169,4 +178,23 @@ def plan(pol: Policy) -> list[Call]:
             for p in parts:
                 calls.append(Call((p.name,), pol.linear[p.name], p.n, p.k, (p.n,), p.rows))
         i = j
-    return calls
+    return _merge_once_per_utterance(calls) if merge_cross_kv else calls
+
+
+def _merge_once_per_utterance(calls: list[Call]) -> list[Call]:
+    """Fused calls on the encoder output (rows 'frames_once') of one format and width merged
+    into one call each (kept at the position of the first of them)."""
+    out: list[Call] = []
+    at: dict[tuple[str, int], int] = {}
+    for c in calls:
+        if not (c.fused and c.rows == "frames_once"):
+            out.append(c)
+            continue
+        key = (c.fmt, c.k)
+        if key not in at:
+            at[key] = len(out)
+            out.append(c)
+            continue
+        m = out[at[key]]
+        out[at[key]] = Call(m.names + c.names, m.fmt, m.n + c.n, m.k, m.split_n + c.split_n, m.rows, merged=True)
+    return out

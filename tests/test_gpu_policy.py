@@ -28,8 +28,8 @@ def _fmt_args(fmt):
     return (wq.WQ_NF4, True) if fmt == "nf4dq" else (wq.format_from_name(fmt), False)
 
 
-def _run_group(orc, pol, members, m, seed):
-    calls = [c for c in P.plan(pol) if set(c.names) <= set(members)]
+def _run_group(orc, pol, members, m, seed, merge_cross_kv=False):
+    calls = [c for c in P.plan(pol, merge_cross_kv) if set(c.names) <= set(members)]
     names = [n for c in calls for n in c.names]
     parts = len(names)
     k = P.D_MODEL
@@ -94,3 +94,16 @@ def test_cross_attention_kv_mixed_at_encoder_frames(orc):
     assert len(fused) == 1 and fused[0].fused and fused[0].fmt == "q4_0"
     mixed = _run_group(orc, P.make_policy("q4_0", {"decoder.3.cross_attn.v": "nvfp4"}), kv, 300, 7200)
     assert [(c.names, c.fmt) for c in mixed] == [((kv[0],), "q4_0"), ((kv[1],), "nvfp4")]
+
+
+def test_cross_attention_kv_merged_across_layers(orc):
+    """All four layers' cross-attention K/V as one merged call (N = 10240) at 300 frames: each
+    part lands in its 1280-column window of the slab; with one layer in another format the
+    other three still merge."""
+    kv = [f"decoder.{l}.cross_attn.{s}" for l in range(4) for s in "kv"]
+    say("policy cross-attn kv merged", 300)
+    merged = _run_group(orc, P.make_policy("nf4dq"), kv, 300, 7300, merge_cross_kv=True)
+    assert len(merged) == 1 and merged[0].merged and merged[0].n == 10240
+    pol = P.make_policy("nf4dq", {"decoder.2.cross_attn.k": "q4_0", "decoder.2.cross_attn.v": "q4_0"})
+    calls = _run_group(orc, pol, kv, 300, 7300, merge_cross_kv=True)
+    assert [(len(c.names), c.fmt, c.merged) for c in calls] == [(6, "nf4dq", True), (2, "q4_0", False)]

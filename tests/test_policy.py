@@ -62,6 +62,28 @@ def test_plan_fuses_groups_of_one_format():
     assert len(per_token) == 24
 
 
+def test_plan_merges_cross_kv_across_layers():
+    calls = P.plan(P.make_policy("nf4dq"), merge_cross_kv=True)
+    kv = [c for c in calls if c.rows == "frames_once"]
+    assert len(kv) == 1
+    c = kv[0]
+    assert c.merged and not c.fused and c.n == 4 * 2560 and c.k == 1280 and c.split_n == (1280,) * 8
+    assert c.names == tuple(f"decoder.{l}.cross_attn.{s}" for l in range(4) for s in "kv")
+    names = [n for c in calls for n in c.names]
+    assert sorted(names) == sorted(l.name for l in P.inventory())
+    assert len(calls) == len(P.plan(P.make_policy("nf4dq"))) - 3
+    # a layer in another format, or split by the fallback, keeps its own calls
+    pol = P.make_policy("nf4dq", {"decoder.1.cross_attn.k": "q8_0", "decoder.2.cross_attn.k": "q8_0",
+                                  "decoder.2.cross_attn.v": "q8_0"})
+    kv = [c for c in P.plan(pol, merge_cross_kv=True) if c.rows == "frames_once"]
+    assert [(c.names, c.fmt, c.merged) for c in kv] == [
+        (("decoder.0.cross_attn.k", "decoder.0.cross_attn.v", "decoder.3.cross_attn.k", "decoder.3.cross_attn.v"),
+         "nf4dq", True),
+        (("decoder.1.cross_attn.k",), "q8_0", False),
+        (("decoder.1.cross_attn.v",), "nf4dq", False),
+        (("decoder.2.cross_attn.k", "decoder.2.cross_attn.v"), "q8_0", False)]
+
+
 def test_mixed_format_group_falls_back_to_separate_calls():
     pol = P.make_policy("nf4dq", {"decoder.2.self_attn.k": "q8_0"})
     calls = [c for c in P.plan(pol) if c.names[0].startswith("decoder.2.self_attn.")]
