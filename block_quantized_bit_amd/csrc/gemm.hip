@@ -536,7 +536,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
         }
         return;
     }
-    // K split: deposit this piece's partial tile; k_splitk_reduce finishes the outputs.
+    // K split: deposit this piece's partial tile; k_splitk_reduce_n finishes the outputs.
     // Staged through LDS like the bf16 output: wave w writes its 128 x 16 NB fp32 block in
     // two halves of 64 rows (rows of RB bytes with 16-byte chunks XOR-swizzled by row),
     // each row then leaving as one RB-byte piece.  The workspace is 16-byte aligned and
@@ -578,90 +578,145 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     }
 }
 
-// y = v * g + bias for quad q (4 consecutive columns of one row), converted and stored.
-__device__ inline void reduce_store(const KArgs& a, int64_t q, const f32x4& v, float g) {
-    const int64_t nq = a.n / 4;
-    const int64_t mm = q / nq, col0 = (q - mm * nq) * 4;
+// Split-K reduce.  Its launch carries everything in the one argument line: the pieces'
+// fp32 partials [ksplit][m][n] in the codes slot (rpartial) and the address of the
+// epilogue factor in the scales slot (rfactor: the NVFP4 global scale, W4A4's g_w * g_x,
+// or null for 1).  Thread t of workgroup b owns the Q quads (4 consecutive columns of
+// one row) b * 256 Q + t + 256 i.  Every memory request of a thread -- its partials, the
+// factor and its bias values -- is issued before its first wait.
+constexpr int kRedQ = 2;   // quads per thread (four measured 0.7-1 us slower on the M = 1500 fc2 shape)
+
+struct RedQuad {
+    int64_t row, col0;
+    bool live;
+};
+
+// Row and first column of quad q; 32-bit arithmetic when every quad index fits.
+__device__ inline RedQuad red_quad(int64_t q, int64_t total, int64_t nq, bool small) {
+    RedQuad r;
+    r.live = q < total;
+    if (!r.live) q = 0;
+    if (small) {
+        const uint32_t m32 = (uint32_t)q / (uint32_t)nq;
+        r.row = m32;
+        r.col0 = (int64_t)((uint32_t)q - m32 * (uint32_t)nq) * 4;
+    } else {
+        r.row = q / nq;
+        r.col0 = (q - r.row * nq) * 4;
+    }
+    return r;
+}
+
+// The 4 bias values of the quad at column col0 as fp32 (one 8-byte load when aligned).
+struct RedBias {
+    uint32_t lo, hi;
+};
+__device__ inline RedBias red_bias_load(const uint16_t* bias, int64_t col0, bool al8) {
+    RedBias b{0u, 0u};
+    if (al8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(bias + col0);
+        b.lo = v.x;
+        b.hi = v.y;
+    } else {
+        b.lo = (uint32_t)bias[col0] | ((uint32_t)bias[col0 + 1] << 16);
+        b.hi = (uint32_t)bias[col0 + 2] | ((uint32_t)bias[col0 + 3] << 16);
+    }
+    return b;
+}
+
+// y = v * g + bias for one quad, converted and stored (global stores, as in put_out).
+typedef __attribute__((address_space(1))) f32x4 gf32x4_t;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) u32x2 gu32x2_t;
+__device__ inline void red_store(const KArgs& a, const RedQuad& q, const f32x4& v, float g, const RedBias& b) {
+    const float bv[4] = {lo_f(b.lo), hi_f(b.lo), lo_f(b.hi), hi_f(b.hi)};
     if (a.out_vec) {
         // the 4 columns lie in one output split and can be written with one store
-        const ColOut c = col_out(a, col0);
+        const ColOut c = col_out_nobias<true>(a, q.col0);
         float o[4];
 #pragma unroll
-        for (int u = 0; u < 4; u++) o[u] = v[u] * g + (a.bias ? bf16_value(a.bias[col0 + u]) : 0.0f);
-        char* p = c.p + mm * c.ld;
-        if (a.f32) *reinterpret_cast<f32x4*>(p) = f32x4{o[0], o[1], o[2], o[3]};
-        else *reinterpret_cast<uint2*>(p) = make_uint2((uint32_t)bf16_rne(o[0]) | ((uint32_t)bf16_rne(o[1]) << 16),
-                                                      (uint32_t)bf16_rne(o[2]) | ((uint32_t)bf16_rne(o[3]) << 16));
+        for (int u = 0; u < 4; u++) o[u] = v[u] * g + bv[u];
+        char* const p = c.p + q.row * c.ld;
+        if (a.f32)
+            *(gf32x4_t*)p = f32x4{o[0], o[1], o[2], o[3]};
+        else
+            *(gu32x2_t*)p = u32x2{(uint32_t)bf16_rne(o[0]) | ((uint32_t)bf16_rne(o[1]) << 16),
+                                  (uint32_t)bf16_rne(o[2]) | ((uint32_t)bf16_rne(o[3]) << 16)};
         return;
     }
 #pragma unroll
-    for (int u = 0; u < 4; u++) put_out(a, col_out(a, col0 + u), mm, v[u], g);
-}
-
-// Sum the K pieces' partials of each output in piece order, add the bias,
-// convert and store.  A thread owns two quads (4 consecutive columns of one
-// row each) 256 quads apart, so eight 16-byte loads are in flight per thread.
-// Runs after k_gemm on the same stream, so every partial is complete and visible.
-__global__ __launch_bounds__(256) void k_splitk_reduce(KArgs a, const float* __restrict__ partial, int global_scale) {
-    const float g = global_scale ? *reinterpret_cast<const float*>(a.gs) : 1.0f;
-    const int64_t total = (int64_t)a.m * (a.n / 4);
-    const int64_t qa = (int64_t)blockIdx.x * 512 + threadIdx.x, qb = qa + 256;
-    if (qa >= total) return;
-    const bool hb = qb < total;
-    const int64_t pstride = (int64_t)a.m * a.n;
-    // the partials are [ksplit][m][n] row-major with n % 4 == 0: quad q starts at element 4q
-    const float* pa = partial + qa * 4;
-    const float* pb = partial + (hb ? qb : qa) * 4;
-    // pieces are summed in order 0, 1, ...; their loads are issued four at a time (indices
-    // past the last piece re-read it and are dropped)
-    f32x4 va = {0.f, 0.f, 0.f, 0.f}, vb = {0.f, 0.f, 0.f, 0.f};
-    for (int s0 = 0; s0 < a.ksplit; s0 += 4) {
-        f32x4 ta[4], tb[4];
-#pragma unroll
-        for (int u = 0; u < 4; u++) {
-            const int64_t off = std::min(s0 + u, a.ksplit - 1) * pstride;
-            ta[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(pa + off));
-            tb[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(pb + off));
-        }
-#pragma unroll
-        for (int u = 0; u < 4; u++)
-            if (s0 + u < a.ksplit) {
-                va += ta[u];
-                vb += tb[u];
-            }
+    for (int u = 0; u < 4; u++) {
+        ColOut c = col_out_nobias<true>(a, q.col0 + u);
+        c.bias = bv[u];
+        put_out(a, c, q.row, v[u], g);
     }
-    reduce_store(a, qa, va, g);
-    if (hb) reduce_store(a, qb, vb, g);
 }
 
-// The same for exactly KS pieces (2 or 4): each thread owns 2 quads, spaced 256 apart,
-// and issues all 2 KS of its partial loads before adding any (pieces in order).  (Four
-// quads per thread at KS = 2 measured 0.7-1 us slower on the M = 1500 fc2 shape.)
+// KS pieces (2 or 4), or a.ksplit of them (KS = 0), summed in order 0, 1, ...
 template <int KS>
-__global__ __launch_bounds__(256) void k_splitk_reduce_n(KArgs a, const float* __restrict__ partial, int global_scale) {
-    constexpr int Q = 2;
-    const float g = global_scale ? *reinterpret_cast<const float*>(a.gs) : 1.0f;
-    const int64_t total = (int64_t)a.m * (a.n / 4);
+__global__ __launch_bounds__(256) void k_splitk_reduce_n(KArgs a) {
+    constexpr int Q = kRedQ;
+    const int64_t nq = a.n / 4;
+    const int64_t total = (int64_t)a.m * nq;
     const int64_t q0 = (int64_t)blockIdx.x * (256 * Q) + threadIdx.x;
     if (q0 >= total) return;
+    const bool small = total <= 0x7FFFFFFF;
     const int64_t pstride = (int64_t)a.m * a.n;
-    f32x4 t[KS][Q];
+    const float* const partial = a.rpartial;
+    RedQuad qd[Q];
 #pragma unroll
-    for (int i = 0; i < Q; i++) {
-        // quads past the end re-read the first one and are dropped
-        const int64_t q = q0 + 256 * i < total ? q0 + 256 * i : q0;
+    for (int i = 0; i < Q; i++) qd[i] = red_quad(q0 + 256 * i, total, nq, small);   // quads past the end re-read quad 0
+    f32x4 v[Q];
+    if constexpr (KS > 0) {
+        f32x4 t[KS][Q];
 #pragma unroll
-        for (int s = 0; s < KS; s++)
-            t[s][i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(partial + s * pstride + q * 4));
+        for (int i = 0; i < Q; i++) {
+#pragma unroll
+            for (int s = 0; s < KS; s++)
+                t[s][i] = __builtin_nontemporal_load(
+                    reinterpret_cast<const f32x4*>(partial + s * pstride + (qd[i].row * a.n + qd[i].col0)));
+        }
+#pragma unroll
+        for (int i = 0; i < Q; i++) {
+            v[i] = t[0][i];
+#pragma unroll
+            for (int s = 1; s < KS; s++) v[i] += t[s][i];
+        }
+    } else {
+        // loads issued four pieces at a time (indices past the last piece re-read it and are dropped)
+#pragma unroll
+        for (int i = 0; i < Q; i++) v[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s0 = 0; s0 < a.ksplit; s0 += 4) {
+            f32x4 t[4][Q];
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const int64_t off = std::min(s0 + u, a.ksplit - 1) * pstride;
+#pragma unroll
+                for (int i = 0; i < Q; i++)
+                    t[u][i] = __builtin_nontemporal_load(
+                        reinterpret_cast<const f32x4*>(partial + off + (qd[i].row * a.n + qd[i].col0)));
+            }
+#pragma unroll
+            for (int u = 0; u < 4; u++)
+                if (s0 + u < a.ksplit) {
+#pragma unroll
+                    for (int i = 0; i < Q; i++) v[i] += t[u][i];
+                }
+        }
+    }
+    const float g = a.rfactor ? load_f32_vmem(reinterpret_cast<const uint8_t*>(a.rfactor)) : 1.0f;
+    RedBias b[Q];
+    if (a.bias) {
+        const bool al8 = (reinterpret_cast<uintptr_t>(a.bias) & 7) == 0;
+#pragma unroll
+        for (int i = 0; i < Q; i++) b[i] = red_bias_load(a.bias, qd[i].col0, al8);
+    } else {
+#pragma unroll
+        for (int i = 0; i < Q; i++) b[i] = RedBias{0u, 0u};
     }
 #pragma unroll
-    for (int i = 0; i < Q; i++) {
-        if (q0 + 256 * i >= total) break;
-        f32x4 v = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < KS; s++) v += t[s][i];
-        reduce_store(a, q0 + 256 * i, v, g);
-    }
+    for (int i = 0; i < Q; i++)
+        if (qd[i].live) red_store(a, qd[i], v[i], g, b[i]);
 }
 
 // ---------------------------------------------------------------------------
@@ -741,13 +796,13 @@ hipError_t launch_gemm(const MatmulProblem& p, hipStream_t st) {
     }
     if (s.ksplit > 1) {
         const int64_t nquads = p.m * (p.n / 4);
-        const int gs = (int)(p.fmt == kNVFP4);
-        if (s.ksplit == 2)
-            hipLaunchKernelGGL(k_splitk_reduce_n<2>, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a, partial, gs);
-        else if (s.ksplit == 4)
-            hipLaunchKernelGGL(k_splitk_reduce_n<4>, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a, partial, gs);
-        else
-            hipLaunchKernelGGL(k_splitk_reduce, dim3((unsigned)((nquads + 511) / 512)), dim3(256), 0, st, a, partial, gs);
+        KArgs ar = a;
+        ar.rpartial = partial;
+        ar.rfactor = p.fmt == kNVFP4 ? reinterpret_cast<const float*>(a.gs) : nullptr;
+        const dim3 rgrid((unsigned)((nquads + 256 * kRedQ - 1) / (256 * kRedQ)));
+        if (s.ksplit == 2) hipLaunchKernelGGL(k_splitk_reduce_n<2>, rgrid, dim3(256), 0, st, ar);
+        else if (s.ksplit == 4) hipLaunchKernelGGL(k_splitk_reduce_n<4>, rgrid, dim3(256), 0, st, ar);
+        else hipLaunchKernelGGL(k_splitk_reduce_n<0>, rgrid, dim3(256), 0, st, ar);
     }
     return hipGetLastError();
 }

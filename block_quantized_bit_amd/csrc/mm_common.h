@@ -54,8 +54,14 @@ constexpr int kLutWords = 256 * 64;   // 256 byte values x 64 lane slots
 // from it rather than read the hidden arguments that follow it.
 struct KArgs {
     const uint16_t* x;       // 0x00
-    const uint8_t* codes;    // 0x08
-    const uint8_t* scales;   // 0x10
+    union {                  // 0x08
+        const uint8_t* codes;
+        const float* rpartial;   // split-K reduce launch: the pieces' fp32 partials [ksplit][m][n]
+    };
+    union {                  // 0x10
+        const uint8_t* scales;
+        const float* rfactor;    // split-K reduce launch: address of the epilogue factor, or null (1)
+    };
     union {                  // 0x18 one per format:
         const uint8_t* gs;   //   NVFP4: address of the fp32 factor applied in the epilogue (the global scale)
         int64_t d_off;       //   NF4+DQ: fp32 group scales    } offsets into scales,
