@@ -228,6 +228,22 @@ __device__ __forceinline__ void gemm_load_x_lds(uint8_t* xs_buf, const GemmSrc& 
                                                  16, xoff[i], uni(st * (BK * 2)), 0, 0);
 }
 
+// Bias of the lane's column in each of its NB bands (0 without a bias).  The loads are
+// issued together and waited for once; bands past the matrix re-read band 0's value,
+// which is never stored.
+template <int NB>
+__device__ __forceinline__ void gemm_bias(const KArgs& a, int64_t band0, int64_t nbands, int r, float (&bias)[NB]) {
+    uint16_t raw[NB];
+#pragma unroll
+    for (int nf = 0; nf < NB; nf++) raw[nf] = 0;
+    if (a.bias) {
+#pragma unroll
+        for (int nf = 0; nf < NB; nf++) raw[nf] = a.bias[(band0 + nf < nbands ? band0 + nf : 0) * 16 + r];
+    }
+#pragma unroll
+    for (int nf = 0; nf < NB; nf++) bias[nf] = bf16_value(raw[nf]);
+}
+
 template <int FMT, bool DQ, int NB>
 __device__ constexpr int gemm_step_loads() { return kXLoads + NB * gemm_w_loads<FMT, DQ>(); }
 
@@ -456,6 +472,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
     wait_vm<0>();   // the last requests (re-reads of the last step) land before the workgroup ends
 
     // ---- epilogue ----
+    // the bias of each of this lane's NB columns, all requested before the first wait
+    float bias[NB];
+    if (a.ksplit == 1) gemm_bias<NB>(a, band0, nbands, r, bias);
     if (a.ksplit == 1 && a.out_v16) {
         // The tile's bf16 results go through LDS (the X buffers are free once every
         // wave's loads have landed), so that each output row is written in whole
@@ -469,12 +488,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
 #pragma unroll
         for (int nf = 0; nf < NB; nf++) {
             if (band0 + nf >= nbands) continue;     // same for the whole wave
-            const float bias = a.bias ? bf16_value(a.bias[(band0 + nf) * 16 + r]) : 0.0f;
 #pragma unroll
             for (int mf = 0; mf < 8; mf++) {
                 float v[4];
 #pragma unroll
-                for (int i = 0; i < 4; i++) v[i] = acc[mf][nf][i] * g + bias;
+                for (int i = 0; i < 4; i++) v[i] = acc[mf][nf][i] * g + bias[nf];
                 quad_transpose(v, t);   // now row 16 mf + 4h + t, columns 16 nf + 4q .. 4q + 3
                 const int row = 16 * mf + 4 * h + t;
                 const int ch = (2 * nf + (q >> 1)) ^ (row & (CH - 1));
@@ -487,7 +505,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
         const int c = lane & (CH - 1);
         const int64_t col = band0 * 16 + 8 * c;
         if (col < N) {
-            const ColOut o = col_out_nobias(a, col);
+            const ColOut o = col_out_nobias<true>(a, col);
 #pragma unroll
             for (int it = 0; it < 2 * CH; it++) {
                 const int row = (64 / CH) * it + lane / CH;
@@ -503,7 +521,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm(KArgs a) {
 #pragma unroll
         for (int nf = 0; nf < NB; nf++) {
             if (band0 + nf >= nbands) continue;     // same for the whole wave
-            const ColOut c = col_out(a, (band0 + nf) * 16 + r);
+            ColOut c = col_out_nobias<true>(a, (band0 + nf) * 16 + r);
+            c.bias = bias[nf];
             if (full) {
                 // lane (h, r) owns rows 16 mf + 4h + i of its column: step through them by the row stride
                 char* p = c.p + (m0 + 4 * h) * c.ld;
