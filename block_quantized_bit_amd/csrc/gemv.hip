@@ -154,28 +154,32 @@ __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const ui
             s0 = __uint_as_float(t.sc[0]);
             s1 = __uint_as_float(t.sc[1]);
         }
+        // the tile's 16 table reads first, then its MFMAs: one LDS round trip per tile
+        u32x4 B[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) B[j][q] = lut_pair(lut, lane4, uw[j], q);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int kb = 0; kb < 2; kb++) {
             f32x4 p = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int jj = 0; jj < 2; jj++) {
-                const int j = kb * 2 + jj;
-                u32x4 B;
-#pragma unroll
-                for (int q = 0; q < 4; q++) B[q] = lut_pair(lut, lane4, uw[j], q);
-                p = mfma(t.A[j], B, p);
-            }
+            for (int jj = 0; jj < 2; jj++) p = mfma(t.A[kb * 2 + jj], B[kb * 2 + jj], p);
             const float s = kb ? s1 : s0;
 #pragma unroll
             for (int i = 0; i < NI; i++) acc[i] += p[i] * s;
         }
     } else if constexpr (FMT == kQ4_0) {
+        u32x4 B[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int q = 0; q < 4; q++) B[j][q] = lut_pair(lut, lane4, uw[j], q);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < 4; j++) {
-            u32x4 B;
-#pragma unroll
-            for (int q = 0; q < 4; q++) B[q] = lut_pair(lut, lane4, uw[j], q);
-            const f32x4 p = mfma(t.A[j], B, f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 p = mfma(t.A[j], B[j], f32x4{0.f, 0.f, 0.f, 0.f});
             const float s = f16_value((uint16_t)(t.sc[j >> 1] >> (16 * (j & 1))));
 #pragma unroll
             for (int i = 0; i < NI; i++) acc[i] += p[i] * s;
