@@ -124,6 +124,8 @@ __device__ inline uint32_t code_bf16(uint32_t c) {
         return nf4_level_bf16_sel(c);
     } else if constexpr (FMT == kQ4_0) {
         return __float_as_uint((float)((int)(c & 15u) - 8)) >> 16;          // exact
+    } else if constexpr (FMT == kQ4_1 || FMT == kQ4_K) {
+        return __float_as_uint((float)(c & 15u)) >> 16;                       // the raw code, exact
     } else {  // NVFP4
         float v = e2m1_mag_value(c & 7u);
         if (c & 8u) v = -v;
