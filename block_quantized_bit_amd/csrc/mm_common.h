@@ -323,9 +323,8 @@ struct ColOut {
 // lane; selecting between plain reads of them lets the compiler fold the per-lane
 // choice of split into one per-lane load from the argument block, a vector memory
 // request whose wait (in-order counting) also waits for every weight request the wave
-// has in flight: the GEMV band loops read them this way.  The GEMM reads them plainly:
-// it stores once, after its last request, and uniform copies held in scalar registers
-// cost its main loop spills.
+// has in flight: the GEMV band loops, the GEMM epilogue and the split-K reduce read them
+// this way (in the GEMM only after its main loop, so the copies do not live through it).
 template <bool UNI>
 __device__ inline uint64_t out_u64(uint64_t v) {
     if constexpr (!UNI) return v;
