@@ -136,14 +136,10 @@ __device__ __forceinline__ void gemv_stage_x(uint16_t* xs, const KArgs& a, int w
     }
 }
 
-// NF4 and Q4_0 codes (their values) become bf16 pairs through the LDS table; so do
-// Q4_1 and Q4_K codes (the raw 0..15) for one token (NI = 1).  With more tokens those two
-// convert in registers like the other formats: the 64 KiB table would cost the launches
-// that stage X in LDS their second workgroup per CU (measured slower at 16 tokens).
-template <int FMT, int NI>
-__host__ __device__ constexpr bool gemv_uses_lut() {
-    return FMT == kNF4 || FMT == kQ4_0 || ((FMT == kQ4_1 || FMT == kQ4_K) && NI == 1);
-}
+// NF4 and Q4_0 codes become bf16 pairs through the LDS table; NVFP4 and Q8_0
+// convert in registers.
+template <int FMT>
+__host__ __device__ constexpr bool gemv_uses_lut() { return FMT == kNF4 || FMT == kQ4_0; }
 
 template <int FMT, bool DQ, int NI>
 __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const uint32_t* lut, uint32_t lane4,
@@ -188,45 +184,10 @@ __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const ui
 #pragma unroll
             for (int i = 0; i < NI; i++) acc[i] += p[i] * s;
         }
-    } else if constexpr ((FMT == kQ4_1 || FMT == kQ4_K) && NI == 1) {
-        // Per 32-value block (K slice j): w^ = c S + T (q4_1: S = d, T = m; q4_k: S = d sc,
-        // T = -dmin m).  The MFMA sums x c on the raw codes (exact in bf16), a second one on
-        // ones sums x, and y += S sum(x c) + T sum(x), in fp32.
-        u32x4 B[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++)
-#pragma unroll
-            for (int q = 0; q < 4; q++) B[j][q] = lut_pair(lut, lane4, uw[j], q);
-        __builtin_amdgcn_sched_barrier(0);
-        const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const f32x4 p = mfma(t.A[j], B[j], f32x4{0.f, 0.f, 0.f, 0.f});
-            const f32x4 xs = mfma(t.A[j], ones, f32x4{0.f, 0.f, 0.f, 0.f});
-            float S, T;
-            if constexpr (FMT == kQ4_1) {
-                S = f16_value((uint16_t)(t.sc[j] & 0xFFFFu));
-                T = f16_value((uint16_t)(t.sc[j] >> 16));
-            } else {
-                float O;
-                q4_k_sub(t.sc[0], t.sc[1], t.sc[2], j, S, O);
-                T = -O;
-            }
-#pragma unroll
-            for (int i = 0; i < NI; i++) acc[i] += p[i] * S + xs[i] * T;
-        }
     } else if constexpr (FMT == kQ4_1) {
         // B = bf16(w^), block j of the row for K slice j
 #pragma unroll
         for (int j = 0; j < 4; j++) acc = mfma(t.A[j], q4_1_operand(uw[j], t.sc[j]), acc);
-    } else if constexpr (FMT == kQ4_K) {
-        // B = bf16(w^), sub-block j of the row for K slice j
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            float S, O;
-            q4_k_sub(t.sc[0], t.sc[1], t.sc[2], j, S, O);
-            acc = mfma(t.A[j], q4_k_operand(uw[j], S, O), acc);
-        }
     } else if constexpr (FMT == kQ6_K) {
         // B = bf16(w^); K slice j spans sub-blocks 2j (h = 0, 1) and 2j + 1 (h = 2, 3)
 #pragma unroll
@@ -234,6 +195,14 @@ __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const ui
             const float S = q6_k_scale(t.sc[0], t.sc[1], t.sc[4], 2 * j + (h >> 1));
             const uint32_t hw = t.sc[2 + (j >> 1)] >> (16 * (j & 1));
             acc = mfma(t.A[j], q6_k_operand(uw[j], hw & 255u, (hw >> 8) & 255u, S), acc);
+        }
+    } else if constexpr (FMT == kQ4_K) {
+        // B = bf16(w^), sub-block j of the row for K slice j
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            float S, O;
+            q4_k_sub(t.sc[0], t.sc[1], t.sc[2], j, S, O);
+            acc = mfma(t.A[j], q4_k_operand(uw[j], S, O), acc);
         }
     } else if constexpr (FMT == kQ5_0) {
         // B = bf16(w^), block j of the row for K slice j; this lane's k are bits 8h .. 8h+7
@@ -379,7 +348,7 @@ __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kG
 //   issued after it) never waits for a weight load.
 template <int FMT, bool DQ, int NI, int C, bool PIPE, bool XL>
 __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArgs a) {
-    __shared__ uint32_t lut[gemv_uses_lut<FMT, NI>() ? kLutWords : 1];
+    __shared__ uint32_t lut[gemv_uses_lut<FMT>() ? kLutWords : 1];
     __shared__ f32x4 red[kGemvWaves][64];
     extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
 
@@ -413,7 +382,7 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
         // is in flight would have to wait for every load.  Otherwise it is filled while the first
         // tiles are in flight.
         if constexpr (XL) {
-            if constexpr (gemv_uses_lut<FMT, NI>()) build_lut<FMT, 64 * kGemvWaves>(lut);
+            if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
             gemv_stage_x(xs_dyn, a, wave, lane);
         }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -425,7 +394,7 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
                 if constexpr (XL) {
                     lds_barrier_vm<gemv_band_loads<FMT, DQ, C>() + kMuLoads>();
                 } else {
-                    if constexpr (gemv_uses_lut<FMT, NI>()) build_lut<FMT, 64 * kGemvWaves>(lut);
+                    if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
                     __syncthreads();
                 }
             }
@@ -438,14 +407,14 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
         DqRow dq0, dq1;
         int64_t band = blockIdx.x;
         if constexpr (XL) {
-            if constexpr (gemv_uses_lut<FMT, NI>()) build_lut<FMT, 64 * kGemvWaves>(lut);
+            if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
             gemv_stage_x(xs_dyn, a, wave, lane);
         }
         gemv_load_band<FMT, DQ, C, XL>(R0, dq0, a, band, 0, wave, lane, r, xrow, KT, mu_first);
         if constexpr (XL) {
             lds_barrier_vm<gemv_band_loads<FMT, DQ, C>() + kMuLoads>();
         } else {
-            if constexpr (gemv_uses_lut<FMT, NI>()) build_lut<FMT, 64 * kGemvWaves>(lut);
+            if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 64 * kGemvWaves>(lut);
             __syncthreads();
         }
         for (; band < nbands; band += 2 * stride) {
@@ -605,7 +574,7 @@ constexpr bool stream_refill() { return FMT == kNF4 && DQ && NI == 1; }
 // re-reads).
 template <int FMT, bool DQ, int NI, int T>
 __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
-    __shared__ uint32_t lut[gemv_uses_lut<FMT, NI>() ? kLutWords : 1];
+    __shared__ uint32_t lut[gemv_uses_lut<FMT>() ? kLutWords : 1];
     __shared__ __attribute__((aligned(16))) uint16_t xs[kStreamXMax + 128];
 
     const int tid = threadIdx.x;
@@ -636,7 +605,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream(KArgs a) {
         *reinterpret_cast<uint4*>(xs + i) = *reinterpret_cast<const uint4*>(a.x + row * a.ldx + col);
     }
     if constexpr (RF) stream_load_band<FMT, DQ, T>(R1, B1, a, std::min<int64_t>(band + stride, last), lane, r, KT);
-    if constexpr (gemv_uses_lut<FMT, NI>()) build_lut<FMT, 256>(lut);
+    if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 256>(lut);
     __syncthreads();
     const uint16_t* xrow = xs + (r < a.m ? r : 0) * a.k + h * 8;
     const uint16_t* xzero = xs + kStreamXMax + h * 8;
@@ -749,7 +718,7 @@ __device__ __forceinline__ void stream_consume_chunk(const StreamChunkTile (&R)[
 template <int FMT, bool DQ, int NI, int T>
 __global__ __launch_bounds__(256, 2) void k_gemv_stream_chunked(KArgs a) {
     static_assert(!(FMT == kNF4 && DQ), "double quant streams through k_gemv_stream");
-    __shared__ uint32_t lut[gemv_uses_lut<FMT, NI>() ? kLutWords : 1];
+    __shared__ uint32_t lut[gemv_uses_lut<FMT>() ? kLutWords : 1];
     __shared__ __attribute__((aligned(16))) uint16_t xs[kStreamXMax + 128];
 
     const int tid = threadIdx.x;
@@ -783,7 +752,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream_chunked(KArgs a) {
         const int64_t row = i / a.k, col = i - row * a.k;
         *reinterpret_cast<uint4*>(xs + i) = *reinterpret_cast<const uint4*>(a.x + row * a.ldx + col);
     }
-    if constexpr (gemv_uses_lut<FMT, NI>()) build_lut<FMT, 256>(lut);
+    if constexpr (gemv_uses_lut<FMT>()) build_lut<FMT, 256>(lut);
     __syncthreads();
     const uint16_t* xrow = xs + (r < a.m ? r : 0) * a.k + h * 8;
     const uint16_t* xzero = xs + kStreamXMax + h * 8;
@@ -819,7 +788,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream_chunked(KArgs a) {
 // would spill at 10.
 template <int FMT, int NI>
 constexpr int stream_chunk_tiles() {
-    return (FMT == kQ5_0 || FMT == kQ4_K || FMT == kQ6_K || (FMT == kQ4_1 && NI == 1) || (FMT == kQ4_0 && NI == 4)) ? 5 : 10;
+    return (FMT == kQ5_0 || FMT == kQ4_K || FMT == kQ6_K || (FMT == kQ4_0 && NI == 4)) ? 5 : 10;
 }
 
 constexpr int64_t kStreamMinBands = 4 * 2 * 4 * kNumCU;   // bands per wave x waves
@@ -842,19 +811,19 @@ constexpr int64_t kGemvXlMax = 32768;   // bf16 elements of X (m * k) copied to 
 // Two workgroups per CU for the small-C kernels (<= 128 VGPRs) when their LDS fits twice:
 // with a code table, an X copy of at most 8 KiB; without one, the reduction buffer and the
 // X copy twice in the CU's 160 KiB.
-template <int FMT, int NI, int C>
+template <int FMT, int C>
 static bool gemv_two_per_cu(size_t xbytes) {
     constexpr size_t kLdsPerCu = 160 * 1024;
     const size_t red = sizeof(f32x4) * kGemvWaves * 64;
     if (C > 2) return false;
-    return gemv_uses_lut<FMT, NI>() ? xbytes <= 8192 : 2 * (red + 16 + xbytes) <= kLdsPerCu;
+    return gemv_uses_lut<FMT>() ? xbytes <= 8192 : 2 * (red + 16 + xbytes) <= kLdsPerCu;
 }
 
 template <int FMT, bool DQ, int NI, int C, bool XL>
 static void gemv_launch_cx(const KArgs& a, int64_t nbands, int64_t KT, hipStream_t st) {
     const dim3 block(64 * kGemvWaves);
     const size_t xbytes = XL ? (size_t)a.m * (size_t)a.k * 2 : 0;
-    const int64_t per_cu = gemv_two_per_cu<FMT, NI, C>(xbytes) ? 2 : 1;
+    const int64_t per_cu = gemv_two_per_cu<FMT, C>(xbytes) ? 2 : 1;
     // band pipelining only where its two register sets fit without spilling (C <= 2), and only
     // when the bands outnumber the workgroups that fit at once
     if constexpr (C <= 2) {
@@ -880,8 +849,8 @@ static void gemv_launch_c(const KArgs& a, int64_t nbands, int64_t KT, hipStream_
     // pipelined per workgroup beats reading 12-16 rows of X from L2 per tile (measured at the
     // fc1 shape, 320 bands: 8 tokens 5.3 vs 5.4 us, 12 tokens 6.1 vs 5.7, 16 tokens 6.7 vs 6.1).
     const bool xl = mk <= kGemvXlMax && nbands <= 2 * kNumCU &&
-                    (mk * 2 <= 8192 || nbands <= kNumCU || (!gemv_uses_lut<FMT, NI>() && gemv_two_per_cu<FMT, NI, C>((size_t)mk * 2)) ||
-                     (gemv_uses_lut<FMT, NI>() && C <= 2 && a.m >= 12));
+                    (mk * 2 <= 8192 || nbands <= kNumCU || (!gemv_uses_lut<FMT>() && gemv_two_per_cu<FMT, C>((size_t)mk * 2)) ||
+                     (gemv_uses_lut<FMT>() && C <= 2 && a.m >= 12));
     if (xl) gemv_launch_cx<FMT, DQ, NI, C, true>(a, nbands, KT, st);
     else gemv_launch_cx<FMT, DQ, NI, C, false>(a, nbands, KT, st);
 }

@@ -9,9 +9,8 @@
 // so a wave turns one 1 KiB tile load (64 lanes x 16 B, fully coalesced) into
 // four MFMA B operands without any data exchange.
 //
-// NF4 codes (and q4_0 codes in the GEMV, and the raw q4_1 / q4_k codes in the one-token
-// GEMV) are decoded through byte-indexed tables in LDS (one entry per code byte, i.e.
-// two values per lookup), replicated per
+// NF4 codes (and q4_0 codes in the GEMV) are decoded through byte-indexed tables
+// in LDS (one entry per code byte, i.e. two values per lookup), replicated per
 // lane so that concurrent lookups of different bytes hit different banks; the LDS
 // address is built with one v_perm_b32.  The GEMV table holds bf16 values (fed
 // straight to the MFMA), the GEMM table fp32 values (scaled exactly, then rounded
@@ -22,9 +21,10 @@
 // GEMV (m <= 16, decode): B = raw code values (NF4 level, q4_0 q-8, q8_0 q),
 //   the per-block scale is applied to the MFMA partial sum of each block; for
 //   NVFP4 (16-value blocks, two per 32-K slice) B = e2m1*scale (exact in bf16);
-//   for q4_1 and q4_k with one token B = the raw codes, and per block y += S sum(x c)
-//   + T sum(x) (w^ = c S + T; sum(x) from an MFMA on ones); for q5_0 (fifth bits),
-//   q6_k (two-level scales) and q4_1 / q4_k with more tokens B = bf16(w^) as in the GEMM.
+//   for q4_1 (scale and minimum), q5_0 (fifth bits), q4_k and q6_k (two-level
+//   scales) B = bf16(w^) as in the GEMM: with an offset, a sum of x c scaled after the
+//   MFMA minus an offset times the sum of x would cancel, and its rounding error would
+//   no longer be bounded by the sum of |x w^|.
 //   K is split over the waves of a workgroup and reduced in LDS.
 // GEMM (m >= 17, encoder): each wave dequantizes 64 columns x 128 K of W per
 //   step to bf16(w^) -- w^ computed exactly as the format defines it, then one
@@ -126,8 +126,6 @@ __device__ inline uint32_t code_bf16(uint32_t c) {
         return nf4_level_bf16_sel(c);
     } else if constexpr (FMT == kQ4_0) {
         return __float_as_uint((float)((int)(c & 15u) - 8)) >> 16;          // exact
-    } else if constexpr (FMT == kQ4_1 || FMT == kQ4_K) {
-        return __float_as_uint((float)(c & 15u)) >> 16;                       // the raw code, exact
     } else {  // NVFP4
         float v = e2m1_mag_value(c & 7u);
         if (c & 8u) v = -v;

@@ -246,7 +246,7 @@ STREAM_N = 131072
     (NF4, False, 384, 16, True, wq.WQ_BF16),     # all 16 rows, K = 3 tiles
     # the chunked streaming kernel: chunks of 5 tiles for the wide-record formats, of 10 for K
     # beyond 10 tiles; ragged last chunks, super-blocks split across chunks, four-row calls
-    (Q4_1, False, 1280, 1, True, wq.WQ_BF16),    # 2 chunks of 5 (one token: raw codes from the table)
+    (Q4_1, False, 1280, 1, True, wq.WQ_BF16),    # 1 chunk of 10
     (Q5_0, False, 640, 3, True, wq.WQ_F32),      # 1 chunk
     (Q4_K, False, 768, 2, True, wq.WQ_BF16),     # 5 + 1 tiles (three super-blocks per row)
     (Q6_K, False, 512, 4, False, wq.WQ_F32),     # 1 chunk of 4
@@ -257,7 +257,7 @@ STREAM_N = 131072
     (NF4, False, 1536, 1, True, wq.WQ_F32),      # 10 + 2 tiles, code table
     (NVFP4, False, 2048, 3, True, wq.WQ_BF16),   # 10 + 6 tiles, four-row accumulators
     (Q4_0, False, 1536, 4, True, wq.WQ_F32),     # four-row q4_0: chunks of 5 (5 + 5 + 2 tiles)
-    (Q4_1, False, 1280, 3, True, wq.WQ_F32),     # q4_1 beyond one token: bf16(w^) operands, 1 chunk of 10
+    (Q4_1, False, 1280, 3, True, wq.WQ_F32),     # four-row accumulators, 1 chunk of 10
 ], ids=["nf4dq-k1280-m1", "nvfp4-k384-m3", "q8_0-k256-m2", "q4_0-k640-m5", "nf4-k512-m15", "nf4-k384-m16",
         "q4_1-k1280-m1", "q5_0-k640-m3", "q4_k-k768-m2", "q6_k-k512-m4", "q6_k-k1280-m1", "q5_0-k1280-m6",
         "q4_k-k1536-m1", "q8_0-k1280-m1", "nf4-k1536-m1", "nvfp4-k2048-m3", "q4_0-k1536-m4", "q4_1-k1280-m3"])
