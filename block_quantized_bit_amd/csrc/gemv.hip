@@ -212,6 +212,47 @@ __device__ inline void gemv_consume(const GemvTile<FMT>& t, f32x4& acc, const ui
             const uint16_t db = (uint16_t)(t.sc[j >> 1] >> (16 * (j & 1)));
             acc = mfma(t.A[j], q5_0_operand(uw[j], (t.sc[2 + j] >> (8 * h)) & 255u, db), acc);
         }
+    } else if constexpr (FMT == kNVFP4 && NI == 1) {
+        // One token leaves 15 of the 16 A rows free, so the E4M3 block scales are applied after
+        // the MFMA, to per-block partial sums.  In K slice j the 16-value block 2j + (h >> 1)
+        // (lanes h = 0, 1: the slice's first 16 k; h = 2, 3: its last 16) puts its x in A row
+        // (2j + (h >> 1)) & 3 and zeros in every other row.  Chained over slices 0-1 (and 2-3),
+        // output row i of column n is then the sum of x * e2m1 over block i (4 + i) of the tile
+        // row alone: exact products, no offset term.  B holds the bare E2M1 values (exact in
+        // bf16: one conversion per code pair).  Lane (0, n) holds rows 0-3 of column n and the
+        // row's 8 scale bytes (block b: byte b & 3 of word b >> 2); lanes h >= 1 hold zero rows.
+        const int r = __lane_id() & 15;
+        f32x4 P[2];
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            f32x4 p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jj = 0; jj < 2; jj++) {
+                const int j = 2 * c + jj;
+                u32x4 B;
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    bf16x2 v;
+                    if (q == 0) v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(uw[j], 1.0f, 0);
+                    else if (q == 1) v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(uw[j], 1.0f, 1);
+                    else if (q == 2) v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(uw[j], 1.0f, 2);
+                    else v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(uw[j], 1.0f, 3);
+                    B[q] = __builtin_bit_cast(uint32_t, v);
+                }
+                const bool live = r == 2 * jj + (h >> 1);
+                const u32x4 A = live ? t.A[j] : u32x4{0u, 0u, 0u, 0u};
+                p = mfma(A, B, p);
+            }
+            P[c] = p;
+        }
+#pragma unroll
+        for (int c = 0; c < 2; c++) {
+            const int sw = (int)t.sc[c];
+            acc[0] += P[c][0] * __builtin_amdgcn_cvt_f32_fp8(sw, 0);
+            acc[0] += P[c][1] * __builtin_amdgcn_cvt_f32_fp8(sw, 1);
+            acc[0] += P[c][2] * __builtin_amdgcn_cvt_f32_fp8(sw, 2);
+            acc[0] += P[c][3] * __builtin_amdgcn_cvt_f32_fp8(sw, 3);
+        }
     } else if constexpr (FMT == kNVFP4) {
         // block 2j + (h >> 1) of the row: byte 2 (j & 1) + (h >> 1) of scale word j >> 1
         const uint32_t hs = 8u * (uint32_t)(h >> 1);
