@@ -258,9 +258,14 @@ STREAM_N = 131072
     (NVFP4, False, 2048, 3, True, wq.WQ_BF16),   # 10 + 6 tiles, four-row accumulators
     (Q4_0, False, 1536, 4, True, wq.WQ_F32),     # four-row q4_0: chunks of 5 (5 + 5 + 2 tiles)
     (Q4_1, False, 1280, 3, True, wq.WQ_F32),     # four-row accumulators, 1 chunk of 10
+    # one-token NVFP4 (block scales applied after the MFMA) in each streaming kernel
+    (NVFP4, False, 384, 1, False, wq.WQ_F32),    # the 4-tile variant
+    (NVFP4, False, 1280, 1, True, wq.WQ_BF16),   # the 10-tile variant
+    (NVFP4, False, 2048, 1, True, wq.WQ_F32),    # chunked, 10 + 6 tiles
 ], ids=["nf4dq-k1280-m1", "nvfp4-k384-m3", "q8_0-k256-m2", "q4_0-k640-m5", "nf4-k512-m15", "nf4-k384-m16",
         "q4_1-k1280-m1", "q5_0-k640-m3", "q4_k-k768-m2", "q6_k-k512-m4", "q6_k-k1280-m1", "q5_0-k1280-m6",
-        "q4_k-k1536-m1", "q8_0-k1280-m1", "nf4-k1536-m1", "nvfp4-k2048-m3", "q4_0-k1536-m4", "q4_1-k1280-m3"])
+        "q4_k-k1536-m1", "q8_0-k1280-m1", "nf4-k1536-m1", "nvfp4-k2048-m3", "q4_0-k1536-m4", "q4_1-k1280-m3",
+        "nvfp4-k384-m1", "nvfp4-k1280-m1", "nvfp4-k2048-m1"])
 def test_streaming_gemv_many_bands(orc, fmt, dq, k, m, use_bias, ydt):
     d, codes, scales, ref, b = quantized(orc, fmt, dq, 6000 + k, STREAM_N, k, outlier_frac=0.001)
     x = gen_x(np.random.default_rng(6100 + k), m, k)
@@ -269,6 +274,21 @@ def test_streaming_gemv_many_bands(orc, fmt, dq, k, m, use_bias, ydt):
     y = gpu_matmul(d, codes, scales, x, b, ydt=ydt, ldy_pad=16)
     check_bound(y, orc.matmul(x, ref["w_hat"], b), abs_dot(x, ref["w_hat"]), bf16_out=ydt == wq.WQ_BF16,
                 what=f"stream {NAMES[fmt]} k={k} m={m}")
+
+
+@pytest.mark.parametrize("n,k", [(272, 640), (1280, 5120), (256, 16384), (10240, 1280), (9600, 3072)],
+                         ids=["lds-x-1tile", "lds-x-5tiles", "lds-x-2rounds-of-8", "band-pipelined", "x-from-l2-4tiles"])
+def test_one_token_nvfp4_general_kernel(orc, n, k):
+    """One NVFP4 token puts each 16-value block's x in its own A row and applies the E4M3 block
+    scales to the per-block MFMA sums.  Every variant of the general GEMV kernel that one token
+    reaches: X copied to LDS with 1, 5 or 2 x 8 tiles per wave, band-pipelined workgroups (more
+    bands than resident workgroups), and X read from L2 (more than 512 bands, 4 tiles per wave).
+    Weights with log-normal row scales spread the block scales over E4M3's range."""
+    d, codes, scales, ref, b = quantized(orc, NVFP4, False, 6500 + n + k, n, k, row_lognormal_sigma=0.5)
+    x = gen_x(np.random.default_rng(6600 + k), 1, k)
+    say("one-token nvfp4", n, k)
+    y = gpu_matmul(d, codes, scales, x, b, ydt=wq.WQ_F32)
+    check_bound(y, orc.matmul(x, ref["w_hat"], b), abs_dot(x, ref["w_hat"]), what=f"nvfp4 m=1 n={n} k={k}")
 
 
 def test_streaming_gemv_qkv_split(orc):
