@@ -20,7 +20,9 @@
 //
 // GEMV (m <= 16, decode): B = raw code values (NF4 level, q4_0 q-8, q8_0 q),
 //   the per-block scale is applied to the MFMA partial sum of each block; for
-//   NVFP4 (16-value blocks, two per 32-K slice) B = e2m1*scale (exact in bf16);
+//   NVFP4 (16-value blocks, two per 32-K slice) B = e2m1*scale (exact in bf16),
+//   except for one token, where each block's x fills its own A row, B = e2m1, and
+//   the block scales are applied to the per-block sums;
 //   for q4_1 (scale and minimum), q5_0 (fifth bits), q4_k and q6_k (two-level
 //   scales) B = bf16(w^) as in the GEMM: with an offset, a sum of x c scaled after the
 //   MFMA minus an offset times the sum of x would cancel, and its rounding error would
