@@ -357,9 +357,25 @@ __device__ __forceinline__ void gemv_consume_band(GemvTile<FMT> (&R)[C], const D
     }
 }
 
+template <int NI>
 __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kGemvWaves][64], const f32x4& acc,
                                                  int64_t band, int wave, int lane, float g) {
     const int r = lane & 15, h = lane >> 4;
+    if constexpr (NI == 1) {
+        // one token: only accumulator 0 of lanes 0-15 (row 0, column r) is ever stored
+        float* red1 = reinterpret_cast<float*>(&red[0][0]);
+        red1[wave * 64 + lane] = acc[0];
+        __syncthreads();
+        if (wave == 0 && h == 0) {
+            float v = red1[lane];
+#pragma unroll
+            for (int w = 1; w < kGemvWaves; w++) v += red1[w * 64 + lane];
+            const ColOut c = col_out<true>(a, band * 16 + r);
+            put_out(a, c, 0, v, g);
+        }
+        __syncthreads();
+        return;
+    }
     red[wave][lane] = acc;
     __syncthreads();
     if (wave == 0) {
@@ -441,7 +457,7 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
             }
             gemv_consume_band<FMT, DQ, NI, C, XL>(R, dq, acc, c0, wave, KT, lut, lane4, h, mu, xl, xm8);
         }
-        gemv_finish_band(a, red, acc, band, wave, lane, g);
+        gemv_finish_band<NI>(a, red, acc, band, wave, lane, g);
     } else {
         const int64_t stride = (int64_t)a.wg_per_cu * kNumCU;   // the grid (gemv_launch_cx)
         GemvTile<FMT> R0[C], R1[C];
@@ -463,13 +479,13 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
             gemv_load_band<FMT, DQ, C, XL>(R1, dq1, a, std::min<int64_t>(band + stride, nbands - 1), 0, wave, lane,
                                           r, xrow, KT);
             gemv_consume_band<FMT, DQ, NI, C, XL>(R0, dq0, acc, 0, wave, KT, lut, lane4, h, mu, xl, xm8);
-            gemv_finish_band(a, red, acc, band, wave, lane, g);
+            gemv_finish_band<NI>(a, red, acc, band, wave, lane, g);
             if (band + stride >= nbands) break;
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
             gemv_load_band<FMT, DQ, C, XL>(R0, dq0, a, std::min<int64_t>(band + 2 * stride, nbands - 1), 0, wave,
                                           lane, r, xrow, KT);
             gemv_consume_band<FMT, DQ, NI, C, XL>(R1, dq1, acc, 0, wave, KT, lut, lane4, h, mu, xl, xm8);
-            gemv_finish_band(a, red, acc, band + stride, wave, lane, g);
+            gemv_finish_band<NI>(a, red, acc, band + stride, wave, lane, g);
         }
     }
 }
