@@ -362,15 +362,23 @@ __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kG
                                                  int64_t band, int wave, int lane, float g) {
     const int r = lane & 15, h = lane >> 4;
     if constexpr (NI == 1) {
-        // one token: only accumulator 0 of lanes 0-15 (row 0, column r) is ever stored
+        // one token: only accumulator 0 of lanes 0-15 (row 0, column r) is ever stored.  Those
+        // lanes request their column's bias before the barrier, and the barrier lets that one
+        // request stay in flight (every earlier request of the wave has been waited for), so
+        // its latency overlaps the wait for the other waves and the sum.
         float* red1 = reinterpret_cast<float*>(&red[0][0]);
         red1[wave * 64 + lane] = acc[0];
-        __syncthreads();
+        // (unconditional, without a branch around it: without a bias it reads X's first row,
+        // always at least 16 elements, and the value is dropped)
+        const uint16_t* const bsrc = a.bias ? a.bias + band * 16 : a.x;
+        const uint16_t braw = bsrc[r];
+        lds_barrier_vm<1>();
         if (wave == 0 && h == 0) {
             float v = red1[lane];
 #pragma unroll
             for (int w = 1; w < kGemvWaves; w++) v += red1[w * 64 + lane];
-            const ColOut c = col_out<true>(a, band * 16 + r);
+            ColOut c = col_out_nobias<true>(a, band * 16 + r);
+            c.bias = a.bias ? bf16_value(braw) : 0.0f;
             put_out(a, c, 0, v, g);
         }
         __syncthreads();
