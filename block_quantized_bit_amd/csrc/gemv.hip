@@ -384,13 +384,17 @@ __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kG
         __syncthreads();
         return;
     }
+    // the bias is requested before the barrier, as for one token
     red[wave][lane] = acc;
-    __syncthreads();
+    const uint16_t* const bsrc = a.bias ? a.bias + band * 16 : a.x;
+    const uint16_t braw = bsrc[r];
+    lds_barrier_vm<1>();
     if (wave == 0) {
         f32x4 v = red[0][lane];
 #pragma unroll
         for (int w = 1; w < kGemvWaves; w++) v += red[w][lane];
-        const ColOut c = col_out<true>(a, band * 16 + r);
+        ColOut c = col_out_nobias<true>(a, band * 16 + r);
+        c.bias = a.bias ? bf16_value(braw) : 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
             const int mm = 4 * h + i;
