@@ -363,9 +363,9 @@ __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kG
     const int r = lane & 15, h = lane >> 4;
     if constexpr (NI == 1) {
         // one token: only accumulator 0 of lanes 0-15 (row 0, column r) is ever stored.  Those
-        // lanes request their column's bias before the barrier, and the barrier lets that one
-        // request stay in flight (every earlier request of the wave has been waited for), so
-        // its latency overlaps the wait for the other waves and the sum.
+        // lanes request their column's bias before the barrier, and the barrier waits for every
+        // request of the wave but that last one (the counter counts in order), so its latency
+        // overlaps the wait for the other waves and the sum.
         float* red1 = reinterpret_cast<float*>(&red[0][0]);
         red1[wave * 64 + lane] = acc[0];
         // (unconditional, without a branch around it: without a bias it reads X's first row,
