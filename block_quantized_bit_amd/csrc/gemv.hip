@@ -357,7 +357,32 @@ __device__ __forceinline__ void gemv_consume_band(GemvTile<FMT> (&R)[C], const D
     }
 }
 
-template <int NI>
+// Output address of column col (< n <= 2^31 - 1) for the GEMV: as col_out_nobias<true>, with
+// the split choice made in 32-bit arithmetic (columns, split ends and row strides are all
+// 32-bit), which keeps the instructions after the band's last barrier few.
+__device__ __forceinline__ ColOut gemv_col_out(const KArgs& a, int64_t col64) {
+    const int col = (int)col64;
+    const int e0 = __builtin_amdgcn_readfirstlane(a.end0), e1 = __builtin_amdgcn_readfirstlane(a.end1);
+    const bool s1 = col >= e0, s2 = col >= e1;
+    char* const y0 = out_p<true>(a.y0);
+    char* const y1 = out_p<true>(a.y1);
+    char* const y2 = out_p<true>(a.y2);
+    char* const base = s2 ? y2 : (s1 ? y1 : y0);
+    const int ld = s2 ? __builtin_amdgcn_readfirstlane(a.ldy2)
+                      : (s1 ? __builtin_amdgcn_readfirstlane(a.ldy1) : __builtin_amdgcn_readfirstlane(a.ldy0));
+    const int c0 = s2 ? e1 : (s1 ? e0 : 0);
+    const int es = a.f32 ? 4 : 2;
+    ColOut c;
+    c.p = base + (int64_t)(uint32_t)(col - c0) * es;
+    c.ld = (int64_t)ld * es;
+    c.bias = 0.0f;
+    return c;
+}
+
+// NPRE: requests of the next band already in flight (band pipelining).  The barriers only need the
+// LDS writes complete; the compiler waits for the bias and for the prefetched tiles where they are
+// used, so the barriers let those requests (and the last store) stay in flight.
+template <int NI, int NPRE = 0>
 __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kGemvWaves][64], const f32x4& acc,
                                                  int64_t band, int wave, int lane, float g) {
     const int r = lane & 15, h = lane >> 4;
@@ -372,28 +397,28 @@ __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kG
         // always at least 16 elements, and the value is dropped)
         const uint16_t* const bsrc = a.bias ? a.bias + band * 16 : a.x;
         const uint16_t braw = bsrc[r];
-        lds_barrier_vm<1>();
+        lds_barrier_vm<NPRE + 1>();
         if (wave == 0 && h == 0) {
             float v = red1[lane];
 #pragma unroll
             for (int w = 1; w < kGemvWaves; w++) v += red1[w * 64 + lane];
-            ColOut c = col_out_nobias<true>(a, band * 16 + r);
+            ColOut c = gemv_col_out(a, band * 16 + r);
             c.bias = a.bias ? bf16_value(braw) : 0.0f;
             put_out(a, c, 0, v, g);
         }
-        __syncthreads();
+        lds_barrier_vm<NPRE + 1>();
         return;
     }
     // the bias is requested before the barrier, as for one token
     red[wave][lane] = acc;
     const uint16_t* const bsrc = a.bias ? a.bias + band * 16 : a.x;
     const uint16_t braw = bsrc[r];
-    lds_barrier_vm<1>();
+    lds_barrier_vm<NPRE + 1>();
     if (wave == 0) {
         f32x4 v = red[0][lane];
 #pragma unroll
         for (int w = 1; w < kGemvWaves; w++) v += red[w][lane];
-        ColOut c = col_out_nobias<true>(a, band * 16 + r);
+        ColOut c = gemv_col_out(a, band * 16 + r);
         c.bias = a.bias ? bf16_value(braw) : 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -401,7 +426,7 @@ __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kG
             if (mm < a.m) put_out(a, c, mm, v[i], g);
         }
     }
-    __syncthreads();
+    lds_barrier_vm<NPRE + 1>();
 }
 
 // PIPE = false: every workgroup owns one band (grid == number of bands), its
@@ -491,13 +516,13 @@ __global__ __launch_bounds__(64 * kGemvWaves, (C <= 2 ? 2 : 1)) void k_gemv(KArg
             gemv_load_band<FMT, DQ, C, XL>(R1, dq1, a, std::min<int64_t>(band + stride, nbands - 1), 0, wave, lane,
                                           r, xrow, KT);
             gemv_consume_band<FMT, DQ, NI, C, XL>(R0, dq0, acc, 0, wave, KT, lut, lane4, h, mu, xl, xm8);
-            gemv_finish_band<NI>(a, red, acc, band, wave, lane, g);
+            gemv_finish_band<NI, gemv_band_loads<FMT, DQ, C>()>(a, red, acc, band, wave, lane, g);
             if (band + stride >= nbands) break;
             acc = f32x4{0.f, 0.f, 0.f, 0.f};
             gemv_load_band<FMT, DQ, C, XL>(R0, dq0, a, std::min<int64_t>(band + 2 * stride, nbands - 1), 0, wave,
                                           lane, r, xrow, KT);
             gemv_consume_band<FMT, DQ, NI, C, XL>(R1, dq1, acc, 0, wave, KT, lut, lane4, h, mu, xl, xm8);
-            gemv_finish_band<NI>(a, red, acc, band + stride, wave, lane, g);
+            gemv_finish_band<NI, gemv_band_loads<FMT, DQ, C>()>(a, red, acc, band + stride, wave, lane, g);
         }
     }
 }
@@ -620,7 +645,7 @@ __device__ __forceinline__ void stream_band(StreamTile (&R)[T], StreamBand& B, c
         __builtin_amdgcn_sched_barrier(0);   // keep tiles in order: bounded register use
     }
     // lane (h, r) holds rows 4h .. 4h+3 of column band * 16 + r
-    ColOut c = col_out_nobias<true>(a, band * 16 + (__lane_id() & 15));
+    ColOut c = gemv_col_out(a, band * 16 + (__lane_id() & 15));
     c.bias = bf16_value((uint16_t)B.braw);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -830,7 +855,7 @@ __global__ __launch_bounds__(256, 2) void k_gemv_stream_chunked(KArgs a) {
     // the band's outputs, after its last chunk: lane (h, r) holds rows 4h .. 4h+3 of column band * 16 + r
     auto finish = [&](int64_t i, uint32_t braw) {
         if (i % nch != nch - 1) return;
-        ColOut c = col_out_nobias<true>(a, item_band(i) * 16 + r);
+        ColOut c = gemv_col_out(a, item_band(i) * 16 + r);
         c.bias = bf16_value((uint16_t)braw);
 #pragma unroll
         for (int q = 0; q < 4; q++) {
