@@ -391,17 +391,22 @@ __device__ __forceinline__ void gemv_finish_band(const KArgs& a, f32x4 (&red)[kG
         // lanes request their column's bias before the barrier, and the barrier waits for every
         // request of the wave but that last one (the counter counts in order), so its latency
         // overlaps the wait for the other waves and the sum.
+        // lane-major: the 8 waves' values for lane r sit side by side, so the storing lane
+        // reads them with two 16-byte reads
         float* red1 = reinterpret_cast<float*>(&red[0][0]);
-        red1[wave * 64 + lane] = acc[0];
+        if (h == 0) red1[lane * kGemvWaves + wave] = acc[0];
         // (unconditional, without a branch around it: without a bias it reads X's first row,
         // always at least 16 elements, and the value is dropped)
         const uint16_t* const bsrc = a.bias ? a.bias + band * 16 : a.x;
         const uint16_t braw = bsrc[r];
         lds_barrier_vm<NPRE + 1>();
         if (wave == 0 && h == 0) {
-            float v = red1[lane];
-#pragma unroll
-            for (int w = 1; w < kGemvWaves; w++) v += red1[w * 64 + lane];
+            static_assert(kGemvWaves == 8, "two 16-byte reads per lane");
+            const f32x4 p0 = *reinterpret_cast<const f32x4*>(red1 + lane * kGemvWaves);
+            const f32x4 p1 = *reinterpret_cast<const f32x4*>(red1 + lane * kGemvWaves + 4);
+            float v = p0[0];   // in wave order, as before
+            v += p0[1]; v += p0[2]; v += p0[3];
+            v += p1[0]; v += p1[1]; v += p1[2]; v += p1[3];
             ColOut c = gemv_col_out(a, band * 16 + r);
             c.bias = a.bias ? bf16_value(braw) : 0.0f;
             put_out(a, c, 0, v, g);
